@@ -1,0 +1,12 @@
+"""CPU oracle for the Relation operator (fp64, materialised).
+
+TEST INFRASTRUCTURE: imported only by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg. The HIP library and its binding never import it.
+See oracle/relation.py for the definitions and the passages they follow.
+
+Pin status: every function here is pinned by a CPU test against something
+other than itself (brute force, the pages' invariants, closed forms, finite
+differences, the tiled scan); see tests/test_oracle.py.
+"""
+from .relation import *  # noqa: F401,F403
+from .relation import __all__  # noqa: F401

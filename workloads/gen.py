@@ -1,0 +1,154 @@
+"""Seeded input recipes for the Relation operator's workloads.
+
+Recipe (shared by every test and by the benchmark):
+  * numpy.random.default_rng(seed); the draw order is lambda, q, k, v, dY,
+    then (decode only) the cache history, the unused cache slots and the
+    per-step q, k_new, v_new.
+  * lambda ~ U(0, 1): the pages make lambda a learnable layer-wise scalar and
+    state no initial value.
+  * q, k, v, dY ~ N(0, 1) drawn as float32; the RoPE workload scales q and k
+    by 1/sqrt(D) and then applies full-head rotary encoding (base 1e4,
+    positions 0..T-1, rotate-half pairing (m, m + D/2)), as the pages apply
+    RoPE to p1 and p2 before the pairwise evidence.
+  * Tensors of the bf16 workloads are rounded to bf16 (round to nearest even)
+    once; the same rounded values feed the GPU and the oracle (which upcasts
+    them to float64).
+
+Nothing here computes any part of the Relation operator itself.
+"""
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "make_inputs",
+    "make_decode_inputs",
+    "apply_rope",
+    "to_dtype",
+    "default_scale",
+]
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    kind: str            # "fwd", "fwdbwd" or "decode"
+    dtype: str           # "f32" or "bf16"
+    B: int
+    H: int
+    D: int
+    T: int = 0           # sequence length (fwd / fwdbwd)
+    rope: bool = False
+    n_hist: int = 0      # decode: cached history length before the first step
+    steps: int = 0       # decode: consecutive steps
+    capacity: int = 0    # decode: cache slots per (b, h)
+    note: str = field(default="", compare=False)
+
+
+WORKLOADS = {
+    "mhr_fwd_f32": Workload("mhr_fwd_f32", "fwd", "f32", B=1, H=2, D=32, T=128,
+                            note="single Multi-Head Relation forward, fp32"),
+    "layer10m_fwd_bf16": Workload("layer10m_fwd_bf16", "fwd", "bf16", B=8, H=8, D=64, T=1024,
+                                  rope=True, note="10M-model-shaped layer, RoPE'd q/k"),
+    "layer30m_fwdbwd_bf16": Workload("layer30m_fwdbwd_bf16", "fwdbwd", "bf16", B=16, H=8, D=64,
+                                     T=2048, note="30M-model-shaped layer"),
+    "layer100m_fwdbwd_bf16": Workload("layer100m_fwdbwd_bf16", "fwdbwd", "bf16", B=8, H=12,
+                                      D=64, T=4096, note="100M-model-shaped layer"),
+    "cache_decode_bf16": Workload("cache_decode_bf16", "decode", "bf16", B=32, H=12, D=64,
+                                  n_hist=4096, steps=256, capacity=4352,
+                                  note="Relation Cache decode, 256 steps from history 4096"),
+}
+
+
+def default_scale(D):
+    """1/sqrt(d_h): the pages' U = p1.p2 / d_h with the square root that the
+    extracted text drops (the textbook scaled dot product)."""
+    return 1.0 / math.sqrt(D)
+
+
+def to_dtype(x, dtype):
+    """float32 numpy array -> CPU torch tensor of the workload dtype (bf16 by
+    round-to-nearest-even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    if dtype == "f32":
+        return t.clone()
+    raise ValueError(dtype)
+
+
+def apply_rope(x, base=10000.0):
+    """Full-head rotary encoding, rotate-half pairing, positions 0..T-1.
+    x: float32 [..., T, D]. Computed in float64, returned as float32."""
+    T, D = x.shape[-2], x.shape[-1]
+    half = D // 2
+    inv = base ** (-(np.arange(half, dtype=np.float64) * 2.0) / D)
+    ang = np.arange(T, dtype=np.float64)[:, None] * inv[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x = x.astype(np.float64)
+    a, b = x[..., :half], x[..., half:]
+    out = np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+    return out.astype(np.float32)
+
+
+def make_inputs(B, H, T, D, dtype, seed, rope=False, with_dy=False, lam=None):
+    """Seeded forward / backward inputs.
+
+    Returns dict(lam, q, k, v[, dy]) where the tensors are CPU torch tensors
+    of the workload dtype, shape [B, H, T, D]. lambda is drawn from the seed
+    unless given.
+    """
+    rng = np.random.default_rng(seed)
+    lam_draw = float(rng.uniform(0.0, 1.0))
+    shape = (B, H, T, D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if rope:
+        q = apply_rope(q / math.sqrt(D))
+        k = apply_rope(k / math.sqrt(D))
+    out = {
+        "lam": lam_draw if lam is None else float(lam),
+        "q": to_dtype(q, dtype),
+        "k": to_dtype(k, dtype),
+        "v": to_dtype(v, dtype),
+    }
+    if with_dy:
+        out["dy"] = to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
+    return out
+
+
+def make_decode_inputs(B, H, D, n_hist, steps, capacity, dtype, seed, lam=None):
+    """Seeded Relation Cache decode inputs.
+
+    Returns dict(lam, k_cache, v_cache [B,H,capacity,D], q, k_new, v_new
+    [steps,B,H,D]). Slots [0, n_hist) hold the history; the unused slots are
+    filled with other random values so that a test can check they are left
+    untouched.
+    """
+    if n_hist + steps > capacity:
+        raise ValueError("capacity too small for n_hist + steps")
+    rng = np.random.default_rng(seed)
+    lam_draw = float(rng.uniform(0.0, 1.0))
+    kc = np.empty((B, H, capacity, D), dtype=np.float32)
+    vc = np.empty((B, H, capacity, D), dtype=np.float32)
+    kc[:, :, :n_hist] = rng.standard_normal((B, H, n_hist, D), dtype=np.float32)
+    vc[:, :, :n_hist] = rng.standard_normal((B, H, n_hist, D), dtype=np.float32)
+    kc[:, :, n_hist:] = rng.standard_normal((B, H, capacity - n_hist, D), dtype=np.float32)
+    vc[:, :, n_hist:] = rng.standard_normal((B, H, capacity - n_hist, D), dtype=np.float32)
+    step_shape = (steps, B, H, D)
+    q = rng.standard_normal(step_shape, dtype=np.float32)
+    kn = rng.standard_normal(step_shape, dtype=np.float32)
+    vn = rng.standard_normal(step_shape, dtype=np.float32)
+    return {
+        "lam": lam_draw if lam is None else float(lam),
+        "k_cache": to_dtype(kc, dtype),
+        "v_cache": to_dtype(vc, dtype),
+        "q": to_dtype(q, dtype),
+        "k_new": to_dtype(kn, dtype),
+        "v_new": to_dtype(vn, dtype),
+    }
