@@ -1,0 +1,308 @@
+"""Benchmark of librelation on one MI355X.
+
+A step is one pass of the Relation hot path over one batch: relation_fwd then
+relation_bwd on the 30M-model-shaped layer (B=16, H=8, T=2048, D=64, bf16,
+causal). The JSON line's `value` is that step's algorithmic throughput in
+TFLOP/s (fwd = 2*B*H*T^2*D flops, bwd = 2.5x fwd). The same run also measures
+the forward alone on the 10M / 30M / 100M layer shapes, forward+backward on
+the 100M shape beside torch's causal scaled-dot-product attention of the same
+shape, and 256 Relation Cache decode steps (B=32, H=12, D=64, history 4096) in
+GB/s, plus the fp64 CPU oracle on a bounded sample (cpu_baseline).
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-extra] [--only {step,fwd,decode}]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "Full Relation fwd / fwd+bwd TFLOP/s and % bf16 MFMA peak; decode GB/s"
+
+
+def fwd_flops(B, H, T, D):
+    return 2.0 * B * H * T * T * D
+
+
+def decode_bytes(B, H, D, n):
+    """Algorithmic bytes of one decode step at history n (bf16): read K and V
+    history (4 B H n D) + q, k_new, v_new reads, cache-slot writes, y write."""
+    return 4.0 * B * H * n * D + 10.0 * B * H * D
+
+
+class EventTimer:
+    """HIP events recorded on the stream the library launches on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        v = [a.elapsed_time(b) for a, b in self.pairs]
+        return sum(v) / len(v) if v else float("nan")
+
+
+def bench_step(rel, torch, dev, steps, warmup, B=16, H=8, T=2048, D=64, seed=42):
+    from workloads import make_inputs
+    inp = make_inputs(B, H, T, D, "bf16", seed=seed, with_dy=True)
+    lam, scale = inp["lam"], 1.0 / math.sqrt(D)
+    q, k, v, dy = (inp[n].to(dev) for n in ("q", "k", "v", "dy"))
+    y = torch.empty_like(q)
+    lse = torch.empty((B, H, T), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dl = torch.empty((1,), device=dev, dtype=torch.float32)
+    ws = torch.empty((rel.relation_bwd_workspace_bytes(torch.bfloat16, B, H, T, D),),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    tf, tb = EventTimer(torch, stream), EventTimer(torch, stream)
+
+    def step(timed):
+        s = tf.start() if timed else None
+        rel.relation_fwd(q, k, v, lam=lam, scale=scale, y=y, lse=lse, want_gate=False)
+        if timed:
+            tf.stop(s)
+            s = tb.start()
+        rel.relation_bwd(q, k, v, y, dy, lse, lam=lam, scale=scale, dq=dq, dk=dk, dv=dv,
+                         dlambda=dl, workspace=ws)
+        if timed:
+            tb.stop(s)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return {"ms_per_step": (t1 - t0) * 1e3 / steps, "fwd_ms": tf.mean_ms(),
+            "bwd_ms": tb.mean_ms(), "flops_fwd": fwd_flops(B, H, T, D)}
+
+
+def bench_fwd(rel, torch, dev, B, H, T, D, reps, rope=False, seed=42):
+    from workloads import make_inputs
+    inp = make_inputs(B, H, T, D, "bf16", seed=seed, rope=rope)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    y = torch.empty_like(q)
+    lse = torch.empty((B, H, T), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+    t = EventTimer(torch, stream)
+    for i in range(reps + 3):
+        s = t.start() if i >= 3 else None
+        rel.relation_fwd(q, k, v, lam=inp["lam"], scale=1 / math.sqrt(D), y=y, lse=lse)
+        if i >= 3:
+            t.stop(s)
+    ms = t.mean_ms()
+    tf = fwd_flops(B, H, T, D) / (ms * 1e-3) / 1e12
+    return {"ms": ms, "tflops": tf, "frac_peak": tf / PEAK_BF16_TFLOPS}
+
+
+def bench_fwdbwd_vs_attention(rel, torch, dev, reps, B=8, H=12, T=4096, D=64, seed=42):
+    from workloads import make_inputs
+    inp = make_inputs(B, H, T, D, "bf16", seed=seed, with_dy=True)
+    q, k, v, dy = (inp[n].to(dev) for n in ("q", "k", "v", "dy"))
+    lam, scale = inp["lam"], 1 / math.sqrt(D)
+    y = torch.empty_like(q)
+    lse = torch.empty((B, H, T), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dl = torch.empty((1,), device=dev, dtype=torch.float32)
+    ws = torch.empty((rel.relation_bwd_workspace_bytes(torch.bfloat16, B, H, T, D),),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    tf_, tfb = EventTimer(torch, stream), EventTimer(torch, stream)
+    for i in range(reps + 2):
+        s = tf_.start() if i >= 2 else None
+        rel.relation_fwd(q, k, v, lam=lam, scale=scale, y=y, lse=lse)
+        if i >= 2:
+            tf_.stop(s)
+        s2 = tfb.start() if i >= 2 else None
+        rel.relation_bwd(q, k, v, y, dy, lse, lam=lam, scale=scale, dq=dq, dk=dk, dv=dv,
+                         dlambda=dl, workspace=ws)
+        if i >= 2:
+            tfb.stop(s2)
+    f = fwd_flops(B, H, T, D)
+    fwd_ms, bwd_ms = tf_.mean_ms(), tfb.mean_ms()
+    out = {"relation_fwd_ms": fwd_ms, "relation_bwd_ms": bwd_ms,
+           "relation_fwd_tflops": f / (fwd_ms * 1e-3) / 1e12,
+           "relation_fwdbwd_tflops": 3.5 * f / ((fwd_ms + bwd_ms) * 1e-3) / 1e12}
+    # reference point: torch's causal softmax attention (SDPA) on the same tensors
+    try:
+        import torch.nn.functional as Fn
+        qa, ka, va = (x.detach().clone().requires_grad_(True) for x in (q, k, v))
+        ta, tab = EventTimer(torch, stream), EventTimer(torch, stream)
+        for i in range(reps + 2):
+            s = ta.start() if i >= 2 else None
+            o = Fn.scaled_dot_product_attention(qa, ka, va, is_causal=True, scale=scale)
+            if i >= 2:
+                ta.stop(s)
+            s2 = tab.start() if i >= 2 else None
+            o.backward(dy)
+            if i >= 2:
+                tab.stop(s2)
+            qa.grad = ka.grad = va.grad = None
+        afwd, abwd = ta.mean_ms(), tab.mean_ms()
+        out.update({"attention": "torch.nn.functional.scaled_dot_product_attention(is_causal=True)",
+                    "attention_fwd_ms": afwd, "attention_bwd_ms": abwd,
+                    "attention_fwd_tflops": f / (afwd * 1e-3) / 1e12,
+                    "attention_fwdbwd_tflops": 3.5 * f / ((afwd + abwd) * 1e-3) / 1e12,
+                    "relation_over_attention_fwd": afwd / fwd_ms,
+                    "relation_over_attention_fwdbwd": (afwd + abwd) / (fwd_ms + bwd_ms)})
+    except Exception as e:  # reference point only; report why it is missing
+        out["attention_error"] = repr(e)[:200]
+    return out
+
+
+def bench_decode(rel, torch, dev, B=32, H=12, D=64, n0=4096, steps=256, cap=4352, seed=42):
+    from workloads import make_decode_inputs
+    d = make_decode_inputs(B, H, D, n0, steps, cap, "bf16", seed=seed)
+    kc, vc = d["k_cache"].to(dev), d["v_cache"].to(dev)
+    qs, kn, vn = d["q"].to(dev), d["k_new"].to(dev), d["v_new"].to(dev)
+    y = torch.empty((B, H, D), device=dev, dtype=torch.bfloat16)
+    ws = torch.empty((rel.relation_decode_workspace_bytes(torch.bfloat16, B, H, D, cap),),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    kc0, vc0 = kc.clone(), vc.clone()
+    # warm-up pass over a copy of the cache, then restore
+    for s in range(4):
+        rel.relation_cache_decode(qs[s], kn[s], vn[s], kc, vc, n0 + s, lam=d["lam"],
+                                  scale=1 / math.sqrt(D), y=y, workspace=ws)
+    kc.copy_(kc0)
+    vc.copy_(vc0)
+    del kc0, vc0
+    t = EventTimer(torch, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        e = t.start()
+        rel.relation_cache_decode(qs[s], kn[s], vn[s], kc, vc, n0 + s, lam=d["lam"],
+                                  scale=1 / math.sqrt(D), y=y, workspace=ws)
+        t.stop(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    byts = sum(decode_bytes(B, H, D, n0 + s) for s in range(steps))
+    call_ms = t.mean_ms()
+    return {"steps": steps, "total_ms": wall * 1e3, "GBps": byts / wall / 1e9,
+            "frac_hbm_peak": byts / wall / 1e9 / PEAK_HBM_GBS, "call_ms": call_ms,
+            "call_GBps": byts / steps / (call_ms * 1e-3) / 1e9, "bytes": byts}
+
+
+def cpu_baseline(budget_s=20.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the step's
+    workload: whole heads of the 30M layer (T=2048), forward + backward, run
+    until about budget_s seconds are spent; scaled to TFLOP/s with the same
+    algorithmic count as the GPU."""
+    import numpy as np
+
+    import oracle
+    from workloads import make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    inp = make_inputs(1, 4, 2048, 64, "bf16", seed=42, with_dy=True)
+    f64 = {n: inp[n].double().numpy() for n in ("q", "k", "v", "dy")}
+    scale = 1 / 8
+    heads, t0 = 0, time.perf_counter()
+    while heads < 4 and (time.perf_counter() - t0) < budget_s:
+        oracle.relation_backward_head(f64["q"][0, heads], f64["k"][0, heads], f64["v"][0, heads],
+                                      f64["dy"][0, heads], scale, 2.0, inp["lam"])
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = 3.5 * fwd_flops(1, heads, 2048, 64)
+    del np
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} whole heads of the B=16,H=8,T=2048,D=64 layer, fwd+bwd "
+                      f"(materialised fp64 numpy), {dt:.1f} s; cpu_count={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", choices=["step", "fwd", "decode", "attn"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(heads are independent: see DESIGN.md for how the operator shards)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exchange_relation_amd as rel
+    rel.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.manual_seed(0)
+
+    if args.only == "fwd":
+        print(json.dumps(bench_fwd(rel, torch, dev, 16, 8, 2048, 64, args.steps)))
+        return
+    if args.only == "decode":
+        print(json.dumps(bench_decode(rel, torch, dev)))
+        return
+    if args.only == "attn":
+        print(json.dumps(bench_fwdbwd_vs_attention(rel, torch, dev, args.steps)))
+        return
+
+    st = bench_step(rel, torch, dev, args.steps, args.warmup)
+    f = st["flops_fwd"]
+    value = 3.5 * f / (st["ms_per_step"] * 1e-3) / 1e12
+    bwd_tf = 2.5 * f / (st["bwd_ms"] * 1e-3) / 1e12
+    fwd_tf = f / (st["fwd_ms"] * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": st["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian q, k, v, dY; no dataset)",
+        "config": {"workload": "layer30m_fwdbwd_bf16", "B": 16, "H": 8, "T": 2048, "D": 64,
+                   "causal": True, "step": "relation_fwd + relation_bwd",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "relation_bwd call (dq zero-fill + "
+                     "bwd_bf16_kernel + dq finalize; preprocess)",
+                     "achieved": bwd_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": bwd_tf / PEAK_BF16_TFLOPS, "traffic": None},
+        "roofline_fwd": {"bound": "mfma", "kernel": "fwd_bf16_kernel (one launch per call)",
+                         "achieved": fwd_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": fwd_tf / PEAK_BF16_TFLOPS, "traffic": None},
+        "fwd_ms": st["fwd_ms"], "bwd_ms": st["bwd_ms"],
+    }
+    if not args.no_extra:
+        rec["fwd_layer10m"] = bench_fwd(rel, torch, dev, 8, 8, 1024, 64, 20, rope=True)
+        rec["fwd_layer100m"] = bench_fwd(rel, torch, dev, 8, 12, 4096, 64, 10)
+        rec["layer100m_vs_attention"] = bench_fwdbwd_vs_attention(rel, torch, dev, 5)
+        dec = bench_decode(rel, torch, dev)
+        rec["decode"] = dec
+        rec["roofline_decode"] = {"bound": "hbm", "kernel": "relation_cache_decode call "
+                                  "(split scan + combine)", "achieved": dec["call_GBps"],
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": dec["call_GBps"] / PEAK_HBM_GBS, "traffic": None}
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

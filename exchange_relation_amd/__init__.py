@@ -1,0 +1,260 @@
+"""Python binding of librelation (exact causal Full / Multi-Head Relation on
+MI355X / gfx950).
+
+Argument marshalling only: tensors are checked and passed as device pointers
+to the C ABI declared in include/relation.h, on torch's current HIP stream.
+Every step of the operator runs in the library's HIP kernels. There is no
+fallback: if librelation.so is missing or fails to load, every call raises.
+
+Build the library with ``python -m exchange_relation_amd.build``.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "RelationError",
+    "lib_path",
+    "load_library",
+    "relation_fwd",
+    "relation_bwd",
+    "relation_bwd_workspace_bytes",
+    "relation_cache_decode",
+    "relation_decode_workspace_bytes",
+    "relation_status_string",
+    "relation_version",
+    "RelationFunction",
+    "relation",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+REL_F32, REL_BF16 = 0, 1
+EXPORTED_SYMBOLS = (
+    "relation_fwd",
+    "relation_bwd_workspace_bytes",
+    "relation_bwd",
+    "relation_decode_workspace_bytes",
+    "relation_cache_decode",
+    "relation_status_string",
+    "relation_version",
+)
+
+
+class RelationError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {relation_status_string(status)} (status {status})")
+
+
+def lib_path():
+    return os.path.join(_HERE, "librelation.so")
+
+
+_LIB = None
+
+
+def load_library():
+    """Loads librelation.so (once) and declares the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m exchange_relation_amd.build`")
+    lib = ctypes.CDLL(path)
+    c_int, c_float, c_size, vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+    lib.relation_fwd.restype = c_int
+    lib.relation_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
+                                 c_float, c_float, c_float, vp]
+    lib.relation_bwd_workspace_bytes.restype = c_size
+    lib.relation_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    lib.relation_bwd.restype = c_int
+    lib.relation_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
+                                 vp, vp, vp, vp, vp, c_size, c_float, c_float, c_float, vp]
+    lib.relation_decode_workspace_bytes.restype = c_size
+    lib.relation_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    lib.relation_cache_decode.restype = c_int
+    lib.relation_cache_decode.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, c_int,
+                                          c_int, vp, vp, vp, c_size, c_float, c_float, c_float,
+                                          vp]
+    lib.relation_status_string.restype = ctypes.c_char_p
+    lib.relation_status_string.argtypes = [c_int]
+    lib.relation_version.restype = c_int
+    lib.relation_version.argtypes = []
+    _LIB = lib
+    return lib
+
+
+def relation_status_string(status):
+    return load_library().relation_status_string(int(status)).decode()
+
+
+def relation_version():
+    return load_library().relation_version()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return REL_F32
+    if t.dtype == torch.bfloat16:
+        return REL_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _scale(D, scale):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def relation_fwd(q, k, v, lam=0.0, scale=None, tau_s=2.0, y=None, lse=None, gate=None,
+                 want_lse=True, want_gate=False, stream=None):
+    """Multi-Head Relation forward. q, k, v: [B, H, T, D] on a GPU, float32 or
+    bfloat16, contiguous. Returns (y, lse, gate); lse / gate are float32
+    [B, H, T] or None. Outputs may be passed in to avoid allocation."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, D]")
+    B, H, T, D = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, dt, q.shape, dev)
+    _check(q, "q", dt, q.shape, dev)
+    if y is None:
+        y = torch.empty_like(q)
+    _check(y, "y", dt, q.shape, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, T), device=dev, dtype=torch.float32)
+    if gate is None and want_gate:
+        gate = torch.empty((B, H, T), device=dev, dtype=torch.float32)
+    for name, t in (("lse", lse), ("gate", gate)):
+        if t is not None:
+            _check(t, name, torch.float32, (B, H, T), dev)
+    st = lib.relation_fwd(code, B, H, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(lse),
+                          _ptr(gate), _scale(D, scale), float(tau_s), float(lam),
+                          _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_fwd")
+    return y, lse, gate
+
+
+def relation_bwd_workspace_bytes(dtype, B, H, T, D):
+    code = REL_BF16 if dtype == torch.bfloat16 else REL_F32
+    return int(load_library().relation_bwd_workspace_bytes(code, B, H, T, D))
+
+
+def relation_bwd(q, k, v, y, dy, lse, lam=0.0, scale=None, tau_s=2.0, dq=None, dk=None, dv=None,
+                 dlambda=None, workspace=None, want_dlambda=True, stream=None):
+    """Backward of relation_fwd. Returns (dq, dk, dv, dlambda) where dlambda is
+    a float32 device tensor of shape [1] (or None)."""
+    lib = load_library()
+    B, H, T, D = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("y", y), ("dy", dy)):
+        _check(t, name, dt, q.shape, dev)
+    _check(lse, "lse", torch.float32, (B, H, T), dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, dt, q.shape, dev)
+    if dlambda is None and want_dlambda:
+        dlambda = torch.empty((1,), device=dev, dtype=torch.float32)
+    need = int(lib.relation_bwd_workspace_bytes(code, B, H, T, D))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), device=dev, dtype=torch.uint8)
+    st = lib.relation_bwd(code, B, H, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy),
+                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlambda),
+                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          _scale(D, scale), float(tau_s), float(lam), _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_bwd")
+    return dq, dk, dv, dlambda
+
+
+def relation_decode_workspace_bytes(dtype, B, H, D, capacity):
+    code = REL_BF16 if dtype == torch.bfloat16 else REL_F32
+    return int(load_library().relation_decode_workspace_bytes(code, B, H, D, capacity))
+
+
+def relation_cache_decode(q, k_new, v_new, k_cache, v_cache, n_hist, lam=0.0, scale=None,
+                          tau_s=2.0, y=None, gate=None, workspace=None, want_gate=False,
+                          stream=None):
+    """One decode step: q, k_new, v_new [B, H, D]; k_cache, v_cache
+    [B, H, capacity, D] (updated in place at slot n_hist). Returns (y, gate)."""
+    lib = load_library()
+    B, H, D = q.shape
+    capacity = k_cache.shape[2]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
+        _check(t, name, dt, (B, H, D), dev)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, name, dt, (B, H, capacity, D), dev)
+    y = torch.empty_like(q) if y is None else y
+    _check(y, "y", dt, (B, H, D), dev)
+    if gate is None and want_gate:
+        gate = torch.empty((B, H), device=dev, dtype=torch.float32)
+    if gate is not None:
+        _check(gate, "gate", torch.float32, (B, H), dev)
+    need = int(lib.relation_decode_workspace_bytes(code, B, H, D, capacity))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), device=dev, dtype=torch.uint8)
+    st = lib.relation_cache_decode(code, B, H, D, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                   _ptr(k_cache), _ptr(v_cache), capacity, int(n_hist), _ptr(y),
+                                   _ptr(gate), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _scale(D, scale), float(tau_s), float(lam),
+                                   _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_cache_decode")
+    return y, gate
+
+
+class RelationFunction(torch.autograd.Function):
+    """autograd wrapper: y = Relation(q, k, v; lambda) with gradients for q,
+    k, v and the layer's lambda (a 1-element tensor)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, lam, scale, tau_s):
+        y, lse, _ = relation_fwd(q, k, v, lam=float(lam), scale=scale, tau_s=tau_s)
+        ctx.save_for_backward(q, k, v, y, lse)
+        ctx.lam, ctx.scale, ctx.tau_s = float(lam), scale, tau_s
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        q, k, v, y, lse = ctx.saved_tensors
+        dq, dk, dv, dlam = relation_bwd(q, k, v, y, dy.contiguous(), lse, lam=ctx.lam,
+                                        scale=ctx.scale, tau_s=ctx.tau_s)
+        return dq, dk, dv, dlam.reshape(()), None, None
+
+
+def relation(q, k, v, lam, scale=None, tau_s=2.0):
+    """Differentiable Multi-Head Relation; lam is a scalar tensor (learnable)."""
+    return RelationFunction.apply(q, k, v, lam, scale, tau_s)

@@ -1,0 +1,126 @@
+// Backward pieces shared by the fp32 and bf16 paths.
+//
+// With G_i = dL/dY_i (App. A.1.7 of the Relation paper), the softmax
+// Jacobian gives dL/dR_ij = F_ij (G_i . v_j - Dr_i) with the row term
+// Dr_i = sum_j F_ij G_i . v_j = G_i . Y_i. Every row of dL/dR sums to zero,
+// so dL/dlambda = sum_{j<i} dL/dR_ij (-ln i) = sum_i ln(i) dL/dR_ii: only the
+// Self entry of each row is needed, F_ii = exp(S_i - LSE_i).
+//
+// bwd_pre_kernel: one lane per row: Dr_i (to the workspace) and the
+// per-block partial of sum ln(i) dL/dR_ii. bwd_dlambda_kernel: one workgroup
+// sums the partials in a fixed order (deterministic) into *dlambda.
+#include <math.h>
+
+#include "bwd_common.hpp"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rel {
+
+template <typename TE, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const TE* __restrict__ q,
+                                                      const TE* __restrict__ k,
+                                                      const TE* __restrict__ v,
+                                                      const TE* __restrict__ y,
+                                                      const TE* __restrict__ dy,
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ Dr,
+                                                      float* __restrict__ part, int T,
+                                                      long long rows, float scale, float tau) {
+  __shared__ float red[256];
+  const long long gr = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  float contrib = 0.f;
+  if (gr < rows) {
+    const size_t off = static_cast<size_t>(gr) * D;
+    float dYY = 0.f, dYV = 0.f, qk = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) {
+      const float g = Elem<TE>::load(dy + off + d);
+      dYY = fmaf(g, Elem<TE>::load(y + off + d), dYY);
+      dYV = fmaf(g, Elem<TE>::load(v + off + d), dYV);
+      qk = fmaf(Elem<TE>::load(q + off + d), Elem<TE>::load(k + off + d), qk);
+    }
+    Dr[gr] = dYY;
+    const int t = static_cast<int>(gr % T);
+    if (t > 0) {  // ln(1) = 0 for row 1
+      const float S = 1.f / (1.f + expf(-scale * qk / tau));
+      const float Fii = expf(S - lse[gr]);
+      contrib = logf(static_cast<float>(t + 1)) * Fii * (dYV - dYY);
+    }
+  }
+  red[threadIdx.x] = contrib;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void bwd_dlambda_kernel(const float* __restrict__ part, int n,
+                                                          float* __restrict__ out) {
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) s += part[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+BwdWorkspace bwd_workspace_layout(int dtype, int B, int H, int T, int D) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  BwdWorkspace w;
+  const size_t rows = static_cast<size_t>(B) * H * T;
+  w.npart = static_cast<int>((rows + 255) / 256);
+  w.off_dr = 0;
+  w.off_part = al(rows * sizeof(float));
+  w.off_dq = w.off_part + al(static_cast<size_t>(w.npart) * sizeof(float));
+  w.total = w.off_dq + (dtype == 1 ? al(rows * D * sizeof(float)) : 0);
+  return w;
+}
+
+size_t bwd_workspace_bytes(int dtype, int B, int H, int T, int D) {
+  return bwd_workspace_layout(dtype, B, H, T, D).total;
+}
+
+template <typename TE, int D>
+hipError_t launch_bwd_pre_t(int B, int H, int T, const TE* q, const TE* k, const TE* v,
+                            const TE* y, const TE* dy, const float* lse, float* dlambda,
+                            const BwdWorkspace& w, char* ws, float scale, float tau,
+                            hipStream_t stream) {
+  const long long rows = static_cast<long long>(B) * H * T;
+  float* Dr = reinterpret_cast<float*>(ws + w.off_dr);
+  float* part = reinterpret_cast<float*>(ws + w.off_part);
+  hipLaunchKernelGGL((bwd_pre_kernel<TE, D>), dim3(w.npart), dim3(256), 0, stream, q, k, v, y, dy,
+                     lse, Dr, part, T, rows, scale, tau);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !dlambda) return e;
+  hipLaunchKernelGGL(bwd_dlambda_kernel, dim3(1), dim3(256), 0, stream, part, w.npart, dlambda);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+                          const void* v, const void* y, const void* dy, const float* lse,
+                          float* dlambda, const BwdWorkspace& w, char* ws, float scale, float tau,
+                          hipStream_t stream) {
+  if (dtype == 1)
+    return launch_bwd_pre_t<uint16_t, 64>(
+        B, H, T, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(y),
+        static_cast<const uint16_t*>(dy), lse, dlambda, w, ws, scale, tau, stream);
+  if (D == 64)
+    return launch_bwd_pre_t<float, 64>(B, H, T, static_cast<const float*>(q),
+                                       static_cast<const float*>(k), static_cast<const float*>(v),
+                                       static_cast<const float*>(y), static_cast<const float*>(dy),
+                                       lse, dlambda, w, ws, scale, tau, stream);
+  return launch_bwd_pre_t<float, 32>(B, H, T, static_cast<const float*>(q),
+                                     static_cast<const float*>(k), static_cast<const float*>(v),
+                                     static_cast<const float*>(y), static_cast<const float*>(dy),
+                                     lse, dlambda, w, ws, scale, tau, stream);
+}
+
+}  // namespace rel

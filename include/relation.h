@@ -1,0 +1,150 @@
+/*
+ * librelation — exact causal Full / Multi-Head Relation on AMD Instinct MI355X
+ * (gfx950). C ABI.
+ *
+ * The operator is the Self-Exchange Relation of "Ask Self, Ask Others:
+ * Relation Is All You Need" (arXiv 2608.20172), Sec. 3.1, applied per head as
+ * in Sec. 3.2 (Multi-Head Relation). For one head with p1 = q, p2 = k, I = v
+ * (each T x D) and 1-based rows i:
+ *
+ *   U_ij = scale * q_i . k_j                               (pairwise evidence)
+ *   S_i  = sigmoid(U_ii / tau_s)                           (Self)
+ *   E_ij = SiLU(U_ij) = U_ij * sigmoid(U_ij),  j < i        (Exchange)
+ *   R_ij = S_i if j = i;  E_ij - lambda * ln(i) if j < i;  -inf if j > i
+ *   F_i  = softmax(R_i);   Y_i = sum_{j <= i} F_ij v_j      (Flow, transport)
+ *
+ * Derived per-row quantities (Sec. 4.2; App. A.1.2): the Exchange mass
+ * g_i = sum_{j<i} F_ij = sigmoid(A_i - S_i) with
+ * A_i = ln sum_{j<i} e^{E_ij} - lambda ln(i), and the row log-normaliser
+ * LSE_i = ln Z_i = ln(e^{S_i} + e^{A_i}). Row 1 has no history: A_1 = -inf,
+ * g_1 = 0, Y_1 = v_1, LSE_1 = S_1 (App. A.1.8).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major and contiguous: [B, H, T, D] with D fastest.
+ *    Element type is given by `dtype` (REL_F32 = float, REL_BF16 = bfloat16).
+ *  - Pointers to tensors are DEVICE pointers (hipMalloc / torch CUDA memory)
+ *    on the current HIP device, 16-byte aligned. Scalars are passed by value.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *    call only enqueues work on that stream and returns; the caller
+ *    synchronises. Call order on one stream defines the data flow.
+ *  - The library allocates no device memory, keeps no state between calls,
+ *    never frees or retains caller memory, and is safe to call from several
+ *    host threads. Outputs must not alias inputs.
+ *  - Validation is synchronous, on the host, before anything is enqueued; on
+ *    any error nothing is written. Errors reported by the HIP runtime at
+ *    launch map to REL_ERR_HIP; faults inside kernels surface at the caller's
+ *    next synchronisation, as for any HIP call.
+ *  - scale: the pages print U = p1.p2 / d_h; their text drops square roots,
+ *    so callers normally pass 1/sqrt(D). Any finite value is accepted.
+ *  - tau_s > 0 (the pages fix tau_s = 2); lambda: any finite value (the
+ *    pages' learnable layer-wise count correction, Sec. 3.1).
+ */
+#ifndef LIBRELATION_RELATION_H
+#define LIBRELATION_RELATION_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  REL_OK = 0,
+  REL_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  REL_ERR_SHAPE = 2,       /* B, H, T < 1, or sizes overflow the index range  */
+  REL_ERR_UNSUPPORTED = 3, /* dtype / head dimension not built                */
+  REL_ERR_PARAM = 4,       /* scale or lambda not finite, tau_s <= 0          */
+  REL_ERR_CAPACITY = 5,    /* decode: n_hist < 0 or n_hist + 1 > capacity     */
+  REL_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned                */
+  REL_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the queried size */
+  REL_ERR_HIP = 8          /* the HIP runtime reported an error               */
+} relation_status;
+
+typedef enum { REL_F32 = 0, REL_BF16 = 1 } relation_dtype;
+
+/* Head dimensions built: REL_F32 forward/backward/decode: D in {32, 64};
+ * REL_BF16 forward/backward/decode: D = 64. Other D -> REL_ERR_UNSUPPORTED. */
+
+/*
+ * relation_fwd — Multi-Head Relation forward (Sec. 3.1 / 3.2), evaluated
+ * exactly by a tiled scan of the historical Exchange entries with running
+ * (m, l, z) (Sec. 5.1; App. A.3) and the row completion of App. A.3.5.
+ *
+ *   q, k, v : in  [B, H, T, D], dtype
+ *   y       : out [B, H, T, D], dtype (round to nearest even from fp32)
+ *   lse     : out [B, H, T] float32, LSE_i = ln Z_i; NULL to skip. Needed by
+ *             relation_bwd.
+ *   gate    : out [B, H, T] float32, the Exchange mass g_i; NULL to skip.
+ */
+relation_status relation_fwd(relation_dtype dtype, int B, int H, int T, int D,
+                             const void* q, const void* k, const void* v,
+                             void* y, float* lse, float* gate,
+                             float scale, float tau_s, float lambda,
+                             void* stream);
+
+/*
+ * relation_bwd — gradients of a scalar loss L through relation_fwd, by
+ * recomputation (nothing T x T is stored): with G_i = dL/dY_i (App. A.1.7),
+ * dL/dF_ij = G_i . v_j, dL/dR_ij = F_ij (G_i . v_j - G_i . Y_i), then through
+ * SiLU (j < i), the Self sigmoid (j = i, factor S_i (1 - S_i) / tau_s) and
+ * U = scale * q k^T.
+ *
+ *   q, k, v, y : in [B, H, T, D], dtype (y = relation_fwd's output)
+ *   dy         : in [B, H, T, D], dtype (dL/dY)
+ *   lse        : in [B, H, T] float32 from relation_fwd
+ *   dq, dk, dv : out [B, H, T, D], dtype, overwritten
+ *   dlambda    : out, one float32 on the device: dL/dlambda summed over every
+ *                batch and head (lambda is one scalar per layer); NULL to skip
+ *   workspace  : device scratch of at least relation_bwd_workspace_bytes()
+ *                bytes, 256-byte aligned; contents on entry are ignored.
+ */
+size_t relation_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D);
+
+relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D,
+                             const void* q, const void* k, const void* v,
+                             const void* y, const void* dy, const float* lse,
+                             void* dq, void* dk, void* dv, float* dlambda,
+                             void* workspace, size_t workspace_bytes,
+                             float scale, float tau_s, float lambda,
+                             void* stream);
+
+/*
+ * relation_cache_decode — one autoregressive step over the KV-style Relation
+ * Cache (named in the paper's first version as its decoding form). The new
+ * token of every sequence is at 1-based position i = n_hist + 1; its output
+ * is the last row of the forward over the concatenated sequence.
+ *
+ *   q, k_new, v_new  : in  [B, H, D], dtype (the new token's q, k and v)
+ *   k_cache, v_cache : in/out [B, H, capacity, D], dtype. Slots [0, n_hist)
+ *                      are read; slot n_hist is overwritten with k_new /
+ *                      v_new (an exact copy); every other slot is untouched.
+ *   capacity, n_hist : host ints, uniform over the batch; 0 <= n_hist and
+ *                      n_hist + 1 <= capacity.
+ *   y                : out [B, H, D], dtype
+ *   gate             : out [B, H] float32 Exchange mass g; NULL to skip
+ *   workspace        : device scratch of at least
+ *                      relation_decode_workspace_bytes() bytes (256-byte
+ *                      aligned); contents on entry are ignored.
+ */
+size_t relation_decode_workspace_bytes(relation_dtype dtype, int B, int H, int D, int capacity);
+
+relation_status relation_cache_decode(relation_dtype dtype, int B, int H, int D,
+                                      const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache,
+                                      int capacity, int n_hist,
+                                      void* y, float* gate,
+                                      void* workspace, size_t workspace_bytes,
+                                      float scale, float tau_s, float lambda,
+                                      void* stream);
+
+/* Static, NUL-terminated description of a status code (host only). */
+const char* relation_status_string(relation_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (host only). */
+int relation_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRELATION_RELATION_H */

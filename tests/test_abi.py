@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/relation.h declares, and rejects bad arguments on the host
+before launching anything (every call below fails validation, so no kernel
+is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exchange_relation_amd as rel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "relation.h")
+
+REL_OK, REL_ERR_NULL, REL_ERR_SHAPE, REL_ERR_UNSUPPORTED, REL_ERR_PARAM = 0, 1, 2, 3, 4
+REL_ERR_CAPACITY, REL_ERR_ALIGN, REL_ERR_WORKSPACE, REL_ERR_HIP = 5, 6, 7, 8
+F32, BF16 = 0, 1
+
+# Fake device addresses: validation never dereferences them, and every call
+# below returns an error before any launch.
+P = ctypes.c_void_p(0x7F0000000000)
+P_MIS = ctypes.c_void_p(0x7F0000000004)  # 4-byte aligned only
+NUL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(relation_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rel.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return rel.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(rel.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    for s in range(9):
+        assert rel.relation_status_string(s)
+    assert rel.relation_status_string(99) == "unknown status"
+    assert rel.relation_version() == 100
+
+
+def fwd(lib, dtype=BF16, B=1, H=1, T=8, D=64, q=P, k=P, v=P, y=P, lse=NUL, gate=NUL,
+        scale=0.125, tau=2.0, lam=0.5):
+    return lib.relation_fwd(dtype, B, H, T, D, q, k, v, y, lse, gate, scale, tau, lam, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, q=NUL) == REL_ERR_NULL
+    assert fwd(lib, y=NUL) == REL_ERR_NULL
+    assert fwd(lib, T=0) == REL_ERR_SHAPE
+    assert fwd(lib, B=-1) == REL_ERR_SHAPE
+    assert fwd(lib, D=48) == REL_ERR_UNSUPPORTED
+    assert fwd(lib, dtype=BF16, D=32) == REL_ERR_UNSUPPORTED
+    assert fwd(lib, dtype=7) == REL_ERR_UNSUPPORTED
+    assert fwd(lib, tau=0.0) == REL_ERR_PARAM
+    assert fwd(lib, tau=-1.0) == REL_ERR_PARAM
+    assert fwd(lib, lam=float("nan")) == REL_ERR_PARAM
+    assert fwd(lib, scale=float("inf")) == REL_ERR_PARAM
+    assert fwd(lib, q=P_MIS) == REL_ERR_ALIGN
+    assert fwd(lib, lse=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+
+
+def test_bwd_validation_and_workspace(lib):
+    need = lib.relation_bwd_workspace_bytes(BF16, 2, 3, 100, 64)
+    # Dr + dlambda partials + fp32 dq accumulator, each 256-byte padded
+    assert need >= 2 * 3 * 100 * 4 + 2 * 3 * 100 * 64 * 4
+    assert lib.relation_bwd_workspace_bytes(F32, 2, 3, 100, 64) < need
+    assert lib.relation_bwd_workspace_bytes(BF16, 2, 3, 100, 48) == 0
+
+    def bwd(ws=P, wsb=None, dq=P, lse=P, tau=2.0, T=100):
+        wsb = need if wsb is None else wsb
+        return lib.relation_bwd(BF16, 2, 3, T, 64, P, P, P, P, P, lse, dq, P, P, NUL, ws, wsb,
+                                0.125, tau, 0.3, None)
+
+    assert bwd(dq=NUL) == REL_ERR_NULL
+    assert bwd(lse=NUL) == REL_ERR_NULL
+    assert bwd(ws=NUL) == REL_ERR_WORKSPACE
+    assert bwd(wsb=need - 1) == REL_ERR_WORKSPACE
+    assert bwd(ws=ctypes.c_void_p(0x7F0000000010)) == REL_ERR_ALIGN
+    assert bwd(tau=0.0) == REL_ERR_PARAM
+    assert bwd(T=0) == REL_ERR_SHAPE
+
+
+def test_decode_validation(lib):
+    need = lib.relation_decode_workspace_bytes(BF16, 2, 3, 64, 4352)
+    assert need > 0
+
+    def dec(n=10, cap=4352, ws=P, wsb=None, q=P, D=64, dtype=BF16):
+        wsb = need if wsb is None else wsb
+        return lib.relation_cache_decode(dtype, 2, 3, D, q, P, P, P, P, cap, n, P, NUL, ws, wsb,
+                                         0.125, 2.0, 0.3, None)
+
+    assert dec(n=4352) == REL_ERR_CAPACITY      # n_hist + 1 > capacity
+    assert dec(n=-1) == REL_ERR_CAPACITY
+    assert dec(q=NUL) == REL_ERR_NULL
+    assert dec(ws=NUL) == REL_ERR_WORKSPACE
+    assert dec(wsb=need - 4) == REL_ERR_WORKSPACE
+    assert dec(D=32) == REL_ERR_UNSUPPORTED
+    assert dec(cap=0, n=0) == REL_ERR_SHAPE
+    assert dec(q=P_MIS) == REL_ERR_ALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(rel, "_LIB", None)
+    monkeypatch.setattr(rel, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        rel.load_library()
