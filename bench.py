@@ -240,7 +240,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["step", "fwd", "decode", "attn"], default=None)
+    ap.add_argument("--only", choices=["step", "fwd", "decode", "attn"], default=None,
+                    help="run one measurement and print its raw numbers")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -256,6 +257,9 @@ def main():
     torch.cuda.set_device(dev)
     torch.manual_seed(0)
 
+    if args.only == "step":
+        print(json.dumps(bench_step(rel, torch, dev, args.steps, args.warmup)))
+        return
     if args.only == "fwd":
         print(json.dumps(bench_fwd(rel, torch, dev, 16, 8, 2048, 64, args.steps)))
         return

@@ -6,9 +6,10 @@
 // so dL/dlambda = sum_{j<i} dL/dR_ij (-ln i) = sum_i ln(i) dL/dR_ii: only the
 // Self entry of each row is needed, F_ii = exp(S_i - LSE_i).
 //
-// bwd_pre_kernel: one lane per row: Dr_i (to the workspace) and the
-// per-block partial of sum ln(i) dL/dR_ii. bwd_dlambda_kernel: one workgroup
-// sums the partials in a fixed order (deterministic) into *dlambda.
+// bwd_pre_kernel: Dr_i (to the workspace), the per-block partial of
+// sum ln(i) dL/dR_ii and (bf16 path) the zero-fill of the fp32 dq
+// accumulator. bwd_dlambda_kernel: one workgroup sums the partials in a fixed
+// order (deterministic) into *dlambda.
 #include <math.h>
 
 #include "bwd_common.hpp"
@@ -17,6 +18,10 @@
 
 namespace rel {
 
+// One row per 8-lane group (32 rows per 256-lane workgroup); each lane reads
+// D/8 consecutive elements of the five row vectors with one vector load, so
+// every wave-wide load covers whole 128-byte rows. When dq_acc is given, the
+// group also zero-fills the row of the fp32 dq accumulator.
 template <typename TE, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const TE* __restrict__ q,
                                                       const TE* __restrict__ k,
@@ -25,36 +30,59 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const TE* __restrict__ q,
                                                       const TE* __restrict__ dy,
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ Dr,
-                                                      float* __restrict__ part, int T,
+                                                      float* __restrict__ part,
+                                                      float* __restrict__ dq_acc, int T,
                                                       long long rows, float scale, float tau) {
-  __shared__ float red[256];
-  const long long gr = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  constexpr int E = D / 8;
+  __shared__ float red[32];
+  const int sub = threadIdx.x & 7;
+  const int grp = threadIdx.x >> 3;
+  const long long gr = static_cast<long long>(blockIdx.x) * 32 + grp;
   float contrib = 0.f;
   if (gr < rows) {
-    const size_t off = static_cast<size_t>(gr) * D;
+    const size_t off = static_cast<size_t>(gr) * D + sub * E;
+    float a[E], b[E];
     float dYY = 0.f, dYV = 0.f, qk = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < D; ++d) {
-      const float g = Elem<TE>::load(dy + off + d);
-      dYY = fmaf(g, Elem<TE>::load(y + off + d), dYY);
-      dYV = fmaf(g, Elem<TE>::load(v + off + d), dYV);
-      qk = fmaf(Elem<TE>::load(q + off + d), Elem<TE>::load(k + off + d), qk);
+    load_row_piece<TE, D>(dy + off, a);
+    load_row_piece<TE, D>(y + off, b);
+#pragma unroll
+    for (int e = 0; e < E; ++e) dYY = fmaf(a[e], b[e], dYY);
+    load_row_piece<TE, D>(v + off, b);
+#pragma unroll
+    for (int e = 0; e < E; ++e) dYV = fmaf(a[e], b[e], dYV);
+    load_row_piece<TE, D>(q + off, a);
+    load_row_piece<TE, D>(k + off, b);
+#pragma unroll
+    for (int e = 0; e < E; ++e) qk = fmaf(a[e], b[e], qk);
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      dYY += __shfl_xor(dYY, o, 8);
+      dYV += __shfl_xor(dYV, o, 8);
+      qk += __shfl_xor(qk, o, 8);
     }
-    Dr[gr] = dYY;
-    const int t = static_cast<int>(gr % T);
-    if (t > 0) {  // ln(1) = 0 for row 1
-      const float S = 1.f / (1.f + expf(-scale * qk / tau));
-      const float Fii = expf(S - lse[gr]);
-      contrib = logf(static_cast<float>(t + 1)) * Fii * (dYV - dYY);
+    if (dq_acc) {
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<float4*>(dq_acc + off + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (sub == 0) {
+      Dr[gr] = dYY;
+      const int t = static_cast<int>(gr % T);
+      if (t > 0) {  // ln(1) = 0 for row 1
+        const float S = 1.f / (1.f + expf(-scale * qk / tau));
+        const float Fii = expf(S - lse[gr]);
+        contrib = logf(static_cast<float>(t + 1)) * Fii * (dYV - dYY);
+      }
     }
   }
-  red[threadIdx.x] = contrib;
+  if (sub == 0) red[grp] = contrib;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
+  if (threadIdx.x < 32) {
+    float s = red[threadIdx.x];
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
+    if (threadIdx.x == 0) part[blockIdx.x] = s;
   }
-  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
 }
 
 __global__ __launch_bounds__(256) void bwd_dlambda_kernel(const float* __restrict__ part, int n,
@@ -75,7 +103,7 @@ BwdWorkspace bwd_workspace_layout(int dtype, int B, int H, int T, int D) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   BwdWorkspace w;
   const size_t rows = static_cast<size_t>(B) * H * T;
-  w.npart = static_cast<int>((rows + 255) / 256);
+  w.npart = static_cast<int>((rows + 31) / 32);
   w.off_dr = 0;
   w.off_part = al(rows * sizeof(float));
   w.off_dq = w.off_part + al(static_cast<size_t>(w.npart) * sizeof(float));
@@ -91,12 +119,13 @@ template <typename TE, int D>
 hipError_t launch_bwd_pre_t(int B, int H, int T, const TE* q, const TE* k, const TE* v,
                             const TE* y, const TE* dy, const float* lse, float* dlambda,
                             const BwdWorkspace& w, char* ws, float scale, float tau,
-                            hipStream_t stream) {
+                            bool zero_dq, hipStream_t stream) {
   const long long rows = static_cast<long long>(B) * H * T;
   float* Dr = reinterpret_cast<float*>(ws + w.off_dr);
   float* part = reinterpret_cast<float*>(ws + w.off_part);
+  float* dq_acc = zero_dq ? reinterpret_cast<float*>(ws + w.off_dq) : nullptr;
   hipLaunchKernelGGL((bwd_pre_kernel<TE, D>), dim3(w.npart), dim3(256), 0, stream, q, k, v, y, dy,
-                     lse, Dr, part, T, rows, scale, tau);
+                     lse, Dr, part, dq_acc, T, rows, scale, tau);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !dlambda) return e;
   hipLaunchKernelGGL(bwd_dlambda_kernel, dim3(1), dim3(256), 0, stream, part, w.npart, dlambda);
@@ -111,16 +140,16 @@ hipError_t launch_bwd_pre(int dtype, int B, int H, int T, int D, const void* q, 
     return launch_bwd_pre_t<uint16_t, 64>(
         B, H, T, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
         static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(y),
-        static_cast<const uint16_t*>(dy), lse, dlambda, w, ws, scale, tau, stream);
+        static_cast<const uint16_t*>(dy), lse, dlambda, w, ws, scale, tau, true, stream);
   if (D == 64)
     return launch_bwd_pre_t<float, 64>(B, H, T, static_cast<const float*>(q),
                                        static_cast<const float*>(k), static_cast<const float*>(v),
                                        static_cast<const float*>(y), static_cast<const float*>(dy),
-                                       lse, dlambda, w, ws, scale, tau, stream);
+                                       lse, dlambda, w, ws, scale, tau, false, stream);
   return launch_bwd_pre_t<float, 32>(B, H, T, static_cast<const float*>(q),
                                      static_cast<const float*>(k), static_cast<const float*>(v),
                                      static_cast<const float*>(y), static_cast<const float*>(dy),
-                                     lse, dlambda, w, ws, scale, tau, stream);
+                                     lse, dlambda, w, ws, scale, tau, false, stream);
 }
 
 }  // namespace rel

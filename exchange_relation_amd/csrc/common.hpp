@@ -40,6 +40,36 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Exchanges between the two 32-lane halves of a wave (v_permlane32_swap):
+// the swap returns {own value in lanes < 32, other half's in lanes >= 32}
+// and {other half's in lanes < 32, own in lanes >= 32}. Call them with both
+// partner lanes active (never inside a lane-divergent branch).
+__device__ __forceinline__ float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+}
+
+// LDS transposing read (ds_read_b64_tr_b16, gfx950). Within each group of 16
+// lanes, lane i receives element (i & 3) of the 8-byte chunks that lanes
+// (i >> 2) + {0, 4, 8, 12} of its group address. So if lane j of a group
+// addresses row (r0 + (j >> 2)), columns c0 + 4 * (j & 3) .. +3 of a
+// row-major bf16 tile, lane i receives rows r0 .. r0 + 3 of column c0 + i:
+// a 4-deep MFMA operand fragment along the row index.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // Element loads/stores for the two storage types.
 template <typename TE> struct Elem;
 template <> struct Elem<float> {
@@ -50,5 +80,33 @@ template <> struct Elem<uint16_t> {
   __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
   __device__ __forceinline__ static void store(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
 };
+
+// One lane's D/8 consecutive elements of a row, widened to fp32, with one
+// vector load (bf16 D=64: 16 B; fp32 D=64: 32 B; fp32 D=32: 16 B).
+template <typename TE, int D>
+__device__ __forceinline__ void load_row_piece(const TE* p, float* x);
+
+template <>
+__device__ __forceinline__ void load_row_piece<uint16_t, 64>(const uint16_t* p, float* x) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(a[i] << 16);
+    x[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load_row_piece<float, 64>(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load_row_piece<float, 32>(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
 
 }  // namespace rel

@@ -30,34 +30,6 @@ constexpr int kUnroll = 4;    // slots per group per iteration (loads in flight)
 
 inline int num_splits(int n) { return (n + kChunk - 1) / kChunk; }
 
-// Vectorised row-piece loads: bf16 D=64 -> 16 B per lane; fp32 D=64 -> 32 B;
-// fp32 D=32 -> 16 B.
-template <typename TE, int D>
-__device__ __forceinline__ void load_piece(const TE* p, float* x);
-
-template <>
-__device__ __forceinline__ void load_piece<uint16_t, 64>(const uint16_t* p, float* x) {
-  const uint4 w = *reinterpret_cast<const uint4*>(p);
-  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(a[i] << 16);
-    x[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void load_piece<float, 64>(const float* p, float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-template <>
-__device__ __forceinline__ void load_piece<float, 32>(const float* p, float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-}
-
 // Partial record per (head, split): [m, l, z_0 .. z_{D-1}] in fp32, base-2
 // domain (m is a log2 stabiliser; l, z are scaled by 2^-m).
 template <typename TE, int D>
@@ -78,7 +50,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int c1 = min(n, c0 + chunk);
 
   float qv[E];
-  load_piece<TE, D>(q + static_cast<size_t>(head) * D + sub * E, qv);
+  load_row_piece<TE, D>(q + static_cast<size_t>(head) * D + sub * E, qv);
 #pragma unroll
   for (int e = 0; e < E; ++e) qv[e] *= qscale;
 
@@ -94,8 +66,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       const int slot = s0 + u * kGroups;
       ok[u] = slot < c1;
       const int sl = ok[u] ? slot : c0;  // in-range dummy for masked slots
-      load_piece<TE, D>(kc + cbase + static_cast<size_t>(sl) * D + sub * E, kx[u]);
-      load_piece<TE, D>(vc + cbase + static_cast<size_t>(sl) * D + sub * E, vx[u]);
+      load_row_piece<TE, D>(kc + cbase + static_cast<size_t>(sl) * D + sub * E, kx[u]);
+      load_row_piece<TE, D>(vc + cbase + static_cast<size_t>(sl) * D + sub * E, vx[u]);
     }
     float ev[kUnroll];
     float mx = m;

@@ -17,8 +17,14 @@
 //     last query blocks of every head first) and the linear block id keeps all
 //     query blocks of a head on the same XCD (ids differ by a multiple of the
 //     head count), so K / V of a head are shared through one L2.
-//   * Key / value tiles of 64 rows are staged in LDS (K row-major, V
-//     transposed) and prefetched into registers one tile ahead.
+//   * Key / value tiles of 64 rows are staged row-major in double-buffered
+//     LDS, loaded one tile ahead into registers, one barrier per tile; the
+//     V^T operand of the second contraction is fetched with the gfx950
+//     transposing LDS read.
+//   * Every tile before the workgroup's own query block is strictly
+//     historical for all its rows: those run a loop with no masking at all.
+//     Only the last two tiles (the block's diagonal) classify each 32-key
+//     sub-block per wave as historical, diagonal or beyond the causal range.
 //   * Per wave and 32-key sub-block: the score tile is computed transposed,
 //     S^T = K Q^T (32 keys x 32 queries), so that each lane holds 16 scores of
 //     ONE query (lane % 32) and the accumulator feeds the second MFMA,
@@ -49,22 +55,119 @@ constexpr int D = 64;
 constexpr int NW = 4;             // waves per workgroup
 constexpr int BM = 32 * NW;       // query rows per workgroup
 constexpr int BN = 64;            // keys per LDS tile
-constexpr int KS = D + 8;         // K tile row stride (bf16): 144 B, 16 B aligned
-constexpr int VS = BN + 4;        // V^T tile row stride (bf16): 136 B, 8 B aligned
+constexpr int KS = D + 8;         // K / V tile row stride (bf16): 144 B, 16 B aligned
 constexpr float kLazy = 8.0f;     // log2-domain slack before rescaling
 
-struct Smem {
-  uint16_t ks[BN * KS];
-  uint16_t vt[D * VS];
+struct Tile {
+  uint16_t ks[BN * KS];  // [key][d]
+  uint16_t vs[BN * KS];  // [key][d]
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Per-lane running state of one query row (this lane's half of the keys).
+struct RowState {
+  f32x16 acc0, acc1;  // Y^T: d in [0, 32) and [32, 64)
+  float m;            // log2-domain stabiliser (upper bound of E' up to 2^kLazy)
+  float lsum;         // sum of bf16(P) over this lane's keys
+  float uself;        // u'_ii, valid in the lane that met the diagonal
+  bool has_self;
+};
+
+// Score tile of 32-key sub-block `sb`: S^T = K Q^T. Element vi of the result
+// is key k0 + (vi>>2)*8 + hf*4 + (vi&3), query q0 + r (raw q . k).
+__device__ __forceinline__ f32x16 score(const Tile& tl, int sb, const bf16x8 (&qf)[4], int r,
+                                        int hf) {
+  f32x16 s = {0};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 kr = *reinterpret_cast<const uint4*>(&tl.ks[(sb * 32 + r) * KS + hf * 8 + 16 * c]);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr), qf[c], s, 0, 0, 0);
+  }
+  return s;
+}
+
+// Consumes the score tile `s` of sub-block `sb`: stabiliser update, P, row
+// sum and Y^T += V^T P^T. DIAG: the sub-block starts at the wave's first
+// query (k0 == q0); keys j >= i are masked and the Self score is captured.
+template <bool DIAG>
+__device__ __forceinline__ void consume(const Tile& tl, int sb, const f32x16& s, float qscale,
+                                        int r, int hf, RowState& st) {
+  float u[16];
+#pragma unroll
+  for (int vi = 0; vi < 16; ++vi) u[vi] = s[vi] * qscale;
+  if (DIAG) {
+    const int vself = ((r >> 3) << 2) + (r & 3);
+    const bool mine = hf == ((r >> 2) & 1);
+#pragma unroll
+    for (int vi = 0; vi < 16; ++vi) {
+      if (mine && vi == vself) st.uself = u[vi];
+      const int kk = (vi >> 2) * 8 + hf * 4 + (vi & 3);
+      if (kk >= r) u[vi] = -INFINITY;  // not strictly historical
+    }
+    st.has_self = mine;
+  }
+  float mx = fmaxf(fmaxf(u[0], u[1]), u[2]);
+#pragma unroll
+  for (int vi = 3; vi < 15; vi += 2) mx = fmaxf(fmaxf(mx, u[vi]), u[vi + 1]);
+  mx = fmaxf(mx, u[15]);
+  mx = max_across_halves(mx);
+  const bool grow = mx > st.m + kLazy;
+  if (__any(grow)) {  // rare: move the stabiliser, rescale this row
+    const float mn = grow ? mx : st.m;
+    const float a = fast_exp2(st.m - mn);
+    st.lsum *= a;
+#pragma unroll
+    for (int vi = 0; vi < 16; ++vi) {
+      st.acc0[vi] *= a;
+      st.acc1[vi] *= a;
+    }
+    st.m = mn;
+  }
+  uint32_t pw[8];
+  const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float p2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float x = u[2 * w + e];
+      const float sg = fast_rcp(1.0f + fast_exp2(-x));
+      float p = fast_exp2(fmaf(x, sg, -st.m));
+      if (DIAG) p = (x == -INFINITY) ? 0.f : p;
+      p2[e] = p;
+    }
+    pw[w] = pack_bf16x2(p2[0], p2[1]);
+    st.lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[w]), one2, st.lsum, false);
+  }
+  // Y^T += V^T P^T. k-slot hf*8 + e of step c <-> key c*16 + (e>>2)*8 +
+  // hf*4 + (e&3) of the sub-block, which is exactly element c*8 + e of P.
+  // V^T (d rows, those keys) by transposing reads: lane (l16, group) reads
+  // key row k0 + (l16>>2), columns d0 + 4*(l16&3), so lane i gets keys
+  // k0..k0+3 of column d0 + i; d0 = 32*db + 16*((lane>>4)&1) makes the
+  // column 32*db + (lane&31).
+  const int l16 = threadIdx.x & 15;
+  const int dcol = 16 * ((threadIdx.x >> 4) & 1) + 4 * (l16 & 3);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
+    const int o = (sb * 32 + c * 16 + hf * 4 + (l16 >> 2)) * KS + dcol;
+    const uint2 a0l = lds_read_tr16(&tl.vs[o]);
+    const uint2 a0h = lds_read_tr16(&tl.vs[o + 8 * KS]);
+    const uint2 a1l = lds_read_tr16(&tl.vs[o + 32]);
+    const uint2 a1h = lds_read_tr16(&tl.vs[o + 8 * KS + 32]);
+    st.acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        as_bf16x8(make_uint4(a0l.x, a0l.y, a0h.x, a0h.y)), pb, st.acc0, 0, 0, 0);
+    st.acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        as_bf16x8(make_uint4(a1l.x, a1l.y, a1h.x, a1h.y)), pb, st.acc1, 0, 0, 0);
+  }
+}
 
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ y, float* __restrict__ lse,
     float* __restrict__ gate, int T, int BH, int nqb, float qscale, float inv_tau, float lam) {
-  __shared__ Smem sm;
+  __shared__ Tile tiles[2];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -80,158 +183,96 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const bool wave_live = q0 < T;
 
   // ---- Q fragment: B operand of S^T = K Q^T. Lane holds query r,
-  // d = hf*8 + 16*s + [0, 8) for s = 0..3.
+  // d = hf*8 + 16*c + [0, 8) for c = 0..3.
   bf16x8 qf[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int c = 0; c < 4; ++c) {
     uint4 raw = make_uint4(0, 0, 0, 0);
-    if (qi < T) raw = *reinterpret_cast<const uint4*>(q + base + static_cast<size_t>(qi) * D + hf * 8 + 16 * s);
-    qf[s] = as_bf16x8(raw);
+    if (qi < T) raw = *reinterpret_cast<const uint4*>(q + base + static_cast<size_t>(qi) * D + hf * 8 + 16 * c);
+    qf[c] = as_bf16x8(raw);
   }
 
-  f32x16 acc0 = {0}, acc1 = {0};  // Y^T, d in [0, 32) and [32, 64), query r
-  float m = 0.f;                  // log2-domain stabiliser (upper bound of E')
-  float lsum = 0.f;               // row sum of bf16(P), this lane's half
-  float uself = 0.f;              // u'_ii, held by the lane that meets the diagonal
-  bool has_self = false;
+  RowState st;
+  st.acc0 = f32x16{0};
+  st.acc1 = f32x16{0};
+  st.m = 0.f;
+  st.lsum = 0.f;
+  st.uself = 0.f;
+  st.has_self = false;
 
   const int kend = min(T, (qb + 1) * BM);
   const int ntiles = (kend + BN - 1) / BN;
+  const int nfull = qb * (BM / BN);  // tiles that are history for every row
 
-  // ---- global -> register prefetch of one tile (K: 2 x 16 B; V: 2 rows x 16 B)
-  const int kc0 = tid, kc1 = tid + 256;  // K chunks: key = c >> 3, dchunk = c & 7
-  const int vkp = tid >> 3, vdc = tid & 7;  // V: key pair, dchunk
+  // ---- global -> register prefetch of one tile: K and V rows, 2 x 16 B
+  // chunks each per thread (chunk c: key c >> 3, d chunk c & 7)
+  const int kc0 = tid, kc1 = tid + 256;
   uint4 pk0, pk1, pv0, pv1;
   auto fetch = [&](int kt) {
     const int key0 = kt * BN + (kc0 >> 3), key1 = kt * BN + (kc1 >> 3);
-    pk0 = (key0 < T) ? *reinterpret_cast<const uint4*>(k + base + static_cast<size_t>(key0) * D + (kc0 & 7) * 8) : make_uint4(0, 0, 0, 0);
-    pk1 = (key1 < T) ? *reinterpret_cast<const uint4*>(k + base + static_cast<size_t>(key1) * D + (kc1 & 7) * 8) : make_uint4(0, 0, 0, 0);
-    const int vk0 = kt * BN + 2 * vkp, vk1 = vk0 + 1;
-    pv0 = (vk0 < T) ? *reinterpret_cast<const uint4*>(v + base + static_cast<size_t>(vk0) * D + vdc * 8) : make_uint4(0, 0, 0, 0);
-    pv1 = (vk1 < T) ? *reinterpret_cast<const uint4*>(v + base + static_cast<size_t>(vk1) * D + vdc * 8) : make_uint4(0, 0, 0, 0);
+    const size_t o0 = base + static_cast<size_t>(key0) * D + (kc0 & 7) * 8;
+    const size_t o1 = base + static_cast<size_t>(key1) * D + (kc1 & 7) * 8;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    pk0 = (key0 < T) ? *reinterpret_cast<const uint4*>(k + o0) : z;
+    pk1 = (key1 < T) ? *reinterpret_cast<const uint4*>(k + o1) : z;
+    pv0 = (key0 < T) ? *reinterpret_cast<const uint4*>(v + o0) : z;
+    pv1 = (key1 < T) ? *reinterpret_cast<const uint4*>(v + o1) : z;
   };
-  auto stash = [&]() {
-    *reinterpret_cast<uint4*>(&sm.ks[(kc0 >> 3) * KS + (kc0 & 7) * 8]) = pk0;
-    *reinterpret_cast<uint4*>(&sm.ks[(kc1 >> 3) * KS + (kc1 & 7) * 8]) = pk1;
-    const uint32_t a[4] = {pv0.x, pv0.y, pv0.z, pv0.w};
-    const uint32_t b[4] = {pv1.x, pv1.y, pv1.z, pv1.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // d = vdc*8 + 2i (low halves) and + 2i + 1 (high halves); keys 2kp, 2kp+1
-      const uint32_t lo = (a[i] & 0xffffu) | (b[i] << 16);
-      const uint32_t hi = (a[i] >> 16) | (b[i] & 0xffff0000u);
-      *reinterpret_cast<uint32_t*>(&sm.vt[(vdc * 8 + 2 * i) * VS + 2 * vkp]) = lo;
-      *reinterpret_cast<uint32_t*>(&sm.vt[(vdc * 8 + 2 * i + 1) * VS + 2 * vkp]) = hi;
-    }
+  auto stash = [&](Tile& tl) {
+    *reinterpret_cast<uint4*>(&tl.ks[(kc0 >> 3) * KS + (kc0 & 7) * 8]) = pk0;
+    *reinterpret_cast<uint4*>(&tl.ks[(kc1 >> 3) * KS + (kc1 & 7) * 8]) = pk1;
+    *reinterpret_cast<uint4*>(&tl.vs[(kc0 >> 3) * KS + (kc0 & 7) * 8]) = pv0;
+    *reinterpret_cast<uint4*>(&tl.vs[(kc1 >> 3) * KS + (kc1 & 7) * 8]) = pv1;
   };
 
   fetch(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();  // previous tile fully consumed
-    stash();
-    __syncthreads();
+  stash(tiles[0]);
+  __syncthreads();
+  int kt = 0;
+  // ---- strictly historical tiles: no masking
+  for (; kt < nfull; ++kt) {
     if (kt + 1 < ntiles) fetch(kt + 1);
-    if (!wave_live) continue;
-
+    const Tile& tl = tiles[kt & 1];
+    // both score tiles first: the second one's MFMAs run under the first
+    // one's VALU work, and the first P V under the second one's
+    const f32x16 s0 = score(tl, 0, qf, r, hf);
+    const f32x16 s1 = score(tl, 1, qf, r, hf);
+    consume<false>(tl, 0, s0, qscale, r, hf, st);
+    consume<false>(tl, 1, s1, qscale, r, hf, st);
+    if (kt + 1 < ntiles) stash(tiles[(kt + 1) & 1]);
+    __syncthreads();
+  }
+  // ---- the workgroup's own block: per-wave historical / diagonal / beyond
+  for (; kt < ntiles; ++kt) {
+    if (kt + 1 < ntiles) fetch(kt + 1);
+    const Tile& tl = tiles[kt & 1];
+    if (wave_live) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int k0 = kt * BN + sb * 32;
-      if (k0 > q0) break;  // whole sub-block beyond this wave's causal range
-      const bool diag = (k0 == q0);
-
-      // ---- S^T = K Q^T: A = K rows (key r, d = hf*8 + 16s + [0,8))
-      f32x16 st = {0};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 kr = *reinterpret_cast<const uint4*>(&sm.ks[(sb * 32 + r) * KS + hf * 8 + 16 * s]);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr), qf[s], st, 0, 0, 0);
-      }
-      // st[vi]: key = k0 + (vi>>2)*8 + hf*4 + (vi&3), query = q0 + r; to u'.
-#pragma unroll
-      for (int vi = 0; vi < 16; ++vi) st[vi] *= qscale;
-
-      // ---- diagonal sub-block: capture Self, mask j >= i
-      if (diag) {
-        const int vself = ((r >> 3) << 2) + (r & 3);
-        const bool mine = hf == ((r >> 2) & 1);
-#pragma unroll
-        for (int vi = 0; vi < 16; ++vi) {
-          const int kk = (vi >> 2) * 8 + hf * 4 + (vi & 3);
-          if (mine && vi == vself) uself = st[vi];
-          if (kk >= r) st[vi] = -INFINITY;  // not strictly historical
-        }
-        has_self = mine;
-      }
-
-      // ---- running stabiliser (lazy)
-      float mx = st[0];
-#pragma unroll
-      for (int vi = 1; vi < 16; ++vi) mx = fmaxf(mx, st[vi]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool grow = mx > m + kLazy;
-      if (__any(grow)) {
-        const float mn = grow ? mx : m;
-        const float a = fast_exp2(m - mn);
-        lsum *= a;
-#pragma unroll
-        for (int vi = 0; vi < 16; ++vi) {
-          acc0[vi] *= a;
-          acc1[vi] *= a;
-        }
-        m = mn;
-      }
-
-      // ---- P = exp2(E' - m'), E' = u' * sigmoid(U); masked entries -> 0
-      float pv[16];
-#pragma unroll
-      for (int vi = 0; vi < 16; ++vi) {
-        const float u = st[vi];
-        const float sg = fast_rcp(1.0f + fast_exp2(-u));
-        float p = fast_exp2(fmaf(u, sg, -m));
-        if (diag) p = (u == -INFINITY) ? 0.f : p;
-        pv[vi] = p;
-      }
-      uint32_t pw[8];
-      const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        pw[w] = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[w]), one2, lsum, false);
-      }
-      const bf16x8 pb[2] = {as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3])),
-                            as_bf16x8(make_uint4(pw[4], pw[5], pw[6], pw[7]))};
-
-      // ---- Y^T += V^T P^T. k-slot hf*8 + e of step c <-> key
-      // c*16 + (e>>2)*8 + hf*4 + (e&3), which is exactly st[c*8 + e].
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int kofs = sb * 32 + c * 16 + hf * 4;
-        const uint2 a0l = *reinterpret_cast<const uint2*>(&sm.vt[r * VS + kofs]);
-        const uint2 a0h = *reinterpret_cast<const uint2*>(&sm.vt[r * VS + kofs + 8]);
-        const uint2 a1l = *reinterpret_cast<const uint2*>(&sm.vt[(32 + r) * VS + kofs]);
-        const uint2 a1h = *reinterpret_cast<const uint2*>(&sm.vt[(32 + r) * VS + kofs + 8]);
-        const bf16x8 va0 = as_bf16x8(make_uint4(a0l.x, a0l.y, a0h.x, a0h.y));
-        const bf16x8 va1 = as_bf16x8(make_uint4(a1l.x, a1l.y, a1h.x, a1h.y));
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb[c], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb[c], acc1, 0, 0, 0);
+      for (int sb = 0; sb < 2; ++sb) {
+        const int k0 = kt * BN + sb * 32;
+        if (k0 < q0) consume<false>(tl, sb, score(tl, sb, qf, r, hf), qscale, r, hf, st);
+        else if (k0 == q0) consume<true>(tl, sb, score(tl, sb, qf, r, hf), qscale, r, hf, st);
       }
     }
+    if (kt + 1 < ntiles) stash(tiles[(kt + 1) & 1]);
+    __syncthreads();
   }
 
   if (!wave_live) return;
   // ---- row completion (App. A.3.5), base-2 domain
-  const float ltot = lsum + __shfl_xor(lsum, 32);
-  const float uo = __shfl_xor(uself, 32);
-  const float us = has_self ? uself : uo;
+  // cross-lane exchanges first, with every lane active, then select
+  const float ltot = sum_across_halves(st.lsum);
+  const float uo = other_half(st.uself);
+  const float us = st.has_self ? st.uself : uo;
   if (qi >= T) return;
   const float S = fast_rcp(1.0f + fast_exp2(-us * inv_tau));  // sigmoid(U_ii / tau)
   const float S2 = S * kLog2e;
   float g, lz;
   if (ltot > 0.f) {
-    const float A2 = m + fast_log2(ltot) - lam * fast_log2(static_cast<float>(qi + 1));
+    const float A2 = st.m + fast_log2(ltot) - lam * fast_log2(static_cast<float>(qi + 1));
     g = fast_rcp(1.0f + fast_exp2(S2 - A2));
     lz = kLn2 * (fmaxf(S2, A2) + fast_log2(1.0f + fast_exp2(-fabsf(S2 - A2))));
-  } else {
+  } else {  // row 1: empty history, A = -inf
     g = 0.f;
     lz = S;
   }
@@ -244,18 +285,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d0 = db * 32 + g4 * 8 + hf * 4;
       const uint2 vr = *reinterpret_cast<const uint2*>(v + row + d0);
-      const uint32_t w[2] = {vr.x, vr.y};
-      uint32_t o[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float z0 = (db == 0 ? acc0 : acc1)[g4 * 4 + 2 * j];
-        const float z1 = (db == 0 ? acc0 : acc1)[g4 * 4 + 2 * j + 1];
-        const float y0 = fmaf(gs, __uint_as_float(w[j] << 16), gl * z0);
-        const float y1 = fmaf(gs, __uint_as_float(w[j] & 0xffff0000u), gl * z1);
-        o[j] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
-               (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
-      }
-      *reinterpret_cast<uint2*>(y + row + d0) = make_uint2(o[0], o[1]);
+      const f32x16& acc = db == 0 ? st.acc0 : st.acc1;
+      const float y0 = fmaf(gs, __uint_as_float(vr.x << 16), gl * acc[g4 * 4 + 0]);
+      const float y1 = fmaf(gs, __uint_as_float(vr.x & 0xffff0000u), gl * acc[g4 * 4 + 1]);
+      const float y2 = fmaf(gs, __uint_as_float(vr.y << 16), gl * acc[g4 * 4 + 2]);
+      const float y3 = fmaf(gs, __uint_as_float(vr.y & 0xffff0000u), gl * acc[g4 * 4 + 3]);
+      *reinterpret_cast<uint2*>(y + row + d0) = make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
     }
   }
   if (hf == 0) {
