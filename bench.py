@@ -203,13 +203,47 @@ def bench_decode(rel, torch, dev, B=32, H=12, D=64, n0=4096, steps=256, cap=4352
             "call_GBps": byts / steps / (call_ms * 1e-3) / 1e9, "bytes": byts}
 
 
-def cpu_baseline(budget_s=20.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the step's
-    workload: whole heads of the 30M layer (T=2048), forward + backward, run
-    until about budget_s seconds are spent; scaled to TFLOP/s with the same
-    algorithmic count as the GPU."""
-    import numpy as np
+def bench_copy(torch, dev, nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size (torch's copy kernel): the
+    calibration for the FETCH_SIZE / WRITE_SIZE counters (reads nbytes and
+    writes nbytes per launch)."""
+    src = torch.ones(nbytes // 2, device=dev, dtype=torch.bfloat16)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    t = EventTimer(torch, stream)
+    for i in range(reps + 1):
+        s = t.start() if i >= 1 else None
+        dst.copy_(src)
+        if i >= 1:
+            t.stop(s)
+    ms = t.mean_ms()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms,
+            "GBps_rw": 2 * nbytes / (ms * 1e-3) / 1e9}
 
+
+def kernel_traffic(name):
+    """HBM bytes per launch of one kernel from the committed counter summary
+    (profiles/traffic.json), or None when the kernel's source has changed
+    since the counters were taken (the summary stores a hash of the source)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[name]
+        src = os.path.join(ROOT, "exchange_relation_amd", "csrc", rec["source"])
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+                return None
+        return rec["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(budget_s=15.0, max_heads=32):
+    """The fp64 oracle, as it stands, on a bounded sample of the step's
+    workload: whole heads of the 30M layer (T=2048, D=64), forward + backward
+    (materialised), run until about budget_s seconds are spent; scaled to
+    TFLOP/s with the same algorithmic count as the GPU."""
     import oracle
     from workloads import make_inputs
     try:
@@ -217,20 +251,19 @@ def cpu_baseline(budget_s=20.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    inp = make_inputs(1, 4, 2048, 64, "bf16", seed=42, with_dy=True)
-    f64 = {n: inp[n].double().numpy() for n in ("q", "k", "v", "dy")}
-    scale = 1 / 8
+    inp = make_inputs(1, max_heads, 2048, 64, "bf16", seed=42, with_dy=True)
+    f64 = {n: inp[n][0].double().numpy() for n in ("q", "k", "v", "dy")}
     heads, t0 = 0, time.perf_counter()
-    while heads < 4 and (time.perf_counter() - t0) < budget_s:
-        oracle.relation_backward_head(f64["q"][0, heads], f64["k"][0, heads], f64["v"][0, heads],
-                                      f64["dy"][0, heads], scale, 2.0, inp["lam"])
+    while heads < max_heads and (time.perf_counter() - t0) < budget_s:
+        oracle.relation_backward_head(f64["q"][heads], f64["k"][heads], f64["v"][heads],
+                                      f64["dy"][heads], 1 / 8, 2.0, inp["lam"])
         heads += 1
     dt = time.perf_counter() - t0
     flops = 3.5 * fwd_flops(1, heads, 2048, 64)
-    del np
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} whole heads of the B=16,H=8,T=2048,D=64 layer, fwd+bwd "
-                      f"(materialised fp64 numpy), {dt:.1f} s; cpu_count={os.cpu_count()}"}
+            "sample": f"{heads} whole heads (of 128) of the B=16,H=8,T=2048,D=64 layer, "
+                      f"fwd+bwd, materialised fp64 numpy, {dt:.1f} s; "
+                      f"host cpu_count={os.cpu_count()}"}
 
 
 def main():
@@ -240,8 +273,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["step", "fwd", "decode", "attn"], default=None,
-                    help="run one measurement and print its raw numbers")
+    ap.add_argument("--only", choices=["step", "fwd", "decode", "attn", "copy"], default=None,
+                    help="run one measurement and print its raw numbers ('copy': a plain "
+                         "device copy of known size, the HBM-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -257,6 +291,9 @@ def main():
     torch.cuda.set_device(dev)
     torch.manual_seed(0)
 
+    if args.only == "copy":
+        print(json.dumps(bench_copy(torch, dev)))
+        return
     if args.only == "step":
         print(json.dumps(bench_step(rel, torch, dev, args.steps, args.warmup)))
         return
@@ -286,10 +323,12 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "relation_bwd call (dq zero-fill + "
                      "bwd_bf16_kernel + dq finalize; preprocess)",
                      "achieved": bwd_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": bwd_tf / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": bwd_tf / PEAK_BF16_TFLOPS,
+                     "traffic": kernel_traffic("bwd_bf16_kernel@layer30m")},
         "roofline_fwd": {"bound": "mfma", "kernel": "fwd_bf16_kernel (one launch per call)",
                          "achieved": fwd_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": fwd_tf / PEAK_BF16_TFLOPS, "traffic": None},
+                         "frac": fwd_tf / PEAK_BF16_TFLOPS,
+                         "traffic": kernel_traffic("fwd_bf16_kernel@layer30m")},
         "fwd_ms": st["fwd_ms"], "bwd_ms": st["bwd_ms"],
     }
     if not args.no_extra:
@@ -301,7 +340,8 @@ def main():
         rec["roofline_decode"] = {"bound": "hbm", "kernel": "relation_cache_decode call "
                                   "(split scan + combine)", "achieved": dec["call_GBps"],
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": dec["call_GBps"] / PEAK_HBM_GBS, "traffic": None}
+                                  "frac": dec["call_GBps"] / PEAK_HBM_GBS,
+                                  "traffic": kernel_traffic("decode_split_kernel@cache4096")}
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
