@@ -12,7 +12,7 @@
 //           dU = dR S (1 - S) / tau
 //   dV = F^T G,  dK = scale dU^T Q,  dQ = scale dU K     (MFMA)
 //
-// Work decomposition: a workgroup of 4 waves owns 128 keys of one (b, h),
+// Work decomposition: a workgroup of 8 waves owns 256 keys of one (b, h),
 // each wave 32 keys, and loops over 64-query tiles from its first key to T
 // (first key blocks, i.e. the longest loops, are dispatched first; all key
 // blocks of a head share an XCD). Scores are computed as S = Q K^T with keys
@@ -21,13 +21,15 @@
 // dK accumulate in registers for the whole loop. All tiles sit in LDS
 // row-major; the transposed operands (G^T, Q^T, and the dQ operands) are
 // fetched with the gfx950 transposing LDS read, so nothing is stored twice.
-// dQ needs the sum over the workgroup's 128 keys: each wave stores its dU
-// tile (keys x queries, 8-byte rows of 4 queries), and after a barrier wave w
-// forms dQ[:, 16w : 16w + 16] for the tile's 64 queries with 16x16x32 MFMAs
+// dQ needs the sum over the workgroup's 256 keys: each wave stores its dU
+// tile (keys x queries, 8-byte rows of 4 queries), and after a barrier each
+// wave forms a 32-query x 16-d share of the tile's dQ with 16x16x32 MFMAs
 // (its K fragments stay in registers for the whole kernel) and adds it into
 // an fp32 accumulator with hardware float atomics, 16 consecutive floats per
-// instruction. A finalize kernel scales and rounds dQ to bf16. dL/dlambda
-// and Dr come from the shared preprocess.
+// instruction. The wide key block halves those atomics (they resolve at
+// memory across XCDs) relative to 128-key blocks. A finalize kernel scales and rounds dQ to bf16 and reduces
+// the dL/dlambda partials; Dr and those partials come from the shared
+// preprocess.
 //
 // Scores use the base-2 domain as in the forward: the fp32 accumulator of
 // q . k is multiplied by scale * log2(e), u' = U log2(e), so
@@ -41,9 +43,15 @@
 namespace rel {
 namespace bwdbf16 {
 
+#ifndef REL_BWD_WAVES
+#define REL_BWD_WAVES 8
+#endif
 constexpr int D = 64;
-constexpr int NW = 4;
-constexpr int BK = 32 * NW;  // keys per workgroup
+constexpr int NW = REL_BWD_WAVES;  // waves per workgroup (4 or 8)
+constexpr int NT = 64 * NW;        // threads per workgroup
+constexpr int BK = 32 * NW;        // keys per workgroup
+constexpr int QBW = 4 * 4 / NW;    // 16-query blocks of the dQ tile per wave (4 or 2)
+constexpr int KST = BK / 32;       // 32-key steps of the dQ contraction
 constexpr int BQ = 64;       // queries per tile
 constexpr int RS = D + 8;    // row-major q / dY / K tile stride (bf16): 144 B
 constexpr int US = BQ + 8;   // dU^T tile stride (bf16): 144 B
@@ -63,7 +71,7 @@ __device__ __forceinline__ bf16x8 cat(uint2 a, uint2 b) {
   return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 
-__global__ __launch_bounds__(256, 2) void bwd_bf16_kernel(
+__global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
     const float* __restrict__ lse, const float* __restrict__ Dr, float* __restrict__ dq_acc,
@@ -97,38 +105,44 @@ __global__ __launch_bounds__(256, 2) void bwd_bf16_kernel(
     kf[c] = as_bf16x8(kr4);
     vf[c] = as_bf16x8(vr4);
   }
-  // ---- the workgroup's 128 key rows to LDS (zero past T)
+  // ---- the workgroup's key rows to LDS (zero past T)
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int c = tid + 256 * pass;  // 1024 chunks of 16 B
+  for (int pass = 0; pass < BK * 8 / NT; ++pass) {
+    const int c = tid + NT * pass;  // chunks of 16 B
     const int key = kb * BK + (c >> 3);
     const uint4 x = (key < T) ? *reinterpret_cast<const uint4*>(k + base + static_cast<size_t>(key) * D + (c & 7) * 8) : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(&sm.kr[(c >> 3) * RS + (c & 7) * 8]) = x;
   }
   __syncthreads();
-  // ---- this wave's dQ B operand (K rows, d in [16 wave, 16 wave + 16)) for
-  // all 128 keys, kept in registers: k-slot e of step st <-> key
-  // 32 st + 8 g16 + e, column d = 16 wave + l16
-  bf16x8 kq[4];
+  // ---- this wave's dQ B operand (K rows, d in [16 dw, 16 dw + 16)) for all
+  // the workgroup's keys, kept in registers: k-slot e of step st <-> key
+  // 32 st + 8 g16 + e, column d = 16 dw + l16
+  const int dw = wave & 3;         // d block of this wave's dQ share
+  const int qw = (wave >> 2) * QBW;  // first 16-query block of this wave's dQ share
+  bf16x8 kq[KST];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
+  for (int st = 0; st < KST; ++st) {
     const int k0 = st * 32 + g16 * 8 + (l16 >> 2);
-    const int d0 = wave * 16 + 4 * (l16 & 3);
+    const int d0 = dw * 16 + 4 * (l16 & 3);
     kq[st] = cat(lds_read_tr16(&sm.kr[k0 * RS + d0]), lds_read_tr16(&sm.kr[(k0 + 4) * RS + d0]));
   }
 
   f32x16 dv0 = {0}, dv1 = {0}, dk0 = {0}, dk1 = {0};  // dV^T, dK^T: key r, d rows
 
-  // ---- query tile prefetch: q and dY rows, 2 x 16 B chunks each per thread
-  const int c0 = tid, c1 = tid + 256;  // chunk: row = c >> 3, dchunk = c & 7
-  uint4 pq0, pq1, pg0, pg1;
+  // ---- query tile prefetch: q and dY rows, 16 B chunks (2 per thread with 4
+  // waves, 1 with 8; chunk c: row c >> 3, d chunk c & 7)
+  constexpr int NCH = BQ * 8 / NT;
+  const int c0 = tid, c1 = tid + NT;
+  uint4 pq0, pq1 = make_uint4(0, 0, 0, 0), pg0, pg1 = make_uint4(0, 0, 0, 0);
   float pc = 0.f, pl = 0.f, pd = 0.f;
   auto fetch = [&](int qt0) {
     const int i0 = qt0 + (c0 >> 3), i1 = qt0 + (c1 >> 3);
     pq0 = (i0 < T) ? *reinterpret_cast<const uint4*>(q + base + static_cast<size_t>(i0) * D + (c0 & 7) * 8) : make_uint4(0, 0, 0, 0);
-    pq1 = (i1 < T) ? *reinterpret_cast<const uint4*>(q + base + static_cast<size_t>(i1) * D + (c1 & 7) * 8) : make_uint4(0, 0, 0, 0);
     pg0 = (i0 < T) ? *reinterpret_cast<const uint4*>(dy + base + static_cast<size_t>(i0) * D + (c0 & 7) * 8) : make_uint4(0, 0, 0, 0);
-    pg1 = (i1 < T) ? *reinterpret_cast<const uint4*>(dy + base + static_cast<size_t>(i1) * D + (c1 & 7) * 8) : make_uint4(0, 0, 0, 0);
+    if (NCH > 1) {
+      pq1 = (i1 < T) ? *reinterpret_cast<const uint4*>(q + base + static_cast<size_t>(i1) * D + (c1 & 7) * 8) : make_uint4(0, 0, 0, 0);
+      pg1 = (i1 < T) ? *reinterpret_cast<const uint4*>(dy + base + static_cast<size_t>(i1) * D + (c1 & 7) * 8) : make_uint4(0, 0, 0, 0);
+    }
     if (tid < BQ) {
       const int i = qt0 + tid;
       if (i < T) {
@@ -145,9 +159,11 @@ __global__ __launch_bounds__(256, 2) void bwd_bf16_kernel(
   };
   auto stash = [&](int b) {
     *reinterpret_cast<uint4*>(&sm.qr[b][(c0 >> 3) * RS + (c0 & 7) * 8]) = pq0;
-    *reinterpret_cast<uint4*>(&sm.qr[b][(c1 >> 3) * RS + (c1 & 7) * 8]) = pq1;
     *reinterpret_cast<uint4*>(&sm.gr[b][(c0 >> 3) * RS + (c0 & 7) * 8]) = pg0;
-    *reinterpret_cast<uint4*>(&sm.gr[b][(c1 >> 3) * RS + (c1 & 7) * 8]) = pg1;
+    if (NCH > 1) {
+      *reinterpret_cast<uint4*>(&sm.qr[b][(c1 >> 3) * RS + (c1 & 7) * 8]) = pq1;
+      *reinterpret_cast<uint4*>(&sm.gr[b][(c1 >> 3) * RS + (c1 & 7) * 8]) = pg1;
+    }
     if (tid < BQ) {
       sm.cq[b][tid] = pc;
       sm.lq[b][tid] = pl;
@@ -264,29 +280,32 @@ __global__ __launch_bounds__(256, 2) void bwd_bf16_kernel(
     }
     __syncthreads();  // dU^T complete; q / dY of this tile no longer read
 
-    // ---- dQ[qt0 .. qt0+63][16 wave .. +15] += dU (64 x 128) K (128 x 16).
-    // A operand (16x16x32: query l16, keys 8 g16 + e of step st) by
-    // transposing reads of dU^T: lane (l16, g16) reads key row
-    // 32 st + 8 g16 + (l16>>2) (+4), columns 16 qb + 4 (l16&3).
+    // ---- dQ[16-query blocks qw .. qw+QBW-1][16 dw .. +15] +=
+    // dU (those queries x BK keys) K (BK keys x 16). A operand (16x16x32:
+    // query l16, keys 8 g16 + e of step st) by transposing reads of dU^T:
+    // lane (l16, g16) reads key row 32 st + 8 g16 + (l16>>2) (+4), columns
+    // 16 qb + 4 (l16&3).
     {
-      f32x4 aq[4] = {{0}, {0}, {0}, {0}};
+      f32x4 aq[QBW];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int b = 0; b < QBW; ++b) aq[b] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < KST; ++st) {
         const int krow = st * 32 + g16 * 8 + (l16 >> 2);
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const int o = krow * US + qb * 16 + 4 * (l16 & 3);
+        for (int b = 0; b < QBW; ++b) {
+          const int o = krow * US + (qw + b) * 16 + 4 * (l16 & 3);
           const bf16x8 a = cat(lds_read_tr16(&sm.ut[o]), lds_read_tr16(&sm.ut[o + 4 * US]));
-          aq[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kq[st], aq[qb], 0, 0, 0);
+          aq[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kq[st], aq[b], 0, 0, 0);
         }
       }
-      // aq[qb][j]: query qt0 + 16 qb + 4 g16 + j, d = 16 wave + l16
+      // aq[b][j]: query qt0 + 16 (qw + b) + 4 g16 + j, d = 16 dw + l16
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
+      for (int b = 0; b < QBW; ++b) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int i = qt0 + qb * 16 + g16 * 4 + j;
-          if (i < T) unsafeAtomicAdd(dq_acc + base + static_cast<size_t>(i) * D + wave * 16 + l16, aq[qb][j]);
+          const int i = qt0 + (qw + b) * 16 + g16 * 4 + j;
+          if (i < T) unsafeAtomicAdd(dq_acc + base + static_cast<size_t>(i) * D + dw * 16 + l16, aq[b][j]);
         }
       }
     }
@@ -313,13 +332,29 @@ __global__ __launch_bounds__(256, 2) void bwd_bf16_kernel(
   }
 }
 
+// dq = bf16(scale * accumulator); workgroup 0 also sums the dL/dlambda
+// partials of the preprocess in a fixed order (deterministic).
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float4* __restrict__ acc,
                                                           uint2* __restrict__ dq, size_t n4,
-                                                          float scale) {
+                                                          float scale,
+                                                          const float* __restrict__ part,
+                                                          int npart, float* __restrict__ dlambda) {
   for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
        i += static_cast<size_t>(gridDim.x) * 256) {
     const float4 a = acc[i];
     dq[i] = make_uint2(pack_bf16x2(a.x * scale, a.y * scale), pack_bf16x2(a.z * scale, a.w * scale));
+  }
+  if (blockIdx.x == 0 && dlambda) {
+    __shared__ float red[256];
+    float s = 0.f;
+    for (int i = threadIdx.x; i < npart; i += 256) s += part[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) *dlambda = red[0];
   }
 }
 
@@ -336,20 +371,20 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
   float* dq_acc = reinterpret_cast<float*>(wsb + w.off_dq);
   const size_t n4 = static_cast<size_t>(B) * H * T * D / 4;
   const unsigned eg = static_cast<unsigned>(n4 < 4096 * 256 ? (n4 + 255) / 256 : 4096);
-  hipError_t e = launch_bwd_pre(1, B, H, T, D, q, k, v, y, dy, lse, dlambda, w, wsb, scale, tau,
+  hipError_t e = launch_bwd_pre(1, B, H, T, D, q, k, v, y, dy, lse, nullptr, w, wsb, scale, tau,
                                 stream);
   if (e != hipSuccess) return e;
   const float* Dr = reinterpret_cast<const float*>(wsb + w.off_dr);
   const int BH = B * H;
   const int nkb = (T + BK - 1) / BK;
-  hipLaunchKernelGGL(bwd_bf16_kernel, dim3(static_cast<unsigned>(nkb) * BH), dim3(256), 0,
+  hipLaunchKernelGGL(bwd_bf16_kernel, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
                      stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e, scale,
                      1.0f / tau, lam);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(dq_finalize_kernel, dim3(eg), dim3(256), 0, stream,
                      reinterpret_cast<const float4*>(dq_acc), reinterpret_cast<uint2*>(dq), n4,
-                     scale);
+                     scale, reinterpret_cast<const float*>(wsb + w.off_part), w.npart, dlambda);
   return hipGetLastError();
 }
 

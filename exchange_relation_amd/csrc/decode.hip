@@ -14,8 +14,10 @@
 // load: fully coalesced streaming. Groups interleave over the chunk and keep
 // their own (m, l, z); the 32 group states are merged in LDS and one partial
 // per chunk goes to the workspace. This kernel is HBM-bound by design.
-// Kernel 2 (combine): one 64-lane workgroup per (b, h) merges the chunk
-// partials, adds Self, writes y / gate and appends k_new / v_new.
+// The first split workgroup of each (b, h) also appends k_new / v_new to slot
+// n_hist (no split reads that slot).
+// Kernel 2 (combine): one 64-lane wave per (b, h) merges the chunk partials
+// (every partial load issued up front), adds Self and writes y / gate.
 #include <math.h>
 
 #include "common.hpp"
@@ -24,9 +26,16 @@
 namespace rel {
 namespace dec {
 
-constexpr int kChunk = 512;   // target slots per split workgroup
-constexpr int kGroups = 32;   // 8-lane groups per 256-lane workgroup
-constexpr int kUnroll = 4;    // slots per group per iteration (loads in flight)
+#ifndef REL_DECODE_CHUNK
+#define REL_DECODE_CHUNK 512
+#endif
+#ifndef REL_DECODE_UNROLL
+#define REL_DECODE_UNROLL 8
+#endif
+constexpr int kChunk = REL_DECODE_CHUNK;    // target slots per split workgroup
+constexpr int kGroups = 32;                 // 8-lane groups per 256-lane workgroup
+constexpr int kUnroll = REL_DECODE_UNROLL;  // slots per group per iteration (loads in flight)
+constexpr int kBatch = 8;                   // partials loaded at once by the combine
 
 inline int num_splits(int n) { return (n + kChunk - 1) / kChunk; }
 
@@ -34,8 +43,9 @@ inline int num_splits(int n) { return (n + kChunk - 1) / kChunk; }
 // domain (m is a log2 stabiliser; l, z are scaled by 2^-m).
 template <typename TE, int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(
-    const TE* __restrict__ q, const TE* __restrict__ kc, const TE* __restrict__ vc,
-    float* __restrict__ part, int capacity, int n, int nsplit, int chunk, float qscale) {
+    const TE* __restrict__ q, const TE* __restrict__ kn, const TE* __restrict__ vn,
+    TE* __restrict__ kc, TE* __restrict__ vc, float* __restrict__ part, int capacity, int n,
+    int nsplit, int chunk, float qscale) {
   constexpr int E = D / 8;
   __shared__ float s_m[kGroups], s_l[kGroups];
   __shared__ float s_z[kGroups][D + 1];
@@ -48,6 +58,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const size_t cbase = static_cast<size_t>(head) * capacity * D;
   const int c0 = split * chunk;
   const int c1 = min(n, c0 + chunk);
+  if (split == 0 && tid < D) {  // append: exact copy of the new token into slot n
+    const size_t slot = cbase + static_cast<size_t>(n) * D + tid;
+    kc[slot] = kn[static_cast<size_t>(head) * D + tid];
+    vc[slot] = vn[static_cast<size_t>(head) * D + tid];
+  }
 
   float qv[E];
   load_row_piece<TE, D>(q + static_cast<size_t>(head) * D + sub * E, qv);
@@ -140,6 +155,13 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   const float qd = act ? Elem<TE>::load(q + hv + tid) : 0.f;
   const float kd = act ? Elem<TE>::load(kn + hv + tid) : 0.f;
   const float vd = act ? Elem<TE>::load(vn + hv + tid) : 0.f;
+  if (nsplit == 0) {  // no history: the append was not done by a split kernel
+    if (act) {
+      const size_t slot = (static_cast<size_t>(head) * capacity + n) * D + tid;
+      kc[slot] = kn[hv + tid];
+      vc[slot] = vn[hv + tid];
+    }
+  }
 
   // Self: u'_ii = scale*log2(e) * q . k_new
   float us = qd * kd;
@@ -147,17 +169,34 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   for (int o = 32; o >= 1; o >>= 1) us += __shfl_xor(us, o);
   us *= qscale;
 
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s)
-    M = fmaxf(M, part[(static_cast<size_t>(head) * nsplit + s) * (D + 2)]);
-  float Ls = 0.f, Z = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float* pr = part + (static_cast<size_t>(head) * nsplit + s) * (D + 2);
-      const float w = fast_exp2(pr[0] - M);
-      Ls = fmaf(w, pr[1], Ls);
-      if (act) Z = fmaf(w, pr[2 + tid], Z);
+  // merge the chunk partials (App. A.3.2), kBatch partials per round with
+  // all their loads issued before any is used
+  float M = -INFINITY, Ls = 0.f, Z = 0.f;
+  const float* ph = part + static_cast<size_t>(head) * nsplit * (D + 2);
+  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+    float pm[kBatch], pl[kBatch], pz[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const bool ok = s0 + b < nsplit;
+      const float* pr = ph + static_cast<size_t>(ok ? s0 + b : 0) * (D + 2);
+      pm[b] = ok ? pr[0] : -INFINITY;
+      pl[b] = ok ? pr[1] : 0.f;
+      pz[b] = (ok && act) ? pr[2 + tid] : 0.f;
     }
+    float Mn = M;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) Mn = fmaxf(Mn, pm[b]);
+    if (Mn == -INFINITY) continue;  // nothing yet
+    const float a = fast_exp2(M - Mn);  // M = -inf -> 0
+    Ls *= a;
+    Z *= a;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const float w = fast_exp2(pm[b] - Mn);  // -inf -> 0
+      Ls = fmaf(w, pl[b], Ls);
+      Z = fmaf(w, pz[b], Z);
+    }
+    M = Mn;
   }
   const float S = fast_rcp(1.0f + fast_exp2(-us * inv_tau));  // sigmoid(U_ii / tau)
   float g = 0.f;
@@ -166,13 +205,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     g = fast_rcp(1.0f + fast_exp2(S * kLog2e - A2));
   }
   const float yd = (1.0f - g) * vd + ((Ls > 0.f) ? g * Z * fast_rcp(Ls) : 0.f);
-  if (act) {
-    Elem<TE>::store(y + hv + tid, yd);
-    // append: exact copy of the new token's k and v into slot n
-    const size_t slot = (static_cast<size_t>(head) * capacity + n) * D + tid;
-    kc[slot] = kn[hv + tid];
-    vc[slot] = vn[hv + tid];
-  }
+  if (act) Elem<TE>::store(y + hv + tid, yd);
   if (tid == 0 && gate) gate[head] = g;
 }
 
@@ -189,8 +222,9 @@ hipError_t run(int BH, const void* q, const void* k_new, const void* v_new, void
     nsplit = (n + chunk - 1) / chunk;
     hipLaunchKernelGGL((decode_split_kernel<TE, D>), dim3(static_cast<unsigned>(nsplit) * BH),
                        dim3(256), 0, stream, static_cast<const TE*>(q),
-                       static_cast<const TE*>(k_cache), static_cast<const TE*>(v_cache), part,
-                       capacity, n, nsplit, chunk, qscale);
+                       static_cast<const TE*>(k_new), static_cast<const TE*>(v_new),
+                       static_cast<TE*>(k_cache), static_cast<TE*>(v_cache), part, capacity, n,
+                       nsplit, chunk, qscale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
