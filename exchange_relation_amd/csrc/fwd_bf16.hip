@@ -17,12 +17,16 @@
 //     last query blocks of every head first) and the linear block id keeps all
 //     query blocks of a head on the same XCD (ids differ by a multiple of the
 //     head count), so K / V of a head are shared through one L2.
-//   * Key / value tiles of 64 rows are staged row-major in double-buffered
-//     LDS, loaded one tile ahead into registers, one barrier per tile; the
-//     V^T operand of the second contraction is fetched with the gfx950
+//   * Key / value tiles of 64 rows are staged row-major in LDS from
+//     registers loaded ahead, one barrier per tile: K in a ring of three
+//     (tiles t and t+1 resident while t+2 lands), V double-buffered. The V^T
+//     operand of the second contraction is fetched with the gfx950
 //     transposing LDS read.
 //   * Every tile before the workgroup's own query block is strictly
-//     historical for all its rows: those run a loop with no masking at all.
+//     historical for all its rows: those run a loop with no masking at all,
+//     software-pipelined so that a wave's score MFMAs for the next 32 keys
+//     are in flight while it works through the exponentials of the current
+//     32 (the matrix unit and the VALU otherwise take turns).
 //     Only the last two tiles (the block's diagonal) classify each 32-key
 //     sub-block per wave as historical, diagonal or beyond the causal range.
 //   * Per wave and 32-key sub-block: the score tile is computed transposed,
@@ -55,13 +59,9 @@ constexpr int D = 64;
 constexpr int NW = 4;             // waves per workgroup
 constexpr int BM = 32 * NW;       // query rows per workgroup
 constexpr int BN = 64;            // keys per LDS tile
-constexpr int KS = D + 8;         // K / V tile row stride (bf16): 144 B, 16 B aligned
+constexpr int KS = D + 8;         // K tile row stride (bf16): 144 B, 16 B aligned
+constexpr int VS = D + 8;         // V tile row stride (bf16)
 constexpr float kLazy = 8.0f;     // log2-domain slack before rescaling
-
-struct Tile {
-  uint16_t ks[BN * KS];  // [key][d]
-  uint16_t vs[BN * KS];  // [key][d]
-};
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -69,50 +69,55 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast
 struct RowState {
   f32x16 acc0, acc1;  // Y^T: d in [0, 32) and [32, 64)
   float m;            // log2-domain stabiliser (upper bound of E' up to 2^kLazy)
+  float mlim;         // m + kLazy
   float lsum;         // sum of bf16(P) over this lane's keys
   float uself;        // u'_ii, valid in the lane that met the diagonal
   bool has_self;
 };
 
-// Score tile of 32-key sub-block `sb`: S^T = K Q^T. Element vi of the result
-// is key k0 + (vi>>2)*8 + hf*4 + (vi&3), query q0 + r (raw q . k).
-__device__ __forceinline__ f32x16 score(const Tile& tl, int sb, const bf16x8 (&qf)[4], int r,
+// Score tile of 32-key sub-block `sb` of the K tile at `ks`: S^T = K Q^T.
+// Element vi of the result is key k0 + (vi>>2)*8 + hf*4 + (vi&3), query
+// q0 + r (raw q . k).
+__device__ __forceinline__ f32x16 score(const uint16_t* ks, int sb, const bf16x8 (&qf)[4], int r,
                                         int hf) {
+  bf16x8 kr[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    kr[c] = as_bf16x8(*reinterpret_cast<const uint4*>(&ks[(sb * 32 + r) * KS + hf * 8 + 16 * c]));
   f32x16 s = {0};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint4 kr = *reinterpret_cast<const uint4*>(&tl.ks[(sb * 32 + r) * KS + hf * 8 + 16 * c]);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr), qf[c], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[c], qf[c], s, 0, 0, 0);
   }
   return s;
 }
 
-// Consumes the score tile `s` of sub-block `sb`: stabiliser update, P, row
-// sum and Y^T += V^T P^T. DIAG: the sub-block starts at the wave's first
-// query (k0 == q0); keys j >= i are masked and the Self score is captured.
+// First half of consuming a score tile: scaling to u' (in place); DIAG (the
+// sub-block starts at the wave's first query, k0 == q0) masks keys j >= i
+// and captures the Self score; then the stabiliser moves if the tile's
+// largest bound exceeds it by more than kLazy (rare), rescaling the row's
+// accumulators.
 template <bool DIAG>
-__device__ __forceinline__ void consume(const Tile& tl, int sb, const f32x16& s, float qscale,
-                                        int r, int hf, RowState& st) {
-  float u[16];
+__device__ __forceinline__ void stabilise(f32x16& s, float qscale, int r, int hf, RowState& st) {
 #pragma unroll
-  for (int vi = 0; vi < 16; ++vi) u[vi] = s[vi] * qscale;
+  for (int vi = 0; vi < 16; ++vi) s[vi] *= qscale;
   if (DIAG) {
     const int vself = ((r >> 3) << 2) + (r & 3);
     const bool mine = hf == ((r >> 2) & 1);
 #pragma unroll
     for (int vi = 0; vi < 16; ++vi) {
-      if (mine && vi == vself) st.uself = u[vi];
+      if (mine && vi == vself) st.uself = s[vi];
       const int kk = (vi >> 2) * 8 + hf * 4 + (vi & 3);
-      if (kk >= r) u[vi] = -INFINITY;  // not strictly historical
+      if (kk >= r) s[vi] = -INFINITY;  // not strictly historical
     }
     st.has_self = mine;
   }
-  float mx = fmaxf(fmaxf(u[0], u[1]), u[2]);
+  float mx = vmax(vmax(s[0], s[1]), s[2]);
 #pragma unroll
-  for (int vi = 3; vi < 15; vi += 2) mx = fmaxf(fmaxf(mx, u[vi]), u[vi + 1]);
-  mx = fmaxf(mx, u[15]);
+  for (int vi = 3; vi < 15; vi += 2) mx = vmax(vmax(mx, s[vi]), s[vi + 1]);
+  mx = vmax(mx, s[15]);
   mx = max_across_halves(mx);
-  const bool grow = mx > st.m + kLazy;
+  const bool grow = mx > st.mlim;
   if (__any(grow)) {  // rare: move the stabiliser, rescale this row
     const float mn = grow ? mx : st.m;
     const float a = fast_exp2(st.m - mn);
@@ -123,7 +128,15 @@ __device__ __forceinline__ void consume(const Tile& tl, int sb, const f32x16& s,
       st.acc1[vi] *= a;
     }
     st.m = mn;
+    st.mlim = mn + kLazy;
   }
+}
+
+// Second half: P = exp(E - m) in bf16, the row sum, and Y^T += V^T P^T with
+// the V tile at `vs`.
+template <bool DIAG>
+__device__ __forceinline__ void accumulate(const uint16_t* vs, int sb, const f32x16& s, int hf,
+                                           RowState& st) {
   uint32_t pw[8];
   const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
@@ -131,7 +144,7 @@ __device__ __forceinline__ void consume(const Tile& tl, int sb, const f32x16& s,
     float p2[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const float x = u[2 * w + e];
+      const float x = s[2 * w + e];
       const float sg = fast_rcp(1.0f + fast_exp2(-x));
       float p = fast_exp2(fmaf(x, sg, -st.m));
       if (DIAG) p = (x == -INFINITY) ? 0.f : p;
@@ -151,11 +164,11 @@ __device__ __forceinline__ void consume(const Tile& tl, int sb, const f32x16& s,
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
-    const int o = (sb * 32 + c * 16 + hf * 4 + (l16 >> 2)) * KS + dcol;
-    const uint2 a0l = lds_read_tr16(&tl.vs[o]);
-    const uint2 a0h = lds_read_tr16(&tl.vs[o + 8 * KS]);
-    const uint2 a1l = lds_read_tr16(&tl.vs[o + 32]);
-    const uint2 a1h = lds_read_tr16(&tl.vs[o + 8 * KS + 32]);
+    const int o = (sb * 32 + c * 16 + hf * 4 + (l16 >> 2)) * VS + dcol;
+    const uint2 a0l = lds_read_tr16(&vs[o]);
+    const uint2 a0h = lds_read_tr16(&vs[o + 8 * VS]);
+    const uint2 a1l = lds_read_tr16(&vs[o + 32]);
+    const uint2 a1h = lds_read_tr16(&vs[o + 8 * VS + 32]);
     st.acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         as_bf16x8(make_uint4(a0l.x, a0l.y, a0h.x, a0h.y)), pb, st.acc0, 0, 0, 0);
     st.acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -163,11 +176,12 @@ __device__ __forceinline__ void consume(const Tile& tl, int sb, const f32x16& s,
   }
 }
 
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ y, float* __restrict__ lse,
     float* __restrict__ gate, int T, int BH, int nqb, float qscale, float inv_tau, float lam) {
-  __shared__ Tile tiles[2];
+  __shared__ uint16_t kbuf[3][BN * KS];  // K ring: tiles t, t+1 resident, t+2 landing
+  __shared__ uint16_t vbuf[2][BN * VS];  // V: tile t resident, t+1 landing
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -182,20 +196,24 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int qi = q0 + r;
   const bool wave_live = q0 < T;
 
-  // ---- Q fragment: B operand of S^T = K Q^T. Lane holds query r,
-  // d = hf*8 + 16*c + [0, 8) for c = 0..3.
+  // ---- Q fragments: B operands of S^T = K Q^T. Lane holds query r,
+  // d = hf*8 + 16*c + [0, 8) for c = 0..3 (rows past T read row T-1 and are
+  // zeroed).
   bf16x8 qf[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (qi < T) raw = *reinterpret_cast<const uint4*>(q + base + static_cast<size_t>(qi) * D + hf * 8 + 16 * c);
-    qf[c] = as_bf16x8(raw);
+    const int qr = qi < T ? qi : T - 1;
+    u32x4 raw = *reinterpret_cast<const u32x4*>(q + base + static_cast<size_t>(qr) * D + hf * 8 + 16 * c);
+    const u32x4 z = {0, 0, 0, 0};
+    raw = qi < T ? raw : z;
+    qf[c] = __builtin_bit_cast(bf16x8, raw);
   }
 
   RowState st;
   st.acc0 = f32x16{0};
   st.acc1 = f32x16{0};
   st.m = 0.f;
+  st.mlim = kLazy;
   st.lsum = 0.f;
   st.uself = 0.f;
   st.has_self = false;
@@ -204,58 +222,101 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int ntiles = (kend + BN - 1) / BN;
   const int nfull = qb * (BM / BN);  // tiles that are history for every row
 
-  // ---- global -> register prefetch of one tile: K and V rows, 2 x 16 B
-  // chunks each per thread (chunk c: key c >> 3, d chunk c & 7)
+  // ---- global -> register prefetch: 16 B chunks kc0, kc1 of a 64-row tile
+  // (chunk c: row c >> 3, d chunk c & 7), as 32-bit offsets from the head's
+  // base. Tiles that may run past T clamp the row and zero the chunk when it
+  // is stored to LDS, so no load waits early and no pointer select turns the
+  // loads into generic ones.
+  const uint16_t* __restrict__ kh = k + base;
+  const uint16_t* __restrict__ vh = v + base;
   const int kc0 = tid, kc1 = tid + 256;
-  uint4 pk0, pk1, pv0, pv1;
-  auto fetch = [&](int kt) {
-    const int key0 = kt * BN + (kc0 >> 3), key1 = kt * BN + (kc1 >> 3);
-    const size_t o0 = base + static_cast<size_t>(key0) * D + (kc0 & 7) * 8;
-    const size_t o1 = base + static_cast<size_t>(key1) * D + (kc1 & 7) * 8;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    pk0 = (key0 < T) ? *reinterpret_cast<const uint4*>(k + o0) : z;
-    pk1 = (key1 < T) ? *reinterpret_cast<const uint4*>(k + o1) : z;
-    pv0 = (key0 < T) ? *reinterpret_cast<const uint4*>(v + o0) : z;
-    pv1 = (key1 < T) ? *reinterpret_cast<const uint4*>(v + o1) : z;
+  const int lo0 = (kc0 >> 3) * KS + (kc0 & 7) * 8, lo1 = (kc1 >> 3) * KS + (kc1 & 7) * 8;
+  const int lv0 = (kc0 >> 3) * VS + (kc0 & 7) * 8, lv1 = (kc1 >> 3) * VS + (kc1 & 7) * 8;
+  struct Chunks {
+    u32x4 a, b;
+    bool oka, okb;
   };
-  auto stash = [&](Tile& tl) {
-    *reinterpret_cast<uint4*>(&tl.ks[(kc0 >> 3) * KS + (kc0 & 7) * 8]) = pk0;
-    *reinterpret_cast<uint4*>(&tl.ks[(kc1 >> 3) * KS + (kc1 & 7) * 8]) = pk1;
-    *reinterpret_cast<uint4*>(&tl.vs[(kc0 >> 3) * KS + (kc0 & 7) * 8]) = pv0;
-    *reinterpret_cast<uint4*>(&tl.vs[(kc1 >> 3) * KS + (kc1 & 7) * 8]) = pv1;
+  auto fetch = [&](const uint16_t* __restrict__ src, int kt, Chunks& c) {
+    const int key0 = kt * BN + (kc0 >> 3), key1 = kt * BN + (kc1 >> 3);
+    c.oka = key0 < T;
+    c.okb = key1 < T;
+    const uint32_t r0 = static_cast<uint32_t>(c.oka ? key0 : T - 1);
+    const uint32_t r1 = static_cast<uint32_t>(c.okb ? key1 : T - 1);
+    c.a = *reinterpret_cast<const u32x4*>(src + (r0 * D + (kc0 & 7) * 8));
+    c.b = *reinterpret_cast<const u32x4*>(src + (r1 * D + (kc1 & 7) * 8));
+  };
+  auto stash = [&](uint16_t* dst, const Chunks& c, int o0, int o1) {
+    const u32x4 z = {0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(&dst[o0]) = c.oka ? c.a : z;
+    *reinterpret_cast<u32x4*>(&dst[o1]) = c.okb ? c.b : z;
   };
 
-  fetch(0);
-  stash(tiles[0]);
-  __syncthreads();
-  int kt = 0;
-  // ---- strictly historical tiles: no masking
-  for (; kt < nfull; ++kt) {
-    if (kt + 1 < ntiles) fetch(kt + 1);
-    const Tile& tl = tiles[kt & 1];
-    // both score tiles first: the second one's MFMAs run under the first
-    // one's VALU work, and the first P V under the second one's
-    const f32x16 s0 = score(tl, 0, qf, r, hf);
-    const f32x16 s1 = score(tl, 1, qf, r, hf);
-    consume<false>(tl, 0, s0, qscale, r, hf, st);
-    consume<false>(tl, 1, s1, qscale, r, hf, st);
-    if (kt + 1 < ntiles) stash(tiles[(kt + 1) & 1]);
-    __syncthreads();
+  // K tile t lives in kbuf[t % 3], V tile t in vbuf[t % 2]; kp0..kp2 point
+  // at K tiles t, t+1, t+2 of the current step.
+  uint16_t* kp0 = kbuf[0];
+  uint16_t* kp1 = kbuf[1];
+  uint16_t* kp2 = kbuf[2];
+  Chunks ck, cv;
+  {
+    Chunks cn;
+    fetch(kh, 0, ck);
+    fetch(vh, 0, cv);
+    if (ntiles > 1) fetch(kh, 1, cn);
+    stash(kp0, ck, lo0, lo1);
+    stash(vbuf[0], cv, lv0, lv1);
+    if (ntiles > 1) stash(kp1, cn, lo0, lo1);
   }
-  // ---- the workgroup's own block: per-wave historical / diagonal / beyond
+  __syncthreads();
+
+  // ---- strictly historical tiles, software-pipelined: sub-block 1's score
+  // MFMAs run under sub-block 0's exponentials, and the next tile's
+  // sub-block 0 score under sub-block 1's. No masking.
+  f32x16 sa = {0};
+  if (nfull > 0) sa = score(kp0, 0, qf, r, hf);
+  int kt = 0;
+  for (; kt < nfull; ++kt) {
+    const bool more_k = kt + 2 < ntiles;  // kt + 1 < ntiles always holds here
+    if (more_k) fetch(kh, kt + 2, ck);
+    fetch(vh, kt + 1, cv);
+    const uint16_t* vs = vbuf[kt & 1];
+    stabilise<false>(sa, qscale, r, hf, st);
+    f32x16 sb = score(kp0, 1, qf, r, hf);
+    accumulate<false>(vs, 0, sa, hf, st);
+    stabilise<false>(sb, qscale, r, hf, st);
+    sa = score(kp1, 0, qf, r, hf);  // tile kt + 1 <= nfull is resident
+    accumulate<false>(vs, 1, sb, hf, st);
+    if (more_k) stash(kp2, ck, lo0, lo1);
+    stash(vbuf[(kt + 1) & 1], cv, lv0, lv1);
+    __syncthreads();
+    uint16_t* kt0 = kp0;
+    kp0 = kp1;
+    kp1 = kp2;
+    kp2 = kt0;
+  }
+  // ---- the workgroup's own block (at most two tiles, K already resident):
+  // per-wave historical / diagonal / beyond
   for (; kt < ntiles; ++kt) {
-    if (kt + 1 < ntiles) fetch(kt + 1);
-    const Tile& tl = tiles[kt & 1];
+    if (kt + 1 < ntiles) fetch(vh, kt + 1, cv);
+    const uint16_t* vs = vbuf[kt & 1];
     if (wave_live) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         const int k0 = kt * BN + sb * 32;
-        if (k0 < q0) consume<false>(tl, sb, score(tl, sb, qf, r, hf), qscale, r, hf, st);
-        else if (k0 == q0) consume<true>(tl, sb, score(tl, sb, qf, r, hf), qscale, r, hf, st);
+        if (k0 < q0) {
+          f32x16 s = score(kp0, sb, qf, r, hf);
+          stabilise<false>(s, qscale, r, hf, st);
+          accumulate<false>(vs, sb, s, hf, st);
+        } else if (k0 == q0) {
+          f32x16 s = score(kp0, sb, qf, r, hf);
+          stabilise<true>(s, qscale, r, hf, st);
+          accumulate<true>(vs, sb, s, hf, st);
+        }
       }
     }
-    if (kt + 1 < ntiles) stash(tiles[(kt + 1) & 1]);
+    if (kt + 1 < ntiles) stash(vbuf[(kt + 1) & 1], cv, lv0, lv1);
     __syncthreads();
+    kp0 = kp1;
+    kp1 = kp2;
   }
 
   if (!wave_live) return;
