@@ -36,6 +36,8 @@
 // exp(-U) = exp2(-u'), F = exp2(u' sg - c'_i) with c'_i = c_i log2(e).
 #include <math.h>
 
+#include <type_traits>
+
 #include "bwd_common.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -56,7 +58,7 @@ constexpr int BQ = 64;       // queries per tile
 constexpr int RS = D + 8;    // row-major q / dY / K tile stride (bf16): 144 B
 constexpr int US = BQ + 8;   // dU^T tile stride (bf16): 144 B
 
-struct Smem {
+struct __align__(16) Smem {
   uint16_t kr[BK * RS];      // the workgroup's keys, [key][d]
   uint16_t qr[2][BQ * RS];   // q tile, [query][d], double-buffered
   uint16_t gr[2][BQ * RS];   // dY tile, [query][d], double-buffered
@@ -114,18 +116,8 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     *reinterpret_cast<uint4*>(&sm.kr[(c >> 3) * RS + (c & 7) * 8]) = x;
   }
   __syncthreads();
-  // ---- this wave's dQ B operand (K rows, d in [16 dw, 16 dw + 16)) for all
-  // the workgroup's keys, kept in registers: k-slot e of step st <-> key
-  // 32 st + 8 g16 + e, column d = 16 dw + l16
   const int dw = wave & 3;         // d block of this wave's dQ share
   const int qw = (wave >> 2) * QBW;  // first 16-query block of this wave's dQ share
-  bf16x8 kq[KST];
-#pragma unroll
-  for (int st = 0; st < KST; ++st) {
-    const int k0 = st * 32 + g16 * 8 + (l16 >> 2);
-    const int d0 = dw * 16 + 4 * (l16 & 3);
-    kq[st] = cat(lds_read_tr16(&sm.kr[k0 * RS + d0]), lds_read_tr16(&sm.kr[(k0 + 4) * RS + d0]));
-  }
 
   f32x16 dv0 = {0}, dv1 = {0}, dk0 = {0}, dk1 = {0};  // dV^T, dK^T: key r, d rows
 
@@ -181,69 +173,82 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     const uint16_t* qr = sm.qr[buf];
     const uint16_t* gr = sm.gr[buf];
 
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int qs0 = qt0 + sub * 32;  // first query of this 32-query sub-tile
+    // One 32-query sub-tile against this wave's 32 keys. DIAG: the sub-tile
+    // starts at the wave's first key (qs0 == kw0); queries before a key are
+    // masked and the Self entry (query == key) takes the App. A.1.7 form.
+    // Otherwise every query follows every key and no entry needs a check.
+    auto subtile = [&](const int sub, auto diag_tag) {
+      constexpr bool DIAG = decltype(diag_tag)::value;
       uint16_t* urow = &sm.ut[(wave * 32 + r) * US + sub * 32 + hf * 4];
-      if (qs0 + 31 < kw0 || kw0 >= T) {  // every query precedes every key: no entries
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          *reinterpret_cast<uint2*>(urow + g4 * 8) = make_uint2(0, 0);
-        continue;
-      }
-      const bool diag = (qs0 == kw0);
-
-      // ---- S = Q K^T and dP = dY V^T (32 queries x 32 keys)
-      f32x16 sc = {0}, dp = {0};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint4 qa = *reinterpret_cast<const uint4*>(&qr[(sub * 32 + r) * RS + hf * 8 + 16 * c]);
-        const uint4 ga = *reinterpret_cast<const uint4*>(&gr[(sub * 32 + r) * RS + hf * 8 + 16 * c]);
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), kf[c], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ga), vf[c], dp, 0, 0, 0);
-      }
-      // sc[vi], dp[vi]: key = kw0 + r, query = qs0 + (vi>>2)*8 + hf*4 + (vi&3)
-
-      float fv[16], uv[16];
+      // per-query constants of this lane's 16 entries: element vi <-> query
+      // sub*32 + (vi>>2)*8 + hf*4 + (vi&3) of the tile
+      float cc[16];
+      f32x16 sc = {0}, dp;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int ql = sub * 32 + g4 * 8 + hf * 4;  // tile-local query of vi = g4*4
+        const int ql = sub * 32 + g4 * 8 + hf * 4;
         const float4 c4 = *reinterpret_cast<const float4*>(&sm.cq[buf][ql]);
         const float4 d4 = *reinterpret_cast<const float4*>(&sm.dr[buf][ql]);
-        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int vi = g4 * 4 + j;
-          const float u = sc[vi] * kscale;
-          const float sg = fast_rcp(1.0f + fast_exp2(-u));
-          float F = fast_exp2(fmaf(u, sg, -cc[j]));
-          float dR = F * (dp[vi] - dd[j]);
-          const float E = u * sg * kLn2;  // SiLU(U) in natural units
-          float dU = dR * fmaf(-E, sg, sg + E);
-          if (diag) {
-            const int qq = g4 * 8 + hf * 4 + j;  // query offset within sub-tile
-            if (qq == r) {  // Self entry
-              const float ll = sm.lq[buf][ql + j];
-              const float S = fast_rcp(1.0f + fast_exp2(-u * inv_tau));
-              F = fast_exp2(S * kLog2e - ll);
-              dR = F * (dp[vi] - dd[j]);
-              dU = dR * S * (1.0f - S) * inv_tau;
-            } else if (qq < r) {  // future key: not in row i
-              F = 0.f;
-              dU = 0.f;
-            }
-          }
-          fv[vi] = F;
-          uv[vi] = dU;
-        }
+        cc[g4 * 4 + 0] = c4.x; cc[g4 * 4 + 1] = c4.y; cc[g4 * 4 + 2] = c4.z; cc[g4 * 4 + 3] = c4.w;
+        dp[g4 * 4 + 0] = -d4.x; dp[g4 * 4 + 1] = -d4.y; dp[g4 * 4 + 2] = -d4.z; dp[g4 * 4 + 3] = -d4.w;
       }
-      // bf16 packing: word w holds elements 2w (low half), 2w + 1 (high half)
+      // ---- S = Q K^T and dP - Dr = dY V^T - Dr (32 queries x 32 keys); all
+      // operand reads are issued first, and the S chain goes first so that
+      // the exponentials can start while dP is still in the matrix unit
+      bf16x8 qa[4], ga[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        qa[c] = as_bf16x8(*reinterpret_cast<const uint4*>(&qr[(sub * 32 + r) * RS + hf * 8 + 16 * c]));
+        ga[c] = as_bf16x8(*reinterpret_cast<const uint4*>(&gr[(sub * 32 + r) * RS + hf * 8 + 16 * c]));
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c], kf[c], sc, 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[c], vf[c], dp, 0, 0, 0);
+      // sc[vi], dp[vi]: key = kw0 + r, query = qs0 + (vi>>2)*8 + hf*4 + (vi&3)
+
+      // Self entry of this lane's key (DIAG): element vself, present in the
+      // lane half that holds query r
+      float fself = 0.f, uself = 0.f;
+      const int vself = ((r >> 3) << 2) + (r & 3);
+      const bool mine = hf == ((r >> 2) & 1);
+      if (DIAG) {
+        float us_ = 0.f, dps = 0.f;
+#pragma unroll
+        for (int vi = 0; vi < 16; ++vi) {
+          us_ = (vi == vself) ? sc[vi] : us_;
+          dps = (vi == vself) ? dp[vi] : dps;
+        }
+        const float ll = sm.lq[buf][sub * 32 + r];
+        const float S = fast_rcp(1.0f + fast_exp2(-us_ * kscale * inv_tau));
+        fself = fast_exp2(S * kLog2e - ll);
+        uself = fself * dps * S * (1.0f - S) * inv_tau;
+      }
+
       uint32_t fw[8], uw[8];
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        fw[w] = pack_bf16x2(fv[2 * w], fv[2 * w + 1]);
-        uw[w] = pack_bf16x2(uv[2 * w], uv[2 * w + 1]);
+        float f2[2], u2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int vi = 2 * w + e;
+          const float u = sc[vi] * kscale;
+          const float sg = fast_rcp(1.0f + fast_exp2(-u));
+          const float us = u * sg;  // SiLU(U) log2(e)
+          float F = fast_exp2(us - cc[vi]);
+          // dR (sg + E (1 - sg)) with E = us ln 2: the SiLU derivative
+          float dU = F * dp[vi] * fmaf(fmaf(-us, sg, us), kLn2, sg);
+          if (DIAG) {
+            const int qq = (vi >> 2) * 8 + hf * 4 + (vi & 3);  // query offset in the sub-tile
+            const bool self = mine && vi == vself;
+            F = (qq < r) ? 0.f : (self ? fself : F);
+            dU = (qq < r) ? 0.f : (self ? uself : dU);
+          }
+          f2[e] = F;
+          u2[e] = dU;
+        }
+        fw[w] = pack_bf16x2(f2[0], f2[1]);
+        uw[w] = pack_bf16x2(u2[0], u2[1]);
       }
 
       // ---- dV^T += G^T F, dK^T += Q^T dU. B operands: k-slot hf*8 + e of
@@ -277,39 +282,72 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
         *reinterpret_cast<uint2*>(urow + g4 * 8) = make_uint2(uw[2 * g4], uw[2 * g4 + 1]);
+    };
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int qs0 = qt0 + sub * 32;  // first query of this 32-query sub-tile
+      if (qs0 + 31 < kw0 || kw0 >= T) {  // every query precedes every key: no entries
+        uint16_t* urow = &sm.ut[(wave * 32 + r) * US + sub * 32 + hf * 4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<uint2*>(urow + g4 * 8) = make_uint2(0, 0);
+      } else if (qs0 == kw0) {
+        subtile(sub, std::true_type{});
+      } else {
+        subtile(sub, std::false_type{});
+      }
     }
     __syncthreads();  // dU^T complete; q / dY of this tile no longer read
 
     // ---- dQ[16-query blocks qw .. qw+QBW-1][16 dw .. +15] +=
-    // dU (those queries x BK keys) K (BK keys x 16). A operand (16x16x32:
-    // query l16, keys 8 g16 + e of step st) by transposing reads of dU^T:
-    // lane (l16, g16) reads key row 32 st + 8 g16 + (l16>>2) (+4), columns
-    // 16 qb + 4 (l16&3).
+    // dU (those queries x BK keys) K (BK keys x 16) with 16x16x32 MFMAs.
+    // Both operands by transposing reads, four 32-key steps in flight:
+    // A (query l16, keys 8 g16 + e of step st) from dU^T, lane (l16, g16)
+    // reading key row 32 st + 8 g16 + (l16>>2) (+4), columns 16 qb +
+    // 4 (l16&3); B (key 32 st + 8 g16 + e, d = 16 dw + l16) from the K rows
+    // the same way.
     {
       f32x4 aq[QBW];
 #pragma unroll
       for (int b = 0; b < QBW; ++b) aq[b] = f32x4{0, 0, 0, 0};
+      constexpr int SG = 4;  // steps per batch of reads
 #pragma unroll
-      for (int st = 0; st < KST; ++st) {
-        const int krow = st * 32 + g16 * 8 + (l16 >> 2);
+      for (int s0 = 0; s0 < KST; s0 += SG) {
+        bf16x8 kq[SG], ua[SG][QBW];
 #pragma unroll
-        for (int b = 0; b < QBW; ++b) {
-          const int o = krow * US + (qw + b) * 16 + 4 * (l16 & 3);
-          const bf16x8 a = cat(lds_read_tr16(&sm.ut[o]), lds_read_tr16(&sm.ut[o + 4 * US]));
-          aq[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kq[st], aq[b], 0, 0, 0);
+        for (int i = 0; i < SG; ++i) {
+          const int krow = (s0 + i) * 32 + g16 * 8 + (l16 >> 2);
+          const int d0 = dw * 16 + 4 * (l16 & 3);
+          kq[i] = cat(lds_read_tr16(&sm.kr[krow * RS + d0]), lds_read_tr16(&sm.kr[(krow + 4) * RS + d0]));
+#pragma unroll
+          for (int b = 0; b < QBW; ++b) {
+            const int o = krow * US + (qw + b) * 16 + 4 * (l16 & 3);
+            ua[i][b] = cat(lds_read_tr16(&sm.ut[o]), lds_read_tr16(&sm.ut[o + 4 * US]));
+          }
         }
+#pragma unroll
+        for (int i = 0; i < SG; ++i)
+#pragma unroll
+          for (int b = 0; b < QBW; ++b)
+            aq[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[i][b], kq[i], aq[b], 0, 0, 0);
       }
       // aq[b][j]: query qt0 + 16 (qw + b) + 4 g16 + j, d = 16 dw + l16
+      // The next tile is staged first: its wait for the prefetch loads then
+      // does not also wait for these atomics, which resolve at memory.
+      if (qt0 + BQ < T) stash(buf ^ 1);
+      // 32-bit offsets from the head's base; only the last tile can hold
+      // queries past T
+      float* __restrict__ dqh = dq_acc + base;
+      const bool full = qt0 + BQ <= T;
 #pragma unroll
       for (int b = 0; b < QBW; ++b) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = qt0 + (qw + b) * 16 + g16 * 4 + j;
-          if (i < T) unsafeAtomicAdd(dq_acc + base + static_cast<size_t>(i) * D + dw * 16 + l16, aq[b][j]);
+          if (full || i < T) unsafeAtomicAdd(dqh + static_cast<uint32_t>(i * D + dw * 16 + l16), aq[b][j]);
         }
       }
     }
-    if (qt0 + BQ < T) stash(buf ^ 1);
     __syncthreads();  // next tile staged; dU^T free for reuse
   }
 
