@@ -269,8 +269,10 @@ def cpu_baseline(budget_s=15.0, max_heads=32):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU's clocks take on the order of 0.1 s of sustained work to ramp;
+    # 200 untimed steps of the 30M-layer step are about that
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", choices=["step", "fwd", "decode", "attn", "copy"], default=None,
