@@ -58,15 +58,19 @@ constexpr int BQ = 64;       // queries per tile
 constexpr int RS = D + 8;    // row-major q / dY / K tile stride (bf16): 144 B
 constexpr int US = BQ + 8;   // dU^T tile stride (bf16): 144 B
 
+// Query tiles are triple-buffered (tile t read, t+1 resident, t+2 landing)
+// and the dU^T tile double-buffered, so one barrier per tile suffices. The
+// workgroup's K rows pass through ut[1] once, before the loop, on their way
+// into registers.
 struct __align__(16) Smem {
-  uint16_t kr[BK * RS];      // the workgroup's keys, [key][d]
-  uint16_t qr[2][BQ * RS];   // q tile, [query][d], double-buffered
-  uint16_t gr[2][BQ * RS];   // dY tile, [query][d], double-buffered
-  uint16_t ut[BK * US];      // dU^T tile, [key][query]
-  float cq[2][BQ];           // c'_i = (lambda ln i + LSE_i) log2 e   (+inf past T)
-  float lq[2][BQ];           // LSE_i log2 e                           (+inf past T)
-  float dr[2][BQ];           // Dr_i
+  uint16_t qr[3][BQ * RS];   // q tile, [query][d]
+  uint16_t gr[3][BQ * RS];   // dY tile, [query][d]
+  uint16_t ut[2][BK * US];   // dU^T tile, [key][query]
+  float cq[3][BQ];           // c'_i = (lambda ln i + LSE_i) log2 e   (+inf past T)
+  float lq[3][BQ];           // LSE_i log2 e                           (+inf past T)
+  float dr[3][BQ];           // -Dr_i (the dP accumulator's seed)
 };
+static_assert(US == RS, "the K staging rows reuse a dU^T buffer");
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 __device__ __forceinline__ bf16x8 cat(uint2 a, uint2 b) {
@@ -107,33 +111,54 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     kf[c] = as_bf16x8(kr4);
     vf[c] = as_bf16x8(vr4);
   }
-  // ---- the workgroup's key rows to LDS (zero past T)
+  // ---- the workgroup's key rows to LDS (zero past T), staged in ut[1]
+  uint16_t* kr = sm.ut[1];
 #pragma unroll
   for (int pass = 0; pass < BK * 8 / NT; ++pass) {
     const int c = tid + NT * pass;  // chunks of 16 B
     const int key = kb * BK + (c >> 3);
-    const uint4 x = (key < T) ? *reinterpret_cast<const uint4*>(k + base + static_cast<size_t>(key) * D + (c & 7) * 8) : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(&sm.kr[(c >> 3) * RS + (c & 7) * 8]) = x;
+    const int kr_ = key < T ? key : T - 1;
+    u32x4 x = *reinterpret_cast<const u32x4*>(k + base + static_cast<size_t>(kr_) * D + (c & 7) * 8);
+    const u32x4 z = {0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(&kr[(c >> 3) * RS + (c & 7) * 8]) = key < T ? x : z;
   }
   __syncthreads();
+  // ---- this wave's dQ B operand (K rows, d in [16 dw, 16 dw + 16)) for all
+  // the workgroup's keys, kept in registers: k-slot e of step st <-> key
+  // 32 st + 8 g16 + e, column d = 16 dw + l16. ut[1] is next written after
+  // the loop's first barrier.
   const int dw = wave & 3;         // d block of this wave's dQ share
   const int qw = (wave >> 2) * QBW;  // first 16-query block of this wave's dQ share
+  bf16x8 kq[KST];
+#pragma unroll
+  for (int st = 0; st < KST; ++st) {
+    const int k0 = st * 32 + g16 * 8 + (l16 >> 2);
+    const int d0 = dw * 16 + 4 * (l16 & 3);
+    kq[st] = cat(lds_read_tr16(&kr[k0 * RS + d0]), lds_read_tr16(&kr[(k0 + 4) * RS + d0]));
+  }
 
   f32x16 dv0 = {0}, dv1 = {0}, dk0 = {0}, dk1 = {0};  // dV^T, dK^T: key r, d rows
 
   // ---- query tile prefetch: q and dY rows, 16 B chunks (2 per thread with 4
   // waves, 1 with 8; chunk c: row c >> 3, d chunk c & 7)
+  // (rows past T are read clamped to T - 1 and zeroed when stored)
   constexpr int NCH = BQ * 8 / NT;
   const int c0 = tid, c1 = tid + NT;
-  uint4 pq0, pq1 = make_uint4(0, 0, 0, 0), pg0, pg1 = make_uint4(0, 0, 0, 0);
+  const u32x4 z4 = {0, 0, 0, 0};
+  u32x4 pq0, pq1 = z4, pg0, pg1 = z4;
+  bool ok0 = false, ok1 = false;
   float pc = 0.f, pl = 0.f, pd = 0.f;
   auto fetch = [&](int qt0) {
     const int i0 = qt0 + (c0 >> 3), i1 = qt0 + (c1 >> 3);
-    pq0 = (i0 < T) ? *reinterpret_cast<const uint4*>(q + base + static_cast<size_t>(i0) * D + (c0 & 7) * 8) : make_uint4(0, 0, 0, 0);
-    pg0 = (i0 < T) ? *reinterpret_cast<const uint4*>(dy + base + static_cast<size_t>(i0) * D + (c0 & 7) * 8) : make_uint4(0, 0, 0, 0);
+    ok0 = i0 < T;
+    ok1 = i1 < T;
+    const size_t o0 = base + static_cast<size_t>(ok0 ? i0 : T - 1) * D + (c0 & 7) * 8;
+    pq0 = *reinterpret_cast<const u32x4*>(q + o0);
+    pg0 = *reinterpret_cast<const u32x4*>(dy + o0);
     if (NCH > 1) {
-      pq1 = (i1 < T) ? *reinterpret_cast<const uint4*>(q + base + static_cast<size_t>(i1) * D + (c1 & 7) * 8) : make_uint4(0, 0, 0, 0);
-      pg1 = (i1 < T) ? *reinterpret_cast<const uint4*>(dy + base + static_cast<size_t>(i1) * D + (c1 & 7) * 8) : make_uint4(0, 0, 0, 0);
+      const size_t o1 = base + static_cast<size_t>(ok1 ? i1 : T - 1) * D + (c1 & 7) * 8;
+      pq1 = *reinterpret_cast<const u32x4*>(q + o1);
+      pg1 = *reinterpret_cast<const u32x4*>(dy + o1);
     }
     if (tid < BQ) {
       const int i = qt0 + tid;
@@ -141,7 +166,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
         const float ls = lse[rbase + i];
         pc = (lam * logf(static_cast<float>(i + 1)) + ls) * kLog2e;
         pl = ls * kLog2e;
-        pd = Dr[rbase + i];
+        pd = -Dr[rbase + i];
       } else {
         pc = INFINITY;
         pl = INFINITY;
@@ -150,11 +175,11 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     }
   };
   auto stash = [&](int b) {
-    *reinterpret_cast<uint4*>(&sm.qr[b][(c0 >> 3) * RS + (c0 & 7) * 8]) = pq0;
-    *reinterpret_cast<uint4*>(&sm.gr[b][(c0 >> 3) * RS + (c0 & 7) * 8]) = pg0;
+    *reinterpret_cast<u32x4*>(&sm.qr[b][(c0 >> 3) * RS + (c0 & 7) * 8]) = ok0 ? pq0 : z4;
+    *reinterpret_cast<u32x4*>(&sm.gr[b][(c0 >> 3) * RS + (c0 & 7) * 8]) = ok0 ? pg0 : z4;
     if (NCH > 1) {
-      *reinterpret_cast<uint4*>(&sm.qr[b][(c1 >> 3) * RS + (c1 & 7) * 8]) = pq1;
-      *reinterpret_cast<uint4*>(&sm.gr[b][(c1 >> 3) * RS + (c1 & 7) * 8]) = pg1;
+      *reinterpret_cast<u32x4*>(&sm.qr[b][(c1 >> 3) * RS + (c1 & 7) * 8]) = ok1 ? pq1 : z4;
+      *reinterpret_cast<u32x4*>(&sm.gr[b][(c1 >> 3) * RS + (c1 & 7) * 8]) = ok1 ? pg1 : z4;
     }
     if (tid < BQ) {
       sm.cq[b][tid] = pc;
@@ -163,15 +188,23 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     }
   };
 
-  const int qstart = kb * BK;
+  const int qstart = kb * BK;  // < T
+  const int ntile = (T - qstart + BQ - 1) / BQ;
   fetch(qstart);
   stash(0);
+  if (ntile > 1) {
+    fetch(qstart + BQ);
+    stash(1);
+  }
   __syncthreads();
-  int buf = 0;
-  for (int qt0 = qstart; qt0 < T; qt0 += BQ, buf ^= 1) {
-    if (qt0 + BQ < T) fetch(qt0 + BQ);
+  int buf = 0;  // query-tile buffer of tile t (t % 3)
+  for (int t = 0; t < ntile; ++t) {
+    const int qt0 = qstart + t * BQ;
+    const bool more = t + 2 < ntile;
+    if (more) fetch(qt0 + 2 * BQ);
     const uint16_t* qr = sm.qr[buf];
     const uint16_t* gr = sm.gr[buf];
+    uint16_t* ut = sm.ut[t & 1];
 
     // One 32-query sub-tile against this wave's 32 keys. DIAG: the sub-tile
     // starts at the wave's first key (qs0 == kw0); queries before a key are
@@ -179,7 +212,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     // Otherwise every query follows every key and no entry needs a check.
     auto subtile = [&](const int sub, auto diag_tag) {
       constexpr bool DIAG = decltype(diag_tag)::value;
-      uint16_t* urow = &sm.ut[(wave * 32 + r) * US + sub * 32 + hf * 4];
+      uint16_t* urow = &ut[(wave * 32 + r) * US + sub * 32 + hf * 4];
       // per-query constants of this lane's 16 entries: element vi <-> query
       // sub*32 + (vi>>2)*8 + hf*4 + (vi&3) of the tile
       float cc[16];
@@ -190,7 +223,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
         const float4 c4 = *reinterpret_cast<const float4*>(&sm.cq[buf][ql]);
         const float4 d4 = *reinterpret_cast<const float4*>(&sm.dr[buf][ql]);
         cc[g4 * 4 + 0] = c4.x; cc[g4 * 4 + 1] = c4.y; cc[g4 * 4 + 2] = c4.z; cc[g4 * 4 + 3] = c4.w;
-        dp[g4 * 4 + 0] = -d4.x; dp[g4 * 4 + 1] = -d4.y; dp[g4 * 4 + 2] = -d4.z; dp[g4 * 4 + 3] = -d4.w;
+        dp[g4 * 4 + 0] = d4.x; dp[g4 * 4 + 1] = d4.y; dp[g4 * 4 + 2] = d4.z; dp[g4 * 4 + 3] = d4.w;
       }
       // ---- S = Q K^T and dP - Dr = dY V^T - Dr (32 queries x 32 keys); all
       // operand reads are issued first, and the S chain goes first so that
@@ -287,7 +320,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     for (int sub = 0; sub < 2; ++sub) {
       const int qs0 = qt0 + sub * 32;  // first query of this 32-query sub-tile
       if (qs0 + 31 < kw0 || kw0 >= T) {  // every query precedes every key: no entries
-        uint16_t* urow = &sm.ut[(wave * 32 + r) * US + sub * 32 + hf * 4];
+        uint16_t* urow = &ut[(wave * 32 + r) * US + sub * 32 + hf * 4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
           *reinterpret_cast<uint2*>(urow + g4 * 8) = make_uint2(0, 0);
@@ -297,15 +330,15 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
         subtile(sub, std::false_type{});
       }
     }
-    __syncthreads();  // dU^T complete; q / dY of this tile no longer read
+    // the one barrier per tile: dU^T of tile t complete; every wave is done
+    // with tile t-1's query buffer (restaged below) and dU^T buffer
+    __syncthreads();
 
     // ---- dQ[16-query blocks qw .. qw+QBW-1][16 dw .. +15] +=
     // dU (those queries x BK keys) K (BK keys x 16) with 16x16x32 MFMAs.
-    // Both operands by transposing reads, four 32-key steps in flight:
-    // A (query l16, keys 8 g16 + e of step st) from dU^T, lane (l16, g16)
-    // reading key row 32 st + 8 g16 + (l16>>2) (+4), columns 16 qb +
-    // 4 (l16&3); B (key 32 st + 8 g16 + e, d = 16 dw + l16) from the K rows
-    // the same way.
+    // A operand (query l16, keys 8 g16 + e of step st) by transposing reads
+    // of dU^T, four 32-key steps in flight: lane (l16, g16) reads key row
+    // 32 st + 8 g16 + (l16>>2) (+4), columns 16 qb + 4 (l16&3).
     {
       f32x4 aq[QBW];
 #pragma unroll
@@ -313,28 +346,27 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
       constexpr int SG = 4;  // steps per batch of reads
 #pragma unroll
       for (int s0 = 0; s0 < KST; s0 += SG) {
-        bf16x8 kq[SG], ua[SG][QBW];
+        bf16x8 ua[SG][QBW];
 #pragma unroll
         for (int i = 0; i < SG; ++i) {
           const int krow = (s0 + i) * 32 + g16 * 8 + (l16 >> 2);
-          const int d0 = dw * 16 + 4 * (l16 & 3);
-          kq[i] = cat(lds_read_tr16(&sm.kr[krow * RS + d0]), lds_read_tr16(&sm.kr[(krow + 4) * RS + d0]));
 #pragma unroll
           for (int b = 0; b < QBW; ++b) {
             const int o = krow * US + (qw + b) * 16 + 4 * (l16 & 3);
-            ua[i][b] = cat(lds_read_tr16(&sm.ut[o]), lds_read_tr16(&sm.ut[o + 4 * US]));
+            ua[i][b] = cat(lds_read_tr16(&ut[o]), lds_read_tr16(&ut[o + 4 * US]));
           }
         }
 #pragma unroll
         for (int i = 0; i < SG; ++i)
 #pragma unroll
           for (int b = 0; b < QBW; ++b)
-            aq[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[i][b], kq[i], aq[b], 0, 0, 0);
+            aq[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[i][b], kq[s0 + i], aq[b], 0, 0, 0);
       }
       // aq[b][j]: query qt0 + 16 (qw + b) + 4 g16 + j, d = 16 dw + l16
-      // The next tile is staged first: its wait for the prefetch loads then
-      // does not also wait for these atomics, which resolve at memory.
-      if (qt0 + BQ < T) stash(buf ^ 1);
+      // Tile t+2 is staged first: its wait for the prefetch loads then does
+      // not also wait for these atomics, which resolve at memory. Its buffer
+      // last held tile t-1, which every wave finished before the barrier.
+      if (more) stash(buf == 0 ? 2 : buf - 1);
       // 32-bit offsets from the head's base; only the last tile can hold
       // queries past T
       float* __restrict__ dqh = dq_acc + base;
@@ -348,7 +380,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
         }
       }
     }
-    __syncthreads();  // next tile staged; dU^T free for reuse
+    buf = buf == 2 ? 0 : buf + 1;
   }
 
   // ---- dK = scale * dK^T^T, dV = dV^T^T (key kj, d rows of the accumulators)
