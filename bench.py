@@ -203,6 +203,48 @@ def bench_decode(rel, torch, dev, B=32, H=12, D=64, n0=4096, steps=256, cap=4352
             "call_GBps": byts / steps / (call_ms * 1e-3) / 1e9, "bytes": byts}
 
 
+def bench_decode_ragged(rel, torch, dev, B=32, H=12, D=64, nmax=4096, steps=64, cap=4352,
+                        seed=42):
+    """Ragged Relation Cache decode: per-sequence history lengths drawn
+    uniformly in [0, nmax] (one sequence at nmax, one at 0), all advanced by
+    one slot per step, over `steps` steps on the decode workload's cache
+    shape. Bytes are the algorithmic ones of each sequence's own length."""
+    from workloads import make_decode_inputs, ragged_decode_lengths
+    lengths = ragged_decode_lengths(B, nmax, seed)
+    d = make_decode_inputs(B, H, D, nmax, steps, cap, "bf16", seed=seed)
+    kc, vc = d["k_cache"].to(dev), d["v_cache"].to(dev)
+    qs, kn, vn = d["q"].to(dev), d["k_new"].to(dev), d["v_new"].to(dev)
+    y = torch.empty((B, H, D), device=dev, dtype=torch.bfloat16)
+    ws = torch.empty((rel.relation_decode_workspace_bytes(torch.bfloat16, B, H, D, cap),),
+                     device=dev, dtype=torch.uint8)
+    nh0 = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    nh = nh0.clone()
+    stream = torch.cuda.current_stream(dev)
+    for s in range(4):  # warm-up; the appended slots are rewritten below
+        rel.relation_cache_decode_ragged(qs[s], kn[s], vn[s], kc, vc, nh, nmax + s,
+                                         lam=d["lam"], scale=1 / math.sqrt(D), y=y, workspace=ws)
+        nh += 1
+    nh.copy_(nh0)
+    t = EventTimer(torch, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        e = t.start()
+        rel.relation_cache_decode_ragged(qs[s], kn[s], vn[s], kc, vc, nh, nmax + s,
+                                         lam=d["lam"], scale=1 / math.sqrt(D), y=y, workspace=ws)
+        t.stop(e)
+        nh += 1  # the caller advances the lengths (one small kernel, outside the calls)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_seq = [decode_bytes(1, H, D, n + s) for s in range(steps) for n in lengths]
+    byts = float(sum(per_seq))
+    call_ms = t.mean_ms()
+    return {"steps": steps, "B": B, "lengths": f"uniform in [0, {nmax}] (seeded), mean "
+            f"{sum(lengths) / B:.0f}", "total_ms": wall * 1e3, "call_ms": call_ms,
+            "call_GBps": byts / steps / (call_ms * 1e-3) / 1e9,
+            "frac_hbm_peak": byts / steps / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": byts}
+
+
 def bench_copy(torch, dev, nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of known size (torch's copy kernel): the
     calibration for the FETCH_SIZE / WRITE_SIZE counters (reads nbytes and
@@ -275,7 +317,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["step", "fwd", "decode", "attn", "copy"], default=None,
+    ap.add_argument("--only", choices=["step", "fwd", "decode", "ragged", "attn", "copy"],
+                    default=None,
                     help="run one measurement and print its raw numbers ('copy': a plain "
                          "device copy of known size, the HBM-counter calibration)")
     args = ap.parse_args()
@@ -304,6 +347,9 @@ def main():
         return
     if args.only == "decode":
         print(json.dumps(bench_decode(rel, torch, dev)))
+        return
+    if args.only == "ragged":
+        print(json.dumps(bench_decode_ragged(rel, torch, dev)))
         return
     if args.only == "attn":
         print(json.dumps(bench_fwdbwd_vs_attention(rel, torch, dev, args.steps)))
@@ -344,6 +390,8 @@ def main():
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": dec["call_GBps"] / PEAK_HBM_GBS,
                                   "traffic": kernel_traffic("decode_split_kernel@cache4096")}
+        torch.cuda.empty_cache()
+        rec["decode_ragged"] = bench_decode_ragged(rel, torch, dev)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()

@@ -23,6 +23,7 @@ __all__ = [
     "relation_bwd_workspace_bytes",
     "relation_cache_decode",
     "relation_decode_workspace_bytes",
+    "relation_cache_decode_ragged",
     "relation_status_string",
     "relation_version",
     "RelationFunction",
@@ -38,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "relation_bwd",
     "relation_decode_workspace_bytes",
     "relation_cache_decode",
+    "relation_cache_decode_ragged",
     "relation_status_string",
     "relation_version",
 )
@@ -80,6 +82,10 @@ def load_library():
     lib.relation_cache_decode.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, c_int,
                                           c_int, vp, vp, vp, c_size, c_float, c_float, c_float,
                                           vp]
+    lib.relation_cache_decode_ragged.restype = c_int
+    lib.relation_cache_decode_ragged.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
+                                                 c_int, vp, c_int, vp, vp, vp, c_size, c_float,
+                                                 c_float, c_float, vp]
     lib.relation_status_string.restype = ctypes.c_char_p
     lib.relation_status_string.argtypes = [c_int]
     lib.relation_version.restype = c_int
@@ -233,6 +239,44 @@ def relation_cache_decode(q, k_new, v_new, k_cache, v_cache, n_hist, lam=0.0, sc
                                    _stream(dev, stream))
     if st != 0:
         raise RelationError(st, "relation_cache_decode")
+    return y, gate
+
+
+def relation_cache_decode_ragged(q, k_new, v_new, k_cache, v_cache, n_hist, max_n_hist=None,
+                                 lam=0.0, scale=None, tau_s=2.0, y=None, gate=None,
+                                 workspace=None, want_gate=False, stream=None):
+    """One decode step over a ragged cache: as relation_cache_decode, with
+    n_hist a device int32 tensor [B] of per-sequence history lengths (not
+    modified) and max_n_hist a host bound of them (default capacity - 1).
+    Returns (y, gate)."""
+    lib = load_library()
+    B, H, D = q.shape
+    capacity = k_cache.shape[2]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
+        _check(t, name, dt, (B, H, D), dev)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, name, dt, (B, H, capacity, D), dev)
+    _check(n_hist, "n_hist", torch.int32, (B,), dev)
+    bound = capacity - 1 if max_n_hist is None else int(max_n_hist)
+    y = torch.empty_like(q) if y is None else y
+    _check(y, "y", dt, (B, H, D), dev)
+    if gate is None and want_gate:
+        gate = torch.empty((B, H), device=dev, dtype=torch.float32)
+    if gate is not None:
+        _check(gate, "gate", torch.float32, (B, H), dev)
+    need = int(lib.relation_decode_workspace_bytes(code, B, H, D, capacity))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), device=dev, dtype=torch.uint8)
+    st = lib.relation_cache_decode_ragged(code, B, H, D, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                          _ptr(k_cache), _ptr(v_cache), capacity, _ptr(n_hist),
+                                          bound, _ptr(y), _ptr(gate), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _scale(D, scale), float(tau_s), float(lam),
+                                          _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_cache_decode_ragged")
     return y, gate
 
 

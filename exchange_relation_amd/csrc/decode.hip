@@ -18,6 +18,12 @@
 // n_hist (no split reads that slot).
 // Kernel 2 (combine): one 64-lane wave per (b, h) merges the chunk partials
 // (every partial load issued up front), adds Self and writes y / gate.
+//
+// Ragged batches: each sequence b has its own history length n_b (a device
+// int array). The launch is sized for an upper bound of the lengths; a split
+// workgroup whose chunk lies past its sequence's n_b exits at once, and the
+// combine does the append. A sequence whose n_b is out of range (negative,
+// above the bound, or without a free slot) gets NaN outputs and no append.
 #include <math.h>
 
 #include "common.hpp"
@@ -37,15 +43,29 @@ constexpr int kGroups = 32;                 // 8-lane groups per 256-lane workgr
 constexpr int kUnroll = REL_DECODE_UNROLL;  // slots per group per iteration (loads in flight)
 constexpr int kBatch = 8;                   // partials loaded at once by the combine
 
-inline int num_splits(int n) { return (n + kChunk - 1) / kChunk; }
+__host__ __device__ inline int num_splits(int n) { return (n + kChunk - 1) / kChunk; }
+
+// Split plan of a history of n >= 1 slots: chunks of a multiple of 32 slots,
+// about kChunk each, and the number of chunks (<= num_splits(n)).
+struct SplitPlan {
+  int nsplit, chunk;
+};
+__host__ __device__ inline SplitPlan split_plan(int n) {
+  const int ns = num_splits(n);
+  const int chunk = ((n + ns - 1) / ns + 31) / 32 * 32;
+  return {(n + chunk - 1) / chunk, chunk};
+}
 
 // Partial record per (head, split): [m, l, z_0 .. z_{D-1}] in fp32, base-2
 // domain (m is a log2 stabiliser; l, z are scaled by 2^-m).
-template <typename TE, int D>
+// Uniform batches pass the common length in n (and nh = NULL); ragged ones
+// pass the per-sequence lengths nh[B], the heads per sequence H and the
+// length bound n (the grid has nsplit = num_splits(bound) chunks per head).
+template <typename TE, int D, bool RAGGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const TE* __restrict__ q, const TE* __restrict__ kn, const TE* __restrict__ vn,
     TE* __restrict__ kc, TE* __restrict__ vc, float* __restrict__ part, int capacity, int n,
-    int nsplit, int chunk, float qscale) {
+    const int* __restrict__ nh, int H, int nsplit, int chunk, float qscale) {
   constexpr int E = D / 8;
   __shared__ float s_m[kGroups], s_l[kGroups];
   __shared__ float s_z[kGroups][D + 1];
@@ -56,9 +76,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int split = blockIdx.x % nsplit;
   const int head = blockIdx.x / nsplit;
   const size_t cbase = static_cast<size_t>(head) * capacity * D;
+  if (RAGGED) {
+    const int bound = n;
+    n = nh[head / H];
+    if (n < 1 || n > bound || n >= capacity) return;  // no history, or out of range
+    const SplitPlan sp = split_plan(n);
+    if (split >= sp.nsplit) return;
+    chunk = sp.chunk;
+  }
   const int c0 = split * chunk;
   const int c1 = min(n, c0 + chunk);
-  if (split == 0 && tid < D) {  // append: exact copy of the new token into slot n
+  if (!RAGGED && split == 0 && tid < D) {  // append: exact copy of the new token into slot n
     const size_t slot = cbase + static_cast<size_t>(n) * D + tid;
     kc[slot] = kn[static_cast<size_t>(head) * D + tid];
     vc[slot] = vn[static_cast<size_t>(head) * D + tid];
@@ -142,20 +170,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 }
 
-template <typename TE, int D>
+// Uniform: n is the common length and nsplit the chunks per head (0 when
+// n = 0). Ragged: n is the length bound, nh[B] the lengths, H the heads per
+// sequence and pstride the chunks per head of the split grid.
+template <typename TE, int D, bool RAGGED>
 __global__ __launch_bounds__(64) void decode_combine_kernel(
     const TE* __restrict__ q, const TE* __restrict__ kn, const TE* __restrict__ vn,
     TE* __restrict__ kc, TE* __restrict__ vc, const float* __restrict__ part, TE* __restrict__ y,
-    float* __restrict__ gate, int capacity, int n, int nsplit, float qscale, float inv_tau,
-    float lam) {
+    float* __restrict__ gate, int capacity, int n, const int* __restrict__ nh, int H, int nsplit,
+    int pstride, float qscale, float inv_tau, float lam) {
   const int tid = threadIdx.x;  // one lane per element d (lanes >= D idle)
   const int head = blockIdx.x;
   const bool act = tid < D;
   const size_t hv = static_cast<size_t>(head) * D;
+  if (RAGGED) {
+    const int bound = n;
+    n = nh[head / H];
+    if (n < 0 || n > bound || n >= capacity) {  // out of range: NaN outputs, no append
+      if (act) Elem<TE>::store(y + hv + tid, NAN);
+      if (tid == 0 && gate) gate[head] = NAN;
+      return;
+    }
+    nsplit = n > 0 ? split_plan(n).nsplit : 0;
+  }
   const float qd = act ? Elem<TE>::load(q + hv + tid) : 0.f;
   const float kd = act ? Elem<TE>::load(kn + hv + tid) : 0.f;
   const float vd = act ? Elem<TE>::load(vn + hv + tid) : 0.f;
-  if (nsplit == 0) {  // no history: the append was not done by a split kernel
+  if (RAGGED || nsplit == 0) {  // the append was not done by a split kernel
     if (act) {
       const size_t slot = (static_cast<size_t>(head) * capacity + n) * D + tid;
       kc[slot] = kn[hv + tid];
@@ -172,7 +213,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   // merge the chunk partials (App. A.3.2), kBatch partials per round with
   // all their loads issued before any is used
   float M = -INFINITY, Ls = 0.f, Z = 0.f;
-  const float* ph = part + static_cast<size_t>(head) * nsplit * (D + 2);
+  const float* ph = part + static_cast<size_t>(head) * (RAGGED ? pstride : nsplit) * (D + 2);
   for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
     float pm[kBatch], pl[kBatch], pz[kBatch];
 #pragma unroll
@@ -209,30 +250,46 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   if (tid == 0 && gate) gate[head] = g;
 }
 
+// nh == NULL: uniform length n. Otherwise per-sequence lengths nh[B] with
+// upper bound n.
 template <typename TE, int D>
-hipError_t run(int BH, const void* q, const void* k_new, const void* v_new, void* k_cache,
-               void* v_cache, int capacity, int n, void* y, float* gate, void* ws, float scale,
-               float tau, float lam, hipStream_t stream) {
+hipError_t run(int BH, int H, const void* q, const void* k_new, const void* v_new, void* k_cache,
+               void* v_cache, int capacity, int n, const int* nh, void* y, float* gate, void* ws,
+               float scale, float tau, float lam, hipStream_t stream) {
   const float qscale = scale * kLog2e;
   float* part = static_cast<float*>(ws);
+  const TE* qt = static_cast<const TE*>(q);
+  const TE* knt = static_cast<const TE*>(k_new);
+  const TE* vnt = static_cast<const TE*>(v_new);
+  TE* kct = static_cast<TE*>(k_cache);
+  TE* vct = static_cast<TE*>(v_cache);
   int nsplit = 0;
+  if (nh == nullptr) {
+    if (n > 0) {
+      const SplitPlan sp = split_plan(n);
+      nsplit = sp.nsplit;
+      hipLaunchKernelGGL((decode_split_kernel<TE, D, false>),
+                         dim3(static_cast<unsigned>(nsplit) * BH), dim3(256), 0, stream, qt, knt,
+                         vnt, kct, vct, part, capacity, n, nullptr, H, nsplit, sp.chunk, qscale);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((decode_combine_kernel<TE, D, false>), dim3(BH), dim3(64), 0, stream, qt,
+                       knt, vnt, kct, vct, part, static_cast<TE*>(y), gate, capacity, n, nullptr,
+                       H, nsplit, nsplit, qscale, 1.0f / tau, lam);
+    return hipGetLastError();
+  }
   if (n > 0) {
-    nsplit = num_splits(n);
-    const int chunk = ((n + nsplit - 1) / nsplit + 31) / 32 * 32;
-    nsplit = (n + chunk - 1) / chunk;
-    hipLaunchKernelGGL((decode_split_kernel<TE, D>), dim3(static_cast<unsigned>(nsplit) * BH),
-                       dim3(256), 0, stream, static_cast<const TE*>(q),
-                       static_cast<const TE*>(k_new), static_cast<const TE*>(v_new),
-                       static_cast<TE*>(k_cache), static_cast<TE*>(v_cache), part, capacity, n,
-                       nsplit, chunk, qscale);
+    nsplit = num_splits(n);  // chunks per head of the grid: enough for any length <= n
+    hipLaunchKernelGGL((decode_split_kernel<TE, D, true>), dim3(static_cast<unsigned>(nsplit) * BH),
+                       dim3(256), 0, stream, qt, knt, vnt, kct, vct, part, capacity, n, nh, H,
+                       nsplit, 0, qscale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_combine_kernel<TE, D>), dim3(BH), dim3(64), 0, stream,
-                     static_cast<const TE*>(q), static_cast<const TE*>(k_new),
-                     static_cast<const TE*>(v_new), static_cast<TE*>(k_cache),
-                     static_cast<TE*>(v_cache), part, static_cast<TE*>(y), gate, capacity, n,
-                     nsplit, qscale, 1.0f / tau, lam);
+  hipLaunchKernelGGL((decode_combine_kernel<TE, D, true>), dim3(BH), dim3(64), 0, stream, qt, knt,
+                     vnt, kct, vct, part, static_cast<TE*>(y), gate, capacity, n, nh, H, 0, nsplit,
+                     qscale, 1.0f / tau, lam);
   return hipGetLastError();
 }
 
@@ -246,17 +303,17 @@ size_t decode_workspace_bytes(int dtype, int B, int H, int D, int capacity) {
 
 hipError_t launch_decode(int dtype, int B, int H, int D, const void* q, const void* k_new,
                          const void* v_new, void* k_cache, void* v_cache, int capacity,
-                         int n_hist, void* y, float* gate, void* ws, float scale, float tau,
-                         float lam, hipStream_t stream) {
+                         int n_hist, const int* n_hist_dev, void* y, float* gate, void* ws,
+                         float scale, float tau, float lam, hipStream_t stream) {
   const int BH = B * H;
   if (dtype == 1)
-    return dec::run<uint16_t, 64>(BH, q, k_new, v_new, k_cache, v_cache, capacity, n_hist, y,
-                                  gate, ws, scale, tau, lam, stream);
+    return dec::run<uint16_t, 64>(BH, H, q, k_new, v_new, k_cache, v_cache, capacity, n_hist,
+                                  n_hist_dev, y, gate, ws, scale, tau, lam, stream);
   if (D == 64)
-    return dec::run<float, 64>(BH, q, k_new, v_new, k_cache, v_cache, capacity, n_hist, y, gate,
-                               ws, scale, tau, lam, stream);
-  return dec::run<float, 32>(BH, q, k_new, v_new, k_cache, v_cache, capacity, n_hist, y, gate,
-                             ws, scale, tau, lam, stream);
+    return dec::run<float, 64>(BH, H, q, k_new, v_new, k_cache, v_cache, capacity, n_hist,
+                               n_hist_dev, y, gate, ws, scale, tau, lam, stream);
+  return dec::run<float, 32>(BH, H, q, k_new, v_new, k_cache, v_cache, capacity, n_hist,
+                             n_hist_dev, y, gate, ws, scale, tau, lam, stream);
 }
 
 }  // namespace rel

@@ -31,11 +31,13 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                            float* dlambda, void* ws, float scale, float tau, float lam,
                            hipStream_t stream);
 
-// Relation Cache decode (one step). dtype 0 = fp32, 1 = bf16.
+// Relation Cache decode (one step). dtype 0 = fp32, 1 = bf16. n_hist_dev
+// NULL: every sequence has n_hist slots of history; otherwise sequence b has
+// n_hist_dev[b] (device ints) and n_hist is their upper bound.
 size_t decode_workspace_bytes(int dtype, int B, int H, int D, int capacity);
 hipError_t launch_decode(int dtype, int B, int H, int D, const void* q, const void* k_new,
                          const void* v_new, void* k_cache, void* v_cache, int capacity,
-                         int n_hist, void* y, float* gate, void* ws, float scale, float tau,
-                         float lam, hipStream_t stream);
+                         int n_hist, const int* n_hist_dev, void* y, float* gate, void* ws,
+                         float scale, float tau, float lam, hipStream_t stream);
 
 }  // namespace rel

@@ -145,8 +145,35 @@ relation_status relation_cache_decode(relation_dtype dtype, int B, int H, int D,
   if (!workspace || workspace_bytes < need) return REL_ERR_WORKSPACE;
   if (!aligned256(workspace)) return REL_ERR_ALIGN;
   return from_hip(rel::launch_decode(dtype == REL_BF16 ? 1 : 0, B, H, D, q, k_new, v_new,
-                                     k_cache, v_cache, capacity, n_hist, y, gate, workspace,
-                                     scale, tau_s, lambda, static_cast<hipStream_t>(stream)));
+                                     k_cache, v_cache, capacity, n_hist, nullptr, y, gate,
+                                     workspace, scale, tau_s, lambda,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H, int D,
+                                             const void* q, const void* k_new, const void* v_new,
+                                             void* k_cache, void* v_cache, int capacity,
+                                             const int* n_hist, int max_n_hist, void* y,
+                                             float* gate, void* workspace, size_t workspace_bytes,
+                                             float scale, float tau_s, float lambda,
+                                             void* stream) {
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !y || !n_hist) return REL_ERR_NULL;
+  relation_status st = check_dtype_dim(dtype, D);
+  if (st != REL_OK) return st;
+  if (B < 1 || H < 1 || capacity < 1) return REL_ERR_SHAPE;
+  if (static_cast<long long>(B) * H * capacity * D > kMaxElems) return REL_ERR_SHAPE;
+  if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
+  if (max_n_hist < 0 || max_n_hist >= capacity) return REL_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(y) || (gate && !aligned4(gate)) || !aligned4(n_hist))
+    return REL_ERR_ALIGN;
+  const size_t need = rel::decode_workspace_bytes(dtype == REL_BF16 ? 1 : 0, B, H, D, capacity);
+  if (!workspace || workspace_bytes < need) return REL_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return REL_ERR_ALIGN;
+  return from_hip(rel::launch_decode(dtype == REL_BF16 ? 1 : 0, B, H, D, q, k_new, v_new,
+                                     k_cache, v_cache, capacity, max_n_hist, n_hist, y, gate,
+                                     workspace, scale, tau_s, lambda,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -137,6 +137,34 @@ relation_status relation_cache_decode(relation_dtype dtype, int B, int H, int D,
                                       float scale, float tau_s, float lambda,
                                       void* stream);
 
+/*
+ * relation_cache_decode_ragged — the same step as relation_cache_decode for a
+ * batch whose sequences have different history lengths (a ragged Relation
+ * Cache). Sequence b's new token is at 1-based position n_hist[b] + 1 and is
+ * computed exactly as relation_cache_decode computes it with
+ * n_hist = n_hist[b].
+ *
+ *   n_hist     : in  DEVICE int32 [B], 4-byte aligned. Read on the device; the
+ *                library does not change it (the caller advances it).
+ *   max_n_hist : host int, an upper bound of n_hist[]: it sizes the launch
+ *                (work scales with the actual lengths, the launch with the
+ *                bound). 0 <= max_n_hist < capacity, else REL_ERR_CAPACITY.
+ *   Other arguments as for relation_cache_decode, with the same workspace
+ *   size (relation_decode_workspace_bytes).
+ *
+ * Device-side values the host cannot check: a sequence with n_hist[b] < 0,
+ * n_hist[b] > max_n_hist or n_hist[b] >= capacity gets NaN in y[b] (and in
+ * gate[b] when gate is given); its cache rows are not touched.
+ */
+relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H, int D,
+                                             const void* q, const void* k_new, const void* v_new,
+                                             void* k_cache, void* v_cache, int capacity,
+                                             const int* n_hist, int max_n_hist,
+                                             void* y, float* gate,
+                                             void* workspace, size_t workspace_bytes,
+                                             float scale, float tau_s, float lambda,
+                                             void* stream);
+
 /* Static, NUL-terminated description of a status code (host only). */
 const char* relation_status_string(relation_status s);
 

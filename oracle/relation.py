@@ -40,6 +40,7 @@ __all__ = [
     "relation_backward_head",
     "relation_backward",
     "relation_decode_step",
+    "relation_decode_step_ragged",
     "brute_force_forward_head",
     "tiled_forward_head",
 ]
@@ -226,6 +227,24 @@ def relation_decode_step(q, k_new, v_new, k_cache, v_cache, n_hist, scale, tau_s
             yy, _, gg = relation_forward_rows(qq, kk, vv, [i], scale, tau_s, lam)
             y[b, h] = yy[0]
             g[b, h] = gg[0]
+    return y, g, kc, vc
+
+
+def relation_decode_step_ragged(q, k_new, v_new, k_cache, v_cache, n_hist, scale, tau_s, lam):
+    """The decode step for a batch whose sequences have different history
+    lengths: sequence b is advanced exactly as relation_decode_step advances
+    a batch of one with n_hist = n_hist[b] (each sequence is its own Relation
+    row; Sec. 3.1). Returns (y, g, k_cache', v_cache') like that function."""
+    B = len(n_hist)
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    y = np.empty((B,) + tuple(np.shape(v_new)[1:]))
+    g = np.empty(np.shape(q)[:2])
+    for b in range(B):
+        yb, gb, kcb, vcb = relation_decode_step(q[b:b + 1], k_new[b:b + 1], v_new[b:b + 1],
+                                                kc[b:b + 1], vc[b:b + 1], int(n_hist[b]),
+                                                scale, tau_s, lam)
+        y[b], g[b], kc[b], vc[b] = yb[0], gb[0], kcb[0], vcb[0]
     return y, g, kc, vc
 
 

@@ -113,6 +113,22 @@ def test_decode_validation(lib):
     assert dec(q=P_MIS) == REL_ERR_ALIGN
 
 
+def test_decode_ragged_validation(lib):
+    need = lib.relation_decode_workspace_bytes(BF16, 2, 3, 64, 4352)
+
+    def dec(bound=10, cap=4352, ws=P, wsb=None, q=P, nh=P, D=64):
+        wsb = need if wsb is None else wsb
+        return lib.relation_cache_decode_ragged(BF16, 2, 3, D, q, P, P, P, P, cap, nh, bound, P,
+                                                NUL, ws, wsb, 0.125, 2.0, 0.3, None)
+
+    assert dec(bound=4352) == REL_ERR_CAPACITY  # bound + 1 > capacity
+    assert dec(bound=-1) == REL_ERR_CAPACITY
+    assert dec(nh=NUL) == REL_ERR_NULL
+    assert dec(nh=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+    assert dec(ws=NUL) == REL_ERR_WORKSPACE
+    assert dec(D=32) == REL_ERR_UNSUPPORTED
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(rel, "_LIB", None)
     monkeypatch.setattr(rel, "lib_path", lambda: str(tmp_path / "missing.so"))

@@ -160,6 +160,29 @@ def test_decode_is_last_row_of_forward(rng):
     assert np.array_equal(vc2[:, :, n + 1:], vc[:, :, n + 1:])
 
 
+def test_decode_ragged_rows_are_last_rows_of_their_forwards(rng):
+    # each sequence's output is the last row of the forward over its own
+    # history + new token, whatever the other sequences' lengths
+    B, H, D, cap = 4, 2, 3, 11
+    ns = [0, 10, 3, 7]
+    kc = rng.standard_normal((B, H, cap, D))
+    vc = rng.standard_normal((B, H, cap, D))
+    q, kn, vn = (rng.standard_normal((B, H, D)) for _ in range(3))
+    y, g, kc2, vc2 = oracle.relation_decode_step_ragged(q, kn, vn, kc, vc, ns, 0.5, 2.0, 0.35)
+    for b, n in enumerate(ns):
+        for h in range(H):
+            K = np.concatenate([kc[b, h, :n], kn[b, h][None]], 0)
+            V = np.concatenate([vc[b, h, :n], vn[b, h][None]], 0)
+            Q = np.zeros((n + 1, D))
+            Q[n] = q[b, h]
+            r = oracle.relation_forward_head(Q, K, V, 0.5, 2.0, 0.35)
+            assert np.abs(y[b, h] - r["Y"][n]).max() < 1e-14
+            assert abs(g[b, h] - r["g"][n]) < 1e-14
+            assert np.array_equal(kc2[b, h, : n + 1], K)
+            assert np.array_equal(kc2[b, h, n + 1:], kc[b, h, n + 1:])
+            assert np.array_equal(vc2[b, h, n + 1:], vc[b, h, n + 1:])
+
+
 def test_decode_empty_history(rng):
     B, H, D = 1, 2, 3
     kc = rng.standard_normal((B, H, 4, D))

@@ -21,7 +21,7 @@ import torch
 
 import exchange_relation_amd as rel
 import oracle
-from workloads import WORKLOADS, make_decode_inputs, make_inputs
+from workloads import WORKLOADS, make_decode_inputs, make_inputs, ragged_decode_lengths
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -327,6 +327,104 @@ def test_decode_full_size_cache_workload():
         Y, G = oracle_decode_rows(dd, s, w.n_hist + s, heads, scale, d["lam"])
         check(f"y step {s}", np.stack([f64(ys[s][b, h]) for b, h in heads]), Y, "bf16")
         check(f"gate step {s}", np.stack([f64(gs[s][b, h]) for b, h in heads]), G, "bf16")
+
+
+# ------------------------------------------------------------ ragged decode
+def ragged_lengths_inputs(B, H, D, lengths, capacity, steps, dtype, seed):
+    """Decode inputs with every cache slot filled (so untouched slots can be
+    checked) and per-sequence history lengths."""
+    d = make_decode_inputs(B, H, D, capacity - steps, steps, capacity, dtype, seed=seed)
+    return d, torch.tensor(lengths, dtype=torch.int32)
+
+
+def run_ragged_steps(d, lengths, steps, scale, bound):
+    kc, vc = d["k_cache"].to(DEV), d["v_cache"].to(DEV)
+    B, H, cap, D = kc.shape
+    nh = lengths.to(DEV)
+    ws = torch.empty(rel.relation_decode_workspace_bytes(kc.dtype, B, H, D, cap), device=DEV,
+                     dtype=torch.uint8)
+    ys, gs = [], []
+    for s in range(steps):
+        y, g = rel.relation_cache_decode_ragged(d["q"][s].to(DEV), d["k_new"][s].to(DEV),
+                                                d["v_new"][s].to(DEV), kc, vc, nh, bound + s,
+                                                lam=d["lam"], scale=scale, tau_s=2.0,
+                                                want_gate=True, workspace=ws)
+        ys.append(y.cpu())
+        gs.append(g.cpu())
+        nh += 1  # the caller advances the lengths
+    torch.cuda.synchronize()
+    return ys, gs, kc.cpu(), vc.cpu()
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 64), ("f32", 32)])
+def test_decode_ragged_vs_oracle(dtype, D):
+    lengths = [0, 1, 31, 512, 513, 700]
+    B, H, cap, steps = len(lengths), 3, 720, 2
+    d, nh = ragged_lengths_inputs(B, H, D, lengths, cap, steps, dtype, seed=410 + D)
+    scale = 1 / math.sqrt(D)
+    ys, gs, kc, vc = run_ragged_steps(d, nh, steps, scale, max(lengths))
+    kfull, vfull = d["k_cache"].clone(), d["v_cache"].clone()
+    for s in range(steps):
+        ns = [n + s for n in lengths]
+        Y, G, kexp, vexp = oracle.relation_decode_step_ragged(
+            f64(d["q"][s]), f64(d["k_new"][s]), f64(d["v_new"][s]), f64(kfull), f64(vfull), ns,
+            scale, 2.0, d["lam"])
+        check(f"ragged y step {s}", f64(ys[s]), Y, dtype)
+        check(f"ragged gate step {s}", f64(gs[s]), G, dtype)
+        for b, n in enumerate(ns):
+            kfull[b, :, n] = d["k_new"][s, b]
+            vfull[b, :, n] = d["v_new"][s, b]
+    assert torch.equal(kc, kfull) and torch.equal(vc, vfull)  # bit-exact appends, rest untouched
+
+
+def test_decode_ragged_equal_lengths_match_uniform_bit_exact():
+    B, H, D, n, cap = 3, 4, 64, 1030, 1040
+    d = make_decode_inputs(B, H, D, n, 1, cap, "bf16", seed=421)
+    scale = 1 / 8
+    yu, gu, kcu, vcu = run_decode_steps(d, n, 1, scale)
+    yr, gr_, kcr, vcr = run_ragged_steps(d, torch.full((B,), n, dtype=torch.int32), 1, scale, n)
+    assert torch.equal(yu[0], yr[0]) and torch.equal(gu[0], gr_[0])
+    assert torch.equal(kcu, kcr) and torch.equal(vcu, vcr)
+
+
+def test_decode_ragged_out_of_range_lengths_give_nan_and_no_write():
+    lengths = [5, 40, -1, 9]  # the bound passed is 20: sequence 1 is above it, 2 negative
+    B, H, D, cap = len(lengths), 2, 64, 64
+    d, nh = ragged_lengths_inputs(B, H, D, lengths, cap, 1, "bf16", seed=433)
+    ys, gs, kc, vc = run_ragged_steps(d, nh, 1, 1 / 8, 20)
+    y, g = f64(ys[0]), f64(gs[0])
+    assert np.isnan(y[1]).all() and np.isnan(y[2]).all() and np.isnan(g[1]).all()
+    assert torch.equal(kc[1], d["k_cache"][1]) and torch.equal(kc[2], d["k_cache"][2])
+    assert torch.equal(vc[1], d["v_cache"][1]) and torch.equal(vc[2], d["v_cache"][2])
+    for b in (0, 3):
+        n = lengths[b]
+        Y, G, _, _ = oracle.relation_decode_step_ragged(
+            f64(d["q"][0, b:b + 1]), f64(d["k_new"][0, b:b + 1]), f64(d["v_new"][0, b:b + 1]),
+            f64(d["k_cache"][b:b + 1]), f64(d["v_cache"][b:b + 1]), [n], 1 / 8, 2.0, d["lam"])
+        check(f"valid row {b}", y[b:b + 1], Y, "bf16")
+        assert torch.equal(kc[b, :, n], d["k_new"][0, b])
+
+
+def test_decode_ragged_full_size_workload():
+    w = WORKLOADS["cache_decode_bf16"]
+    lengths = ragged_decode_lengths(w.B, w.n_hist, seed=42)
+    steps = 3
+    d, nh = ragged_lengths_inputs(w.B, w.H, w.D, lengths, w.capacity, steps, "bf16", seed=42)
+    scale = 1 / math.sqrt(w.D)
+    ys, gs, kc, vc = run_ragged_steps(d, nh, steps, scale, w.n_hist)
+    kfull, vfull = d["k_cache"].clone(), d["v_cache"].clone()
+    for s in range(steps):
+        ns = [n + s for n in lengths]
+        bs = list(range(0, w.B, 5)) if s < steps - 1 else list(range(w.B))
+        for b in bs:
+            Y, G, _, _ = oracle.relation_decode_step_ragged(
+                f64(d["q"][s, b:b + 1]), f64(d["k_new"][s, b:b + 1]), f64(d["v_new"][s, b:b + 1]),
+                f64(kfull[b:b + 1]), f64(vfull[b:b + 1]), [ns[b]], scale, 2.0, d["lam"])
+            check(f"ragged full y step {s} seq {b}", f64(ys[s][b:b + 1]), Y, "bf16")
+        for b, n in enumerate(ns):
+            kfull[b, :, n] = d["k_new"][s, b]
+            vfull[b, :, n] = d["v_new"][s, b]
+    assert torch.equal(kc, kfull) and torch.equal(vc, vfull)
 
 
 # ------------------------------------------------------ bit-exact properties

@@ -27,6 +27,7 @@ __all__ = [
     "WORKLOADS",
     "make_inputs",
     "make_decode_inputs",
+    "ragged_decode_lengths",
     "apply_rope",
     "to_dtype",
     "default_scale",
@@ -62,6 +63,18 @@ WORKLOADS = {
                                   n_hist=4096, steps=256, capacity=4352,
                                   note="Relation Cache decode, 256 steps from history 4096"),
 }
+
+
+def ragged_decode_lengths(B, max_n, seed):
+    """Seeded per-sequence history lengths for a ragged Relation Cache batch:
+    uniform integers in [0, max_n], with sequence 0 at max_n and sequence 1
+    at 0 so that both extremes are always present."""
+    rng = np.random.default_rng(seed + 7919)
+    n = rng.integers(0, max_n + 1, size=B)
+    n[0] = max_n
+    if B > 1:
+        n[1] = 0
+    return [int(x) for x in n]
 
 
 def default_scale(D):
