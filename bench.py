@@ -245,6 +245,43 @@ def bench_decode_ragged(rel, torch, dev, B=32, H=12, D=64, nmax=4096, steps=64, 
             "frac_hbm_peak": byts / steps / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": byts}
 
 
+def bench_mhr(rel, torch, dev, reps, B=16, H=8, T=2048, D=64, seed=42):
+    """Multi-Head Relation with its upstream maps (RoPE of p1 / p2 from
+    [T, D/2] tables, Givens mixing of I, pairing M_B) on the 30M layer shape:
+    forward and forward+backward, next to the plain operator on the same
+    tensors. Flops are the operator's (the maps are O(T D) per head)."""
+    from workloads import make_inputs, make_mhr_maps
+    inp = make_inputs(B, H, T, D, "bf16", seed=seed, with_dy=True)
+    p1, p2, I, dy = (inp[n].to(dev) for n in ("q", "k", "v", "dy"))
+    cs, sn, th = (t.to(dev) for t in make_mhr_maps(T, D, H, seed))
+    lam, scale = inp["lam"], 1 / math.sqrt(D)
+    lib = rel.load_library()
+    wsf = torch.empty((lib.relation_mhr_fwd_workspace_bytes(1, B, H, T, D),), device=dev,
+                      dtype=torch.uint8)
+    wsb = torch.empty((lib.relation_mhr_bwd_workspace_bytes(1, B, H, T, D),), device=dev,
+                      dtype=torch.uint8)
+    y = torch.empty_like(I)
+    lse = torch.empty((B, H, T), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+    tf, tb = EventTimer(torch, stream), EventTimer(torch, stream)
+    for i in range(reps + 3):
+        s0 = tf.start() if i >= 3 else None
+        rel.relation_mhr_fwd(p1, p2, I, cs, sn, th, 1, lam=lam, scale=scale, y=y, lse=lse,
+                             workspace=wsf)
+        if i >= 3:
+            tf.stop(s0)
+        s1 = tb.start() if i >= 3 else None
+        rel.relation_mhr_bwd(p1, p2, I, y, dy, lse, cs, sn, th, 1, lam=lam, scale=scale,
+                             workspace=wsb)
+        if i >= 3:
+            tb.stop(s1)
+    f = fwd_flops(B, H, T, D)
+    fm, bm = tf.mean_ms(), tb.mean_ms()
+    return {"workload": "layer30m MHR (RoPE + Givens M_B)", "fwd_ms": fm, "bwd_ms": bm,
+            "fwd_tflops": f / (fm * 1e-3) / 1e12,
+            "fwdbwd_tflops": 3.5 * f / ((fm + bm) * 1e-3) / 1e12}
+
+
 def bench_copy(torch, dev, nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of known size (torch's copy kernel): the
     calibration for the FETCH_SIZE / WRITE_SIZE counters (reads nbytes and
@@ -317,7 +354,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["step", "fwd", "decode", "ragged", "attn", "copy"],
+    ap.add_argument("--only", choices=["step", "fwd", "decode", "ragged", "mhr", "attn", "copy"],
                     default=None,
                     help="run one measurement and print its raw numbers ('copy': a plain "
                          "device copy of known size, the HBM-counter calibration)")
@@ -350,6 +387,9 @@ def main():
         return
     if args.only == "ragged":
         print(json.dumps(bench_decode_ragged(rel, torch, dev)))
+        return
+    if args.only == "mhr":
+        print(json.dumps(bench_mhr(rel, torch, dev, args.steps)))
         return
     if args.only == "attn":
         print(json.dumps(bench_fwdbwd_vs_attention(rel, torch, dev, args.steps)))
@@ -391,6 +431,7 @@ def main():
                                   "frac": dec["call_GBps"] / PEAK_HBM_GBS,
                                   "traffic": kernel_traffic("decode_split_kernel@cache4096")}
         torch.cuda.empty_cache()
+        rec["mhr_layer30m"] = bench_mhr(rel, torch, dev, 10)
         rec["decode_ragged"] = bench_decode_ragged(rel, torch, dev)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

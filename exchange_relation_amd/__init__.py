@@ -24,6 +24,8 @@ __all__ = [
     "relation_cache_decode",
     "relation_decode_workspace_bytes",
     "relation_cache_decode_ragged",
+    "relation_mhr_fwd",
+    "relation_mhr_bwd",
     "relation_status_string",
     "relation_version",
     "RelationFunction",
@@ -40,6 +42,10 @@ EXPORTED_SYMBOLS = (
     "relation_decode_workspace_bytes",
     "relation_cache_decode",
     "relation_cache_decode_ragged",
+    "relation_mhr_fwd_workspace_bytes",
+    "relation_mhr_fwd",
+    "relation_mhr_bwd_workspace_bytes",
+    "relation_mhr_bwd",
     "relation_status_string",
     "relation_version",
 )
@@ -86,6 +92,17 @@ def load_library():
     lib.relation_cache_decode_ragged.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
                                                  c_int, vp, c_int, vp, vp, vp, c_size, c_float,
                                                  c_float, c_float, vp]
+    lib.relation_mhr_fwd_workspace_bytes.restype = c_size
+    lib.relation_mhr_fwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    lib.relation_mhr_fwd.restype = c_int
+    lib.relation_mhr_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
+                                     c_int, vp, vp, vp, vp, c_size, c_float, c_float, c_float, vp]
+    lib.relation_mhr_bwd_workspace_bytes.restype = c_size
+    lib.relation_mhr_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    lib.relation_mhr_bwd.restype = c_int
+    lib.relation_mhr_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
+                                     c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size, c_float,
+                                     c_float, c_float, vp]
     lib.relation_status_string.restype = ctypes.c_char_p
     lib.relation_status_string.argtypes = [c_int]
     lib.relation_version.restype = c_int
@@ -278,6 +295,81 @@ def relation_cache_decode_ragged(q, k_new, v_new, k_cache, v_cache, n_hist, max_
     if st != 0:
         raise RelationError(st, "relation_cache_decode_ragged")
     return y, gate
+
+
+def _mhr_maps(p1, rope_cos, rope_sin, theta):
+    B, H, T, D = p1.shape
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("rope_cos and rope_sin go together")
+    if rope_cos is not None:
+        _check(rope_cos, "rope_cos", torch.float32, (T, D // 2), p1.device)
+        _check(rope_sin, "rope_sin", torch.float32, (T, D // 2), p1.device)
+    if theta is not None:
+        _check(theta, "theta", torch.float32, (H // 2,), p1.device)
+
+
+def relation_mhr_fwd(p1, p2, I, rope_cos=None, rope_sin=None, theta=None, pairing=0, lam=0.0,
+                     scale=None, tau_s=2.0, y=None, lse=None, gate=None, want_gate=False,
+                     workspace=None, stream=None):
+    """Multi-Head Relation forward with RoPE of p1, p2 (tables [T, D/2]) and
+    Givens mixing of I (angles [H/2], pairing 0 or 1). Returns (y, lse, gate)."""
+    lib = load_library()
+    B, H, T, D = p1.shape
+    dev, dt = p1.device, p1.dtype
+    code = _dtype_code(p1)
+    for name, t in (("p1", p1), ("p2", p2), ("I", I)):
+        _check(t, name, dt, (B, H, T, D), dev)
+    _mhr_maps(p1, rope_cos, rope_sin, theta)
+    y = torch.empty_like(I) if y is None else y
+    lse = torch.empty((B, H, T), device=dev, dtype=torch.float32) if lse is None else lse
+    _check(y, "y", dt, (B, H, T, D), dev)
+    _check(lse, "lse", torch.float32, (B, H, T), dev)
+    if gate is None and want_gate:
+        gate = torch.empty((B, H, T), device=dev, dtype=torch.float32)
+    need = int(lib.relation_mhr_fwd_workspace_bytes(code, B, H, T, D))
+    if workspace is None and need:
+        workspace = torch.empty((need,), device=dev, dtype=torch.uint8)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.relation_mhr_fwd(code, B, H, T, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(rope_cos),
+                              _ptr(rope_sin), _ptr(theta), int(pairing), _ptr(y), _ptr(lse),
+                              _ptr(gate), _ptr(workspace), wsb, _scale(D, scale), float(tau_s),
+                              float(lam), _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_mhr_fwd")
+    return y, lse, gate
+
+
+def relation_mhr_bwd(p1, p2, I, y, dy, lse, rope_cos=None, rope_sin=None, theta=None, pairing=0,
+                     lam=0.0, scale=None, tau_s=2.0, dp1=None, dp2=None, dI=None, dlambda=None,
+                     dtheta=None, workspace=None, stream=None):
+    """Gradients of relation_mhr_fwd. Returns (dp1, dp2, dI, dlambda [1],
+    dtheta [H/2] or None)."""
+    lib = load_library()
+    B, H, T, D = p1.shape
+    dev, dt = p1.device, p1.dtype
+    code = _dtype_code(p1)
+    for name, t in (("p1", p1), ("p2", p2), ("I", I), ("y", y), ("dy", dy)):
+        _check(t, name, dt, (B, H, T, D), dev)
+    _check(lse, "lse", torch.float32, (B, H, T), dev)
+    _mhr_maps(p1, rope_cos, rope_sin, theta)
+    dp1 = torch.empty_like(p1) if dp1 is None else dp1
+    dp2 = torch.empty_like(p2) if dp2 is None else dp2
+    dI = torch.empty_like(I) if dI is None else dI
+    dlambda = torch.empty((1,), device=dev, dtype=torch.float32) if dlambda is None else dlambda
+    if theta is not None and dtheta is None:
+        dtheta = torch.empty((H // 2,), device=dev, dtype=torch.float32)
+    need = int(lib.relation_mhr_bwd_workspace_bytes(code, B, H, T, D))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), device=dev, dtype=torch.uint8)
+    st = lib.relation_mhr_bwd(code, B, H, T, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(rope_cos),
+                              _ptr(rope_sin), _ptr(theta), int(pairing), _ptr(y), _ptr(dy),
+                              _ptr(lse), _ptr(dp1), _ptr(dp2), _ptr(dI), _ptr(dlambda),
+                              _ptr(dtheta), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _scale(D, scale),
+                              float(tau_s), float(lam), _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_mhr_bwd")
+    return dp1, dp2, dI, dlambda, dtheta
 
 
 class RelationFunction(torch.autograd.Function):

@@ -25,6 +25,7 @@ SOURCES = [
     "bwd_f32.hip",
     "bwd_bf16.hip",
     "decode.hip",
+    "mhr.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

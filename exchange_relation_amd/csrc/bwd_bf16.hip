@@ -82,7 +82,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
     const float* __restrict__ lse, const float* __restrict__ Dr, float* __restrict__ dq_acc,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int T, int BH, float kscale,
-    float scale, float inv_tau, float lam) {
+    float scale, float inv_tau, float lam, float* __restrict__ dk32, float* __restrict__ dv32) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -386,6 +386,23 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
   // ---- dK = scale * dK^T^T, dV = dV^T^T (key kj, d rows of the accumulators)
   if (kj >= T) return;
   const size_t row = base + static_cast<size_t>(kj) * D;
+  if (dk32) {  // fp32 results for a later pass (Multi-Head Relation's transposes)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + g4 * 8 + hf * 4;
+        const f32x16& ka = db == 0 ? dk0 : dk1;
+        const f32x16& va = db == 0 ? dv0 : dv1;
+        *reinterpret_cast<f32x4*>(dk32 + row + d0) =
+            f32x4{ka[g4 * 4] * scale, ka[g4 * 4 + 1] * scale, ka[g4 * 4 + 2] * scale,
+                  ka[g4 * 4 + 3] * scale};
+        *reinterpret_cast<f32x4*>(dv32 + row + d0) =
+            f32x4{va[g4 * 4], va[g4 * 4 + 1], va[g4 * 4 + 2], va[g4 * 4 + 3]};
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -434,7 +451,7 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                            const uint16_t* v, const uint16_t* y, const uint16_t* dy,
                            const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                            float* dlambda, void* ws, float scale, float tau, float lam,
-                           hipStream_t stream) {
+                           hipStream_t stream, float* dk32, float* dv32) {
   using namespace bwdbf16;
   const BwdWorkspace w = bwd_workspace_layout(1, B, H, T, D);
   char* wsb = static_cast<char*>(ws);
@@ -449,12 +466,15 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
   const int nkb = (T + BK - 1) / BK;
   hipLaunchKernelGGL(bwd_bf16_kernel, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
                      stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e, scale,
-                     1.0f / tau, lam);
+                     1.0f / tau, lam, dk32, dv32);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dq_finalize_kernel, dim3(eg), dim3(256), 0, stream,
-                     reinterpret_cast<const float4*>(dq_acc), reinterpret_cast<uint2*>(dq), n4,
-                     scale, reinterpret_cast<const float*>(wsb + w.off_part), w.npart, dlambda);
+  // with fp32 results requested, dq stays in the accumulator (the caller
+  // scales it) and only the dL/dlambda reduction runs
+  hipLaunchKernelGGL(dq_finalize_kernel, dim3(dk32 ? 1u : eg), dim3(256), 0, stream,
+                     reinterpret_cast<const float4*>(dq_acc), reinterpret_cast<uint2*>(dq),
+                     dk32 ? size_t{0} : n4, scale,
+                     reinterpret_cast<const float*>(wsb + w.off_part), w.npart, dlambda);
   return hipGetLastError();
 }
 

@@ -114,4 +114,66 @@ __device__ __forceinline__ void load_row_piece<float, 32>(const float* p, float*
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
 }
 
+// 8 bf16 <-> 8 fp32
+__device__ __forceinline__ void unpack8(u32x4 w, float (&x)[8]) {
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(a[i] << 16);
+    x[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
+  const u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                   pack_bf16x2(x[6], x[7])};
+  return w;
+}
+// RoPE of 8 pairs (lo_e, hi_e) = (x_d, x_{d+D/2}) at one position (Sec. 3.1,
+// rotate-half pairing): lo' = lo cos - hi sin, hi' = lo sin + hi cos.
+__device__ __forceinline__ void rope8(u32x4& lo, u32x4& hi, const f32x4 (&cs)[2],
+                                      const f32x4 (&sn)[2]) {
+  float a[8], b[8];
+  unpack8(lo, a);
+  unpack8(hi, b);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float c = cs[e >> 2][e & 3], s_ = sn[e >> 2][e & 3];
+    const float a2 = fmaf(a[e], c, -b[e] * s_);
+    b[e] = fmaf(a[e], s_, b[e] * c);
+    a[e] = a2;
+  }
+  lo = pack8(a);
+  hi = pack8(b);
+}
+
+// Multi-Head Relation's upstream maps (Sec. 3.1-3.2, App. A.2.2-A.2.3): rotary tables cos / sin [T, D/2] fp32 (NULL: none) and
+// one Givens angle per head pair (NULL: no mixing) with the pairing pattern
+// (0: heads (0,1), (2,3), ...; 1: (1,2), ..., (H-1,0)) of H heads.
+struct Mhr {
+  const float* cos;
+  const float* sin;
+  const float* theta;
+  int pairing;
+  int H;
+};
+
+// Givens role of head h: its pair, its partner and the sign of the partner's
+// term, I'_h = cos I_h + sgn sin I_partner (first of a pair: +, second: -).
+__device__ __forceinline__ void givens_role(int h, int H, int pairing, int& pair, int& partner,
+                                            float& sgn) {
+  if (pairing == 0) {
+    pair = h >> 1;
+    partner = h ^ 1;
+    sgn = (h & 1) ? -1.f : 1.f;
+  } else if (h & 1) {  // first of (2p+1, 2p+2)
+    pair = h >> 1;
+    partner = (h + 1) % H;
+    sgn = 1.f;
+  } else {  // second of (h-1, h); head 0 closes the ring with head H-1
+    pair = (h == 0 ? H : h) / 2 - 1;
+    partner = (h + H - 1) % H;
+    sgn = -1.f;
+  }
+}
+
 }  // namespace rel

@@ -176,10 +176,12 @@ __device__ __forceinline__ void accumulate(const uint16_t* vs, int sb, const f32
   }
 }
 
+template <bool MHR>
 __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ y, float* __restrict__ lse,
-    float* __restrict__ gate, int T, int BH, int nqb, float qscale, float inv_tau, float lam) {
+    float* __restrict__ gate, int T, int BH, int nqb, float qscale, float inv_tau, float lam,
+    Mhr mh) {
   __shared__ uint16_t kbuf[3][BN * KS];  // K ring: tiles t, t+1 resident, t+2 landing
   __shared__ uint16_t vbuf[2][BN * VS];  // V: tile t resident, t+1 landing
   const int tid = threadIdx.x;
@@ -195,18 +197,36 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
   const int q0 = qb * BM + wave * 32;
   const int qi = q0 + r;
   const bool wave_live = q0 < T;
+  // Multi-Head Relation: RoPE of this head's query rows, fused into the Q
+  // fragment load (keys and values arrive already rotated / mixed)
+  const bool rope = MHR && mh.cos != nullptr;
 
   // ---- Q fragments: B operands of S^T = K Q^T. Lane holds query r,
   // d = hf*8 + 16*c + [0, 8) for c = 0..3 (rows past T read row T-1 and are
-  // zeroed).
+  // zeroed); c and c + 2 hold a RoPE pair (d, d + 32).
   bf16x8 qf[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  {
     const int qr = qi < T ? qi : T - 1;
-    u32x4 raw = *reinterpret_cast<const u32x4*>(q + base + static_cast<size_t>(qr) * D + hf * 8 + 16 * c);
-    const u32x4 z = {0, 0, 0, 0};
-    raw = qi < T ? raw : z;
-    qf[c] = __builtin_bit_cast(bf16x8, raw);
+    u32x4 raw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      raw[c] = *reinterpret_cast<const u32x4*>(q + base + static_cast<size_t>(qr) * D + hf * 8 + 16 * c);
+      const u32x4 z = {0, 0, 0, 0};
+      raw[c] = qi < T ? raw[c] : z;
+    }
+    if (rope) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const size_t t0 = static_cast<size_t>(qr) * (D / 2) + 16 * c + hf * 8;
+        const f32x4 cs[2] = {*reinterpret_cast<const f32x4*>(mh.cos + t0),
+                             *reinterpret_cast<const f32x4*>(mh.cos + t0 + 4)};
+        const f32x4 sn[2] = {*reinterpret_cast<const f32x4*>(mh.sin + t0),
+                             *reinterpret_cast<const f32x4*>(mh.sin + t0 + 4)};
+        rope8(raw[c], raw[c + 2], cs, sn);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
   }
 
   RowState st;
@@ -365,13 +385,19 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
 
 hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale,
-                           float tau, float lam, hipStream_t stream) {
+                           float tau, float lam, hipStream_t stream, const float* rope_cos,
+                           const float* rope_sin) {
   (void)D;
   const int BH = B * H;
   const int nqb = (T + fwdbf16::BM - 1) / fwdbf16::BM;
   const dim3 grid(static_cast<unsigned>(nqb) * BH);
-  hipLaunchKernelGGL(fwdbf16::fwd_bf16_kernel, grid, dim3(256), 0, stream, q, k, v, y, lse, gate,
-                     T, BH, nqb, scale * kLog2e, 1.0f / tau, lam);
+  const Mhr mh{rope_cos, rope_sin, nullptr, 0, H};
+  if (rope_cos == nullptr)
+    hipLaunchKernelGGL(fwdbf16::fwd_bf16_kernel<false>, grid, dim3(256), 0, stream, q, k, v, y,
+                       lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh);
+  else
+    hipLaunchKernelGGL(fwdbf16::fwd_bf16_kernel<true>, grid, dim3(256), 0, stream, q, k, v, y,
+                       lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh);
   return hipGetLastError();
 }
 

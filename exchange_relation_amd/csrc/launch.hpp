@@ -15,9 +15,13 @@ hipError_t launch_fwd_f32(int B, int H, int T, int D, const float* q, const floa
                           float tau, float lam, hipStream_t stream);
 
 // Forward, bf16 storage, bf16 MFMA contractions with fp32 accumulation, D = 64.
+// rope_cos / rope_sin ([T, D/2] fp32, or NULL): RoPE of q fused into the Q
+// fragment load (Multi-Head Relation; k and v come in already rotated /
+// mixed).
 hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale,
-                           float tau, float lam, hipStream_t stream);
+                           float tau, float lam, hipStream_t stream,
+                           const float* rope_cos = nullptr, const float* rope_sin = nullptr);
 
 // Backward. Workspace layout and size are owned by the launcher.
 size_t bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
@@ -25,11 +29,14 @@ hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const floa
                           const float* v, const float* y, const float* dy, const float* lse,
                           float* dq, float* dk, float* dv, float* dlambda, void* ws, float scale,
                           float tau, float lam, hipStream_t stream);
+// dk32 / dv32 non-NULL: dk (scaled) and dv go there in fp32, and dq is left
+// unscaled in the workspace accumulator (bwd_workspace_layout(...).off_dq).
 hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const uint16_t* y, const uint16_t* dy,
                            const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                            float* dlambda, void* ws, float scale, float tau, float lam,
-                           hipStream_t stream);
+                           hipStream_t stream, float* dk32 = nullptr,
+                           float* dv32 = nullptr);
 
 // Relation Cache decode (one step). dtype 0 = fp32, 1 = bf16. n_hist_dev
 // NULL: every sequence has n_hist slots of history; otherwise sequence b has
@@ -39,5 +46,21 @@ hipError_t launch_decode(int dtype, int B, int H, int D, const void* q, const vo
                          const void* v_new, void* k_cache, void* v_cache, int capacity,
                          int n_hist, const int* n_hist_dev, void* y, float* gate, void* ws,
                          float scale, float tau, float lam, hipStream_t stream);
+
+// Multi-Head Relation passes (mhr.hip): RoPE of p1 / p2 into q / k and the
+// Givens mixing of vi into v (an output pointer NULL: not produced); and the
+// transposes of both on fp32 gradients (dq scaled by dq_scale), rounded once
+// into dp1, dp2, dI, with dtheta [H/2] reduced from `part` (mhr_part_floats
+// floats). dtype 0 = fp32, 1 = bf16.
+size_t mhr_part_floats(int B, int H, int T, int D);
+hipError_t launch_mhr_prepare(int dtype, int B, int H, int T, int D, const void* p1,
+                              const void* p2, const void* vi, void* q, void* k, void* v,
+                              const float* rope_cos, const float* rope_sin, const float* theta,
+                              int pairing, hipStream_t stream);
+hipError_t launch_mhr_post(int dtype, int B, int H, int T, int D, const float* dq, float dq_scale,
+                           const float* dk, const float* dv, const void* vmix, void* dp1,
+                           void* dp2, void* dI, float* dtheta, float* part,
+                           const float* rope_cos, const float* rope_sin, const float* theta,
+                           int pairing, hipStream_t stream);
 
 }  // namespace rel

@@ -1,0 +1,314 @@
+// Multi-Head Relation's upstream maps around the Relation operator, as
+// separate bandwidth-bound passes (Sec. 3.1-3.2; App. A.2.2-A.2.3):
+//
+//   prepare : q = RoPE(p1), k = RoPE(p2), v = Givens(I) into a workspace, so
+//             the plain kernels run on them. Keys and values are rotated /
+//             mixed once here rather than in the forward's tile loads, where
+//             every query block of a head would redo them on the VALU the
+//             forward is bound by; the bf16 forward only fuses the rotation
+//             of its own query rows, with the same arithmetic (rope8), so
+//             forward and backward see bit-identical q, k, v;
+//   unrotate: dp = RoPE^T(dq) for dq and dk, in fp32, rounded once into the
+//             output dtype;
+//   unmix   : dI = Givens^T(dv) for both heads of every pair, and the angle
+//             gradient dtheta_p = sum(dv_a v_b - dv_b v_a) (the rotation's
+//             derivative maps v_a -> v_b and v_b -> -v_a), reduced per
+//             workgroup and then over workgroups in a fixed order.
+//
+// RoPE pairs element d with d + D/2 and reads the caller's tables cos, sin
+// [T, D/2] (fp32) at the row's position. Thread layout of every pass: one
+// thread per (row, 8 pairs) - the chunk j of elements d = 8j..8j+7 and the
+// matching chunk of d + D/2 - so D/16 threads per row.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rel {
+namespace mhr {
+
+template <typename TE> struct Io;
+template <> struct Io<uint16_t> {  // 8 bf16 per chunk
+  __device__ static void load(const uint16_t* p, float (&x)[8]) {
+    unpack8(*reinterpret_cast<const u32x4*>(p), x);
+  }
+  __device__ static void store(uint16_t* p, const float (&x)[8]) {
+    *reinterpret_cast<u32x4*>(p) = pack8(x);
+  }
+};
+template <> struct Io<float> {  // 8 floats per chunk
+  __device__ static void load(const float* p, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+  }
+  __device__ static void store(float* p, const float (&x)[8]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  }
+};
+__device__ __forceinline__ void load8f(const float* p, float (&x)[8]) { Io<float>::load(p, x); }
+
+// Thread -> (row of [B*H*T], chunk j) for a tensor of D-wide rows.
+struct Slot {
+  size_t row;
+  int j;
+  bool ok;
+};
+template <int D>
+__device__ __forceinline__ Slot slot_of(size_t rows) {
+  constexpr int CPR = D / 16;  // chunks of 8 pairs per row
+  const size_t g = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  return {g / CPR, static_cast<int>(g % CPR), g / CPR < rows};
+}
+
+// The same arithmetic as rope8 / the fused forward's mixing, on fp32 lanes.
+__device__ __forceinline__ void rope_pairs(float (&a)[8], float (&b)[8], const float (&c)[8],
+                                           const float (&s)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float a2 = fmaf(a[e], c[e], -b[e] * s[e]);
+    b[e] = fmaf(a[e], s[e], b[e] * c[e]);
+    a[e] = a2;
+  }
+}
+__device__ __forceinline__ void rope_pairs_t(float (&a)[8], float (&b)[8], const float (&c)[8],
+                                             const float (&s)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float a2 = fmaf(a[e], c[e], b[e] * s[e]);
+    b[e] = fmaf(-a[e], s[e], b[e] * c[e]);
+    a[e] = a2;
+  }
+}
+
+// q = RoPE(p1), k = RoPE(p2), v = Givens(I); rows = B*H*T. A NULL output is
+// not produced (q, k need the RoPE tables, v the angles).
+template <typename TE, int D>
+__global__ __launch_bounds__(256) void prepare_kernel(const TE* __restrict__ p1,
+                                                      const TE* __restrict__ p2,
+                                                      const TE* __restrict__ vi, TE* __restrict__ q,
+                                                      TE* __restrict__ k, TE* __restrict__ v,
+                                                      size_t rows, int T, Mhr mh) {
+  const Slot sl = slot_of<D>(rows);
+  if (!sl.ok) return;
+  const int t = static_cast<int>(sl.row % T);
+  const size_t o = sl.row * D + sl.j * 8;
+  float a[8], b[8];
+  if (q || k) {  // RoPE tables of the row (requested only with RoPE)
+    float c[8], s[8];
+    load8f(mh.cos + static_cast<size_t>(t) * (D / 2) + sl.j * 8, c);
+    load8f(mh.sin + static_cast<size_t>(t) * (D / 2) + sl.j * 8, s);
+    if (q) {
+      Io<TE>::load(p1 + o, a);
+      Io<TE>::load(p1 + o + D / 2, b);
+      rope_pairs(a, b, c, s);
+      Io<TE>::store(q + o, a);
+      Io<TE>::store(q + o + D / 2, b);
+    }
+    if (k) {
+      Io<TE>::load(p2 + o, a);
+      Io<TE>::load(p2 + o + D / 2, b);
+      rope_pairs(a, b, c, s);
+      Io<TE>::store(k + o, a);
+      Io<TE>::store(k + o + D / 2, b);
+    }
+  }
+  if (!v) return;
+  Io<TE>::load(vi + o, a);
+  Io<TE>::load(vi + o + D / 2, b);
+  {
+    const size_t head = sl.row / T;
+    const int h = static_cast<int>(head % mh.H);
+    int pair, partner;
+    float sgn;
+    givens_role(h, mh.H, mh.pairing, pair, partner, sgn);
+    const float mixc = cosf(mh.theta[pair]), mixs = sgn * sinf(mh.theta[pair]);
+    const size_t po = o + (static_cast<size_t>(partner) - h) * T * D;
+    float pa[8], pb[8];
+    Io<TE>::load(vi + po, pa);
+    Io<TE>::load(vi + po + D / 2, pb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = fmaf(mixc, a[e], mixs * pa[e]);
+      b[e] = fmaf(mixc, b[e], mixs * pb[e]);
+    }
+  }
+  Io<TE>::store(v + o, a);
+  Io<TE>::store(v + o + D / 2, b);
+}
+
+// dp = RoPE^T(scale * g) for one gradient tensor (g fp32, may alias dp when
+// TE = float: every thread reads its elements before writing them).
+template <typename TE, int D>
+__global__ __launch_bounds__(256) void unrotate_kernel(const float* g, TE* dp, size_t rows, int T,
+                                                       float scale, const float* __restrict__ cs,
+                                                       const float* __restrict__ sn) {
+  const Slot sl = slot_of<D>(rows);
+  if (!sl.ok) return;
+  const int t = static_cast<int>(sl.row % T);
+  const size_t o = sl.row * D + sl.j * 8;
+  float a[8], b[8];
+  load8f(g + o, a);
+  load8f(g + o + D / 2, b);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] *= scale;
+    b[e] *= scale;
+  }
+  if (cs) {
+    float c[8], s[8];
+    load8f(cs + static_cast<size_t>(t) * (D / 2) + sl.j * 8, c);
+    load8f(sn + static_cast<size_t>(t) * (D / 2) + sl.j * 8, s);
+    rope_pairs_t(a, b, c, s);
+  }
+  Io<TE>::store(dp + o, a);
+  Io<TE>::store(dp + o + D / 2, b);
+}
+
+// dI = Givens^T(dv) and the dtheta partials. One thread per (pair p, batch b,
+// position t, chunk j); blockIdx.y = p * B + b, so a workgroup never mixes
+// pairs and its partial belongs to pair p alone. dv (fp32) may alias dI when
+// TE = float. v holds the mixed values (the forward's I').
+template <typename TE, int D>
+__global__ __launch_bounds__(256) void unmix_kernel(const float* dv, TE* dI,
+                                                    const TE* __restrict__ v, int B, int T,
+                                                    Mhr mh, float* __restrict__ part) {
+  __shared__ float red[256];
+  constexpr int CPR = D / 16;
+  const int p = blockIdx.y / B, b = blockIdx.y % B;
+  const size_t g = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const size_t t = g / CPR;
+  const int j = static_cast<int>(g % CPR);
+  float acc = 0.f;
+  if (t < static_cast<size_t>(T)) {
+    // the pair's heads: first a (sign +), second bb
+    const int ha = mh.pairing == 0 ? 2 * p : 2 * p + 1;
+    const int hb = mh.pairing == 0 ? 2 * p + 1 : (2 * p + 2) % mh.H;
+    const float c = cosf(mh.theta[p]), s = sinf(mh.theta[p]);
+    const size_t oa = ((static_cast<size_t>(b) * mh.H + ha) * T + t) * D + j * 8;
+    const size_t ob = ((static_cast<size_t>(b) * mh.H + hb) * T + t) * D + j * 8;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const size_t xa = oa + half * (D / 2), xb = ob + half * (D / 2);
+      float ga[8], gb[8], va[8], vb[8];
+      load8f(dv + xa, ga);
+      load8f(dv + xb, gb);
+      Io<TE>::load(v + xa, va);
+      Io<TE>::load(v + xb, vb);
+      float ia[8], ib[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc = fmaf(ga[e], vb[e], acc);
+        acc = fmaf(-gb[e], va[e], acc);
+        ia[e] = fmaf(c, ga[e], -s * gb[e]);
+        ib[e] = fmaf(s, ga[e], c * gb[e]);
+      }
+      Io<TE>::store(dI + xa, ia);
+      Io<TE>::store(dI + xb, ib);
+    }
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[static_cast<size_t>(blockIdx.y) * gridDim.x + blockIdx.x] = red[0];
+}
+
+// dtheta[p] = sum of pair p's partials, in a fixed order (deterministic).
+__global__ __launch_bounds__(256) void dtheta_kernel(const float* __restrict__ part, int nper,
+                                                     float* __restrict__ dtheta) {
+  __shared__ float red[256];
+  const float* pp = part + static_cast<size_t>(blockIdx.x) * nper;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < nper; i += 256) s += pp[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dtheta[blockIdx.x] = red[0];
+}
+
+template <typename TE, int D>
+hipError_t run_prepare(int B, int H, int T, const void* p1, const void* p2, const void* vi,
+                       void* q, void* k, void* v, const Mhr& mh, hipStream_t stream) {
+  const size_t rows = static_cast<size_t>(B) * H * T;
+  const size_t threads = rows * (D / 16);
+  hipLaunchKernelGGL((prepare_kernel<TE, D>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                     dim3(256), 0, stream, static_cast<const TE*>(p1), static_cast<const TE*>(p2),
+                     static_cast<const TE*>(vi), static_cast<TE*>(q), static_cast<TE*>(k),
+                     static_cast<TE*>(v), rows, T, mh);
+  return hipGetLastError();
+}
+
+template <typename TE, int D>
+hipError_t run_post(int B, int H, int T, const float* dq, float dq_scale, const float* dk,
+                    const float* dv, const void* vmix, void* dp1, void* dp2, void* dI,
+                    float* dtheta, float* part, const Mhr& mh, hipStream_t stream) {
+  const size_t rows = static_cast<size_t>(B) * H * T;
+  const unsigned nb = static_cast<unsigned>((rows * (D / 16) + 255) / 256);
+  hipLaunchKernelGGL((unrotate_kernel<TE, D>), dim3(nb), dim3(256), 0, stream, dq,
+                     static_cast<TE*>(dp1), rows, T, dq_scale, mh.cos, mh.sin);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((unrotate_kernel<TE, D>), dim3(nb), dim3(256), 0, stream, dk,
+                     static_cast<TE*>(dp2), rows, T, 1.0f, mh.cos, mh.sin);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (mh.theta == nullptr) {  // no mixing: dI = dv (a plain copy / rounding)
+    hipLaunchKernelGGL((unrotate_kernel<TE, D>), dim3(nb), dim3(256), 0, stream, dv,
+                       static_cast<TE*>(dI), rows, T, 1.0f, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  const unsigned nx = static_cast<unsigned>((static_cast<size_t>(T) * (D / 16) + 255) / 256);
+  hipLaunchKernelGGL((unmix_kernel<TE, D>), dim3(nx, static_cast<unsigned>(H / 2 * B)), dim3(256),
+                     0, stream, dv, static_cast<TE*>(dI), static_cast<const TE*>(vmix), B, T, mh,
+                     part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dtheta) {
+    hipLaunchKernelGGL(dtheta_kernel, dim3(static_cast<unsigned>(H / 2)), dim3(256), 0, stream,
+                       part, static_cast<int>(nx) * B, dtheta);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace mhr
+
+size_t mhr_part_floats(int B, int H, int T, int D) {
+  const size_t nx = (static_cast<size_t>(T) * (D / 16) + 255) / 256;
+  return nx * static_cast<size_t>(B) * (H / 2 > 0 ? H / 2 : 1);
+}
+
+hipError_t launch_mhr_prepare(int dtype, int B, int H, int T, int D, const void* p1,
+                              const void* p2, const void* vi, void* q, void* k, void* v,
+                              const float* rope_cos, const float* rope_sin, const float* theta,
+                              int pairing, hipStream_t stream) {
+  const Mhr mh{rope_cos, rope_sin, theta, pairing, H};
+  if (dtype == 1) return mhr::run_prepare<uint16_t, 64>(B, H, T, p1, p2, vi, q, k, v, mh, stream);
+  if (D == 64) return mhr::run_prepare<float, 64>(B, H, T, p1, p2, vi, q, k, v, mh, stream);
+  return mhr::run_prepare<float, 32>(B, H, T, p1, p2, vi, q, k, v, mh, stream);
+}
+
+hipError_t launch_mhr_post(int dtype, int B, int H, int T, int D, const float* dq, float dq_scale,
+                           const float* dk, const float* dv, const void* vmix, void* dp1,
+                           void* dp2, void* dI, float* dtheta, float* part,
+                           const float* rope_cos, const float* rope_sin, const float* theta,
+                           int pairing, hipStream_t stream) {
+  const Mhr mh{rope_cos, rope_sin, theta, pairing, H};
+  if (dtype == 1)
+    return mhr::run_post<uint16_t, 64>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta,
+                                       part, mh, stream);
+  if (D == 64)
+    return mhr::run_post<float, 64>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta,
+                                    part, mh, stream);
+  return mhr::run_post<float, 32>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta, part,
+                                  mh, stream);
+}
+
+}  // namespace rel

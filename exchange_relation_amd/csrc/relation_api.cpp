@@ -7,6 +7,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "bwd_common.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -39,6 +40,50 @@ relation_status check_shape(int B, int H, int T, int D) {
 }
 
 relation_status from_hip(hipError_t e) { return e == hipSuccess ? REL_OK : REL_ERR_HIP; }
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of the Multi-Head Relation entry points: the rotated / mixed
+// q, k, v (the bf16 forward rotates its queries in registers and needs only
+// k and v), then for the backward the plain backward's workspace, fp32 dk
+// and dv (bf16 only) and the dtheta partials.
+struct MhrLayout {
+  size_t q, k, v, bwd, dk32, dv32, part, total;
+};
+MhrLayout mhr_layout(bool backward, relation_dtype dt, int B, int H, int T, int D) {
+  MhrLayout L{};
+  const size_t n = static_cast<size_t>(B) * H * T * D;
+  const size_t esz = dt == REL_BF16 ? 2 : 4;
+  size_t off = 0;
+  if (backward || dt == REL_F32) {
+    L.q = off; off += round256(n * esz);
+  }
+  L.k = off; off += round256(n * esz);
+  L.v = off; off += round256(n * esz);
+  if (backward) {
+    L.bwd = off; off += round256(rel::bwd_workspace_bytes(dt == REL_BF16 ? 1 : 0, B, H, T, D));
+    if (dt == REL_BF16) {
+      L.dk32 = off; off += round256(n * 4);
+      L.dv32 = off; off += round256(n * 4);
+    }
+    L.part = off; off += round256(rel::mhr_part_floats(B, H, T, D) * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+// Checks shared by the Multi-Head Relation entry points (tables and angles).
+relation_status check_mhr(int H, const float* rope_cos, const float* rope_sin, const float* theta,
+                          int pairing) {
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return REL_ERR_NULL;
+  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return REL_ERR_ALIGN;
+  if (theta) {
+    if (H % 2) return REL_ERR_SHAPE;
+    if (pairing != 0 && pairing != 1) return REL_ERR_PARAM;
+    if (!aligned4(theta)) return REL_ERR_ALIGN;
+  }
+  return REL_OK;
+}
 
 }  // namespace
 
@@ -174,6 +219,123 @@ relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H,
                                      k_cache, v_cache, capacity, max_n_hist, n_hist, y, gate,
                                      workspace, scale, tau_s, lambda,
                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t relation_mhr_fwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
+  if (check_dtype_dim(dtype, D) != REL_OK || check_shape(B, H, T, D) != REL_OK) return 0;
+  return mhr_layout(false, dtype, B, H, T, D).total;
+}
+
+relation_status relation_mhr_fwd(relation_dtype dtype, int B, int H, int T, int D, const void* p1,
+                                 const void* p2, const void* I, const float* rope_cos,
+                                 const float* rope_sin, const float* theta, int pairing, void* y,
+                                 float* lse, float* gate, void* workspace, size_t workspace_bytes,
+                                 float scale, float tau_s, float lambda, void* stream) {
+  if (!p1 || !p2 || !I || !y) return REL_ERR_NULL;
+  relation_status st = check_dtype_dim(dtype, D);
+  if (st != REL_OK) return st;
+  if ((st = check_shape(B, H, T, D)) != REL_OK) return st;
+  if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
+  if ((st = check_mhr(H, rope_cos, rope_sin, theta, pairing)) != REL_OK) return st;
+  if (!aligned16(p1) || !aligned16(p2) || !aligned16(I) || !aligned16(y) ||
+      (lse && !aligned4(lse)) || (gate && !aligned4(gate)))
+    return REL_ERR_ALIGN;
+  const MhrLayout L = mhr_layout(false, dtype, B, H, T, D);
+  if (!workspace || workspace_bytes < L.total) return REL_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return REL_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  const bool bf = dtype == REL_BF16;
+  // rotated keys / mixed values once, in a pre-pass; the bf16 kernel rotates
+  // its own query rows in registers
+  void* q = (rope_cos && !bf) ? w + L.q : nullptr;
+  void* k = rope_cos ? w + L.k : nullptr;
+  void* v = theta ? w + L.v : nullptr;
+  if ((q || k || v) && rel::launch_mhr_prepare(bf ? 1 : 0, B, H, T, D, p1, p2, I, q, k, v,
+                                               rope_cos, rope_sin, theta, pairing,
+                                               s) != hipSuccess)
+    return REL_ERR_HIP;
+  const void* qe = q ? q : p1;
+  const void* ke = k ? k : p2;
+  const void* ve = v ? v : I;
+  if (bf)
+    return from_hip(rel::launch_fwd_bf16(
+        B, H, T, D, static_cast<const uint16_t*>(qe), static_cast<const uint16_t*>(ke),
+        static_cast<const uint16_t*>(ve), static_cast<uint16_t*>(y), lse, gate, scale, tau_s,
+        lambda, s, rope_cos, rope_sin));
+  return from_hip(rel::launch_fwd_f32(B, H, T, D, static_cast<const float*>(qe),
+                                      static_cast<const float*>(ke), static_cast<const float*>(ve),
+                                      static_cast<float*>(y), lse, gate, scale, tau_s, lambda, s));
+}
+
+size_t relation_mhr_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
+  if (check_dtype_dim(dtype, D) != REL_OK || check_shape(B, H, T, D) != REL_OK) return 0;
+  return mhr_layout(true, dtype, B, H, T, D).total;
+}
+
+relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int D, const void* p1,
+                                 const void* p2, const void* I, const float* rope_cos,
+                                 const float* rope_sin, const float* theta, int pairing,
+                                 const void* y, const void* dy, const float* lse, void* dp1,
+                                 void* dp2, void* dI, float* dlambda, float* dtheta,
+                                 void* workspace, size_t workspace_bytes, float scale,
+                                 float tau_s, float lambda, void* stream) {
+  if (!p1 || !p2 || !I || !y || !dy || !lse || !dp1 || !dp2 || !dI) return REL_ERR_NULL;
+  relation_status st = check_dtype_dim(dtype, D);
+  if (st != REL_OK) return st;
+  if ((st = check_shape(B, H, T, D)) != REL_OK) return st;
+  if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
+  if ((st = check_mhr(H, rope_cos, rope_sin, theta, pairing)) != REL_OK) return st;
+  if (!aligned16(p1) || !aligned16(p2) || !aligned16(I) || !aligned16(y) || !aligned16(dy) ||
+      !aligned4(lse) || !aligned16(dp1) || !aligned16(dp2) || !aligned16(dI) ||
+      (dlambda && !aligned4(dlambda)) || (dtheta && !aligned4(dtheta)))
+    return REL_ERR_ALIGN;
+  const MhrLayout L = mhr_layout(true, dtype, B, H, T, D);
+  if (!workspace || workspace_bytes < L.total) return REL_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return REL_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  void* q = rope_cos ? w + L.q : nullptr;
+  void* k = rope_cos ? w + L.k : nullptr;
+  void* v = theta ? w + L.v : nullptr;
+  float* part = reinterpret_cast<float*>(w + L.part);
+  const float* th = theta;
+  float* dth = theta ? dtheta : nullptr;
+  const int dcode = dtype == REL_BF16 ? 1 : 0;
+  if ((q || v) && rel::launch_mhr_prepare(dcode, B, H, T, D, p1, p2, I, q, k, v, rope_cos,
+                                          rope_sin, th, pairing, s) != hipSuccess)
+    return REL_ERR_HIP;
+  if (!q) q = const_cast<void*>(p1);
+  if (!k) k = const_cast<void*>(p2);
+  if (!v) v = const_cast<void*>(I);
+  if (dtype == REL_F32) {
+    // the plain backward writes dq, dk, dv of the rotated / mixed tensors into
+    // the outputs; the transposes then run in place
+    if (rel::launch_bwd_f32(B, H, T, D, static_cast<const float*>(q),
+                            static_cast<const float*>(k), static_cast<const float*>(v),
+                            static_cast<const float*>(y), static_cast<const float*>(dy), lse,
+                            static_cast<float*>(dp1), static_cast<float*>(dp2),
+                            static_cast<float*>(dI), dlambda, w + L.bwd, scale, tau_s, lambda,
+                            s) != hipSuccess)
+      return REL_ERR_HIP;
+    return from_hip(rel::launch_mhr_post(0, B, H, T, D, static_cast<const float*>(dp1), 1.0f,
+                                         static_cast<const float*>(dp2),
+                                         static_cast<const float*>(dI), v, dp1, dp2, dI, dth,
+                                         part, rope_cos, rope_sin, th, pairing, s));
+  }
+  float* dk32 = reinterpret_cast<float*>(w + L.dk32);
+  float* dv32 = reinterpret_cast<float*>(w + L.dv32);
+  if (rel::launch_bwd_bf16(B, H, T, D, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                           static_cast<const uint16_t*>(y), static_cast<const uint16_t*>(dy), lse,
+                           static_cast<uint16_t*>(dp1), static_cast<uint16_t*>(dp2),
+                           static_cast<uint16_t*>(dI), dlambda, w + L.bwd, scale, tau_s, lambda,
+                           s, dk32, dv32) != hipSuccess)
+    return REL_ERR_HIP;
+  const float* dq_acc =
+      reinterpret_cast<const float*>(w + L.bwd + rel::bwd_workspace_layout(1, B, H, T, D).off_dq);
+  return from_hip(rel::launch_mhr_post(1, B, H, T, D, dq_acc, scale, dk32, dv32, v, dp1, dp2, dI,
+                                       dth, part, rope_cos, rope_sin, th, pairing, s));
 }
 
 }  // extern "C"

@@ -165,6 +165,76 @@ relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H,
                                              float scale, float tau_s, float lambda,
                                              void* stream);
 
+/*
+ * relation_mhr_fwd / relation_mhr_bwd — Multi-Head Relation with the two maps
+ * that precede the Relation operator in a layer (Sec. 3.1-3.2; App. A.2.2-
+ * A.2.3), fused or chained inside the call:
+ *
+ *   q = RoPE(p1), k = RoPE(p2)   rotary position encoding of the head-wise
+ *                                p1, p2 (Sec. 3.1; App. B.3: full head, base
+ *                                1e4). Element d pairs with d + D/2 and the
+ *                                pair j of the row at 0-based position t
+ *                                turns by the angle whose cosine and sine are
+ *                                rope_cos[t, j], rope_sin[t, j].
+ *   I' = Givens(I)               adjacent information slices mixed pairwise:
+ *                                for each pair (a, b) with angle theta[p],
+ *                                I'_a = cos I_a + sin I_b,
+ *                                I'_b = -sin I_a + cos I_b.
+ *                                pairing 0: pairs (1,2), (3,4), ..., (H-1,H);
+ *                                pairing 1: (2,3), (4,5), ..., (H,1)
+ *                                (1-based heads; the pattern alternates
+ *                                between layers). H must be even.
+ *   Y = Relation(q, k, I')       exactly as relation_fwd (I' is the only
+ *                                information state the head sees, Self term
+ *                                included).
+ *
+ *   p1, p2, I        : in  [B, H, T, D], dtype (unrotated, unmixed)
+ *   rope_cos/rope_sin: in  DEVICE float32 [T, D/2], 16-byte aligned; both
+ *                      NULL to skip RoPE (one NULL alone: REL_ERR_NULL)
+ *   theta            : in  DEVICE float32 [H/2]; NULL to skip the mixing
+ *   pairing          : 0 or 1 (REL_ERR_PARAM otherwise; odd H with theta:
+ *                      REL_ERR_SHAPE)
+ *   y, lse, gate     : as relation_fwd
+ *   workspace        : relation_mhr_fwd_workspace_bytes() bytes, 256-byte
+ *                      aligned: the rotated keys and mixed values are formed
+ *                      there once by a bandwidth-bound pass (every query
+ *                      block reads every key tile, so rotating them inside
+ *                      the tile loop would repeat the work); REL_BF16 rotates
+ *                      its query rows in registers, REL_F32 in the workspace.
+ *
+ * relation_mhr_bwd: gradients with respect to p1, p2, I, lambda and theta.
+ *   dp1, dp2, dI     : out [B, H, T, D], dtype
+ *   dlambda          : out DEVICE float32 scalar (NULL to skip)
+ *   dtheta           : out DEVICE float32 [H/2] (NULL to skip; ignored
+ *                      without theta)
+ *   workspace        : relation_mhr_bwd_workspace_bytes() bytes, 256-byte
+ *                      aligned; contents on entry are ignored.
+ *   Other arguments as relation_bwd; y and lse are the forward's outputs.
+ */
+size_t relation_mhr_fwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D);
+
+relation_status relation_mhr_fwd(relation_dtype dtype, int B, int H, int T, int D,
+                                 const void* p1, const void* p2, const void* I,
+                                 const float* rope_cos, const float* rope_sin,
+                                 const float* theta, int pairing,
+                                 void* y, float* lse, float* gate,
+                                 void* workspace, size_t workspace_bytes,
+                                 float scale, float tau_s, float lambda,
+                                 void* stream);
+
+size_t relation_mhr_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D);
+
+relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int D,
+                                 const void* p1, const void* p2, const void* I,
+                                 const float* rope_cos, const float* rope_sin,
+                                 const float* theta, int pairing,
+                                 const void* y, const void* dy, const float* lse,
+                                 void* dp1, void* dp2, void* dI,
+                                 float* dlambda, float* dtheta,
+                                 void* workspace, size_t workspace_bytes,
+                                 float scale, float tau_s, float lambda,
+                                 void* stream);
+
 /* Static, NUL-terminated description of a status code (host only). */
 const char* relation_status_string(relation_status s);
 

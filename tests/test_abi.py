@@ -129,6 +129,35 @@ def test_decode_ragged_validation(lib):
     assert dec(D=32) == REL_ERR_UNSUPPORTED
 
 
+def test_mhr_validation(lib):
+    n = 2 * 4 * 128 * 64
+    # bf16: rotated keys + mixed values (queries are rotated in registers);
+    # fp32: queries too
+    assert lib.relation_mhr_fwd_workspace_bytes(BF16, 2, 4, 128, 64) == 2 * n * 2
+    assert lib.relation_mhr_fwd_workspace_bytes(F32, 2, 4, 128, 64) == 3 * n * 4
+    need = lib.relation_mhr_bwd_workspace_bytes(BF16, 2, 4, 128, 64)
+    assert need > lib.relation_bwd_workspace_bytes(BF16, 2, 4, 128, 64)
+
+    def fwd(H=4, cs=P, sn=P, th=P, pairing=0, dtype=BF16, ws=NUL, wsb=0):
+        return lib.relation_mhr_fwd(dtype, 2, H, 128, 64, P, P, P, cs, sn, th, pairing, P, NUL,
+                                    NUL, ws, wsb, 0.125, 2.0, 0.3, None)
+
+    assert fwd(cs=NUL) == REL_ERR_NULL               # tables go together
+    assert fwd(H=5) == REL_ERR_SHAPE                 # Givens pairs need even H
+    assert fwd(pairing=2) == REL_ERR_PARAM
+    assert fwd(th=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+    assert fwd(cs=P_MIS) == REL_ERR_ALIGN
+    assert fwd() == REL_ERR_WORKSPACE                # keys / values go through a workspace
+
+    def bwd(ws=P, wsb=None):
+        wsb = need if wsb is None else wsb
+        return lib.relation_mhr_bwd(BF16, 2, 4, 128, 64, P, P, P, P, P, P, 0, P, P, P, P, P, P,
+                                    NUL, NUL, ws, wsb, 0.125, 2.0, 0.3, None)
+
+    assert bwd(wsb=need - 256) == REL_ERR_WORKSPACE
+    assert bwd(ws=NUL) == REL_ERR_WORKSPACE
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(rel, "_LIB", None)
     monkeypatch.setattr(rel, "lib_path", lambda: str(tmp_path / "missing.so"))

@@ -147,3 +147,15 @@ def test_mhr_without_rope_and_mixing_is_the_plain_operator(rng):
     f = oracle.relation_mhr_forward(p1, p2, I, None, None, None, 0, 0.5, 2.0, 0.3)
     Y, LSE, g = oracle.relation_forward(p1, p2, I, 0.5, 2.0, 0.3)
     assert np.array_equal(f["Y"], Y) and np.array_equal(f["LSE"], LSE)
+
+
+def test_input_generator_tables_are_the_rope_definition_in_fp32():
+    # the tables both sides consume are the oracle's fp64 tables rounded once
+    import torch  # noqa: F401  (the generator returns torch tensors)
+    from workloads import make_mhr_maps
+    T, D, H = 300, 64, 8
+    cs, sn, th = make_mhr_maps(T, D, H, seed=1)
+    c64, s64 = oracle.rope_tables(T, D)
+    assert np.array_equal(cs.numpy(), c64.astype(np.float32))
+    assert np.array_equal(sn.numpy(), s64.astype(np.float32))
+    assert th.shape == (H // 2,) and np.all(np.abs(th.numpy()) <= math.pi)

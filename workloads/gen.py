@@ -28,6 +28,7 @@ __all__ = [
     "make_inputs",
     "make_decode_inputs",
     "ragged_decode_lengths",
+    "make_mhr_maps",
     "apply_rope",
     "to_dtype",
     "default_scale",
@@ -75,6 +76,20 @@ def ragged_decode_lengths(B, max_n, seed):
     if B > 1:
         n[1] = 0
     return [int(x) for x in n]
+
+
+def make_mhr_maps(T, D, H, seed, base=1.0e4):
+    """Inputs of Multi-Head Relation's upstream maps: RoPE tables cos, sin
+    [T, D/2] float32 (angle t * base^(-2j/D) at position t, evaluated in
+    float64 and rounded once) and seeded Givens angles theta [H/2] float32,
+    uniform in [-pi, pi]. CPU torch tensors."""
+    j = np.arange(D // 2, dtype=np.float64)
+    ang = np.arange(T, dtype=np.float64)[:, None] * base ** (-2.0 * j / D)[None, :]
+    rng = np.random.default_rng(seed + 104729)
+    th = rng.uniform(-math.pi, math.pi, size=max(H // 2, 1))
+    return (torch.from_numpy(np.cos(ang).astype(np.float32)),
+            torch.from_numpy(np.sin(ang).astype(np.float32)),
+            torch.from_numpy(th.astype(np.float32)))
 
 
 def default_scale(D):
