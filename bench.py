@@ -245,6 +245,34 @@ def bench_decode_ragged(rel, torch, dev, B=32, H=12, D=64, nmax=4096, steps=64, 
             "frac_hbm_peak": byts / steps / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": byts}
 
 
+def bench_prefill(rel, torch, dev, reps, B=32, H=12, D=64, m=256, cap=4352, seed=42):
+    """Chunked prefill into the Relation Cache on the decode workload's cache
+    shape: m new tokens per sequence at ragged history lengths (uniform in
+    [0, cap - m], seeded). Flops count the causal entries of the new rows,
+    4 D per entry (both contractions), as for the forward."""
+    from workloads import make_decode_inputs, ragged_decode_lengths
+    ns = ragged_decode_lengths(B, cap - m, seed)
+    d = make_decode_inputs(B, H, D, cap - m, m, cap, "bf16", seed=seed)
+    q, kn, vn = (d[n].permute(1, 2, 0, 3).contiguous().to(dev) for n in ("q", "k_new", "v_new"))
+    kc, vc = d["k_cache"].to(dev), d["v_cache"].to(dev)
+    nh = torch.tensor(ns, dtype=torch.int32, device=dev)
+    y = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    t = EventTimer(torch, stream)
+    for i in range(reps + 3):
+        s0 = t.start() if i >= 3 else None
+        rel.relation_cache_prefill(q, kn, vn, kc, vc, nh, cap - m, lam=d["lam"],
+                                   scale=1 / math.sqrt(D), y=y)
+        if i >= 3:
+            t.stop(s0)
+    ms = t.mean_ms()
+    entries = sum(m * n + m * (m + 1) / 2 for n in ns) * H
+    tf = 4 * D * entries / (ms * 1e-3) / 1e12
+    return {"workload": f"prefill {m} tokens x {B} sequences x {H} heads, ragged history "
+            f"(mean {sum(ns) / B:.0f})", "ms": ms, "tflops": tf,
+            "frac_peak": tf / PEAK_BF16_TFLOPS}
+
+
 def bench_mhr(rel, torch, dev, reps, B=16, H=8, T=2048, D=64, seed=42):
     """Multi-Head Relation with its upstream maps (RoPE of p1 / p2 from
     [T, D/2] tables, Givens mixing of I, pairing M_B) on the 30M layer shape:
@@ -354,7 +382,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["step", "fwd", "decode", "ragged", "mhr", "attn", "copy"],
+    ap.add_argument("--only", choices=["step", "fwd", "decode", "ragged", "mhr", "prefill", "attn",
+                             "copy"],
                     default=None,
                     help="run one measurement and print its raw numbers ('copy': a plain "
                          "device copy of known size, the HBM-counter calibration)")
@@ -390,6 +419,9 @@ def main():
         return
     if args.only == "mhr":
         print(json.dumps(bench_mhr(rel, torch, dev, args.steps)))
+        return
+    if args.only == "prefill":
+        print(json.dumps(bench_prefill(rel, torch, dev, args.steps)))
         return
     if args.only == "attn":
         print(json.dumps(bench_fwdbwd_vs_attention(rel, torch, dev, args.steps)))
@@ -432,6 +464,7 @@ def main():
                                   "traffic": kernel_traffic("decode_split_kernel@cache4096")}
         torch.cuda.empty_cache()
         rec["mhr_layer30m"] = bench_mhr(rel, torch, dev, 10)
+        rec["prefill_cache"] = bench_prefill(rel, torch, dev, 10)
         rec["decode_ragged"] = bench_decode_ragged(rel, torch, dev)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

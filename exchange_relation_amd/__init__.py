@@ -24,6 +24,7 @@ __all__ = [
     "relation_cache_decode",
     "relation_decode_workspace_bytes",
     "relation_cache_decode_ragged",
+    "relation_cache_prefill",
     "relation_mhr_fwd",
     "relation_mhr_bwd",
     "relation_status_string",
@@ -42,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "relation_decode_workspace_bytes",
     "relation_cache_decode",
     "relation_cache_decode_ragged",
+    "relation_cache_prefill",
     "relation_mhr_fwd_workspace_bytes",
     "relation_mhr_fwd",
     "relation_mhr_bwd_workspace_bytes",
@@ -92,6 +94,10 @@ def load_library():
     lib.relation_cache_decode_ragged.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
                                                  c_int, vp, c_int, vp, vp, vp, c_size, c_float,
                                                  c_float, c_float, vp]
+    lib.relation_cache_prefill.restype = c_int
+    lib.relation_cache_prefill.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
+                                           c_int, vp, c_int, vp, vp, vp, c_float, c_float,
+                                           c_float, vp]
     lib.relation_mhr_fwd_workspace_bytes.restype = c_size
     lib.relation_mhr_fwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_mhr_fwd.restype = c_int
@@ -295,6 +301,41 @@ def relation_cache_decode_ragged(q, k_new, v_new, k_cache, v_cache, n_hist, max_
     if st != 0:
         raise RelationError(st, "relation_cache_decode_ragged")
     return y, gate
+
+
+def relation_cache_prefill(q, k_new, v_new, k_cache, v_cache, n_hist, max_n_hist=None, lam=0.0,
+                           scale=None, tau_s=2.0, y=None, lse=None, gate=None, want_stats=False,
+                           stream=None):
+    """m new tokens per sequence: q, k_new, v_new [B, H, m, D] appended at
+    slot n_hist (an int, or a device int32 tensor [B] with max_n_hist its
+    bound, default capacity - m) of k_cache, v_cache [B, H, capacity, D].
+    Returns (y, lse, gate); lse and gate only with want_stats."""
+    lib = load_library()
+    B, H, m, D = q.shape
+    capacity = k_cache.shape[2]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
+        _check(t, name, dt, (B, H, m, D), dev)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, name, dt, (B, H, capacity, D), dev)
+    if isinstance(n_hist, torch.Tensor):
+        _check(n_hist, "n_hist", torch.int32, (B,), dev)
+        nh, n = n_hist, capacity - m if max_n_hist is None else int(max_n_hist)
+    else:
+        nh, n = None, int(n_hist)
+    y = torch.empty_like(q) if y is None else y
+    _check(y, "y", dt, (B, H, m, D), dev)
+    if want_stats:
+        lse = torch.empty((B, H, m), device=dev, dtype=torch.float32) if lse is None else lse
+        gate = torch.empty((B, H, m), device=dev, dtype=torch.float32) if gate is None else gate
+    st = lib.relation_cache_prefill(code, B, H, D, m, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                    _ptr(k_cache), _ptr(v_cache), capacity, _ptr(nh), n, _ptr(y),
+                                    _ptr(lse), _ptr(gate), _scale(D, scale), float(tau_s),
+                                    float(lam), _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_cache_prefill")
+    return y, lse, gate
 
 
 def _mhr_maps(p1, rope_cos, rope_sin, theta):

@@ -93,24 +93,25 @@ __device__ __forceinline__ f32x16 score(const uint16_t* ks, int sb, const bf16x8
 }
 
 // First half of consuming a score tile: scaling to u' (in place); DIAG (the
-// sub-block starts at the wave's first query, k0 == q0) masks keys j >= i
-// and captures the Self score; then the stabiliser moves if the tile's
-// largest bound exceeds it by more than kLazy (rare), rescaling the row's
-// accumulators.
+// sub-block reaches this lane's query) masks keys j >= i and captures the
+// Self score, with rd = the lane's query position minus the sub-block's
+// first key (rd = r when the sub-block starts at the wave's first query);
+// then the stabiliser moves if the tile's largest bound exceeds it by more
+// than kLazy (rare), rescaling the row's accumulators.
 template <bool DIAG>
-__device__ __forceinline__ void stabilise(f32x16& s, float qscale, int r, int hf, RowState& st) {
+__device__ __forceinline__ void stabilise(f32x16& s, float qscale, int rd, int hf, RowState& st) {
 #pragma unroll
   for (int vi = 0; vi < 16; ++vi) s[vi] *= qscale;
   if (DIAG) {
-    const int vself = ((r >> 3) << 2) + (r & 3);
-    const bool mine = hf == ((r >> 2) & 1);
+    const int vself = ((rd >> 3) << 2) + (rd & 3);
+    const bool mine = rd >= 0 && rd < 32 && hf == ((rd >> 2) & 1);
 #pragma unroll
     for (int vi = 0; vi < 16; ++vi) {
       if (mine && vi == vself) st.uself = s[vi];
       const int kk = (vi >> 2) * 8 + hf * 4 + (vi & 3);
-      if (kk >= r) s[vi] = -INFINITY;  // not strictly historical
+      if (kk >= rd) s[vi] = -INFINITY;  // not strictly historical
     }
-    st.has_self = mine;
+    st.has_self = st.has_self || mine;
   }
   float mx = vmax(vmax(s[0], s[1]), s[2]);
 #pragma unroll
@@ -176,12 +177,22 @@ __device__ __forceinline__ void accumulate(const uint16_t* vs, int sb, const f32
   }
 }
 
-template <bool MHR>
+// Rows at an offset (OFF: prefill into a Relation Cache): the T query rows
+// of every head (q, y: [BH, T, D]) sit at positions pos0 .. pos0 + T - 1 of
+// their sequence, pos0 = p0s[b] (device lengths) or p0 (uniform); keys and
+// values are the cache's rows 0 .. pos0 + T - 1 (head stride ld rows).
+// Sequences with pos0 < 0, pos0 > bound or pos0 + T > ld get NaN rows.
+struct Seg {
+  const int* p0s;
+  int p0, bound, ld, H;
+};
+
+template <bool MHR, bool OFF>
 __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ y, float* __restrict__ lse,
     float* __restrict__ gate, int T, int BH, int nqb, float qscale, float inv_tau, float lam,
-    Mhr mh) {
+    Mhr mh, Seg sg) {
   __shared__ uint16_t kbuf[3][BN * KS];  // K ring: tiles t, t+1 resident, t+2 landing
   __shared__ uint16_t vbuf[2][BN * VS];  // V: tile t resident, t+1 landing
   const int tid = threadIdx.x;
@@ -197,6 +208,24 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
   const int q0 = qb * BM + wave * 32;
   const int qi = q0 + r;
   const bool wave_live = q0 < T;
+  // keys / values: this head's T rows, or (OFF) the cache's rows
+  // 0 .. pos0 + T - 1 with the query rows at positions pos0 + [0, T)
+  size_t kvbase = base;
+  int pos0 = 0, Tk = T;
+  if (OFF) {
+    pos0 = sg.p0s ? sg.p0s[head / sg.H] : sg.p0;
+    if (pos0 < 0 || pos0 > sg.bound || pos0 + T > sg.ld) {  // out of range: NaN rows
+      const int r0 = qb * BM, r1 = min(T, r0 + BM);
+      for (int e = tid; e < (r1 - r0) * D; e += 256) y[base + static_cast<size_t>(r0) * D + e] = 0x7fc0;
+      for (int i = r0 + tid; i < r1; i += 256) {
+        if (lse) lse[static_cast<size_t>(head) * T + i] = NAN;
+        if (gate) gate[static_cast<size_t>(head) * T + i] = NAN;
+      }
+      return;
+    }
+    kvbase = static_cast<size_t>(head) * sg.ld * D;
+    Tk = pos0 + T;
+  }
   // Multi-Head Relation: RoPE of this head's query rows, fused into the Q
   // fragment load (keys and values arrive already rotated / mixed)
   const bool rope = MHR && mh.cos != nullptr;
@@ -238,17 +267,19 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
   st.uself = 0.f;
   st.has_self = false;
 
-  const int kend = min(T, (qb + 1) * BM);
+  // tiles of keys before the block's first query position are history for
+  // every row of the block
+  const int kend = min(Tk, pos0 + (qb + 1) * BM);
   const int ntiles = (kend + BN - 1) / BN;
-  const int nfull = qb * (BM / BN);  // tiles that are history for every row
+  const int nfull = (pos0 + qb * BM) / BN;
 
   // ---- global -> register prefetch: 16 B chunks kc0, kc1 of a 64-row tile
   // (chunk c: row c >> 3, d chunk c & 7), as 32-bit offsets from the head's
   // base. Tiles that may run past T clamp the row and zero the chunk when it
   // is stored to LDS, so no load waits early and no pointer select turns the
   // loads into generic ones.
-  const uint16_t* __restrict__ kh = k + base;
-  const uint16_t* __restrict__ vh = v + base;
+  const uint16_t* __restrict__ kh = k + kvbase;
+  const uint16_t* __restrict__ vh = v + kvbase;
   const int kc0 = tid, kc1 = tid + 256;
   const int lo0 = (kc0 >> 3) * KS + (kc0 & 7) * 8, lo1 = (kc1 >> 3) * KS + (kc1 & 7) * 8;
   const int lv0 = (kc0 >> 3) * VS + (kc0 & 7) * 8, lv1 = (kc1 >> 3) * VS + (kc1 & 7) * 8;
@@ -258,10 +289,10 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
   };
   auto fetch = [&](const uint16_t* __restrict__ src, int kt, Chunks& c) {
     const int key0 = kt * BN + (kc0 >> 3), key1 = kt * BN + (kc1 >> 3);
-    c.oka = key0 < T;
-    c.okb = key1 < T;
-    const uint32_t r0 = static_cast<uint32_t>(c.oka ? key0 : T - 1);
-    const uint32_t r1 = static_cast<uint32_t>(c.okb ? key1 : T - 1);
+    c.oka = key0 < Tk;
+    c.okb = key1 < Tk;
+    const uint32_t r0 = static_cast<uint32_t>(c.oka ? key0 : Tk - 1);
+    const uint32_t r1 = static_cast<uint32_t>(c.okb ? key1 : Tk - 1);
     c.a = *reinterpret_cast<const u32x4*>(src + (r0 * D + (kc0 & 7) * 8));
     c.b = *reinterpret_cast<const u32x4*>(src + (r1 * D + (kc1 & 7) * 8));
   };
@@ -313,30 +344,37 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
     kp1 = kp2;
     kp2 = kt0;
   }
-  // ---- the workgroup's own block (at most two tiles, K already resident):
-  // per-wave historical / diagonal / beyond
+  // ---- the workgroup's own block: per-wave historical / diagonal /
+  // beyond. Aligned rows (pos0 = 0) span at most two tiles, both resident;
+  // rows at an offset may span three, so K keeps streaming two tiles ahead.
   for (; kt < ntiles; ++kt) {
+    const bool more_k = kt + 2 < ntiles;
+    if (more_k) fetch(kh, kt + 2, ck);
     if (kt + 1 < ntiles) fetch(vh, kt + 1, cv);
     const uint16_t* vs = vbuf[kt & 1];
     if (wave_live) {
+      const int pw = pos0 + q0;  // position of the wave's first query
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         const int k0 = kt * BN + sb * 32;
-        if (k0 < q0) {
+        if (k0 + 31 < pw) {  // history for every row of the wave
           f32x16 s = score(kp0, sb, qf, r, hf);
           stabilise<false>(s, qscale, r, hf, st);
           accumulate<false>(vs, sb, s, hf, st);
-        } else if (k0 == q0) {
+        } else if (k0 <= pw + 31) {  // reaches the wave's queries: mask + Self
           f32x16 s = score(kp0, sb, qf, r, hf);
-          stabilise<true>(s, qscale, r, hf, st);
+          stabilise<true>(s, qscale, pw + r - k0, hf, st);
           accumulate<true>(vs, sb, s, hf, st);
         }
       }
     }
+    if (more_k) stash(kp2, ck, lo0, lo1);
     if (kt + 1 < ntiles) stash(vbuf[(kt + 1) & 1], cv, lv0, lv1);
     __syncthreads();
+    uint16_t* kt0 = kp0;
     kp0 = kp1;
     kp1 = kp2;
+    kp2 = kt0;
   }
 
   if (!wave_live) return;
@@ -350,7 +388,7 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
   const float S2 = S * kLog2e;
   float g, lz;
   if (ltot > 0.f) {
-    const float A2 = st.m + fast_log2(ltot) - lam * fast_log2(static_cast<float>(qi + 1));
+    const float A2 = st.m + fast_log2(ltot) - lam * fast_log2(static_cast<float>(pos0 + qi + 1));
     g = fast_rcp(1.0f + fast_exp2(S2 - A2));
     lz = kLn2 * (fmaxf(S2, A2) + fast_log2(1.0f + fast_exp2(-fabsf(S2 - A2))));
   } else {  // row 1: empty history, A = -inf
@@ -360,12 +398,13 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
   const float gl = (ltot > 0.f) ? g * fast_rcp(ltot) : 0.f;
   const float gs = 1.0f - g;
   const size_t row = base + static_cast<size_t>(qi) * D;
+  const size_t vrow = kvbase + static_cast<size_t>(pos0 + qi) * D;  // I_i, the row's own value
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d0 = db * 32 + g4 * 8 + hf * 4;
-      const uint2 vr = *reinterpret_cast<const uint2*>(v + row + d0);
+      const uint2 vr = *reinterpret_cast<const uint2*>(v + vrow + d0);
       const f32x16& acc = db == 0 ? st.acc0 : st.acc1;
       const float y0 = fmaf(gs, __uint_as_float(vr.x << 16), gl * acc[g4 * 4 + 0]);
       const float y1 = fmaf(gs, __uint_as_float(vr.x & 0xffff0000u), gl * acc[g4 * 4 + 1]);
@@ -392,12 +431,57 @@ hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
   const int nqb = (T + fwdbf16::BM - 1) / fwdbf16::BM;
   const dim3 grid(static_cast<unsigned>(nqb) * BH);
   const Mhr mh{rope_cos, rope_sin, nullptr, 0, H};
+  const fwdbf16::Seg sg{nullptr, 0, 0, T, H};
   if (rope_cos == nullptr)
-    hipLaunchKernelGGL(fwdbf16::fwd_bf16_kernel<false>, grid, dim3(256), 0, stream, q, k, v, y,
-                       lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh);
+    hipLaunchKernelGGL((fwdbf16::fwd_bf16_kernel<false, false>), grid, dim3(256), 0, stream, q, k,
+                       v, y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
   else
-    hipLaunchKernelGGL(fwdbf16::fwd_bf16_kernel<true>, grid, dim3(256), 0, stream, q, k, v, y,
-                       lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh);
+    hipLaunchKernelGGL((fwdbf16::fwd_bf16_kernel<true, false>), grid, dim3(256), 0, stream, q, k,
+                       v, y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
+  return hipGetLastError();
+}
+
+namespace fwdbf16 {
+// Appends the m new tokens of every (b, h) to cache slots n_b .. n_b + m - 1
+// (an exact 16-bit copy); sequences out of range are left untouched.
+__global__ __launch_bounds__(256) void append_kernel(const uint16_t* __restrict__ kn,
+                                                     const uint16_t* __restrict__ vn,
+                                                     uint16_t* __restrict__ kc,
+                                                     uint16_t* __restrict__ vc, size_t rows, int m,
+                                                     int H, int cap, const int* __restrict__ nh,
+                                                     int n, int bound) {
+  const size_t g = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const size_t row = g >> 3;  // (head, t) of the new tokens
+  if (row >= rows) return;
+  const int c = static_cast<int>(g & 7);
+  const size_t head = row / m;
+  const int t = static_cast<int>(row % m);
+  const int p0 = nh ? nh[head / H] : n;
+  if (p0 < 0 || p0 > bound || p0 + m > cap) return;
+  const size_t dst = (head * cap + p0 + t) * D + c * 8;
+  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(kn + row * D + c * 8);
+  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(vn + row * D + c * 8);
+}
+}  // namespace fwdbf16
+
+hipError_t launch_prefill_bf16(int B, int H, int m, const uint16_t* q, const uint16_t* k_new,
+                               const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache,
+                               int capacity, const int* n_hist_dev, int n_hist, uint16_t* y,
+                               float* lse, float* gate, float scale, float tau, float lam,
+                               hipStream_t stream) {
+  const int BH = B * H;
+  const size_t rows = static_cast<size_t>(BH) * m;
+  hipLaunchKernelGGL(fwdbf16::append_kernel, dim3(static_cast<unsigned>((rows * 8 + 255) / 256)),
+                     dim3(256), 0, stream, k_new, v_new, k_cache, v_cache, rows, m, H, capacity,
+                     n_hist_dev, n_hist, n_hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqb = (m + fwdbf16::BM - 1) / fwdbf16::BM;
+  const Mhr mh{nullptr, nullptr, nullptr, 0, H};
+  const fwdbf16::Seg sg{n_hist_dev, n_hist, n_hist, capacity, H};
+  hipLaunchKernelGGL((fwdbf16::fwd_bf16_kernel<false, true>),
+                     dim3(static_cast<unsigned>(nqb) * BH), dim3(256), 0, stream, q, k_cache,
+                     v_cache, y, lse, gate, m, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
   return hipGetLastError();
 }
 

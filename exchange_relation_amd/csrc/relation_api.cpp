@@ -221,6 +221,31 @@ relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H,
                                      static_cast<hipStream_t>(stream)));
 }
 
+relation_status relation_cache_prefill(relation_dtype dtype, int B, int H, int D, int m,
+                                       const void* q, const void* k_new, const void* v_new,
+                                       void* k_cache, void* v_cache, int capacity,
+                                       const int* n_hist_dev, int n_hist, void* y, float* lse,
+                                       float* gate, float scale, float tau_s, float lambda,
+                                       void* stream) {
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !y) return REL_ERR_NULL;
+  if (dtype != REL_BF16 || D != 64) return REL_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || m < 1 || capacity < 1) return REL_ERR_SHAPE;
+  if (static_cast<long long>(B) * H * capacity * D > kMaxElems) return REL_ERR_SHAPE;
+  if (static_cast<long long>(B) * H * ((m + 31) / 32) > 0x7fffffffLL) return REL_ERR_SHAPE;
+  relation_status st = check_params(scale, tau_s, lambda);
+  if (st != REL_OK) return st;
+  if (n_hist < 0 || static_cast<long long>(n_hist) + m > capacity) return REL_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(y) || (lse && !aligned4(lse)) ||
+      (gate && !aligned4(gate)) || (n_hist_dev && !aligned4(n_hist_dev)))
+    return REL_ERR_ALIGN;
+  return from_hip(rel::launch_prefill_bf16(
+      B, H, m, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
+      static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache),
+      static_cast<uint16_t*>(v_cache), capacity, n_hist_dev, n_hist, static_cast<uint16_t*>(y),
+      lse, gate, scale, tau_s, lambda, static_cast<hipStream_t>(stream)));
+}
+
 size_t relation_mhr_fwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
   if (check_dtype_dim(dtype, D) != REL_OK || check_shape(B, H, T, D) != REL_OK) return 0;
   return mhr_layout(false, dtype, B, H, T, D).total;

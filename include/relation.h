@@ -166,6 +166,35 @@ relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H,
                                              void* stream);
 
 /*
+ * relation_cache_prefill — m new tokens per sequence at once (chunked
+ * prefill into the Relation Cache). Sequence b's new tokens sit at 0-based
+ * positions n_b .. n_b + m - 1 (1-based i = n_b + t + 1): they are appended
+ * to cache slots n_b .. n_b + m - 1 (an exact copy) and each one's row is
+ * computed against the cache rows before it and the new tokens up to
+ * itself, i.e. rows n_b + 1 .. n_b + m of the forward over the whole
+ * sequence (Sec. 3.1; lambda ln i uses the global position).
+ *
+ *   q, k_new, v_new  : in  [B, H, m, D], bf16 (REL_BF16 and D = 64 only;
+ *                      otherwise REL_ERR_UNSUPPORTED)
+ *   k_cache, v_cache : in/out [B, H, capacity, D]
+ *   n_hist_dev       : NULL: every sequence has n_hist slots of history.
+ *                      Otherwise DEVICE int32 [B] per-sequence lengths with
+ *                      n_hist their upper bound; a sequence whose length is
+ *                      negative, above the bound or leaves no room for m
+ *                      tokens gets NaN rows and no append.
+ *   n_hist           : 0 <= n_hist and n_hist + m <= capacity, else
+ *                      REL_ERR_CAPACITY.
+ *   y                : out [B, H, m, D]; lse, gate: out [B, H, m] fp32 or NULL
+ */
+relation_status relation_cache_prefill(relation_dtype dtype, int B, int H, int D, int m,
+                                       const void* q, const void* k_new, const void* v_new,
+                                       void* k_cache, void* v_cache, int capacity,
+                                       const int* n_hist_dev, int n_hist,
+                                       void* y, float* lse, float* gate,
+                                       float scale, float tau_s, float lambda,
+                                       void* stream);
+
+/*
  * relation_mhr_fwd / relation_mhr_bwd — Multi-Head Relation with the two maps
  * that precede the Relation operator in a layer (Sec. 3.1-3.2; App. A.2.2-
  * A.2.3), fused or chained inside the call:

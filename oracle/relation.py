@@ -41,6 +41,7 @@ __all__ = [
     "relation_backward",
     "relation_decode_step",
     "relation_decode_step_ragged",
+    "relation_prefill_rows",
     "brute_force_forward_head",
     "tiled_forward_head",
 ]
@@ -246,6 +247,36 @@ def relation_decode_step_ragged(q, k_new, v_new, k_cache, v_cache, n_hist, scale
                                                 scale, tau_s, lam)
         y[b], g[b], kc[b], vc[b] = yb[0], gb[0], kcb[0], vcb[0]
     return y, g, kc, vc
+
+
+def relation_prefill_rows(q, k_new, v_new, k_cache, v_cache, n_hist, scale, tau_s, lam):
+    """Chunked prefill into the Relation Cache: sequence b's m new tokens
+    take cache slots n_hist[b] .. n_hist[b] + m - 1 and their rows are rows
+    n_hist[b] + 1 .. n_hist[b] + m (1-based) of the forward over the whole
+    sequence (Sec. 3.1), each straight from the definition.
+
+    q, k_new, v_new: [B, H, m, D]; caches [B, H, capacity, D]; n_hist: a
+    length per sequence. Returns (y [B,H,m,D], LSE [B,H,m], g [B,H,m],
+    k_cache', v_cache')."""
+    q, k_new, v_new = _as64(q), _as64(k_new), _as64(v_new)
+    B, H, m, D = q.shape
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    y = np.empty((B, H, m, v_new.shape[-1]))
+    lse = np.empty((B, H, m))
+    g = np.empty((B, H, m))
+    for b in range(B):
+        n = int(n_hist[b])
+        kc[b, :, n:n + m] = k_new[b]
+        vc[b, :, n:n + m] = v_new[b]
+        for h in range(H):
+            kk = _as64(kc[b, h, :n + m])
+            vv = _as64(vc[b, h, :n + m])
+            qq = np.zeros((n + m, D))
+            qq[n:] = q[b, h]
+            y[b, h], lse[b, h], g[b, h] = relation_forward_rows(
+                qq, kk, vv, range(n + 1, n + m + 1), scale, tau_s, lam)
+    return y, lse, g, kc, vc
 
 
 def brute_force_forward_head(q, k, v, scale, tau_s, lam):

@@ -129,6 +129,21 @@ def test_decode_ragged_validation(lib):
     assert dec(D=32) == REL_ERR_UNSUPPORTED
 
 
+def test_prefill_validation(lib):
+    def pf(m=16, n=10, cap=64, dtype=BF16, D=64, q=P, nh=NUL):
+        return lib.relation_cache_prefill(dtype, 2, 3, D, m, q, P, P, P, P, cap, nh, n, P, NUL,
+                                          NUL, 0.125, 2.0, 0.3, None)
+
+    assert pf(n=49) == REL_ERR_CAPACITY   # 49 + 16 > 64
+    assert pf(n=-1) == REL_ERR_CAPACITY
+    assert pf(m=0) == REL_ERR_SHAPE
+    assert pf(dtype=F32) == REL_ERR_UNSUPPORTED
+    assert pf(D=32) == REL_ERR_UNSUPPORTED
+    assert pf(q=NUL) == REL_ERR_NULL
+    assert pf(q=P_MIS) == REL_ERR_ALIGN
+    assert pf(nh=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+
+
 def test_mhr_validation(lib):
     n = 2 * 4 * 128 * 64
     # bf16: rotated keys + mixed values (queries are rotated in registers);

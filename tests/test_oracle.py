@@ -183,6 +183,32 @@ def test_decode_ragged_rows_are_last_rows_of_their_forwards(rng):
             assert np.array_equal(vc2[b, h, n + 1:], vc[b, h, n + 1:])
 
 
+def test_prefill_rows_are_the_forwards_last_rows_and_m1_is_decode(rng):
+    B, H, D, cap, m = 2, 2, 3, 14, 4
+    ns = [5, 0]
+    kc = rng.standard_normal((B, H, cap, D))
+    vc = rng.standard_normal((B, H, cap, D))
+    q, kn, vn = (rng.standard_normal((B, H, m, D)) for _ in range(3))
+    y, lse, g, kc2, vc2 = oracle.relation_prefill_rows(q, kn, vn, kc, vc, ns, 0.5, 2.0, 0.35)
+    for b, n in enumerate(ns):
+        for h in range(H):
+            K = np.concatenate([kc[b, h, :n], kn[b, h]], 0)
+            V = np.concatenate([vc[b, h, :n], vn[b, h]], 0)
+            Q = np.concatenate([rng.standard_normal((n, D)), q[b, h]], 0)
+            r = oracle.relation_forward_head(Q, K, V, 0.5, 2.0, 0.35)
+            assert np.abs(y[b, h] - r["Y"][n:]).max() < 1e-13
+            assert np.abs(lse[b, h] - r["LSE"][n:]).max() < 1e-13
+            assert np.abs(g[b, h] - r["g"][n:]).max() < 1e-13
+            assert np.array_equal(kc2[b, h, :n + m], K)
+            assert np.array_equal(kc2[b, h, n + m:], kc[b, h, n + m:])
+    # one token at a time is the decode step
+    y1, _, g1, _, _ = oracle.relation_prefill_rows(q[:, :, :1], kn[:, :, :1], vn[:, :, :1], kc,
+                                                   vc, ns, 0.5, 2.0, 0.35)
+    yd, gd, _, _ = oracle.relation_decode_step_ragged(q[:, :, 0], kn[:, :, 0], vn[:, :, 0], kc,
+                                                      vc, ns, 0.5, 2.0, 0.35)
+    assert np.abs(y1[:, :, 0] - yd).max() < 1e-14 and np.abs(g1[:, :, 0] - gd).max() < 1e-14
+
+
 def test_decode_empty_history(rng):
     B, H, D = 1, 2, 3
     kc = rng.standard_normal((B, H, 4, D))
