@@ -108,6 +108,26 @@ __device__ __forceinline__ void load_row_piece<float, 64>(const float* p, float*
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
+// bf16 rows of 48 or 80 elements: a lane's piece (6 or 10 elements) starts
+// only 4-byte aligned, so it is read as 32-bit words.
+template <int E>
+__device__ __forceinline__ void load_bf16_words(const uint16_t* p, float* x) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+  for (int i = 0; i < E / 2; ++i) {
+    const uint32_t a = w[i];
+    x[2 * i] = __uint_as_float(a << 16);
+    x[2 * i + 1] = __uint_as_float(a & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load_row_piece<uint16_t, 48>(const uint16_t* p, float* x) {
+  load_bf16_words<6>(p, x);
+}
+template <>
+__device__ __forceinline__ void load_row_piece<uint16_t, 80>(const uint16_t* p, float* x) {
+  load_bf16_words<10>(p, x);
+}
 template <>
 __device__ __forceinline__ void load_row_piece<float, 32>(const float* p, float* x) {
   const float4 a = *reinterpret_cast<const float4*>(p);

@@ -16,7 +16,8 @@
 // per chunk goes to the workspace. This kernel is HBM-bound by design.
 // The first split workgroup of each (b, h) also appends k_new / v_new to slot
 // n_hist (no split reads that slot).
-// Kernel 2 (combine): one 64-lane wave per (b, h) merges the chunk partials
+// Kernel 2 (combine): one 64-lane wave per (b, h) (lane: elements d = lane +
+// 64 e) merges the chunk partials
 // (every partial load issued up front), adds Self and writes y / gate.
 //
 // Ragged batches: each sequence b has its own history length n_b (a device
@@ -179,50 +180,68 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     TE* __restrict__ kc, TE* __restrict__ vc, const float* __restrict__ part, TE* __restrict__ y,
     float* __restrict__ gate, int capacity, int n, const int* __restrict__ nh, int H, int nsplit,
     int pstride, float qscale, float inv_tau, float lam) {
-  const int tid = threadIdx.x;  // one lane per element d (lanes >= D idle)
+  constexpr int EL = (D + 63) / 64;  // elements per lane: d = lane + 64 e
+  const int tid = threadIdx.x;
   const int head = blockIdx.x;
-  const bool act = tid < D;
   const size_t hv = static_cast<size_t>(head) * D;
+  bool act[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) act[e] = tid + 64 * e < D;
   if (RAGGED) {
     const int bound = n;
     n = nh[head / H];
     if (n < 0 || n > bound || n >= capacity) {  // out of range: NaN outputs, no append
-      if (act) Elem<TE>::store(y + hv + tid, NAN);
+#pragma unroll
+      for (int e = 0; e < EL; ++e)
+        if (act[e]) Elem<TE>::store(y + hv + tid + 64 * e, NAN);
       if (tid == 0 && gate) gate[head] = NAN;
       return;
     }
     nsplit = n > 0 ? split_plan(n).nsplit : 0;
   }
-  const float qd = act ? Elem<TE>::load(q + hv + tid) : 0.f;
-  const float kd = act ? Elem<TE>::load(kn + hv + tid) : 0.f;
-  const float vd = act ? Elem<TE>::load(vn + hv + tid) : 0.f;
+  float qd[EL], kd[EL], vd[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) {
+    const int d = tid + 64 * e;
+    qd[e] = act[e] ? Elem<TE>::load(q + hv + d) : 0.f;
+    kd[e] = act[e] ? Elem<TE>::load(kn + hv + d) : 0.f;
+    vd[e] = act[e] ? Elem<TE>::load(vn + hv + d) : 0.f;
+  }
   if (RAGGED || nsplit == 0) {  // the append was not done by a split kernel
-    if (act) {
-      const size_t slot = (static_cast<size_t>(head) * capacity + n) * D + tid;
-      kc[slot] = kn[hv + tid];
-      vc[slot] = vn[hv + tid];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      if (!act[e]) continue;
+      const int d = tid + 64 * e;
+      const size_t slot = (static_cast<size_t>(head) * capacity + n) * D + d;
+      kc[slot] = kn[hv + d];
+      vc[slot] = vn[hv + d];
     }
   }
 
   // Self: u'_ii = scale*log2(e) * q . k_new
-  float us = qd * kd;
+  float us = 0.f;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) us = fmaf(qd[e], kd[e], us);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) us += __shfl_xor(us, o);
   us *= qscale;
 
   // merge the chunk partials (App. A.3.2), kBatch partials per round with
   // all their loads issued before any is used
-  float M = -INFINITY, Ls = 0.f, Z = 0.f;
+  float M = -INFINITY, Ls = 0.f, Z[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) Z[e] = 0.f;
   const float* ph = part + static_cast<size_t>(head) * (RAGGED ? pstride : nsplit) * (D + 2);
   for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
-    float pm[kBatch], pl[kBatch], pz[kBatch];
+    float pm[kBatch], pl[kBatch], pz[kBatch][EL];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const bool ok = s0 + b < nsplit;
       const float* pr = ph + static_cast<size_t>(ok ? s0 + b : 0) * (D + 2);
       pm[b] = ok ? pr[0] : -INFINITY;
       pl[b] = ok ? pr[1] : 0.f;
-      pz[b] = (ok && act) ? pr[2 + tid] : 0.f;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) pz[b][e] = (ok && act[e]) ? pr[2 + tid + 64 * e] : 0.f;
     }
     float Mn = M;
 #pragma unroll
@@ -230,12 +249,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     if (Mn == -INFINITY) continue;  // nothing yet
     const float a = fast_exp2(M - Mn);  // M = -inf -> 0
     Ls *= a;
-    Z *= a;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) Z[e] *= a;
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const float w = fast_exp2(pm[b] - Mn);  // -inf -> 0
       Ls = fmaf(w, pl[b], Ls);
-      Z = fmaf(w, pz[b], Z);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) Z[e] = fmaf(w, pz[b][e], Z[e]);
     }
     M = Mn;
   }
@@ -245,8 +266,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float A2 = M + fast_log2(Ls) - lam * fast_log2(static_cast<float>(n + 1));
     g = fast_rcp(1.0f + fast_exp2(S * kLog2e - A2));
   }
-  const float yd = (1.0f - g) * vd + ((Ls > 0.f) ? g * Z * fast_rcp(Ls) : 0.f);
-  if (act) Elem<TE>::store(y + hv + tid, yd);
+  const float gl = (Ls > 0.f) ? g * fast_rcp(Ls) : 0.f;
+#pragma unroll
+  for (int e = 0; e < EL; ++e)
+    if (act[e]) Elem<TE>::store(y + hv + tid + 64 * e, (1.0f - g) * vd[e] + gl * Z[e]);
   if (tid == 0 && gate) gate[head] = g;
 }
 
@@ -306,6 +329,12 @@ hipError_t launch_decode(int dtype, int B, int H, int D, const void* q, const vo
                          int n_hist, const int* n_hist_dev, void* y, float* gate, void* ws,
                          float scale, float tau, float lam, hipStream_t stream) {
   const int BH = B * H;
+  if (dtype == 1 && D == 48)
+    return dec::run<uint16_t, 48>(BH, H, q, k_new, v_new, k_cache, v_cache, capacity, n_hist,
+                                  n_hist_dev, y, gate, ws, scale, tau, lam, stream);
+  if (dtype == 1 && D == 80)
+    return dec::run<uint16_t, 80>(BH, H, q, k_new, v_new, k_cache, v_cache, capacity, n_hist,
+                                  n_hist_dev, y, gate, ws, scale, tau, lam, stream);
   if (dtype == 1)
     return dec::run<uint16_t, 64>(BH, H, q, k_new, v_new, k_cache, v_cache, capacity, n_hist,
                                   n_hist_dev, y, gate, ws, scale, tau, lam, stream);

@@ -55,19 +55,33 @@
 namespace rel {
 namespace fwdbf16 {
 
-constexpr int D = 64;
 constexpr int NW = 4;             // waves per workgroup
 constexpr int BM = 32 * NW;       // query rows per workgroup
 constexpr int BN = 64;            // keys per LDS tile
-constexpr int KS = D + 8;         // K tile row stride (bf16): 144 B, 16 B aligned
-constexpr int VS = D + 8;         // V tile row stride (bf16)
 constexpr float kLazy = 8.0f;     // log2-domain slack before rescaling
+
+// Shapes for head dimension DR (a multiple of 16: 48, 64 or 80). The score
+// contraction runs DR / 16 K-steps; the P V contraction produces ND blocks of
+// 32 value columns, the last one zero-padded past DR (the V tile in LDS has
+// ND * 32 columns, the padding zeroed once). HBM rows are DR wide.
+template <int DR>
+struct Dims {
+  static constexpr int D = DR;
+  static constexpr int NQ = DR / 16;                  // score K-steps
+  static constexpr int ND = (DR + 31) / 32;           // value column blocks
+  static constexpr int KS = DR + 8;                   // K tile row stride (bf16), 16 B aligned
+  static constexpr int VS = ND * 32 + 8;              // V tile row stride (bf16)
+  static constexpr int CPR = DR / 8;                  // 16 B chunks per row
+  static constexpr int NCH = (BN * CPR + 255) / 256;  // chunks per thread per tile
+  static_assert(DR % 16 == 0, "head dimension must be a multiple of 16");
+};
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 // Per-lane running state of one query row (this lane's half of the keys).
+template <int ND>
 struct RowState {
-  f32x16 acc0, acc1;  // Y^T: d in [0, 32) and [32, 64)
+  f32x16 acc[ND];     // Y^T: d in [32 db, 32 db + 32)
   float m;            // log2-domain stabiliser (upper bound of E' up to 2^kLazy)
   float mlim;         // m + kLazy
   float lsum;         // sum of bf16(P) over this lane's keys
@@ -78,15 +92,17 @@ struct RowState {
 // Score tile of 32-key sub-block `sb` of the K tile at `ks`: S^T = K Q^T.
 // Element vi of the result is key k0 + (vi>>2)*8 + hf*4 + (vi&3), query
 // q0 + r (raw q . k).
-__device__ __forceinline__ f32x16 score(const uint16_t* ks, int sb, const bf16x8 (&qf)[4], int r,
-                                        int hf) {
-  bf16x8 kr[4];
+template <int DR>
+__device__ __forceinline__ f32x16 score(const uint16_t* ks, int sb,
+                                        const bf16x8 (&qf)[Dims<DR>::NQ], int r, int hf) {
+  constexpr int NQ = Dims<DR>::NQ, KS = Dims<DR>::KS;
+  bf16x8 kr[NQ];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < NQ; ++c)
     kr[c] = as_bf16x8(*reinterpret_cast<const uint4*>(&ks[(sb * 32 + r) * KS + hf * 8 + 16 * c]));
   f32x16 s = {0};
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < NQ; ++c) {
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[c], qf[c], s, 0, 0, 0);
   }
   return s;
@@ -98,8 +114,9 @@ __device__ __forceinline__ f32x16 score(const uint16_t* ks, int sb, const bf16x8
 // first key (rd = r when the sub-block starts at the wave's first query);
 // then the stabiliser moves if the tile's largest bound exceeds it by more
 // than kLazy (rare), rescaling the row's accumulators.
-template <bool DIAG>
-__device__ __forceinline__ void stabilise(f32x16& s, float qscale, int rd, int hf, RowState& st) {
+template <bool DIAG, int ND>
+__device__ __forceinline__ void stabilise(f32x16& s, float qscale, int rd, int hf,
+                                          RowState<ND>& st) {
 #pragma unroll
   for (int vi = 0; vi < 16; ++vi) s[vi] *= qscale;
   if (DIAG) {
@@ -124,10 +141,9 @@ __device__ __forceinline__ void stabilise(f32x16& s, float qscale, int rd, int h
     const float a = fast_exp2(st.m - mn);
     st.lsum *= a;
 #pragma unroll
-    for (int vi = 0; vi < 16; ++vi) {
-      st.acc0[vi] *= a;
-      st.acc1[vi] *= a;
-    }
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int vi = 0; vi < 16; ++vi) st.acc[db][vi] *= a;
     st.m = mn;
     st.mlim = mn + kLazy;
   }
@@ -135,9 +151,10 @@ __device__ __forceinline__ void stabilise(f32x16& s, float qscale, int rd, int h
 
 // Second half: P = exp(E - m) in bf16, the row sum, and Y^T += V^T P^T with
 // the V tile at `vs`.
-template <bool DIAG>
+template <bool DIAG, int DR>
 __device__ __forceinline__ void accumulate(const uint16_t* vs, int sb, const f32x16& s, int hf,
-                                           RowState& st) {
+                                           RowState<Dims<DR>::ND>& st) {
+  constexpr int ND = Dims<DR>::ND, VS = Dims<DR>::VS;
   uint32_t pw[8];
   const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
@@ -166,14 +183,13 @@ __device__ __forceinline__ void accumulate(const uint16_t* vs, int sb, const f32
   for (int c = 0; c < 2; ++c) {
     const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
     const int o = (sb * 32 + c * 16 + hf * 4 + (l16 >> 2)) * VS + dcol;
-    const uint2 a0l = lds_read_tr16(&vs[o]);
-    const uint2 a0h = lds_read_tr16(&vs[o + 8 * VS]);
-    const uint2 a1l = lds_read_tr16(&vs[o + 32]);
-    const uint2 a1h = lds_read_tr16(&vs[o + 8 * VS + 32]);
-    st.acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        as_bf16x8(make_uint4(a0l.x, a0l.y, a0h.x, a0h.y)), pb, st.acc0, 0, 0, 0);
-    st.acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        as_bf16x8(make_uint4(a1l.x, a1l.y, a1h.x, a1h.y)), pb, st.acc1, 0, 0, 0);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const uint2 al = lds_read_tr16(&vs[o + 32 * db]);
+      const uint2 ah = lds_read_tr16(&vs[o + 8 * VS + 32 * db]);
+      st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          as_bf16x8(make_uint4(al.x, al.y, ah.x, ah.y)), pb, st.acc[db], 0, 0, 0);
+    }
   }
 }
 
@@ -187,12 +203,15 @@ struct Seg {
   int p0, bound, ld, H;
 };
 
-template <bool MHR, bool OFF>
-__global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
+template <bool MHR, bool OFF, int DR>
+__global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ y, float* __restrict__ lse,
     float* __restrict__ gate, int T, int BH, int nqb, float qscale, float inv_tau, float lam,
     Mhr mh, Seg sg) {
+  using Dm = Dims<DR>;
+  constexpr int D = Dm::D, NQ = Dm::NQ, ND = Dm::ND, KS = Dm::KS, VS = Dm::VS;
+  constexpr int CPR = Dm::CPR, NCH = Dm::NCH;
   __shared__ uint16_t kbuf[3][BN * KS];  // K ring: tiles t, t+1 resident, t+2 landing
   __shared__ uint16_t vbuf[2][BN * VS];  // V: tile t resident, t+1 landing
   const int tid = threadIdx.x;
@@ -227,23 +246,24 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
     Tk = pos0 + T;
   }
   // Multi-Head Relation: RoPE of this head's query rows, fused into the Q
-  // fragment load (keys and values arrive already rotated / mixed)
-  const bool rope = MHR && mh.cos != nullptr;
+  // fragment load (keys and values arrive already rotated / mixed; the
+  // fragment pairing below needs D = 64)
+  const bool rope = MHR && DR == 64 && mh.cos != nullptr;
 
   // ---- Q fragments: B operands of S^T = K Q^T. Lane holds query r,
   // d = hf*8 + 16*c + [0, 8) for c = 0..3 (rows past T read row T-1 and are
-  // zeroed); c and c + 2 hold a RoPE pair (d, d + 32).
-  bf16x8 qf[4];
+  // zeroed); c and c + 2 hold a RoPE pair (d, d + 32) when D = 64.
+  bf16x8 qf[NQ];
   {
     const int qr = qi < T ? qi : T - 1;
-    u32x4 raw[4];
+    u32x4 raw[NQ];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NQ; ++c) {
       raw[c] = *reinterpret_cast<const u32x4*>(q + base + static_cast<size_t>(qr) * D + hf * 8 + 16 * c);
       const u32x4 z = {0, 0, 0, 0};
       raw[c] = qi < T ? raw[c] : z;
     }
-    if (rope) {
+    if constexpr (DR == 64) if (rope) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const size_t t0 = static_cast<size_t>(qr) * (D / 2) + 16 * c + hf * 8;
@@ -255,12 +275,12 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
       }
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
+    for (int c = 0; c < NQ; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
   }
 
-  RowState st;
-  st.acc0 = f32x16{0};
-  st.acc1 = f32x16{0};
+  RowState<ND> st;
+#pragma unroll
+  for (int db = 0; db < ND; ++db) st.acc[db] = f32x16{0};
   st.m = 0.f;
   st.mlim = kLazy;
   st.lsum = 0.f;
@@ -273,34 +293,48 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
   const int ntiles = (kend + BN - 1) / BN;
   const int nfull = (pos0 + qb * BM) / BN;
 
-  // ---- global -> register prefetch: 16 B chunks kc0, kc1 of a 64-row tile
-  // (chunk c: row c >> 3, d chunk c & 7), as 32-bit offsets from the head's
-  // base. Tiles that may run past T clamp the row and zero the chunk when it
-  // is stored to LDS, so no load waits early and no pointer select turns the
-  // loads into generic ones.
+  // ---- global -> register prefetch: the tile's 16 B chunks c = tid + 256 i
+  // (row c / CPR, column chunk c % CPR; i < NCH), as 32-bit offsets from the
+  // head's base. Tiles that may run past the keys clamp the row and zero the
+  // chunk when it is stored to LDS, so no load waits early and no pointer
+  // select turns the loads into generic ones.
   const uint16_t* __restrict__ kh = k + kvbase;
   const uint16_t* __restrict__ vh = v + kvbase;
-  const int kc0 = tid, kc1 = tid + 256;
-  const int lo0 = (kc0 >> 3) * KS + (kc0 & 7) * 8, lo1 = (kc1 >> 3) * KS + (kc1 & 7) * 8;
-  const int lv0 = (kc0 >> 3) * VS + (kc0 & 7) * 8, lv1 = (kc1 >> 3) * VS + (kc1 & 7) * 8;
+  int crow[NCH], ccol[NCH];
+  bool cin[NCH];  // chunk exists (BN * CPR need not be a multiple of 256)
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + 256 * i;
+    cin[i] = c < BN * CPR;
+    crow[i] = cin[i] ? c / CPR : 0;
+    ccol[i] = cin[i] ? c % CPR : 0;
+  }
   struct Chunks {
-    u32x4 a, b;
-    bool oka, okb;
+    u32x4 a[NCH];
+    bool ok[NCH];
   };
   auto fetch = [&](const uint16_t* __restrict__ src, int kt, Chunks& c) {
-    const int key0 = kt * BN + (kc0 >> 3), key1 = kt * BN + (kc1 >> 3);
-    c.oka = key0 < Tk;
-    c.okb = key1 < Tk;
-    const uint32_t r0 = static_cast<uint32_t>(c.oka ? key0 : Tk - 1);
-    const uint32_t r1 = static_cast<uint32_t>(c.okb ? key1 : Tk - 1);
-    c.a = *reinterpret_cast<const u32x4*>(src + (r0 * D + (kc0 & 7) * 8));
-    c.b = *reinterpret_cast<const u32x4*>(src + (r1 * D + (kc1 & 7) * 8));
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int key = kt * BN + crow[i];
+      c.ok[i] = cin[i] && key < Tk;
+      const uint32_t r0 = static_cast<uint32_t>(key < Tk ? key : Tk - 1);
+      c.a[i] = *reinterpret_cast<const u32x4*>(src + (r0 * D + ccol[i] * 8));
+    }
   };
-  auto stash = [&](uint16_t* dst, const Chunks& c, int o0, int o1) {
+  auto stash = [&](uint16_t* dst, const Chunks& c, int stride) {
     const u32x4 z = {0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(&dst[o0]) = c.oka ? c.a : z;
-    *reinterpret_cast<u32x4*>(&dst[o1]) = c.okb ? c.b : z;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (cin[i]) *reinterpret_cast<u32x4*>(&dst[crow[i] * stride + ccol[i] * 8]) = c.ok[i] ? c.a[i] : z;
   };
+  if (ND * 32 > DR) {  // zero the V tiles' padding columns once (never stored to again)
+    for (int e = tid; e < 2 * BN * (ND * 32 - DR) / 8; e += 256) {
+      const int bufi = e / (BN * (ND * 32 - DR) / 8), rem = e % (BN * (ND * 32 - DR) / 8);
+      const int rowp = rem / ((ND * 32 - DR) / 8), colp = DR + 8 * (rem % ((ND * 32 - DR) / 8));
+      *reinterpret_cast<u32x4*>(&vbuf[bufi][rowp * VS + colp]) = u32x4{0, 0, 0, 0};
+    }
+  }
 
   // K tile t lives in kbuf[t % 3], V tile t in vbuf[t % 2]; kp0..kp2 point
   // at K tiles t, t+1, t+2 of the current step.
@@ -313,9 +347,9 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
     fetch(kh, 0, ck);
     fetch(vh, 0, cv);
     if (ntiles > 1) fetch(kh, 1, cn);
-    stash(kp0, ck, lo0, lo1);
-    stash(vbuf[0], cv, lv0, lv1);
-    if (ntiles > 1) stash(kp1, cn, lo0, lo1);
+    stash(kp0, ck, KS);
+    stash(vbuf[0], cv, VS);
+    if (ntiles > 1) stash(kp1, cn, KS);
   }
   __syncthreads();
 
@@ -323,7 +357,7 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
   // MFMAs run under sub-block 0's exponentials, and the next tile's
   // sub-block 0 score under sub-block 1's. No masking.
   f32x16 sa = {0};
-  if (nfull > 0) sa = score(kp0, 0, qf, r, hf);
+  if (nfull > 0) sa = score<DR>(kp0, 0, qf, r, hf);
   int kt = 0;
   for (; kt < nfull; ++kt) {
     const bool more_k = kt + 2 < ntiles;  // kt + 1 < ntiles always holds here
@@ -331,13 +365,13 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
     fetch(vh, kt + 1, cv);
     const uint16_t* vs = vbuf[kt & 1];
     stabilise<false>(sa, qscale, r, hf, st);
-    f32x16 sb = score(kp0, 1, qf, r, hf);
-    accumulate<false>(vs, 0, sa, hf, st);
+    f32x16 sb = score<DR>(kp0, 1, qf, r, hf);
+    accumulate<false, DR>(vs, 0, sa, hf, st);
     stabilise<false>(sb, qscale, r, hf, st);
-    sa = score(kp1, 0, qf, r, hf);  // tile kt + 1 <= nfull is resident
-    accumulate<false>(vs, 1, sb, hf, st);
-    if (more_k) stash(kp2, ck, lo0, lo1);
-    stash(vbuf[(kt + 1) & 1], cv, lv0, lv1);
+    sa = score<DR>(kp1, 0, qf, r, hf);  // tile kt + 1 <= nfull is resident
+    accumulate<false, DR>(vs, 1, sb, hf, st);
+    if (more_k) stash(kp2, ck, KS);
+    stash(vbuf[(kt + 1) & 1], cv, VS);
     __syncthreads();
     uint16_t* kt0 = kp0;
     kp0 = kp1;
@@ -358,18 +392,18 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
       for (int sb = 0; sb < 2; ++sb) {
         const int k0 = kt * BN + sb * 32;
         if (k0 + 31 < pw) {  // history for every row of the wave
-          f32x16 s = score(kp0, sb, qf, r, hf);
+          f32x16 s = score<DR>(kp0, sb, qf, r, hf);
           stabilise<false>(s, qscale, r, hf, st);
-          accumulate<false>(vs, sb, s, hf, st);
+          accumulate<false, DR>(vs, sb, s, hf, st);
         } else if (k0 <= pw + 31) {  // reaches the wave's queries: mask + Self
-          f32x16 s = score(kp0, sb, qf, r, hf);
+          f32x16 s = score<DR>(kp0, sb, qf, r, hf);
           stabilise<true>(s, qscale, pw + r - k0, hf, st);
-          accumulate<true>(vs, sb, s, hf, st);
+          accumulate<true, DR>(vs, sb, s, hf, st);
         }
       }
     }
-    if (more_k) stash(kp2, ck, lo0, lo1);
-    if (kt + 1 < ntiles) stash(vbuf[(kt + 1) & 1], cv, lv0, lv1);
+    if (more_k) stash(kp2, ck, KS);
+    if (kt + 1 < ntiles) stash(vbuf[(kt + 1) & 1], cv, VS);
     __syncthreads();
     uint16_t* kt0 = kp0;
     kp0 = kp1;
@@ -400,12 +434,13 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
   const size_t row = base + static_cast<size_t>(qi) * D;
   const size_t vrow = kvbase + static_cast<size_t>(pos0 + qi) * D;  // I_i, the row's own value
 #pragma unroll
-  for (int db = 0; db < 2; ++db) {
+  for (int db = 0; db < ND; ++db) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d0 = db * 32 + g4 * 8 + hf * 4;
+      if (d0 >= DR) continue;  // padding columns
       const uint2 vr = *reinterpret_cast<const uint2*>(v + vrow + d0);
-      const f32x16& acc = db == 0 ? st.acc0 : st.acc1;
+      const f32x16& acc = st.acc[db];
       const float y0 = fmaf(gs, __uint_as_float(vr.x << 16), gl * acc[g4 * 4 + 0]);
       const float y1 = fmaf(gs, __uint_as_float(vr.x & 0xffff0000u), gl * acc[g4 * 4 + 1]);
       const float y2 = fmaf(gs, __uint_as_float(vr.y << 16), gl * acc[g4 * 4 + 2]);
@@ -422,67 +457,98 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(
 
 }  // namespace fwdbf16
 
-hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
-                           const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale,
-                           float tau, float lam, hipStream_t stream, const float* rope_cos,
-                           const float* rope_sin) {
-  (void)D;
-  const int BH = B * H;
-  const int nqb = (T + fwdbf16::BM - 1) / fwdbf16::BM;
+namespace fwdbf16 {
+template <int DR>
+hipError_t run_fwd(int BH, int H, int T, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale, float tau,
+                   float lam, hipStream_t stream, const float* rope_cos, const float* rope_sin) {
+  const int nqb = (T + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(nqb) * BH);
   const Mhr mh{rope_cos, rope_sin, nullptr, 0, H};
-  const fwdbf16::Seg sg{nullptr, 0, 0, T, H};
-  if (rope_cos == nullptr)
-    hipLaunchKernelGGL((fwdbf16::fwd_bf16_kernel<false, false>), grid, dim3(256), 0, stream, q, k,
-                       v, y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
+  const Seg sg{nullptr, 0, 0, T, H};
+  if (rope_cos == nullptr || DR != 64)
+    hipLaunchKernelGGL((fwd_bf16_kernel<false, false, DR>), grid, dim3(256), 0, stream, q, k, v,
+                       y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
   else
-    hipLaunchKernelGGL((fwdbf16::fwd_bf16_kernel<true, false>), grid, dim3(256), 0, stream, q, k,
-                       v, y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
+    hipLaunchKernelGGL((fwd_bf16_kernel<true, false, DR>), grid, dim3(256), 0, stream, q, k, v,
+                       y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
   return hipGetLastError();
 }
 
-namespace fwdbf16 {
 // Appends the m new tokens of every (b, h) to cache slots n_b .. n_b + m - 1
 // (an exact 16-bit copy); sequences out of range are left untouched.
+template <int DR>
 __global__ __launch_bounds__(256) void append_kernel(const uint16_t* __restrict__ kn,
                                                      const uint16_t* __restrict__ vn,
                                                      uint16_t* __restrict__ kc,
                                                      uint16_t* __restrict__ vc, size_t rows, int m,
                                                      int H, int cap, const int* __restrict__ nh,
                                                      int n, int bound) {
+  constexpr int CPR = DR / 8;
   const size_t g = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const size_t row = g >> 3;  // (head, t) of the new tokens
+  const size_t row = g / CPR;  // (head, t) of the new tokens
   if (row >= rows) return;
-  const int c = static_cast<int>(g & 7);
+  const int c = static_cast<int>(g % CPR);
   const size_t head = row / m;
   const int t = static_cast<int>(row % m);
   const int p0 = nh ? nh[head / H] : n;
   if (p0 < 0 || p0 > bound || p0 + m > cap) return;
-  const size_t dst = (head * cap + p0 + t) * D + c * 8;
-  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(kn + row * D + c * 8);
-  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(vn + row * D + c * 8);
+  const size_t dst = (head * cap + p0 + t) * DR + c * 8;
+  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(kn + row * DR + c * 8);
+  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(vn + row * DR + c * 8);
 }
-}  // namespace fwdbf16
 
-hipError_t launch_prefill_bf16(int B, int H, int m, const uint16_t* q, const uint16_t* k_new,
-                               const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache,
-                               int capacity, const int* n_hist_dev, int n_hist, uint16_t* y,
-                               float* lse, float* gate, float scale, float tau, float lam,
-                               hipStream_t stream) {
-  const int BH = B * H;
+template <int DR>
+hipError_t run_prefill(int BH, int H, int m, const uint16_t* q, const uint16_t* k_new,
+                       const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache, int capacity,
+                       const int* n_hist_dev, int n_hist, uint16_t* y, float* lse, float* gate,
+                       float scale, float tau, float lam, hipStream_t stream) {
   const size_t rows = static_cast<size_t>(BH) * m;
-  hipLaunchKernelGGL(fwdbf16::append_kernel, dim3(static_cast<unsigned>((rows * 8 + 255) / 256)),
+  const size_t threads = rows * (DR / 8);
+  hipLaunchKernelGGL((append_kernel<DR>), dim3(static_cast<unsigned>((threads + 255) / 256)),
                      dim3(256), 0, stream, k_new, v_new, k_cache, v_cache, rows, m, H, capacity,
                      n_hist_dev, n_hist, n_hist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nqb = (m + fwdbf16::BM - 1) / fwdbf16::BM;
+  const int nqb = (m + BM - 1) / BM;
   const Mhr mh{nullptr, nullptr, nullptr, 0, H};
-  const fwdbf16::Seg sg{n_hist_dev, n_hist, n_hist, capacity, H};
-  hipLaunchKernelGGL((fwdbf16::fwd_bf16_kernel<false, true>),
-                     dim3(static_cast<unsigned>(nqb) * BH), dim3(256), 0, stream, q, k_cache,
-                     v_cache, y, lse, gate, m, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
+  const Seg sg{n_hist_dev, n_hist, n_hist, capacity, H};
+  hipLaunchKernelGGL((fwd_bf16_kernel<false, true, DR>), dim3(static_cast<unsigned>(nqb) * BH),
+                     dim3(256), 0, stream, q, k_cache, v_cache, y, lse, gate, m, BH, nqb,
+                     scale * kLog2e, 1.0f / tau, lam, mh, sg);
   return hipGetLastError();
+}
+}  // namespace fwdbf16
+
+hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale,
+                           float tau, float lam, hipStream_t stream, const float* rope_cos,
+                           const float* rope_sin) {
+  const int BH = B * H;
+  if (D == 48)
+    return fwdbf16::run_fwd<48>(BH, H, T, q, k, v, y, lse, gate, scale, tau, lam, stream,
+                                rope_cos, rope_sin);
+  if (D == 80)
+    return fwdbf16::run_fwd<80>(BH, H, T, q, k, v, y, lse, gate, scale, tau, lam, stream,
+                                rope_cos, rope_sin);
+  return fwdbf16::run_fwd<64>(BH, H, T, q, k, v, y, lse, gate, scale, tau, lam, stream, rope_cos,
+                              rope_sin);
+}
+
+hipError_t launch_prefill_bf16(int B, int H, int D, int m, const uint16_t* q,
+                               const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
+                               uint16_t* v_cache, int capacity, const int* n_hist_dev, int n_hist,
+                               uint16_t* y, float* lse, float* gate, float scale, float tau,
+                               float lam, hipStream_t stream) {
+  const int BH = B * H;
+  if (D == 48)
+    return fwdbf16::run_prefill<48>(BH, H, m, q, k_new, v_new, k_cache, v_cache, capacity,
+                                    n_hist_dev, n_hist, y, lse, gate, scale, tau, lam, stream);
+  if (D == 80)
+    return fwdbf16::run_prefill<80>(BH, H, m, q, k_new, v_new, k_cache, v_cache, capacity,
+                                    n_hist_dev, n_hist, y, lse, gate, scale, tau, lam, stream);
+  return fwdbf16::run_prefill<64>(BH, H, m, q, k_new, v_new, k_cache, v_cache, capacity,
+                                  n_hist_dev, n_hist, y, lse, gate, scale, tau, lam, stream);
 }
 
 }  // namespace rel

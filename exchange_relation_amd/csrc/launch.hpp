@@ -38,11 +38,11 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                            hipStream_t stream, float* dk32 = nullptr,
                            float* dv32 = nullptr);
 
-// Relation Cache prefill (bf16, D = 64): appends m new tokens per (b, h) at
+// Relation Cache prefill (bf16, D in {48, 64, 80}): appends m new tokens per (b, h) at
 // slot n_b (n_hist_dev[b] on the device, or the uniform n_hist when NULL;
 // with the device array n_hist is their upper bound) and computes their rows
 // against cache rows 0 .. n_b + m - 1.
-hipError_t launch_prefill_bf16(int B, int H, int m, const uint16_t* q, const uint16_t* k_new,
+hipError_t launch_prefill_bf16(int B, int H, int D, int m, const uint16_t* q, const uint16_t* k_new,
                                const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache,
                                int capacity, const int* n_hist_dev, int n_hist, uint16_t* y,
                                float* lse, float* gate, float scale, float tau, float lam,

@@ -290,6 +290,10 @@ hipError_t launch_mhr_prepare(int dtype, int B, int H, int T, int D, const void*
                               const float* rope_cos, const float* rope_sin, const float* theta,
                               int pairing, hipStream_t stream) {
   const Mhr mh{rope_cos, rope_sin, theta, pairing, H};
+  if (dtype == 1 && D == 48)
+    return mhr::run_prepare<uint16_t, 48>(B, H, T, p1, p2, vi, q, k, v, mh, stream);
+  if (dtype == 1 && D == 80)
+    return mhr::run_prepare<uint16_t, 80>(B, H, T, p1, p2, vi, q, k, v, mh, stream);
   if (dtype == 1) return mhr::run_prepare<uint16_t, 64>(B, H, T, p1, p2, vi, q, k, v, mh, stream);
   if (D == 64) return mhr::run_prepare<float, 64>(B, H, T, p1, p2, vi, q, k, v, mh, stream);
   return mhr::run_prepare<float, 32>(B, H, T, p1, p2, vi, q, k, v, mh, stream);

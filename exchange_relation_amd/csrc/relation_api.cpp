@@ -24,9 +24,17 @@ relation_status check_params(float scale, float tau_s, float lambda) {
   return REL_OK;
 }
 
+// Head dimensions built: fp32 (accurate VALU paths) D in {32, 64}; bf16
+// forward, decode and prefill D in {48, 64, 80} (the paper's 10M / 30M /
+// 100M head widths), bf16 backward D = 64.
 relation_status check_dtype_dim(relation_dtype dt, int D) {
   if (dt == REL_F32) return (D == 32 || D == 64) ? REL_OK : REL_ERR_UNSUPPORTED;
-  if (dt == REL_BF16) return (D == 64) ? REL_OK : REL_ERR_UNSUPPORTED;
+  if (dt == REL_BF16) return (D == 48 || D == 64 || D == 80) ? REL_OK : REL_ERR_UNSUPPORTED;
+  return REL_ERR_UNSUPPORTED;
+}
+relation_status check_dtype_dim_bwd(relation_dtype dt, int D) {
+  if (dt == REL_F32) return (D == 32 || D == 64) ? REL_OK : REL_ERR_UNSUPPORTED;
+  if (dt == REL_BF16) return D == 64 ? REL_OK : REL_ERR_UNSUPPORTED;
   return REL_ERR_UNSUPPORTED;
 }
 
@@ -55,7 +63,7 @@ MhrLayout mhr_layout(bool backward, relation_dtype dt, int B, int H, int T, int 
   const size_t n = static_cast<size_t>(B) * H * T * D;
   const size_t esz = dt == REL_BF16 ? 2 : 4;
   size_t off = 0;
-  if (backward || dt == REL_F32) {
+  if (backward || dt == REL_F32 || D != 64) {  // the bf16 kernel rotates queries itself at D = 64
     L.q = off; off += round256(n * esz);
   }
   L.k = off; off += round256(n * esz);
@@ -130,7 +138,7 @@ relation_status relation_fwd(relation_dtype dtype, int B, int H, int T, int D, c
 }
 
 size_t relation_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
-  if (check_dtype_dim(dtype, D) != REL_OK || check_shape(B, H, T, D) != REL_OK) return 0;
+  if (check_dtype_dim_bwd(dtype, D) != REL_OK || check_shape(B, H, T, D) != REL_OK) return 0;
   return rel::bwd_workspace_bytes(dtype == REL_BF16 ? 1 : 0, B, H, T, D);
 }
 
@@ -140,7 +148,7 @@ relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D, c
                              void* workspace, size_t workspace_bytes, float scale, float tau_s,
                              float lambda, void* stream) {
   if (!q || !k || !v || !y || !dy || !lse || !dq || !dk || !dv) return REL_ERR_NULL;
-  relation_status st = check_dtype_dim(dtype, D);
+  relation_status st = check_dtype_dim_bwd(dtype, D);
   if (st != REL_OK) return st;
   if ((st = check_shape(B, H, T, D)) != REL_OK) return st;
   if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
@@ -228,7 +236,7 @@ relation_status relation_cache_prefill(relation_dtype dtype, int B, int H, int D
                                        float* gate, float scale, float tau_s, float lambda,
                                        void* stream) {
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !y) return REL_ERR_NULL;
-  if (dtype != REL_BF16 || D != 64) return REL_ERR_UNSUPPORTED;
+  if (dtype != REL_BF16 || check_dtype_dim(dtype, D) != REL_OK) return REL_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || m < 1 || capacity < 1) return REL_ERR_SHAPE;
   if (static_cast<long long>(B) * H * capacity * D > kMaxElems) return REL_ERR_SHAPE;
   if (static_cast<long long>(B) * H * ((m + 31) / 32) > 0x7fffffffLL) return REL_ERR_SHAPE;
@@ -240,7 +248,7 @@ relation_status relation_cache_prefill(relation_dtype dtype, int B, int H, int D
       (gate && !aligned4(gate)) || (n_hist_dev && !aligned4(n_hist_dev)))
     return REL_ERR_ALIGN;
   return from_hip(rel::launch_prefill_bf16(
-      B, H, m, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
+      B, H, D, m, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
       static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache),
       static_cast<uint16_t*>(v_cache), capacity, n_hist_dev, n_hist, static_cast<uint16_t*>(y),
       lse, gate, scale, tau_s, lambda, static_cast<hipStream_t>(stream)));
@@ -273,7 +281,7 @@ relation_status relation_mhr_fwd(relation_dtype dtype, int B, int H, int T, int 
   const bool bf = dtype == REL_BF16;
   // rotated keys / mixed values once, in a pre-pass; the bf16 kernel rotates
   // its own query rows in registers
-  void* q = (rope_cos && !bf) ? w + L.q : nullptr;
+  void* q = (rope_cos && (!bf || D != 64)) ? w + L.q : nullptr;
   void* k = rope_cos ? w + L.k : nullptr;
   void* v = theta ? w + L.v : nullptr;
   if ((q || k || v) && rel::launch_mhr_prepare(bf ? 1 : 0, B, H, T, D, p1, p2, I, q, k, v,
@@ -287,14 +295,14 @@ relation_status relation_mhr_fwd(relation_dtype dtype, int B, int H, int T, int 
     return from_hip(rel::launch_fwd_bf16(
         B, H, T, D, static_cast<const uint16_t*>(qe), static_cast<const uint16_t*>(ke),
         static_cast<const uint16_t*>(ve), static_cast<uint16_t*>(y), lse, gate, scale, tau_s,
-        lambda, s, rope_cos, rope_sin));
+        lambda, s, q ? nullptr : rope_cos, q ? nullptr : rope_sin));
   return from_hip(rel::launch_fwd_f32(B, H, T, D, static_cast<const float*>(qe),
                                       static_cast<const float*>(ke), static_cast<const float*>(ve),
                                       static_cast<float*>(y), lse, gate, scale, tau_s, lambda, s));
 }
 
 size_t relation_mhr_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
-  if (check_dtype_dim(dtype, D) != REL_OK || check_shape(B, H, T, D) != REL_OK) return 0;
+  if (check_dtype_dim_bwd(dtype, D) != REL_OK || check_shape(B, H, T, D) != REL_OK) return 0;
   return mhr_layout(true, dtype, B, H, T, D).total;
 }
 
@@ -306,7 +314,7 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                                  void* workspace, size_t workspace_bytes, float scale,
                                  float tau_s, float lambda, void* stream) {
   if (!p1 || !p2 || !I || !y || !dy || !lse || !dp1 || !dp2 || !dI) return REL_ERR_NULL;
-  relation_status st = check_dtype_dim(dtype, D);
+  relation_status st = check_dtype_dim_bwd(dtype, D);
   if (st != REL_OK) return st;
   if ((st = check_shape(B, H, T, D)) != REL_OK) return st;
   if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;

@@ -63,7 +63,9 @@ typedef enum {
 typedef enum { REL_F32 = 0, REL_BF16 = 1 } relation_dtype;
 
 /* Head dimensions built: REL_F32 forward/backward/decode: D in {32, 64};
- * REL_BF16 forward/backward/decode: D = 64. Other D -> REL_ERR_UNSUPPORTED. */
+ * REL_BF16 forward, decode and prefill: D in {48, 64, 80} (the paper's 10M,
+ * 30M and 100M head widths); REL_BF16 backward: D = 64. Other (dtype, D)
+ * pairs -> REL_ERR_UNSUPPORTED. */
 
 /*
  * relation_fwd — Multi-Head Relation forward (Sec. 3.1 / 3.2), evaluated

@@ -62,8 +62,9 @@ def test_fwd_validation(lib):
     assert fwd(lib, y=NUL) == REL_ERR_NULL
     assert fwd(lib, T=0) == REL_ERR_SHAPE
     assert fwd(lib, B=-1) == REL_ERR_SHAPE
-    assert fwd(lib, D=48) == REL_ERR_UNSUPPORTED
+    assert fwd(lib, dtype=F32, D=48) == REL_ERR_UNSUPPORTED
     assert fwd(lib, dtype=BF16, D=32) == REL_ERR_UNSUPPORTED
+    assert fwd(lib, dtype=BF16, D=96) == REL_ERR_UNSUPPORTED
     assert fwd(lib, dtype=7) == REL_ERR_UNSUPPORTED
     assert fwd(lib, tau=0.0) == REL_ERR_PARAM
     assert fwd(lib, tau=-1.0) == REL_ERR_PARAM

@@ -1,0 +1,144 @@
+"""GPU parity at the paper's other head widths (d_h = 48 for its 10M model and
+80 for its 100M model; App. B, Table 6): bf16 forward, decode (uniform and
+ragged), prefill and the Multi-Head Relation forward, against the fp64
+oracle. Tolerances as everywhere for bf16: max-abs <= 2e-2 and mean-abs
+<= 3e-3; caches bit for bit. The bf16 backward is built for D = 64 only; the
+other widths must be rejected before anything runs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exchange_relation_amd as rel
+import oracle
+from workloads import make_decode_inputs, make_inputs, make_mhr_maps
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+BF16_MAX, BF16_MEAN = 2e-2, 3e-3
+
+
+def f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def check(name, got, ref):
+    err = np.abs(np.asarray(got, dtype=np.float64) - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    print(f"  {name}: max-abs {mx:.3e} mean-abs {mean:.3e}")
+    assert mx <= BF16_MAX, f"{name}: max-abs {mx:.3e} > {BF16_MAX}"
+    assert mean <= BF16_MEAN, f"{name}: mean-abs {mean:.3e} > {BF16_MEAN}"
+
+
+@pytest.mark.parametrize("D", [48, 80])
+@pytest.mark.parametrize("T", [1, 33, 130, 300])
+def test_fwd_head_dims_vs_oracle(D, T):
+    B, H = 2, 2
+    inp = make_inputs(B, H, T, D, "bf16", seed=1000 + D + T)
+    scale = 1 / math.sqrt(D)
+    y, lse, g = rel.relation_fwd(*(inp[n].to(DEV) for n in ("q", "k", "v")), lam=inp["lam"],
+                                 scale=scale, want_gate=True)
+    torch.cuda.synchronize()
+    Y, L, G = oracle.relation_forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), scale, 2.0,
+                                      inp["lam"])
+    check("y", f64(y), Y)
+    check("lse", f64(lse), L)
+    check("gate", f64(g), G)
+
+
+@pytest.mark.parametrize("B,H,T,D", [(8, 8, 1024, 48), (8, 8, 4096, 80)])
+def test_fwd_paper_geometries_sampled_heads(B, H, T, D):
+    """The paper's 10M (8 heads x 48) and 100M (8 heads x 80) layer shapes;
+    whole heads from the oracle."""
+    inp = make_inputs(B, H, T, D, "bf16", seed=42)
+    scale = 1 / math.sqrt(D)
+    y, lse, _ = rel.relation_fwd(*(inp[n].to(DEV) for n in ("q", "k", "v")), lam=inp["lam"],
+                                 scale=scale)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (B - 1, H - 1), (3, 5)):
+        r = oracle.relation_forward_head(f64(inp["q"][b, h]), f64(inp["k"][b, h]),
+                                         f64(inp["v"][b, h]), scale, 2.0, inp["lam"])
+        check(f"y[{b},{h}]", f64(y[b, h]), r["Y"])
+        check(f"lse[{b},{h}]", f64(lse[b, h]), r["LSE"])
+
+
+@pytest.mark.parametrize("D", [48, 80])
+@pytest.mark.parametrize("n0", [0, 1, 513])
+def test_decode_head_dims_vs_oracle(D, n0):
+    B, H, steps = 2, 3, 2
+    d = make_decode_inputs(B, H, D, n0, steps, n0 + steps + 3, "bf16", seed=1100 + D + n0)
+    scale = 1 / math.sqrt(D)
+    kc, vc = d["k_cache"].to(DEV), d["v_cache"].to(DEV)
+    kfull, vfull = d["k_cache"].clone(), d["v_cache"].clone()
+    for s in range(steps):
+        y, g = rel.relation_cache_decode(d["q"][s].to(DEV), d["k_new"][s].to(DEV),
+                                         d["v_new"][s].to(DEV), kc, vc, n0 + s, lam=d["lam"],
+                                         scale=scale, want_gate=True)
+        torch.cuda.synchronize()
+        Y, G, kfull_n, vfull_n = oracle.relation_decode_step(
+            f64(d["q"][s]), f64(d["k_new"][s]), f64(d["v_new"][s]), f64(kfull), f64(vfull),
+            n0 + s, scale, 2.0, d["lam"])
+        check(f"y step {s}", f64(y), Y)
+        check(f"gate step {s}", f64(g), G)
+        kfull[:, :, n0 + s] = d["k_new"][s]
+        vfull[:, :, n0 + s] = d["v_new"][s]
+    assert torch.equal(kc.cpu(), kfull) and torch.equal(vc.cpu(), vfull)
+
+
+@pytest.mark.parametrize("D", [48, 80])
+def test_decode_ragged_and_prefill_head_dims(D):
+    B, H, cap, m = 3, 2, 300, 40
+    ns = [0, 77, 250]
+    d = make_decode_inputs(B, H, D, cap - m, m, cap, "bf16", seed=1200 + D)
+    scale = 1 / math.sqrt(D)
+    # one ragged decode step
+    kc, vc = d["k_cache"].to(DEV), d["v_cache"].to(DEV)
+    nh = torch.tensor(ns, dtype=torch.int32, device=DEV)
+    y, g = rel.relation_cache_decode_ragged(d["q"][0].to(DEV), d["k_new"][0].to(DEV),
+                                            d["v_new"][0].to(DEV), kc, vc, nh, max(ns),
+                                            lam=d["lam"], scale=scale, want_gate=True)
+    torch.cuda.synchronize()
+    Y, G, KC, VC = oracle.relation_decode_step_ragged(
+        f64(d["q"][0]), f64(d["k_new"][0]), f64(d["v_new"][0]), f64(d["k_cache"]),
+        f64(d["v_cache"]), ns, scale, 2.0, d["lam"])
+    check("ragged y", f64(y), Y)
+    assert np.array_equal(f64(kc), KC) and np.array_equal(f64(vc), VC)
+    # prefill of m tokens at the same ragged offsets, on a fresh cache
+    kc, vc = d["k_cache"].to(DEV), d["v_cache"].to(DEV)
+    new = {n: d[n].permute(1, 2, 0, 3).contiguous() for n in ("q", "k_new", "v_new")}
+    y, lse, _ = rel.relation_cache_prefill(new["q"].to(DEV), new["k_new"].to(DEV),
+                                           new["v_new"].to(DEV), kc, vc, nh, max(ns),
+                                           lam=d["lam"], scale=scale, want_stats=True)
+    torch.cuda.synchronize()
+    Y, L, _, KC, VC = oracle.relation_prefill_rows(
+        f64(new["q"]), f64(new["k_new"]), f64(new["v_new"]), f64(d["k_cache"]),
+        f64(d["v_cache"]), ns, scale, 2.0, d["lam"])
+    check("prefill y", f64(y), Y)
+    check("prefill lse", f64(lse), L)
+    assert np.array_equal(f64(kc), KC) and np.array_equal(f64(vc), VC)
+
+
+@pytest.mark.parametrize("D", [48, 80])
+def test_mhr_fwd_head_dims(D):
+    B, H, T = 1, 4, 130
+    inp = make_inputs(B, H, T, D, "bf16", seed=1300 + D)
+    cs, sn, th = make_mhr_maps(T, D, H, 1300 + D)
+    scale = 1 / math.sqrt(D)
+    y, lse, _ = rel.relation_mhr_fwd(*(inp[n].to(DEV) for n in ("q", "k", "v")), cs.to(DEV),
+                                     sn.to(DEV), th.to(DEV), 0, lam=inp["lam"], scale=scale)
+    torch.cuda.synchronize()
+    r = oracle.relation_mhr_forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(cs),
+                                    f64(sn), f64(th), 0, scale, 2.0, inp["lam"])
+    check("mhr y", f64(y), r["Y"])
+    check("mhr lse", f64(lse), r["LSE"])
+
+
+@pytest.mark.parametrize("D", [48, 80])
+def test_bwd_other_head_dims_rejected(D):
+    inp = make_inputs(1, 1, 16, D, "bf16", seed=1, with_dy=True)
+    q, k, v, dy = (inp[n].to(DEV) for n in ("q", "k", "v", "dy"))
+    y, lse, _ = rel.relation_fwd(q, k, v, lam=0.3)
+    with pytest.raises(rel.RelationError):
+        rel.relation_bwd(q, k, v, y, dy, lse, lam=0.3)
