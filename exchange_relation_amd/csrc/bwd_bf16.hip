@@ -48,7 +48,7 @@ namespace bwdbf16 {
 #ifndef REL_BWD_WAVES
 #define REL_BWD_WAVES 8
 #endif
-constexpr int D = 64;
+constexpr int D = 64;          // head width of the tiles and MFMAs (real widths <= 64 zero-padded)
 constexpr int NW = REL_BWD_WAVES;  // waves per workgroup (4 or 8)
 constexpr int NT = 64 * NW;        // threads per workgroup
 constexpr int BK = 32 * NW;        // keys per workgroup
@@ -77,6 +77,9 @@ __device__ __forceinline__ bf16x8 cat(uint2 a, uint2 b) {
   return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 
+// DR: the real head width (48 or 64); HBM rows are DR wide and everything
+// past DR is zero in the tiles and never stored.
+template <int DR>
 __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
@@ -94,7 +97,8 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
   const int L = blockIdx.x;
   const int head = L % BH;
   const int kb = L / BH;  // first key blocks (longest query loops) first
-  const size_t base = static_cast<size_t>(head) * T * D;
+  static_assert(DR % 16 == 0 && DR <= D, "real head width");
+  const size_t base = static_cast<size_t>(head) * T * DR;
   const size_t rbase = static_cast<size_t>(head) * T;
   const int kw0 = kb * BK + wave * 32;  // this wave's first key
   const int kj = kw0 + r;               // this lane's key
@@ -104,9 +108,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     uint4 kr4 = make_uint4(0, 0, 0, 0), vr4 = make_uint4(0, 0, 0, 0);
-    if (kj < T) {
-      kr4 = *reinterpret_cast<const uint4*>(k + base + static_cast<size_t>(kj) * D + hf * 8 + 16 * c);
-      vr4 = *reinterpret_cast<const uint4*>(v + base + static_cast<size_t>(kj) * D + hf * 8 + 16 * c);
+    if (kj < T && 16 * c + hf * 8 < DR) {
+      kr4 = *reinterpret_cast<const uint4*>(k + base + static_cast<size_t>(kj) * DR + hf * 8 + 16 * c);
+      vr4 = *reinterpret_cast<const uint4*>(v + base + static_cast<size_t>(kj) * DR + hf * 8 + 16 * c);
     }
     kf[c] = as_bf16x8(kr4);
     vf[c] = as_bf16x8(vr4);
@@ -118,9 +122,10 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     const int c = tid + NT * pass;  // chunks of 16 B
     const int key = kb * BK + (c >> 3);
     const int kr_ = key < T ? key : T - 1;
-    u32x4 x = *reinterpret_cast<const u32x4*>(k + base + static_cast<size_t>(kr_) * D + (c & 7) * 8);
+    const int cc = (c & 7) < DR / 8 ? (c & 7) : 0;  // columns past DR: zero
+    u32x4 x = *reinterpret_cast<const u32x4*>(k + base + static_cast<size_t>(kr_) * DR + cc * 8);
     const u32x4 z = {0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(&kr[(c >> 3) * RS + (c & 7) * 8]) = key < T ? x : z;
+    *reinterpret_cast<u32x4*>(&kr[(c >> 3) * RS + (c & 7) * 8]) = (key < T && (c & 7) < DR / 8) ? x : z;
   }
   __syncthreads();
   // ---- this wave's dQ B operand (K rows, d in [16 dw, 16 dw + 16)) for all
@@ -150,13 +155,15 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
   float pc = 0.f, pl = 0.f, pd = 0.f;
   auto fetch = [&](int qt0) {
     const int i0 = qt0 + (c0 >> 3), i1 = qt0 + (c1 >> 3);
-    ok0 = i0 < T;
-    ok1 = i1 < T;
-    const size_t o0 = base + static_cast<size_t>(ok0 ? i0 : T - 1) * D + (c0 & 7) * 8;
+    ok0 = i0 < T && (c0 & 7) < DR / 8;
+    ok1 = i1 < T && (c1 & 7) < DR / 8;
+    const size_t o0 = base + static_cast<size_t>(i0 < T ? i0 : T - 1) * DR +
+                      ((c0 & 7) < DR / 8 ? (c0 & 7) : 0) * 8;
     pq0 = *reinterpret_cast<const u32x4*>(q + o0);
     pg0 = *reinterpret_cast<const u32x4*>(dy + o0);
     if (NCH > 1) {
-      const size_t o1 = base + static_cast<size_t>(ok1 ? i1 : T - 1) * D + (c1 & 7) * 8;
+      const size_t o1 = base + static_cast<size_t>(i1 < T ? i1 : T - 1) * DR +
+                        ((c1 & 7) < DR / 8 ? (c1 & 7) : 0) * 8;
       pq1 = *reinterpret_cast<const u32x4*>(q + o1);
       pg1 = *reinterpret_cast<const u32x4*>(dy + o1);
     }
@@ -376,7 +383,8 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = qt0 + (qw + b) * 16 + g16 * 4 + j;
-          if (full || i < T) unsafeAtomicAdd(dqh + static_cast<uint32_t>(i * D + dw * 16 + l16), aq[b][j]);
+          if ((full || i < T) && dw * 16 < DR)
+            unsafeAtomicAdd(dqh + static_cast<uint32_t>(i * DR + dw * 16 + l16), aq[b][j]);
         }
       }
     }
@@ -385,13 +393,14 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
 
   // ---- dK = scale * dK^T^T, dV = dV^T^T (key kj, d rows of the accumulators)
   if (kj >= T) return;
-  const size_t row = base + static_cast<size_t>(kj) * D;
+  const size_t row = base + static_cast<size_t>(kj) * DR;
   if (dk32) {  // fp32 results for a later pass (Multi-Head Relation's transposes)
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = db * 32 + g4 * 8 + hf * 4;
+        if (d0 >= DR) continue;
         const f32x16& ka = db == 0 ? dk0 : dk1;
         const f32x16& va = db == 0 ? dv0 : dv1;
         *reinterpret_cast<f32x4*>(dk32 + row + d0) =
@@ -408,6 +417,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d0 = db * 32 + g4 * 8 + hf * 4;
+      if (d0 >= DR) continue;
       const f32x16& ka = db == 0 ? dk0 : dk1;
       const f32x16& va = db == 0 ? dv0 : dv1;
       *reinterpret_cast<uint2*>(dk + row + d0) =
@@ -464,9 +474,14 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
   const float* Dr = reinterpret_cast<const float*>(wsb + w.off_dr);
   const int BH = B * H;
   const int nkb = (T + BK - 1) / BK;
-  hipLaunchKernelGGL(bwd_bf16_kernel, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
-                     stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e, scale,
-                     1.0f / tau, lam, dk32, dv32);
+  if (D == 48)
+    hipLaunchKernelGGL(bwd_bf16_kernel<48>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
+                       stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e, scale,
+                       1.0f / tau, lam, dk32, dv32);
+  else
+    hipLaunchKernelGGL(bwd_bf16_kernel<64>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
+                       stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e, scale,
+                       1.0f / tau, lam, dk32, dv32);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // with fp32 results requested, dq stays in the accumulator (the caller

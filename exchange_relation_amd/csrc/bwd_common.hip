@@ -61,9 +61,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const TE* __restrict__ q,
       qk += __shfl_xor(qk, o, 8);
     }
     if (dq_acc) {
+      if constexpr (E % 4 == 0) {
 #pragma unroll
-      for (int e = 0; e < E; e += 4)
-        *reinterpret_cast<float4*>(dq_acc + off + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int e = 0; e < E; e += 4)
+          *reinterpret_cast<float4*>(dq_acc + off + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {  // E = 6: the piece is only 8-byte aligned
+#pragma unroll
+        for (int e = 0; e < E; e += 2)
+          *reinterpret_cast<float2*>(dq_acc + off + e) = make_float2(0.f, 0.f);
+      }
     }
     if (sub == 0) {
       Dr[gr] = dYY;
@@ -136,6 +142,11 @@ hipError_t launch_bwd_pre(int dtype, int B, int H, int T, int D, const void* q, 
                           const void* v, const void* y, const void* dy, const float* lse,
                           float* dlambda, const BwdWorkspace& w, char* ws, float scale, float tau,
                           hipStream_t stream) {
+  if (dtype == 1 && D == 48)
+    return launch_bwd_pre_t<uint16_t, 48>(
+        B, H, T, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(y),
+        static_cast<const uint16_t*>(dy), lse, dlambda, w, ws, scale, tau, true, stream);
   if (dtype == 1)
     return launch_bwd_pre_t<uint16_t, 64>(
         B, H, T, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),

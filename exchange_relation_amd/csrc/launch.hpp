@@ -14,9 +14,9 @@ hipError_t launch_fwd_f32(int B, int H, int T, int D, const float* q, const floa
                           const float* v, float* y, float* lse, float* gate, float scale,
                           float tau, float lam, hipStream_t stream);
 
-// Forward, bf16 storage, bf16 MFMA contractions with fp32 accumulation, D = 64.
-// rope_cos / rope_sin ([T, D/2] fp32, or NULL): RoPE of q fused into the Q
-// fragment load (Multi-Head Relation; k and v come in already rotated /
+// Forward, bf16 storage, bf16 MFMA contractions with fp32 accumulation,
+// D in {48, 64, 80}. rope_cos / rope_sin ([T, D/2] fp32, or NULL; D = 64
+// only): RoPE of q fused into the Q fragment load (Multi-Head Relation; k and v come in already rotated /
 // mixed).
 hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale,
@@ -29,6 +29,7 @@ hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const floa
                           const float* v, const float* y, const float* dy, const float* lse,
                           float* dq, float* dk, float* dv, float* dlambda, void* ws, float scale,
                           float tau, float lam, hipStream_t stream);
+// bf16 D in {48, 64} (48 runs in the 64-wide tiles with zero columns).
 // dk32 / dv32 non-NULL: dk (scaled) and dv go there in fp32, and dq is left
 // unscaled in the workspace accumulator (bwd_workspace_layout(...).off_dq).
 hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,

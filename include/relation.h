@@ -64,8 +64,8 @@ typedef enum { REL_F32 = 0, REL_BF16 = 1 } relation_dtype;
 
 /* Head dimensions built: REL_F32 forward/backward/decode: D in {32, 64};
  * REL_BF16 forward, decode and prefill: D in {48, 64, 80} (the paper's 10M,
- * 30M and 100M head widths); REL_BF16 backward: D = 64. Other (dtype, D)
- * pairs -> REL_ERR_UNSUPPORTED. */
+ * 30M and 100M head widths); REL_BF16 backward: D in {48, 64}. Other
+ * (dtype, D) pairs -> REL_ERR_UNSUPPORTED. */
 
 /*
  * relation_fwd — Multi-Head Relation forward (Sec. 3.1 / 3.2), evaluated
@@ -176,8 +176,8 @@ relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H,
  * itself, i.e. rows n_b + 1 .. n_b + m of the forward over the whole
  * sequence (Sec. 3.1; lambda ln i uses the global position).
  *
- *   q, k_new, v_new  : in  [B, H, m, D], bf16 (REL_BF16 and D = 64 only;
- *                      otherwise REL_ERR_UNSUPPORTED)
+ *   q, k_new, v_new  : in  [B, H, m, D], bf16 (REL_BF16 and D in
+ *                      {48, 64, 80} only; otherwise REL_ERR_UNSUPPORTED)
  *   k_cache, v_cache : in/out [B, H, capacity, D]
  *   n_hist_dev       : NULL: every sequence has n_hist slots of history.
  *                      Otherwise DEVICE int32 [B] per-sequence lengths with
