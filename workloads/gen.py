@@ -14,6 +14,14 @@ Recipe (shared by every test and by the benchmark):
     once; the same rounded values feed the GPU and the oracle (which upcasts
     them to float64).
 
+Linear Relation inputs (make_linear_inputs): p1, p2, I, dY ~ N(0, 1) rounded
+to bf16 as above, and the log retention g <= 0 (float32) drawn with the
+spread that the pages' KDA-style retention map has at initialisation: per
+(b, h, channel) a magnitude m = U(1, 16) * exp(U(ln 1e-3, ln 1e-1)), per token
+|g| = m * exp(0.5 z), z ~ N(0, 1). The "resets" option sets a random 1 % of
+(token, channel) entries to g = -60 (near-total retention loss) and the
+"keep" option a random 1/8 of channels to g = 0 (no loss).
+
 Nothing here computes any part of the Relation operator itself.
 """
 import math
@@ -28,6 +36,7 @@ __all__ = [
     "make_inputs",
     "make_decode_inputs",
     "ragged_decode_lengths",
+    "make_linear_inputs",
     "make_mhr_maps",
     "apply_rope",
     "to_dtype",
@@ -180,3 +189,26 @@ def make_decode_inputs(B, H, D, n_hist, steps, capacity, dtype, seed, lam=None):
         "k_new": to_dtype(kn, dtype),
         "v_new": to_dtype(vn, dtype),
     }
+
+
+def make_linear_inputs(B, H, T, D, seed, with_dy=False, resets=False, keep=False):
+    """Seeded Linear Relation inputs: dict(p1, p2, I[, dy]) bf16 and g float32,
+    CPU tensors of shape [B, H, T, D] (recipe in the module docstring)."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, T, D)
+    p1 = rng.standard_normal(shape, dtype=np.float32)
+    p2 = rng.standard_normal(shape, dtype=np.float32)
+    iv = rng.standard_normal(shape, dtype=np.float32)
+    mag = rng.uniform(1.0, 16.0, (B, H, 1, D)) * np.exp(
+        rng.uniform(math.log(1e-3), math.log(1e-1), (B, H, 1, D)))
+    z = rng.standard_normal(shape)
+    g = -(mag * np.exp(0.5 * z))
+    if resets:
+        g[rng.uniform(size=shape) < 0.01] = -60.0
+    if keep:
+        g[np.broadcast_to(rng.uniform(size=(B, H, 1, D)) < 0.125, shape)] = 0.0
+    out = {"p1": to_dtype(p1, "bf16"), "p2": to_dtype(p2, "bf16"), "I": to_dtype(iv, "bf16"),
+           "g": torch.from_numpy(g.astype(np.float32))}
+    if with_dy:
+        out["dy"] = to_dtype(rng.standard_normal(shape, dtype=np.float32), "bf16")
+    return out
