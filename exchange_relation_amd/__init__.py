@@ -27,6 +27,8 @@ __all__ = [
     "relation_cache_prefill",
     "relation_mhr_fwd",
     "relation_mhr_bwd",
+    "relation_linear_fwd",
+    "relation_linear_step",
     "relation_status_string",
     "relation_version",
     "RelationFunction",
@@ -48,6 +50,8 @@ EXPORTED_SYMBOLS = (
     "relation_mhr_fwd",
     "relation_mhr_bwd_workspace_bytes",
     "relation_mhr_bwd",
+    "relation_linear_fwd",
+    "relation_linear_step",
     "relation_status_string",
     "relation_version",
 )
@@ -109,6 +113,12 @@ def load_library():
     lib.relation_mhr_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                      c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size, c_float,
                                      c_float, c_float, vp]
+    lib.relation_linear_fwd.restype = c_int
+    lib.relation_linear_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, c_float, c_float, vp]
+    lib.relation_linear_step.restype = c_int
+    lib.relation_linear_step.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, c_float, c_float, vp]
     lib.relation_status_string.restype = ctypes.c_char_p
     lib.relation_status_string.argtypes = [c_int]
     lib.relation_version.restype = c_int
@@ -411,6 +421,63 @@ def relation_mhr_bwd(p1, p2, I, y, dy, lse, rope_cos=None, rope_sin=None, theta=
     if st != 0:
         raise RelationError(st, "relation_mhr_bwd")
     return dp1, dp2, dI, dlambda, dtheta
+
+
+def relation_linear_fwd(p1, p2, I, g, rope_cos=None, rope_sin=None, state_in=None,
+                        want_state=False, scale=None, tau_s=2.0, y=None, state_out=None,
+                        stream=None):
+    """Linear Relation forward (bf16 p1, p2, I [B, H, T, 64]; fp32 log
+    retention g of the same shape). Optional RoPE tables [T, 32] and initial
+    state [B, H, 64, 64] fp32. Returns (y, state_out or None)."""
+    lib = load_library()
+    B, H, T, D = p1.shape
+    dev, dt = p1.device, p1.dtype
+    for name, t in (("p1", p1), ("p2", p2), ("I", I)):
+        _check(t, name, dt, (B, H, T, D), dev)
+    _check(g, "g", torch.float32, (B, H, T, D), dev)
+    _mhr_maps(p1, rope_cos, rope_sin, None)
+    if state_in is not None:
+        _check(state_in, "state_in", torch.float32, (B, H, D, D), dev)
+    y = torch.empty_like(I) if y is None else y
+    _check(y, "y", dt, (B, H, T, D), dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, D, D), device=dev, dtype=torch.float32)
+    if state_out is not None:
+        _check(state_out, "state_out", torch.float32, (B, H, D, D), dev)
+    st = lib.relation_linear_fwd(_dtype_code(p1), B, H, T, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(g),
+                                 _ptr(rope_cos), _ptr(rope_sin), _ptr(state_in), _ptr(y),
+                                 _ptr(state_out), _scale(D, scale), float(tau_s),
+                                 _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_linear_fwd")
+    return y, state_out
+
+
+def relation_linear_step(p1, p2, I, g, state, rope_cos=None, rope_sin=None, scale=None,
+                         tau_s=2.0, y=None, stream=None):
+    """One Linear Relation decode step: p1, p2, I [B, H, 64] bf16, g [B, H, 64]
+    fp32, state [B, H, 64, 64] fp32 updated in place; rope rows [32] or None.
+    Returns y [B, H, 64]."""
+    lib = load_library()
+    B, H, D = p1.shape
+    dev, dt = p1.device, p1.dtype
+    for name, t in (("p1", p1), ("p2", p2), ("I", I)):
+        _check(t, name, dt, (B, H, D), dev)
+    _check(g, "g", torch.float32, (B, H, D), dev)
+    _check(state, "state", torch.float32, (B, H, D, D), dev)
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("rope_cos and rope_sin go together")
+    if rope_cos is not None:
+        _check(rope_cos, "rope_cos", torch.float32, (D // 2,), dev)
+        _check(rope_sin, "rope_sin", torch.float32, (D // 2,), dev)
+    y = torch.empty_like(I) if y is None else y
+    _check(y, "y", dt, (B, H, D), dev)
+    st = lib.relation_linear_step(_dtype_code(p1), B, H, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(g),
+                                  _ptr(rope_cos), _ptr(rope_sin), _ptr(state), _ptr(y),
+                                  _scale(D, scale), float(tau_s), _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_linear_step")
+    return y
 
 
 class RelationFunction(torch.autograd.Function):

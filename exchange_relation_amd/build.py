@@ -26,6 +26,7 @@ SOURCES = [
     "bwd_bf16.hip",
     "decode.hip",
     "mhr.hip",
+    "linear.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

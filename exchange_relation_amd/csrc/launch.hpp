@@ -74,4 +74,21 @@ hipError_t launch_mhr_post(int dtype, int B, int H, int T, int D, const float* d
                            const float* rope_cos, const float* rope_sin, const float* theta,
                            int pairing, hipStream_t stream);
 
+// Linear Relation (linear.hip), bf16, D = 64. g = log retention (fp32, same
+// shape as p1). rope tables [T, D/2] or NULL; state_in / state_out [B, H, D, D]
+// fp32 or NULL; states (or NULL): the state before every chunk of
+// linear_chunk_rows() tokens, [B, H, nchunks, D, D] fp32.
+int linear_chunk_rows();
+hipError_t launch_linear_fwd(int B, int H, int T, const uint16_t* p1, const uint16_t* p2,
+                             const uint16_t* iv, const float* g, const float* rope_cos,
+                             const float* rope_sin, const float* state_in, uint16_t* y,
+                             float* state_out, float* states, float scale, float tau,
+                             hipStream_t stream);
+// One token per head; state [B, H, D, D] fp32 updated in place; rope tables
+// are the [D/2] rows of the token's position, or NULL.
+hipError_t launch_linear_step(int B, int H, const uint16_t* p1, const uint16_t* p2,
+                              const uint16_t* iv, const float* g, const float* rope_cos,
+                              const float* rope_sin, float* state, uint16_t* y, float scale,
+                              float tau, hipStream_t stream);
+
 }  // namespace rel

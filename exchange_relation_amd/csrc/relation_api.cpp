@@ -372,4 +372,44 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                                        dth, part, rope_cos, rope_sin, th, pairing, s));
 }
 
+relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, int D,
+                                    const void* p1, const void* p2, const void* I,
+                                    const float* g, const float* rope_cos, const float* rope_sin,
+                                    const float* state_in, void* y, float* state_out, float scale,
+                                    float tau_s, void* stream) {
+  if (!p1 || !p2 || !I || !g || !y) return REL_ERR_NULL;
+  if (!rope_cos != !rope_sin) return REL_ERR_NULL;
+  if (dtype != REL_BF16 || D != 64) return REL_ERR_UNSUPPORTED;
+  relation_status st = check_shape(B, H, T, D);
+  if (st != REL_OK) return st;
+  if ((st = check_params(scale, tau_s, 0.f)) != REL_OK) return st;
+  if (!aligned16(p1) || !aligned16(p2) || !aligned16(I) || !aligned16(g) || !aligned16(y) ||
+      (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) ||
+      (state_in && !aligned4(state_in)) || (state_out && !aligned4(state_out)))
+    return REL_ERR_ALIGN;
+  return from_hip(rel::launch_linear_fwd(
+      B, H, T, static_cast<const uint16_t*>(p1), static_cast<const uint16_t*>(p2),
+      static_cast<const uint16_t*>(I), g, rope_cos, rope_sin, state_in, static_cast<uint16_t*>(y),
+      state_out, nullptr, scale, tau_s, static_cast<hipStream_t>(stream)));
+}
+
+relation_status relation_linear_step(relation_dtype dtype, int B, int H, int D, const void* p1,
+                                     const void* p2, const void* I, const float* g,
+                                     const float* rope_cos, const float* rope_sin, float* state,
+                                     void* y, float scale, float tau_s, void* stream) {
+  if (!p1 || !p2 || !I || !g || !state || !y) return REL_ERR_NULL;
+  if (!rope_cos != !rope_sin) return REL_ERR_NULL;
+  if (dtype != REL_BF16 || D != 64) return REL_ERR_UNSUPPORTED;
+  relation_status st = check_shape(B, H, 1, D);
+  if (st != REL_OK) return st;
+  if ((st = check_params(scale, tau_s, 0.f)) != REL_OK) return st;
+  if (!aligned4(p1) || !aligned4(p2) || !aligned4(I) || !aligned4(g) || !aligned4(y) ||
+      !aligned4(state) || (rope_cos && (!aligned4(rope_cos) || !aligned4(rope_sin))))
+    return REL_ERR_ALIGN;
+  return from_hip(rel::launch_linear_step(
+      B, H, static_cast<const uint16_t*>(p1), static_cast<const uint16_t*>(p2),
+      static_cast<const uint16_t*>(I), g, rope_cos, rope_sin, state, static_cast<uint16_t*>(y),
+      scale, tau_s, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -266,6 +266,56 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                                  float scale, float tau_s, float lambda,
                                  void* stream);
 
+/*
+ * relation_linear_fwd — Linear Relation (Sec. 5.2; App. A.4): historical
+ * Others compressed into a D x D state with channel-wise retention, read
+ * before the current token is written:
+ *   S_t  = sigmoid(scale * p1_t . p2_t / tau_s)       (Self; RoPE leaves it
+ *                                                      unchanged)
+ *   x^   = x / ||x|| for the rotated p1_t, p2_t (a zero row stays zero)
+ *   E_t  = S_t (Diag(alpha_t) C_{t-1})^T p1^_t,  alpha_t = exp(g_t)
+ *   Y_t  = I_t + E_t
+ *   C_t  = Diag(alpha_t) C_{t-1} + S_t p2^_t I_t^T     (rows: key channel)
+ * computed by chunks of 128 tokens (one workgroup per head); exact up to
+ * rounding, also under total retention loss (g = -inf gives alpha = 0).
+ *
+ *   dtype            : REL_BF16 with D = 64 (else REL_ERR_UNSUPPORTED)
+ *   p1, p2, I        : in  [B, H, T, D] bf16, 16-byte aligned
+ *   g                : in  [B, H, T, D] fp32 log retention (<= 0; the
+ *                      upstream retention map of Sec. 5.2 produces it)
+ *   rope_cos/rope_sin: in  DEVICE fp32 [T, D/2] as for relation_mhr_fwd
+ *                      (row t = 0-based position in this call); both NULL
+ *                      to skip RoPE (one NULL alone: REL_ERR_NULL)
+ *   state_in         : in  DEVICE fp32 [B, H, D, D] C_0, or NULL for zero
+ *   y                : out [B, H, T, D] bf16
+ *   state_out        : out DEVICE fp32 [B, H, D, D] the state after the last
+ *                      token, or NULL (a later call continues from it)
+ *   scale, tau_s     : finite scale, tau_s > 0 (else REL_ERR_PARAM)
+ */
+relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, int D,
+                                    const void* p1, const void* p2, const void* I,
+                                    const float* g, const float* rope_cos,
+                                    const float* rope_sin, const float* state_in,
+                                    void* y, float* state_out,
+                                    float scale, float tau_s, void* stream);
+
+/*
+ * relation_linear_step — one decode step of Linear Relation (the recurrent
+ * step of Sec. 5.2) for one new token per sequence: the O(D^2) state is the
+ * whole decode state (Table 1).
+ *   p1, p2, I        : in  [B, H, D] bf16;  g: in [B, H, D] fp32
+ *   rope_cos/rope_sin: in  DEVICE fp32 [D/2], the table row of the token's
+ *                      position, or both NULL
+ *   state            : in/out DEVICE fp32 [B, H, D, D] (C_{t-1} -> C_t)
+ *   y                : out [B, H, D] bf16
+ * REL_BF16, D = 64 only; 4-byte alignment.
+ */
+relation_status relation_linear_step(relation_dtype dtype, int B, int H, int D,
+                                     const void* p1, const void* p2, const void* I,
+                                     const float* g, const float* rope_cos,
+                                     const float* rope_sin, float* state, void* y,
+                                     float scale, float tau_s, void* stream);
+
 /* Static, NUL-terminated description of a status code (host only). */
 const char* relation_status_string(relation_status s);
 

@@ -175,6 +175,39 @@ def test_mhr_validation(lib):
     assert bwd(ws=NUL) == REL_ERR_WORKSPACE
 
 
+def test_linear_validation(lib):
+    def lfwd(dtype=BF16, B=1, H=1, T=8, D=64, p1=P, g=P, y=P, rc=NUL, rs=NUL, cin=NUL,
+             cout=NUL, scale=0.125, tau=2.0):
+        return lib.relation_linear_fwd(dtype, B, H, T, D, p1, P, P, g, rc, rs, cin, y, cout,
+                                       scale, tau, None)
+
+    assert lfwd(p1=NUL) == REL_ERR_NULL
+    assert lfwd(g=NUL) == REL_ERR_NULL
+    assert lfwd(y=NUL) == REL_ERR_NULL
+    assert lfwd(rc=P) == REL_ERR_NULL  # one table alone
+    assert lfwd(dtype=F32) == REL_ERR_UNSUPPORTED
+    assert lfwd(D=48) == REL_ERR_UNSUPPORTED
+    assert lfwd(T=0) == REL_ERR_SHAPE
+    assert lfwd(tau=0.0) == REL_ERR_PARAM
+    assert lfwd(scale=float("nan")) == REL_ERR_PARAM
+    assert lfwd(p1=P_MIS) == REL_ERR_ALIGN
+    assert lfwd(g=P_MIS) == REL_ERR_ALIGN
+    assert lfwd(rc=P_MIS, rs=P) == REL_ERR_ALIGN
+    assert lfwd(cout=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+
+    def lstep(dtype=BF16, B=1, H=1, D=64, st=P, y=P, tau=2.0):
+        return lib.relation_linear_step(dtype, B, H, D, P, P, P, P, NUL, NUL, st, y, 0.125, tau,
+                                        None)
+
+    assert lstep(st=NUL) == REL_ERR_NULL
+    assert lstep(y=NUL) == REL_ERR_NULL
+    assert lstep(dtype=F32) == REL_ERR_UNSUPPORTED
+    assert lstep(D=80) == REL_ERR_UNSUPPORTED
+    assert lstep(B=0) == REL_ERR_SHAPE
+    assert lstep(tau=-1.0) == REL_ERR_PARAM
+    assert lstep(st=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(rel, "_LIB", None)
     monkeypatch.setattr(rel, "lib_path", lambda: str(tmp_path / "missing.so"))

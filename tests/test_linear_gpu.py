@@ -1,0 +1,162 @@
+"""GPU parity of Linear Relation (Sec. 5.2; App. A.4): relation_linear_fwd and
+relation_linear_step through the C ABI against the fp64 oracle
+(oracle/linear.py) on the same seeded inputs (workloads.make_linear_inputs).
+
+Tolerances. y = I + E is not a convex combination of values, so unlike the
+Full Relation output its magnitude is not bounded by max|I|; rounding y to
+bf16 alone costs up to 2^-9 |y| (0.016 at |y| = 8). Each element must be
+within 2e-2 * max(1, |Y|/4) of the oracle (2e-2 absolute up to |Y| = 4,
+then 5e-3 relative, 2.5 times the half-ulp), and the mean-abs error within
+3e-3. The fp32 state (read through a bf16 hi + lo split, updated with bf16
+operands) must be within 2e-2 * max(1, max|C|). Total retention loss
+(g = -1e4, alpha = 0) must give y = I bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exchange_relation_amd as rel
+import oracle
+from workloads import make_linear_inputs, make_mhr_maps
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+BF16_MAX, BF16_MEAN = 2e-2, 3e-3
+SCALE, TAU = 1 / 8, 2.0
+
+
+def f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def check(name, got, ref):
+    err = np.abs(np.asarray(got, dtype=np.float64) - ref)
+    bound = BF16_MAX * np.maximum(1.0, np.abs(ref) / 4.0)
+    worst = float((err / bound).max())
+    mx, mean = float(err.max()), float(err.mean())
+    print(f"  {name}: max-abs {mx:.3e} mean-abs {mean:.3e} worst err/bound {worst:.3f}")
+    assert worst <= 1.0, f"{name}: error {worst:.3f} x the bound"
+    assert mean <= BF16_MEAN, f"{name}: mean-abs {mean:.3e} > {BF16_MEAN}"
+
+
+def check_state(name, got, ref):
+    err = np.abs(np.asarray(got, dtype=np.float64) - ref)
+    tol = BF16_MAX * max(1.0, float(np.abs(ref).max()))
+    print(f"  {name}: max-abs {float(err.max()):.3e} (bound {tol:.3e})")
+    assert float(err.max()) <= tol
+
+
+def tables(T, D=64):
+    cs, sn, _ = make_mhr_maps(T, D, 2, 0)
+    return cs, sn
+
+
+def run_fwd(d, rope=None, state_in=None):
+    cs, sn = rope if rope is not None else (None, None)
+    y, c = rel.relation_linear_fwd(
+        *(d[n].to(DEV) for n in ("p1", "p2", "I", "g")),
+        rope_cos=None if cs is None else cs.to(DEV), rope_sin=None if sn is None else sn.to(DEV),
+        state_in=None if state_in is None else state_in.to(DEV), want_state=True, scale=SCALE,
+        tau_s=TAU)
+    torch.cuda.synchronize()
+    return y.cpu(), c.cpu()
+
+
+def oracle_fwd(d, rope=None, C0=None):
+    cs, sn = (None, None) if rope is None else (f64(rope[0]), f64(rope[1]))
+    return oracle.linear_relation_forward(f64(d["p1"]), f64(d["p2"]), f64(d["I"]), f64(d["g"]),
+                                          SCALE, TAU, cs, sn,
+                                          C0=None if C0 is None else f64(C0))
+
+
+@pytest.mark.parametrize("use_rope", [False, True])
+@pytest.mark.parametrize("T", [1, 17, 128, 129, 300, 520])
+def test_linear_fwd_vs_oracle(T, use_rope):
+    d = make_linear_inputs(2, 2, T, 64, seed=2000 + T)
+    rope = tables(T) if use_rope else None
+    y, c = run_fwd(d, rope)
+    r = oracle_fwd(d, rope)
+    check("y", f64(y), r["Y"])
+    check_state("state", f64(c), r["C"])
+
+
+@pytest.mark.parametrize("resets,keep", [(True, False), (False, True), (True, True)])
+def test_linear_fwd_extreme_retention(resets, keep):
+    """Near-total resets (g = -60 on 1 % of entries: the per-pair path of the
+    diagonal blocks) and channels without loss (g = 0)."""
+    d = make_linear_inputs(2, 3, 400, 64, seed=2100, resets=resets, keep=keep)
+    y, c = run_fwd(d)
+    r = oracle_fwd(d)
+    check("y", f64(y), r["Y"])
+    check_state("state", f64(c), r["C"])
+
+
+def test_linear_total_retention_loss_is_identity():
+    d = make_linear_inputs(1, 2, 260, 64, seed=2200)
+    d["g"] = torch.full_like(d["g"], -1.0e4)
+    y, c = run_fwd(d)
+    assert torch.equal(y, d["I"])
+    r = oracle_fwd(d)
+    check_state("state", f64(c), r["C"])
+
+
+def test_linear_state_in_and_handoff():
+    B, H, T, T1 = 2, 2, 300, 128 + 37
+    d = make_linear_inputs(B, H, T, 64, seed=2300)
+    rope = tables(T)
+    C0 = torch.from_numpy(np.random.default_rng(1).standard_normal((B, H, 64, 64)).astype(np.float32))
+    y, c = run_fwd(d, rope, state_in=C0)
+    r = oracle_fwd(d, rope, C0=C0)
+    check("y with C0", f64(y), r["Y"])
+    check_state("state with C0", f64(c), r["C"])
+    # two calls chained through the state equal one call
+    a = {k: v[:, :, :T1].contiguous() for k, v in d.items()}
+    b = {k: v[:, :, T1:].contiguous() for k, v in d.items()}
+    ya, ca = run_fwd(a, (rope[0][:T1].contiguous(), rope[1][:T1].contiguous()), state_in=C0)
+    yb, cb = run_fwd(b, (rope[0][T1:].contiguous(), rope[1][T1:].contiguous()), state_in=ca)
+    check("y chained", f64(torch.cat([ya, yb], dim=2)), r["Y"])
+    check_state("state chained", f64(cb), r["C"])
+
+
+@pytest.mark.parametrize("use_rope", [False, True])
+def test_linear_step_vs_oracle_and_forward(use_rope):
+    B, H, T = 3, 4, 40
+    d = make_linear_inputs(B, H, T, 64, seed=2400, with_dy=False)
+    rope = tables(T) if use_rope else None
+    state = torch.zeros((B, H, 64, 64), device=DEV, dtype=torch.float32)
+    C = np.zeros((B, H, 64, 64))
+    ys = []
+    for t in range(T):
+        args = [d[n][:, :, t].contiguous().to(DEV) for n in ("p1", "p2", "I", "g")]
+        kw = {}
+        if rope is not None:
+            kw = {"rope_cos": rope[0][t].contiguous().to(DEV),
+                  "rope_sin": rope[1][t].contiguous().to(DEV)}
+        y = rel.relation_linear_step(*args, state, scale=SCALE, tau_s=TAU, **kw)
+        ys.append(y.cpu())
+        yo, C = oracle.linear_relation_step(
+            f64(d["p1"][:, :, t]), f64(d["p2"][:, :, t]), f64(d["I"][:, :, t]),
+            f64(d["g"][:, :, t]), C, SCALE, TAU,
+            None if rope is None else f64(rope[0][t]), None if rope is None else f64(rope[1][t]))
+        check(f"step {t} y", f64(ys[-1]), yo)
+    torch.cuda.synchronize()
+    check_state("step state", f64(state), C)
+    yf, cf = run_fwd(d, rope)
+    check("steps vs forward", f64(torch.stack(ys, dim=2)), f64(yf).astype(np.float64))
+
+
+def test_linear_fwd_30m_layer_shape_sampled_heads():
+    """The 30M-class Linear Relation layer at its steady-state micro-batch
+    (B=32, H=8, T=1024, d_h=64; paper App. H, Table 16) in the benchmark's
+    launch shape, with RoPE; sampled heads from the oracle."""
+    B, H, T = 32, 8, 1024
+    d = make_linear_inputs(B, H, T, 64, seed=42)
+    rope = tables(T)
+    y, c = run_fwd(d, rope)
+    for b, h in ((0, 0), (31, 7), (13, 4)):
+        sub = {k: v[b:b + 1, h:h + 1] for k, v in d.items()}
+        r = oracle_fwd(sub, rope)
+        check(f"y[{b},{h}]", f64(y[b:b + 1, h:h + 1]), r["Y"])
+        check_state(f"state[{b},{h}]", f64(c[b:b + 1, h:h + 1]), r["C"])
