@@ -310,6 +310,53 @@ def bench_mhr(rel, torch, dev, reps, B=16, H=8, T=2048, D=64, seed=42):
             "fwdbwd_tflops": 3.5 * f / ((fm + bm) * 1e-3) / 1e12}
 
 
+def bench_linear(rel, torch, dev, reps, B=32, H=8, T=1024, D=64, seed=42):
+    """Linear Relation forward with RoPE on the 30M-class layer at the pages'
+    steady-state micro-batch (B=32, H=8, T=1024, d_h=64; App. H, Table 16).
+    Algorithmic HBM bytes per token and head: p1, p2, I, y in bf16 and the
+    fp32 log retention g, 12 D."""
+    from workloads import make_linear_inputs, make_mhr_maps
+    d = make_linear_inputs(B, H, T, D, seed)
+    p1, p2, I, g = (d[n].to(dev) for n in ("p1", "p2", "I", "g"))
+    cs, sn, _ = (t.to(dev) for t in make_mhr_maps(T, D, 2, seed))
+    y = torch.empty_like(I)
+    stream = torch.cuda.current_stream(dev)
+    tf = EventTimer(torch, stream)
+    warm = 100  # a few ms of work: the clocks ramp under sustained load
+    for i in range(reps + warm):
+        s0 = tf.start() if i >= warm else None
+        rel.relation_linear_fwd(p1, p2, I, g, cs, sn, scale=1 / math.sqrt(D), y=y)
+        if i >= warm:
+            tf.stop(s0)
+    fm = tf.mean_ms()
+    nbytes = 12 * D * B * H * T
+    return {"workload": f"linear relation fwd, RoPE, B={B} H={H} T={T} D={D}", "fwd_ms": fm,
+            "tokens_per_s": B * T / (fm * 1e-3), "fwd_GBps": nbytes / (fm * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (fm * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def bench_linear_step(rel, torch, dev, reps=200, B=32, H=12, D=64, seed=42):
+    """One Linear Relation decode step per sequence on the cache workload's
+    batch (32 sequences x 12 heads): the fp32 D x D state is read and
+    written once; bytes per head 8 D^2 + 10 D."""
+    from workloads import make_linear_inputs
+    d = make_linear_inputs(B, H, 1, D, seed)
+    p1, p2, I, g = (d[n][:, :, 0].contiguous().to(dev) for n in ("p1", "p2", "I", "g"))
+    state = torch.zeros((B, H, D, D), device=dev, dtype=torch.float32)
+    y = torch.empty_like(I)
+    stream = torch.cuda.current_stream(dev)
+    t = EventTimer(torch, stream)
+    for i in range(reps + 10):
+        s0 = t.start() if i >= 10 else None
+        rel.relation_linear_step(p1, p2, I, g, state, scale=1 / math.sqrt(D), y=y)
+        if i >= 10:
+            t.stop(s0)
+    ms = t.mean_ms()
+    nbytes = (8 * D * D + 10 * D) * B * H
+    return {"workload": f"linear relation decode step, B={B} H={H} D={D}", "ms": ms,
+            "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+
 def bench_copy(torch, dev, nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of known size (torch's copy kernel): the
     calibration for the FETCH_SIZE / WRITE_SIZE counters (reads nbytes and
@@ -383,7 +430,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", choices=["step", "fwd", "decode", "ragged", "mhr", "prefill", "attn",
-                             "copy"],
+                             "linear", "copy"],
                     default=None,
                     help="run one measurement and print its raw numbers ('copy': a plain "
                          "device copy of known size, the HBM-counter calibration)")
@@ -422,6 +469,10 @@ def main():
         return
     if args.only == "prefill":
         print(json.dumps(bench_prefill(rel, torch, dev, args.steps)))
+        return
+    if args.only == "linear":
+        print(json.dumps({"fwd": bench_linear(rel, torch, dev, args.steps),
+                          "step": bench_linear_step(rel, torch, dev)}))
         return
     if args.only == "attn":
         print(json.dumps(bench_fwdbwd_vs_attention(rel, torch, dev, args.steps)))

@@ -101,10 +101,13 @@ __device__ __forceinline__ float min_groups(float x) {
 }
 
 // One chunk's raw rows for one lane (slot s: channels 32s + 8g .. +7).
+// Rows past T are loaded clamped and zeroed only where they are consumed
+// (a select right after the load would make the prefetch wait for it).
 struct Raw {
   u32x4 a1[2], a2[2], iv[2];
   f32x4 gg[4];
   f32x4 cs[2], sn[2];
+  bool ok;
 };
 
 template <bool ROPE>
@@ -112,22 +115,16 @@ __device__ __forceinline__ void load_raw(Raw& r, const uint16_t* p1, const uint1
                                          const uint16_t* iv, const float* g, const float* rc,
                                          const float* rs, size_t base, int t, int T, int grp) {
   const bool ok = t < T;
+  r.ok = ok;
   const size_t row = base + static_cast<size_t>(ok ? t : T - 1) * D + 8 * grp;
-  const u32x4 z = {0, 0, 0, 0};
-  const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const u32x4 x1 = *reinterpret_cast<const u32x4*>(p1 + row + 32 * s);
-    const u32x4 x2 = *reinterpret_cast<const u32x4*>(p2 + row + 32 * s);
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(iv + row + 32 * s);
-    r.a1[s] = ok ? x1 : z;
-    r.a2[s] = ok ? x2 : z;
-    r.iv[s] = ok ? xv : z;
+    r.a1[s] = *reinterpret_cast<const u32x4*>(p1 + row + 32 * s);
+    r.a2[s] = *reinterpret_cast<const u32x4*>(p2 + row + 32 * s);
+    r.iv[s] = *reinterpret_cast<const u32x4*>(iv + row + 32 * s);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(g + row + 32 * s + 4 * h);
-      r.gg[2 * s + h] = ok ? x : zf;
-    }
+    for (int h = 0; h < 2; ++h)
+      r.gg[2 * s + h] = *reinterpret_cast<const f32x4*>(g + row + 32 * s + 4 * h);
   }
   if constexpr (ROPE) {
     const size_t tr = static_cast<size_t>(ok ? t : T - 1) * (D / 2) + 8 * grp;
@@ -189,6 +186,18 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
     const int trow = t0 + 16 * w + l16;  // this lane's row
     // ---------------- row-local: coordinates, Self, q, k, prefix of g
     float a1[16], a2[16], q[16], k[16], b2[16];
+    {
+      const u32x4 z = {0, 0, 0, 0};
+      const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        raw.a1[s] = raw.ok ? raw.a1[s] : z;
+        raw.a2[s] = raw.ok ? raw.a2[s] : z;
+        raw.iv[s] = raw.ok ? raw.iv[s] : z;
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h) raw.gg[h] = raw.ok ? raw.gg[h] : zf;
+    }
     unpack8(raw.a1[0], *reinterpret_cast<float(*)[8]>(&a1[0]));
     unpack8(raw.a1[1], *reinterpret_cast<float(*)[8]>(&a1[8]));
     unpack8(raw.a2[0], *reinterpret_cast<float(*)[8]>(&a2[0]));
