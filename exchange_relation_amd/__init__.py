@@ -28,6 +28,7 @@ __all__ = [
     "relation_mhr_fwd",
     "relation_mhr_bwd",
     "relation_linear_fwd",
+    "relation_linear_bwd",
     "relation_linear_step",
     "relation_status_string",
     "relation_version",
@@ -51,6 +52,8 @@ EXPORTED_SYMBOLS = (
     "relation_mhr_bwd_workspace_bytes",
     "relation_mhr_bwd",
     "relation_linear_fwd",
+    "relation_linear_bwd_workspace_bytes",
+    "relation_linear_bwd",
     "relation_linear_step",
     "relation_status_string",
     "relation_version",
@@ -116,6 +119,12 @@ def load_library():
     lib.relation_linear_fwd.restype = c_int
     lib.relation_linear_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, c_float, c_float, vp]
+    lib.relation_linear_bwd_workspace_bytes.restype = c_size
+    lib.relation_linear_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    lib.relation_linear_bwd.restype = c_int
+    lib.relation_linear_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size, c_float,
+                                        c_float, vp]
     lib.relation_linear_step.restype = c_int
     lib.relation_linear_step.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, vp,
                                          vp, c_float, c_float, vp]
@@ -451,6 +460,39 @@ def relation_linear_fwd(p1, p2, I, g, rope_cos=None, rope_sin=None, state_in=Non
     if st != 0:
         raise RelationError(st, "relation_linear_fwd")
     return y, state_out
+
+
+def relation_linear_bwd(p1, p2, I, g, dy, rope_cos=None, rope_sin=None, state_in=None,
+                        dstate_out=None, want_dstate_in=False, scale=None, tau_s=2.0,
+                        workspace=None, stream=None):
+    """Gradients of relation_linear_fwd. Returns (dp1, dp2, dI, dg,
+    dstate_in or None); dg is fp32 like g."""
+    lib = load_library()
+    B, H, T, D = p1.shape
+    dev, dt = p1.device, p1.dtype
+    for name, t in (("p1", p1), ("p2", p2), ("I", I), ("dy", dy)):
+        _check(t, name, dt, (B, H, T, D), dev)
+    _check(g, "g", torch.float32, (B, H, T, D), dev)
+    _mhr_maps(p1, rope_cos, rope_sin, None)
+    for name, t in (("state_in", state_in), ("dstate_out", dstate_out)):
+        if t is not None:
+            _check(t, name, torch.float32, (B, H, D, D), dev)
+    dp1, dp2, dI = torch.empty_like(p1), torch.empty_like(p2), torch.empty_like(I)
+    dg = torch.empty_like(g)
+    dstate_in = (torch.empty((B, H, D, D), device=dev, dtype=torch.float32)
+                 if want_dstate_in else None)
+    need = int(lib.relation_linear_bwd_workspace_bytes(_dtype_code(p1), B, H, T, D))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), device=dev, dtype=torch.uint8)
+    st = lib.relation_linear_bwd(_dtype_code(p1), B, H, T, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(g),
+                                 _ptr(rope_cos), _ptr(rope_sin), _ptr(state_in), _ptr(dy),
+                                 _ptr(dstate_out), _ptr(dp1), _ptr(dp2), _ptr(dI), _ptr(dg),
+                                 _ptr(dstate_in), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _scale(D, scale),
+                                 float(tau_s), _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_linear_bwd")
+    return dp1, dp2, dI, dg, dstate_in
 
 
 def relation_linear_step(p1, p2, I, g, state, rope_cos=None, rope_sin=None, scale=None,

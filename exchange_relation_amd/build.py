@@ -27,6 +27,7 @@ SOURCES = [
     "decode.hip",
     "mhr.hip",
     "linear.hip",
+    "linear_bwd.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -84,6 +84,16 @@ hipError_t launch_linear_fwd(int B, int H, int T, const uint16_t* p1, const uint
                              const float* rope_sin, const float* state_in, uint16_t* y,
                              float* state_out, float* states, float scale, float tau,
                              hipStream_t stream);
+// Backward: gradients of relation_linear_fwd. ws: linear_bwd_workspace_bytes()
+// (the state before every chunk, then the final state); dstate_out, the
+// gradient of the final state, or NULL; dstate_in (out) or NULL.
+size_t linear_bwd_workspace_bytes(int B, int H, int T);
+hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint16_t* p2,
+                             const uint16_t* iv, const float* g, const float* rope_cos,
+                             const float* rope_sin, const float* state_in, const uint16_t* dy,
+                             const float* dstate_out, uint16_t* dp1, uint16_t* dp2, uint16_t* dI,
+                             float* dg, float* dstate_in, float* ws, float scale, float tau,
+                             hipStream_t stream);
 // One token per head; state [B, H, D, D] fp32 updated in place; rope tables
 // are the [D/2] rows of the token's position, or NULL.
 hipError_t launch_linear_step(int B, int H, const uint16_t* p1, const uint16_t* p2,

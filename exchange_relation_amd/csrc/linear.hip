@@ -29,23 +29,11 @@
 //  * the state (fp32, in registers: 2 blocks of 16 x 16 per wave) feeds the
 //    next chunk through LDS as bf16 hi + lo, so the read of the state keeps
 //    about 16 bits of its mantissa.
-#include "common.hpp"
 #include "launch.hpp"
+#include "linear_common.hpp"
 
 namespace rel {
 namespace linrel {
-
-constexpr int D = 64;
-constexpr int NW = 8;        // waves per workgroup
-constexpr int NT = NW * 64;  // threads
-constexpr int CH = NW * 16;  // tokens per chunk
-constexpr int IS = 72;       // bf16 row stride of the tiles in LDS
-constexpr int KS = 68;       // fp32 row stride of the k tile
-// A sub-chunk whose retention over its 16 tokens is above 2^-60 on every
-// channel uses the ratio form for its diagonal block.
-constexpr float kSafeLog2 = -60.f;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 struct Smem {
   uint16_t iv[2][CH * IS];  // I rows of the chunk, by chunk parity
@@ -57,88 +45,10 @@ struct Smem {
   float dec[2][NW][D];      // e^{L_s[c]}: retention over sub-chunk s, by parity
 };
 
-__device__ __forceinline__ bf16x8 cat(uint2 a, uint2 b) {
-  const u32x4 w = {a.x, a.y, b.x, b.y};
-  return __builtin_bit_cast(bf16x8, w);
-}
-__device__ __forceinline__ bf16x8 pack_x8(const float* x) {
-  float t[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = x[e];
-  return __builtin_bit_cast(bf16x8, pack8(t));
-}
-__device__ __forceinline__ s16x4 pack_x4(f32x4 a) {
-  const uint2 w = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-  return __builtin_bit_cast(s16x4, w);
-}
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-// inclusive prefix sum over the 16 lanes of a DPP row
-template <int N>
-__device__ __forceinline__ float row_shr(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row_prefix(float x) {
-  x += row_shr<1>(x);
-  x += row_shr<2>(x);
-  x += row_shr<4>(x);
-  x += row_shr<8>(x);
-  return x;
-}
-// sum over the four 16-lane groups (the four channel groups of a row)
-__device__ __forceinline__ float sum_groups(float x) {
-  x += __shfl_xor(x, 16);
-  return sum_across_halves(x);
-}
-__device__ __forceinline__ float min_groups(float x) {
-  x = fminf(x, __shfl_xor(x, 16));
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// One chunk's raw rows for one lane (slot s: channels 32s + 8g .. +7).
-// Rows past T are loaded clamped and zeroed only where they are consumed
-// (a select right after the load would make the prefetch wait for it).
-struct Raw {
-  u32x4 a1[2], a2[2], iv[2];
-  f32x4 gg[4];
-  f32x4 cs[2], sn[2];
-  bool ok;
-};
-
-template <bool ROPE>
-__device__ __forceinline__ void load_raw(Raw& r, const uint16_t* p1, const uint16_t* p2,
-                                         const uint16_t* iv, const float* g, const float* rc,
-                                         const float* rs, size_t base, int t, int T, int grp) {
-  const bool ok = t < T;
-  r.ok = ok;
-  const size_t row = base + static_cast<size_t>(ok ? t : T - 1) * D + 8 * grp;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    r.a1[s] = *reinterpret_cast<const u32x4*>(p1 + row + 32 * s);
-    r.a2[s] = *reinterpret_cast<const u32x4*>(p2 + row + 32 * s);
-    r.iv[s] = *reinterpret_cast<const u32x4*>(iv + row + 32 * s);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      r.gg[2 * s + h] = *reinterpret_cast<const f32x4*>(g + row + 32 * s + 4 * h);
-  }
-  if constexpr (ROPE) {
-    const size_t tr = static_cast<size_t>(ok ? t : T - 1) * (D / 2) + 8 * grp;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      r.cs[h] = *reinterpret_cast<const f32x4*>(rc + tr + 4 * h);
-      r.sn[h] = *reinterpret_cast<const f32x4*>(rs + tr + 4 * h);
-    }
-  }
-}
-
 // blockIdx.x = head (b * H + h). states (optional): the state before every
-// chunk, [BH][nch][D][D] fp32, for the backward.
-template <bool ROPE>
+// chunk, [BH][nch][D][D] fp32, for the backward. YOUT false: the state pass
+// alone (no Y; the backward's first pass).
+template <bool ROPE, bool YOUT>
 __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
     const uint16_t* __restrict__ p1, const uint16_t* __restrict__ p2,
     const uint16_t* __restrict__ iv, const float* __restrict__ g, const float* __restrict__ rc,
@@ -185,60 +95,13 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
     const int t0 = n * CH;
     const int trow = t0 + 16 * w + l16;  // this lane's row
     // ---------------- row-local: coordinates, Self, q, k, prefix of g
-    float a1[16], a2[16], q[16], k[16], b2[16];
-    {
-      const u32x4 z = {0, 0, 0, 0};
-      const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        raw.a1[s] = raw.ok ? raw.a1[s] : z;
-        raw.a2[s] = raw.ok ? raw.a2[s] : z;
-        raw.iv[s] = raw.ok ? raw.iv[s] : z;
-      }
-#pragma unroll
-      for (int h = 0; h < 4; ++h) raw.gg[h] = raw.ok ? raw.gg[h] : zf;
-    }
-    unpack8(raw.a1[0], *reinterpret_cast<float(*)[8]>(&a1[0]));
-    unpack8(raw.a1[1], *reinterpret_cast<float(*)[8]>(&a1[8]));
-    unpack8(raw.a2[0], *reinterpret_cast<float(*)[8]>(&a2[0]));
-    unpack8(raw.a2[1], *reinterpret_cast<float(*)[8]>(&a2[8]));
-    if constexpr (ROPE) {  // rotate-half pairs (c, c + 32) sit in one lane
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float c = raw.cs[e >> 2][e & 3], s_ = raw.sn[e >> 2][e & 3];
-        float x = a1[e], z = a1[8 + e];
-        a1[e] = fmaf(x, c, -z * s_);
-        a1[8 + e] = fmaf(x, s_, z * c);
-        x = a2[e];
-        z = a2[8 + e];
-        a2[e] = fmaf(x, c, -z * s_);
-        a2[8 + e] = fmaf(x, s_, z * c);
-      }
-    }
-    float dot = 0.f, n1 = 0.f, n2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dot = fmaf(a1[i], a2[i], dot);
-      n1 = fmaf(a1[i], a1[i], n1);
-      n2 = fmaf(a2[i], a2[i], n2);
-    }
-    dot = sum_groups(dot);
-    n1 = sum_groups(n1);
-    n2 = sum_groups(n2);
-    const float S = fast_rcp(1.f + fast_exp2(-sl2 * dot));
-    const float r1 = n1 > 0.f ? S * __builtin_amdgcn_rsqf(n1) : 0.f;
-    const float r2 = n2 > 0.f ? S * __builtin_amdgcn_rsqf(n2) : 0.f;
-    float lw[16], lmin = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      q[i] = a1[i] * r1;
-      k[i] = a2[i] * r2;
-      b2[i] = row_prefix(raw.gg[i >> 2][i & 3] * kLog2e);
-      lw[i] = __shfl(b2[i], (lane & 48) | 15);
-      lmin = fminf(lmin, lw[i]);
-    }
-    // every lane holds the wave's minimum; make the branch scalar
-    const bool safe = __builtin_amdgcn_readfirstlane(min_groups(lmin) >= kSafeLog2 ? 1 : 0) != 0;
+    RowLocal rl;
+    row_local<ROPE>(raw, sl2, lane, rl);
+    const float* q = rl.q;
+    const float* k = rl.k;
+    const float* b2 = rl.b2;
+    const float* lw = rl.lw;
+    const bool safe = rl.safe;
     // retention factors relative to the sub-chunk's boundaries (all <= 1)
     float qq[16], kk[16], dw[16];
 #pragma unroll
@@ -272,7 +135,8 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
     const bf16x8 bq0 = pack_x8(&qq[0]), bq1 = pack_x8(&qq[8]);
     // ---------------- diagonal block A^T[j][t], j < t inside the sub-chunk
     f32x4 ad = {0.f, 0.f, 0.f, 0.f};
-    if (safe) {
+    if (!YOUT) {
+    } else if (safe) {
       float kd[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) kd[i] = kk[i] * fast_rcp(dw[i]);  // k e^{B_start - B_j}
@@ -307,6 +171,7 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
     __syncthreads();  // (1) k, I, retentions of every sub-chunk published
 
     const uint16_t* ivb = sm.iv[par];
+    if constexpr (YOUT) {
     f32x4 acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -383,6 +248,7 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
         sm.ys[(16 * w + 4 * grp + r) * IS + 16 * b + l16] = f32_to_bf16_bits(iv_ + acc[b][r]);
       }
     }
+    }  // YOUT
     // K~ = k e^{B_L - B_j} = kk * prod_{s > w} e^{L_s}
     {
       float after[16];
@@ -448,7 +314,7 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
       put_state();
     }
     // ---------------- Y rows of this wave, coalesced
-    if (trow < T) {
+    if (YOUT && trow < T) {
       const uint16_t* yr = &sm.ys[(16 * w + l16) * IS + 8 * grp];
       uint16_t* yo = y + base + static_cast<size_t>(trow) * D + 8 * grp;
       *reinterpret_cast<u32x4*>(yo) = *reinterpret_cast<const u32x4*>(yr);
@@ -525,12 +391,18 @@ hipError_t launch_linear_fwd(int B, int H, int T, const uint16_t* p1, const uint
   using namespace linrel;
   const float sl2 = scale * kLog2e / tau;
   const dim3 grid(static_cast<unsigned>(B) * H);
-  if (rope_cos)
-    hipLaunchKernelGGL(linear_fwd_kernel<true>, grid, dim3(NT), 0, stream, p1, p2, iv, g, rope_cos,
-                       rope_sin, state_in, y, state_out, states, T, sl2);
-  else
-    hipLaunchKernelGGL(linear_fwd_kernel<false>, grid, dim3(NT), 0, stream, p1, p2, iv, g,
+  if (rope_cos && y)
+    hipLaunchKernelGGL((linear_fwd_kernel<true, true>), grid, dim3(NT), 0, stream, p1, p2, iv, g,
+                       rope_cos, rope_sin, state_in, y, state_out, states, T, sl2);
+  else if (y)
+    hipLaunchKernelGGL((linear_fwd_kernel<false, true>), grid, dim3(NT), 0, stream, p1, p2, iv, g,
                        nullptr, nullptr, state_in, y, state_out, states, T, sl2);
+  else if (rope_cos)
+    hipLaunchKernelGGL((linear_fwd_kernel<true, false>), grid, dim3(NT), 0, stream, p1, p2, iv, g,
+                       rope_cos, rope_sin, state_in, y, state_out, states, T, sl2);
+  else
+    hipLaunchKernelGGL((linear_fwd_kernel<false, false>), grid, dim3(NT), 0, stream, p1, p2, iv,
+                       g, nullptr, nullptr, state_in, y, state_out, states, T, sl2);
   return hipGetLastError();
 }
 

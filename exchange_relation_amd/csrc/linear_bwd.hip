@@ -1,0 +1,625 @@
+// Linear Relation backward, bf16 storage, D = 64.
+//
+// Gradients of the recurrence of Sec. 5.2 (App. A.4) with respect to p1, p2,
+// I, the log retention g and the initial state. With q = S p^_1, k = S p^_2,
+// B_t the cumulative log retention and dE = dY, per chunk of 128 tokens
+// (C_prev: the state before it, dC: the gradient of the state after it):
+//   dq_t  = sum_{j<t} dA_tj k_j e^{B_t - B_j} + e^{B_t - B_0} (C_prev dE_t)
+//   dk_j  = sum_{t>j} dA_tj q_t e^{B_t - B_j} + e^{B_L - B_j} (dC I_j)
+//   dI_j  = dY_j + sum_{t>j} A_tj dE_t + (k_j e^{B_L - B_j})^T dC
+//   dA_tj = dE_t . I_j,   A_tj = sum_c q_t k_j e^{B_t - B_j}
+//   dC_prev = e^{B_L - B_0} dC + sum_t (q_t e^{B_t - B_0}) dE_t^T
+//   dB_t  = q_t dq_t - k_t dk_t  (+ sum_v dC_T C_T at the last token),
+//   dg_t  = sum_{t' >= t} dB_t'
+// then the chain rule through S = sigmoid(s x1.x2 / tau), the normalisation
+// and RoPE. Every e^{.} factor is split at sub-chunk boundaries into factors
+// <= 1 exactly as in the forward (linear.hip); the diagonal 16 x 16 blocks use
+// the ratio form unless a sub-chunk's retention span is beyond 2^60, where an
+// exact per-pair path runs instead.
+//
+// One workgroup (8 waves) per head walks the chunks from the last to the
+// first; the state before every chunk comes from the forward's state pass.
+// Wave w owns the 16 rows of sub-chunk w and does, for them, dq against key
+// blocks s' <= w and dk / dI against query blocks w' >= w: nine block pairs on
+// every wave.
+#include "launch.hpp"
+#include "linear_common.hpp"
+
+namespace rel {
+namespace linrel {
+
+struct SmemB {
+  uint16_t iv[CH * IS];   // I rows
+  uint16_t dy[CH * IS];   // dY rows
+  uint16_t qq[CH * IS];   // q e^{B_t - B_start(sub)}
+  uint16_t kk[CH * IS];   // k e^{B_end(sub) - B_j}
+  uint16_t chi[D * IS];   // state before the chunk, [c][v], bf16 hi / lo
+  uint16_t clo[D * IS];
+  uint16_t dhi[D * IS];   // gradient of the state after the chunk, hi / lo
+  uint16_t dlo[D * IS];
+  float stage[NW][16 * KS];  // per-wave layout change (MFMA output -> rows)
+  float dec[NW][D];          // e^{L_s[c]}
+  float tot[NW][D];          // sum of dB over each sub-chunk
+  float fin[D];              // sum_v dC_T C_T: dB of the last token
+  float carry[2][D];         // sum of dB over the chunks after the current one,
+                             // by chunk parity
+};
+
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+template <bool ROPE>
+__global__ __launch_bounds__(NT, 1) void linear_bwd_kernel(
+    const uint16_t* __restrict__ p1, const uint16_t* __restrict__ p2,
+    const uint16_t* __restrict__ iv, const float* __restrict__ g, const float* __restrict__ rc,
+    const float* __restrict__ rs, const uint16_t* __restrict__ dy,
+    const float* __restrict__ states, const float* __restrict__ cT, const float* __restrict__ dcT,
+    uint16_t* __restrict__ dp1, uint16_t* __restrict__ dp2, uint16_t* __restrict__ dI,
+    float* __restrict__ dg, float* __restrict__ dc0, int T, float sl2, float slope) {
+  __shared__ SmemB sm;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int head = blockIdx.x;
+  const size_t base = static_cast<size_t>(head) * T * D;
+  const size_t sbase = static_cast<size_t>(head) * D * D;
+  const int nch = (T + CH - 1) / CH;
+
+  // ---- gradient of the state after the current chunk: wave w holds rows
+  // 16 rb .. +15, column blocks cb0, cb0 + 1 (as the forward's state)
+  const int rb = w >> 1, cb0 = 2 * (w & 1);
+  f32x4 dcs[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      dcs[i][r] = dcT ? dcT[sbase + (16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] : 0.f;
+  auto put_dstate = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int o = (16 * rb + 4 * grp + r) * IS + 16 * (cb0 + i) + l16;
+        const float x = dcs[i][r];
+        const uint16_t hb = f32_to_bf16_bits(x);
+        sm.dhi[o] = hb;
+        sm.dlo[o] = f32_to_bf16_bits(x - bf16_bits_to_f32(hb));
+      }
+    }
+  };
+  put_dstate();
+  // dB of the last token gains sum_v dC_T[c][v] C_T[c][v]
+  {
+    const int c = tid >> 3, part = tid & 7;
+    float f = 0.f;
+    if (dcT) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const size_t o = sbase + c * D + 8 * part + e;
+        f = fmaf(dcT[o], cT[o], f);
+      }
+    }
+    f += __shfl_xor(f, 1);
+    f += __shfl_xor(f, 2);
+    f += __shfl_xor(f, 4);
+    if (part == 0) sm.fin[c] = f;
+  }
+  if (tid < D) sm.carry[(nch - 1) & 1][tid] = 0.f;
+
+  // prefetch of one chunk: rows, dY rows and the state before it (8
+  // consecutive elements of row c = tid / 8)
+  Raw raw;
+  u32x4 rdy[2];
+  f32x4 cpre[2];
+  auto prefetch = [&](int n) {
+    const int t = n * CH + 16 * w + l16;
+    load_raw<ROPE>(raw, p1, p2, iv, g, rc, rs, base, t, T, grp);
+    const size_t row = base + static_cast<size_t>(t < T ? t : T - 1) * D + 8 * grp;
+    rdy[0] = *reinterpret_cast<const u32x4*>(dy + row);
+    rdy[1] = *reinterpret_cast<const u32x4*>(dy + row + 32);
+    const float* sp = states + (static_cast<size_t>(head) * nch + n) * D * D + 8 * tid;
+    cpre[0] = *reinterpret_cast<const f32x4*>(sp);
+    cpre[1] = *reinterpret_cast<const f32x4*>(sp + 4);
+  };
+  prefetch(nch - 1);
+
+  for (int n = nch - 1; n >= 0; --n) {
+    const int trow = n * CH + 16 * w + l16;
+    // ---------------- row-local recompute
+    RowLocal rl;
+    row_local<ROPE>(raw, sl2, lane, rl);
+    const bool ok = raw.ok;
+    const bool safe = rl.safe;
+    {
+      const u32x4 z = {0, 0, 0, 0};
+      rdy[0] = ok ? rdy[0] : z;
+      rdy[1] = ok ? rdy[1] : z;
+    }
+    float qq[16], kk[16], dw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      qq[i] = rl.q[i] * fast_exp2(rl.b2[i]);
+      kk[i] = rl.k[i] * fast_exp2(rl.lw[i] - rl.b2[i]);
+      dw[i] = fast_exp2(rl.lw[i]);
+    }
+    // the prefix of g waits in this wave's staging area until the row
+    // updates at the end of the chunk (the registers are needed meanwhile)
+    float* st = sm.stage[w];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<f32x4*>(&st[l16 * KS + 32 * s + 8 * grp + 4 * h]) =
+            f32x4{rl.b2[8 * s + 4 * h], rl.b2[8 * s + 4 * h + 1], rl.b2[8 * s + 4 * h + 2],
+                  rl.b2[8 * s + 4 * h + 3]};
+    const bf16x8 bqq[2] = {pack_x8(&qq[0]), pack_x8(&qq[8])};
+    const bf16x8 bdy[2] = {__builtin_bit_cast(bf16x8, rdy[0]), __builtin_bit_cast(bf16x8, rdy[1])};
+    const bf16x8 biv[2] = {__builtin_bit_cast(bf16x8, raw.iv[0]), __builtin_bit_cast(bf16x8, raw.iv[1])};
+    // ---------------- publish
+    {
+      const int o = (16 * w + l16) * IS + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        *reinterpret_cast<u32x4*>(&sm.iv[o + 32 * s]) = raw.iv[s];
+        *reinterpret_cast<u32x4*>(&sm.dy[o + 32 * s]) = rdy[s];
+        *reinterpret_cast<u32x4*>(&sm.qq[o + 32 * s]) = __builtin_bit_cast(u32x4, bqq[s]);
+        *reinterpret_cast<u32x4*>(&sm.kk[o + 32 * s]) = __builtin_bit_cast(u32x4, pack_x8(&kk[8 * s]));
+      }
+      if (l16 == 15) {
+        float* dr = &sm.dec[w][8 * grp];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          *reinterpret_cast<f32x4*>(dr + 32 * s) = f32x4{dw[8 * s], dw[8 * s + 1], dw[8 * s + 2], dw[8 * s + 3]};
+          *reinterpret_cast<f32x4*>(dr + 32 * s + 4) =
+              f32x4{dw[8 * s + 4], dw[8 * s + 5], dw[8 * s + 6], dw[8 * s + 7]};
+        }
+      }
+      // the state before the chunk, hi / lo
+      const int c = tid >> 3, v0 = 8 * (tid & 7);
+      float x[8] = {cpre[0][0], cpre[0][1], cpre[0][2], cpre[0][3],
+                    cpre[1][0], cpre[1][1], cpre[1][2], cpre[1][3]};
+      float lo[8];
+      const u32x4 hi = pack8(x);
+      float hx[8];
+      unpack8(hi, hx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lo[e] = x[e] - hx[e];
+      *reinterpret_cast<u32x4*>(&sm.chi[c * IS + v0]) = hi;
+      *reinterpret_cast<u32x4*>(&sm.clo[c * IS + v0]) = pack8(lo);
+    }
+    __syncthreads();  // (1) rows, retentions, C_prev published
+
+    // per-lane column factors read from the sub-chunk retentions:
+    // dec of sub-chunk s at the lane's MFMA-output columns 16 cb + l16
+    auto dec_col = [&](int s, int cb) { return sm.dec[s][16 * cb + l16]; };
+
+    f32x4 dqa[4], dka[4], dia[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      dqa[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dka[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dia[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // ---- dq against key blocks s' = w .. 0: dA^T[j][t] = I_j . dE_t, then
+    // dq_raw[t][c] += fac[c] sum_j dA[t][j] kk[j][c]
+    float fac[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) fac[cb] = fast_rcp(dec_col(w, cb));  // diagonal: k e^{B_start - B_j}
+    f32x4 dat_diag = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int sp = w; sp >= 0; --sp) {
+      f32x4 dat = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* ir = &sm.iv[(16 * sp + l16) * IS + 8 * grp];
+      dat = mfma32(ld_bf16x8(ir), bdy[0], dat);
+      dat = mfma32(ld_bf16x8(ir + 32), bdy[1], dat);
+      if (sp == w) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * grp + r >= l16) dat[r] = 0.f;
+        dat_diag = dat;
+      }
+      if (sp < w || safe) {
+        const s16x4 a = pack_x4(dat);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const uint2 kv =
+              lds_read_tr16(&sm.kk[(16 * sp + 4 * grp + (l16 >> 2)) * IS + 16 * cb + 4 * (l16 & 3)]);
+          const f32x4 t = mfma16(a, __builtin_bit_cast(s16x4, kv), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dqa[cb][r] = fmaf(t[r], fac[cb], dqa[cb][r]);
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) fac[cb] = sp == w ? 1.f : fac[cb] * dec_col(sp, cb);
+    }
+    // fac = e^{B_start(w) - B_0}: the inter-chunk factor of dq
+    float before[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) before[cb] = w == 0 ? 1.f : fac[cb];
+
+    // ---- dk, dI against query blocks w' = w .. 7
+    float ch16[16], fac4[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ch16[i] = fast_rcp(dw[i]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) fac4[cb] = fast_rcp(dec_col(w, cb));
+    f32x4 da_diag = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int wq = w; wq < NW; ++wq) {
+      const uint16_t* qr = &sm.qq[(16 * wq + l16) * IS + 8 * grp];
+      const uint16_t* yr = &sm.dy[(16 * wq + l16) * IS + 8 * grp];
+      // A[t][j] (rows t of block wq, columns j of this wave)
+      float kx[16];
+      {
+        const int o = (16 * w + l16) * IS + 8 * grp;
+        float u[16];
+        unpack8(*reinterpret_cast<const u32x4*>(&sm.kk[o]), *reinterpret_cast<float(*)[8]>(&u[0]));
+        unpack8(*reinterpret_cast<const u32x4*>(&sm.kk[o + 32]), *reinterpret_cast<float(*)[8]>(&u[8]));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kx[i] = u[i] * ch16[i];
+      }
+      f32x4 at = {0.f, 0.f, 0.f, 0.f};
+      at = mfma32(ld_bf16x8(qr), pack_x8(&kx[0]), at);
+      at = mfma32(ld_bf16x8(qr + 32), pack_x8(&kx[8]), at);
+      // dA[t][j] = dE_t . I_j
+      f32x4 da = {0.f, 0.f, 0.f, 0.f};
+      da = mfma32(ld_bf16x8(yr), biv[0], da);
+      da = mfma32(ld_bf16x8(yr + 32), biv[1], da);
+      if (wq == w) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * grp + r <= l16) {
+            at[r] = 0.f;
+            da[r] = 0.f;
+          }
+        da_diag = da;
+      }
+      if (wq > w || safe) {
+        const s16x4 aa = pack_x4(da);   // dA^T[j = l16][t = 4 grp + r]
+        const s16x4 ab = pack_x4(at);   // A^T[j = l16][t = 4 grp + r]
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const int o = (16 * wq + 4 * grp + (l16 >> 2)) * IS + 16 * cb + 4 * (l16 & 3);
+          const f32x4 t = mfma16(aa, __builtin_bit_cast(s16x4, lds_read_tr16(&sm.qq[o])),
+                                 f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dka[cb][r] = fmaf(t[r], fac4[cb], dka[cb][r]);
+          dia[cb] = mfma16(ab, __builtin_bit_cast(s16x4, lds_read_tr16(&sm.dy[o])), dia[cb]);
+        }
+      }
+      // chain(wq + 1, w) = 1 after the diagonal, then times e^{L_wq}
+      const float* dr = &sm.dec[wq][8 * grp];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const f32x4 u0 = *reinterpret_cast<const f32x4*>(dr + 32 * s);
+        const f32x4 u1 = *reinterpret_cast<const f32x4*>(dr + 32 * s + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ch16[8 * s + e] = wq == w ? 1.f : ch16[8 * s + e] * u0[e];
+          ch16[8 * s + 4 + e] = wq == w ? 1.f : ch16[8 * s + 4 + e] * u1[e];
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) fac4[cb] = wq == w ? 1.f : fac4[cb] * dec_col(wq, cb);
+    }
+    // ch16 / fac4 = e^{B_L - B_end(w)}: the inter-chunk factors of dk and dI
+    float after[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) after[cb] = w == NW - 1 ? 1.f : fac4[cb];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ch16[i] = w == NW - 1 ? 1.f : ch16[i];
+
+    // ---- inter-chunk terms
+    {
+      float kt[16];
+      {
+        const int o = (16 * w + l16) * IS + 8 * grp;
+        float u[16];
+        unpack8(*reinterpret_cast<const u32x4*>(&sm.kk[o]), *reinterpret_cast<float(*)[8]>(&u[0]));
+        unpack8(*reinterpret_cast<const u32x4*>(&sm.kk[o + 32]), *reinterpret_cast<float(*)[8]>(&u[8]));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kt[i] = u[i] * ch16[i];  // k e^{B_L - B_j}
+      }
+      const bf16x8 kt0 = pack_x8(&kt[0]), kt1 = pack_x8(&kt[8]);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int ro = (16 * cb + l16) * IS + 8 * grp;
+        f32x4 tq = {0.f, 0.f, 0.f, 0.f}, tk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          tq = mfma32(bdy[ks], ld_bf16x8(&sm.chi[ro + 32 * ks]), tq);  // (dE C_prev^T)[t][c]
+          tq = mfma32(bdy[ks], ld_bf16x8(&sm.clo[ro + 32 * ks]), tq);
+          tk = mfma32(biv[ks], ld_bf16x8(&sm.dhi[ro + 32 * ks]), tk);  // (I dC^T)[j][c]
+          tk = mfma32(biv[ks], ld_bf16x8(&sm.dlo[ro + 32 * ks]), tk);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dqa[cb][r] = fmaf(tq[r], before[cb], dqa[cb][r]);
+          dka[cb][r] = fmaf(tk[r], after[cb], dka[cb][r]);
+        }
+        // dI_j += (k e^{B_L - B_j})_j^T dC  (K = c)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int o = (32 * ks + 8 * grp + (l16 >> 2)) * IS + 16 * cb + 4 * (l16 & 3);
+          const bf16x8 dh = cat(lds_read_tr16(&sm.dhi[o]), lds_read_tr16(&sm.dhi[o + 4 * IS]));
+          const bf16x8 dl = cat(lds_read_tr16(&sm.dlo[o]), lds_read_tr16(&sm.dlo[o + 4 * IS]));
+          dia[cb] = mfma32(ks ? kt1 : kt0, dh, dia[cb]);
+          dia[cb] = mfma32(ks ? kt1 : kt0, dl, dia[cb]);
+        }
+      }
+    }
+    __syncthreads();  // (2) every wave is done reading C_prev and dC
+
+    // ---- dC_prev = e^{B_L - B_0} dC + sum_t (q_t e^{B_t - B_0}) dE_t^T
+    {
+      f32x4 tot4 = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+      for (int s = 0; s < NW; ++s) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.dec[s][16 * rb + 4 * grp]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot4[r] *= u[r];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dcs[i][r] *= tot4[r];
+      f32x4 pb = {1.f, 1.f, 1.f, 1.f};  // e^{B_start(s) - B_0} at rows 16 rb + 4 grp + r
+#pragma unroll
+      for (int s = 0; s < NW; ++s) {
+        const int o = (16 * s + 4 * grp + (l16 >> 2)) * IS + 4 * (l16 & 3);
+        // A operand q^T[c = 16 rb + l16][t = 16 s + 4 grp + r], B operand dE[t][v]
+        const s16x4 a = __builtin_bit_cast(s16x4, lds_read_tr16(&sm.qq[o + 16 * rb]));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const f32x4 t = mfma16(
+              a, __builtin_bit_cast(s16x4, lds_read_tr16(&sm.dy[o + 16 * (cb0 + i)])),
+              f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dcs[i][r] = fmaf(t[r], pb[r], dcs[i][r]);
+        }
+        const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.dec[s][16 * rb + 4 * grp]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pb[r] *= u[r];
+      }
+    }
+    put_dstate();
+
+    float b2[16], lw[16];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(&st[l16 * KS + 32 * s + 8 * grp + 4 * h]);
+        const f32x4 z = *reinterpret_cast<const f32x4*>(&st[15 * KS + 32 * s + 8 * grp + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          b2[8 * s + 4 * h + e] = u[e];
+          lw[8 * s + 4 * h + e] = z[e];
+        }
+      }
+    // ---- exact diagonal block for a sub-chunk with a near-total reset
+    float dq_ex[16], dk_ex[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dq_ex[i] = 0.f;
+      dk_ex[i] = 0.f;
+    }
+    if (!safe) {  // the tiles are still valid: barrier (3) is ahead
+      f32x4 aexact = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+      for (int jj = 0; jj < 16; ++jj) {
+        const int src = (lane & 48) | jj;
+        // dq_t += dA[t][jj] k_jj e^{B_t - B_jj} (t = l16 > jj)
+        float dsel = dat_diag[0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r)
+          if ((jj & 3) == r) dsel = dat_diag[r];
+        const float dAq = __shfl(dsel, l16 + 16 * (jj >> 2));
+        // dk_j += dA[jj][j] q_jj e^{B_jj - B_j} (j = l16 < jj)
+        float esel = da_diag[0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r)
+          if ((jj & 3) == r) esel = da_diag[r];
+        const float dAk = __shfl(esel, l16 + 16 * (jj >> 2));
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float kj = __shfl(rl.k[i], src), qj = __shfl(rl.q[i], src);
+          const float bj = __shfl(b2[i], src);
+          const float eq = fast_exp2(fminf(b2[i] - bj, 0.f));  // t = l16 after jj
+          const float ek = fast_exp2(fminf(bj - b2[i], 0.f));  // jj after j = l16
+          dq_ex[i] = fmaf(jj < l16 ? dAq * kj : 0.f, eq, dq_ex[i]);
+          dk_ex[i] = fmaf(jj > l16 ? dAk * qj : 0.f, ek, dk_ex[i]);
+          part = fmaf(qj * rl.k[i], ek, part);  // A[jj][j = l16]
+        }
+        part = sum_groups(part);
+        if ((jj >> 2) == grp) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if ((jj & 3) == r) aexact[r] = jj > l16 ? part : 0.f;
+        }
+      }
+      const s16x4 ab = pack_x4(aexact);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int o = (16 * w + 4 * grp + (l16 >> 2)) * IS + 16 * cb + 4 * (l16 & 3);
+        dia[cb] = mfma16(ab, __builtin_bit_cast(s16x4, lds_read_tr16(&sm.dy[o])), dia[cb]);
+      }
+    }
+
+    // ---- this wave's rows: MFMA-output layout -> row layout (wave-private
+    // staging; a wave's LDS accesses complete in order)
+    auto to_rows = [&](const f32x4 (&acc)[4], float (&out)[16]) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[(4 * grp + r) * KS + 16 * cb + l16] = acc[cb][r];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 u = *reinterpret_cast<const f32x4*>(&st[l16 * KS + 32 * s + 8 * grp + 4 * h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[8 * s + 4 * h + e] = u[e];
+        }
+    };
+    float dq[16], dk[16], di[16];
+    to_rows(dqa, dq);
+    to_rows(dka, dk);
+    to_rows(dia, di);
+    // the next chunk's rows and state (they land during the rest)
+    if (n > 0) prefetch(n - 1);
+    const bool last = trow == T - 1;
+    float dB[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dq[i] = fmaf(fast_exp2(b2[i]), dq[i], dq_ex[i]);
+      dk[i] = fmaf(fast_exp2(lw[i] - b2[i]), dk[i], dk_ex[i]);
+      const int c = 32 * (i >> 3) + 8 * grp + (i & 7);
+      dB[i] = fmaf(rl.q[i], dq[i], -rl.k[i] * dk[i]) + (last ? sm.fin[c] : 0.f);
+    }
+    // dI = dY + the contractions
+    {
+      const int o = (16 * w + l16) * IS + 8 * grp;
+      float yv[16];
+      unpack8(*reinterpret_cast<const u32x4*>(&sm.dy[o]), *reinterpret_cast<float(*)[8]>(&yv[0]));
+      unpack8(*reinterpret_cast<const u32x4*>(&sm.dy[o + 32]), *reinterpret_cast<float(*)[8]>(&yv[8]));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) di[i] += yv[i];
+    }
+    // chain rule through S, the normalisation and RoPE. The coordinates are
+    // recovered from q = S x1 / ||x1||, k = S x2 / ||x2|| (S > 0); a zero row
+    // has q = 0 and x = 0.
+    const float S = rl.S;
+    const float rS = fast_rcp(S);
+    const float u1 = rl.inv1 > 0.f ? fast_rcp(S * rl.inv1) : 0.f;  // x1 = u1 q
+    const float u2 = rl.inv2 > 0.f ? fast_rcp(S * rl.inv2) : 0.f;
+    float dot1 = 0.f, dot2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dot1 = fmaf(rl.q[i] * rS, dq[i], dot1);  // p^_1 . dq
+      dot2 = fmaf(rl.k[i] * rS, dk[i], dot2);
+    }
+    dot1 = sum_groups(dot1);
+    dot2 = sum_groups(dot2);
+    const float da = (dot1 + dot2) * S * (1.f - S) * slope;
+    const float f1 = S * rl.inv1, f2 = S * rl.inv2;
+    float dx1[16], dx2[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dx1[i] = fmaf(f1, fmaf(-rl.q[i] * rS, dot1, dq[i]), da * u2 * rl.k[i]);
+      dx2[i] = fmaf(f2, fmaf(-rl.k[i] * rS, dot2, dk[i]), da * u1 * rl.q[i]);
+    }
+    if constexpr (ROPE) {  // transpose of the rotate-half map
+      const size_t tr = static_cast<size_t>(ok ? trow : T - 1) * (D / 2) + 8 * grp;
+      f32x4 tcs[2], tsn[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        tcs[h] = *reinterpret_cast<const f32x4*>(rc + tr + 4 * h);
+        tsn[h] = *reinterpret_cast<const f32x4*>(rs + tr + 4 * h);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float c = tcs[e >> 2][e & 3], s_ = tsn[e >> 2][e & 3];
+        float a = dx1[e], b = dx1[8 + e];
+        dx1[e] = fmaf(a, c, b * s_);
+        dx1[8 + e] = fmaf(-a, s_, b * c);
+        a = dx2[e];
+        b = dx2[8 + e];
+        dx2[e] = fmaf(a, c, b * s_);
+        dx2[8 + e] = fmaf(-a, s_, b * c);
+      }
+    }
+    float sfx[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sfx[i] = row_suffix(dB[i]);
+    if (l16 == 0) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        *reinterpret_cast<f32x4*>(&sm.tot[w][32 * s + 8 * grp]) =
+            f32x4{sfx[8 * s], sfx[8 * s + 1], sfx[8 * s + 2], sfx[8 * s + 3]};
+        *reinterpret_cast<f32x4*>(&sm.tot[w][32 * s + 8 * grp + 4]) =
+            f32x4{sfx[8 * s + 4], sfx[8 * s + 5], sfx[8 * s + 6], sfx[8 * s + 7]};
+      }
+    }
+    if (ok) {
+      const size_t row = base + static_cast<size_t>(trow) * D + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        *reinterpret_cast<u32x4*>(dp1 + row + 32 * s) = pack8(*reinterpret_cast<float(*)[8]>(&dx1[8 * s]));
+        *reinterpret_cast<u32x4*>(dp2 + row + 32 * s) = pack8(*reinterpret_cast<float(*)[8]>(&dx2[8 * s]));
+        *reinterpret_cast<u32x4*>(dI + row + 32 * s) = pack8(*reinterpret_cast<float(*)[8]>(&di[8 * s]));
+      }
+    }
+    __syncthreads();  // (3) sub-chunk sums of dB published; tiles free for the next chunk
+
+    // dg_t = sum over t' >= t of dB
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 32 * (i >> 3) + 8 * grp + (i & 7);
+      float later = 0.f, all = 0.f;
+#pragma unroll
+      for (int s = 0; s < NW; ++s) {
+        const float v = sm.tot[s][c];
+        later += s > w ? v : 0.f;
+        all += v;
+      }
+      const float cin = sm.carry[n & 1][c];
+      sfx[i] += later + cin;
+      if (w == 0 && l16 == 0) sm.carry[(n & 1) ^ 1][c] = cin + all;
+    }
+    if (ok) {
+      float* gr = dg + base + static_cast<size_t>(trow) * D + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        *reinterpret_cast<f32x4*>(gr + 32 * s) = f32x4{sfx[8 * s], sfx[8 * s + 1], sfx[8 * s + 2], sfx[8 * s + 3]};
+        *reinterpret_cast<f32x4*>(gr + 32 * s + 4) =
+            f32x4{sfx[8 * s + 4], sfx[8 * s + 5], sfx[8 * s + 6], sfx[8 * s + 7]};
+      }
+    }
+  }
+  if (dc0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dc0[sbase + (16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] = dcs[i][r];
+  }
+}
+
+}  // namespace linrel
+
+hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint16_t* p2,
+                             const uint16_t* iv, const float* g, const float* rope_cos,
+                             const float* rope_sin, const float* state_in, const uint16_t* dy,
+                             const float* dstate_out, uint16_t* dp1, uint16_t* dp2, uint16_t* dI,
+                             float* dg, float* dstate_in, float* ws, float scale, float tau,
+                             hipStream_t stream) {
+  using namespace linrel;
+  const int nch = (T + CH - 1) / CH;
+  float* states = ws;
+  float* cT = ws + static_cast<size_t>(B) * H * nch * D * D;
+  // the state before every chunk (and the final state for dC_T's term)
+  hipError_t e = launch_linear_fwd(B, H, T, p1, p2, iv, g, rope_cos, rope_sin, state_in, nullptr,
+                                   dstate_out ? cT : nullptr, states, scale, tau, stream);
+  if (e != hipSuccess) return e;
+  const float sl2 = scale * kLog2e / tau, slope = scale / tau;
+  const dim3 grid(static_cast<unsigned>(B) * H);
+  if (rope_cos)
+    hipLaunchKernelGGL(linear_bwd_kernel<true>, grid, dim3(NT), 0, stream, p1, p2, iv, g, rope_cos,
+                       rope_sin, dy, states, cT, dstate_out, dp1, dp2, dI, dg, dstate_in, T, sl2,
+                       slope);
+  else
+    hipLaunchKernelGGL(linear_bwd_kernel<false>, grid, dim3(NT), 0, stream, p1, p2, iv, g, nullptr,
+                       nullptr, dy, states, cT, dstate_out, dp1, dp2, dI, dg, dstate_in, T, sl2,
+                       slope);
+  return hipGetLastError();
+}
+
+size_t linear_bwd_workspace_bytes(int B, int H, int T) {
+  using namespace linrel;
+  const size_t nch = (T + CH - 1) / CH;
+  return (static_cast<size_t>(B) * H * (nch + 1) * D * D) * sizeof(float);
+}
+
+}  // namespace rel

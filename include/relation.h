@@ -300,6 +300,34 @@ relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, i
                                     float scale, float tau_s, void* stream);
 
 /*
+ * relation_linear_bwd — gradients of relation_linear_fwd with respect to p1,
+ * p2, I, g and state_in, given dy and (optionally) the gradient of the final
+ * state. Recomputes the state before every 128-token chunk into the
+ * workspace, then walks the chunks from the last to the first.
+ *
+ *   p1, p2, I, g, rope_cos/rope_sin, state_in : as relation_linear_fwd
+ *   dy               : in  [B, H, T, D] bf16, gradient of y
+ *   dstate_out       : in  DEVICE fp32 [B, H, D, D] gradient of state_out,
+ *                      or NULL for zero
+ *   dp1, dp2, dI     : out [B, H, T, D] bf16
+ *   dg               : out [B, H, T, D] fp32, gradient of the log retention
+ *   dstate_in        : out DEVICE fp32 [B, H, D, D] gradient of state_in, or
+ *                      NULL
+ *   workspace        : relation_linear_bwd_workspace_bytes() bytes, 256-byte
+ *                      aligned (B * H * (ceil(T / 128) + 1) * D * D floats)
+ */
+size_t relation_linear_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D);
+relation_status relation_linear_bwd(relation_dtype dtype, int B, int H, int T, int D,
+                                    const void* p1, const void* p2, const void* I,
+                                    const float* g, const float* rope_cos,
+                                    const float* rope_sin, const float* state_in,
+                                    const void* dy, const float* dstate_out,
+                                    void* dp1, void* dp2, void* dI, float* dg,
+                                    float* dstate_in, void* workspace,
+                                    size_t workspace_bytes, float scale, float tau_s,
+                                    void* stream);
+
+/*
  * relation_linear_step — one decode step of Linear Relation (the recurrent
  * step of Sec. 5.2) for one new token per sequence: the O(D^2) state is the
  * whole decode state (Table 1).

@@ -195,6 +195,26 @@ def test_linear_validation(lib):
     assert lfwd(rc=P_MIS, rs=P) == REL_ERR_ALIGN
     assert lfwd(cout=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
 
+    need = lib.relation_linear_bwd_workspace_bytes(BF16, 2, 3, 300, 64)
+    assert need == 2 * 3 * (3 + 1) * 64 * 64 * 4  # the state per 128-token chunk + the final one
+    assert lib.relation_linear_bwd_workspace_bytes(F32, 2, 3, 300, 64) == 0
+    assert lib.relation_linear_bwd_workspace_bytes(BF16, 2, 3, 300, 48) == 0
+
+    def lbwd(dtype=BF16, D=64, dy=P, dg=P, ws=P, wsb=need, dsin=NUL, tau=2.0):
+        return lib.relation_linear_bwd(dtype, 2, 3, 300, D, P, P, P, P, NUL, NUL, NUL, dy, NUL,
+                                       P, P, P, dg, dsin, ws, wsb, 0.125, tau, None)
+
+    assert lbwd(dy=NUL) == REL_ERR_NULL
+    assert lbwd(dg=NUL) == REL_ERR_NULL
+    assert lbwd(dtype=F32) == REL_ERR_UNSUPPORTED
+    assert lbwd(D=80) == REL_ERR_UNSUPPORTED
+    assert lbwd(tau=0.0) == REL_ERR_PARAM
+    assert lbwd(ws=NUL) == REL_ERR_WORKSPACE
+    assert lbwd(wsb=need - 1) == REL_ERR_WORKSPACE
+    assert lbwd(ws=ctypes.c_void_p(0x7F0000000010)) == REL_ERR_ALIGN
+    assert lbwd(dg=P_MIS) == REL_ERR_ALIGN
+    assert lbwd(dsin=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+
     def lstep(dtype=BF16, B=1, H=1, D=64, st=P, y=P, tau=2.0):
         return lib.relation_linear_step(dtype, B, H, D, P, P, P, P, NUL, NUL, st, y, 0.125, tau,
                                         None)

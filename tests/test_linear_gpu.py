@@ -160,3 +160,80 @@ def test_linear_fwd_30m_layer_shape_sampled_heads():
         r = oracle_fwd(sub, rope)
         check(f"y[{b},{h}]", f64(y[b:b + 1, h:h + 1]), r["Y"])
         check_state(f"state[{b},{h}]", f64(c[b:b + 1, h:h + 1]), r["C"])
+
+
+# ---------------------------------------------------------------- backward
+def run_bwd(d, rope=None, C0=None, dCT=None):
+    cs, sn = rope if rope is not None else (None, None)
+    out = rel.relation_linear_bwd(
+        *(d[n].to(DEV) for n in ("p1", "p2", "I", "g", "dy")),
+        rope_cos=None if cs is None else cs.to(DEV), rope_sin=None if sn is None else sn.to(DEV),
+        state_in=None if C0 is None else C0.to(DEV), dstate_out=None if dCT is None else dCT.to(DEV),
+        want_dstate_in=True, scale=SCALE, tau_s=TAU)
+    torch.cuda.synchronize()
+    return [t.cpu() for t in out]
+
+
+def oracle_bwd(d, rope=None, C0=None, dCT=None):
+    cs, sn = (None, None) if rope is None else (f64(rope[0]), f64(rope[1]))
+    return oracle.linear_relation_backward(
+        f64(d["p1"]), f64(d["p2"]), f64(d["I"]), f64(d["g"]), f64(d["dy"]), SCALE, TAU, cs, sn,
+        C0=None if C0 is None else f64(C0), dC_T=None if dCT is None else f64(dCT))
+
+
+def check_dg(got, ref):
+    """dg_t = sum_{t' >= t} dB_t': each dB carries the bf16 operands' relative
+    error (about 2^-8 of its terms), and those add up over the suffix like a
+    random walk, so element t must be within 2e-2 + 2^-7 sqrt(sum_{t'>=t}
+    dB_t'^2) (dB from the oracle's dg), and on average within a quarter of
+    that bound."""
+    dB = ref - np.concatenate([ref[..., 1:, :], np.zeros_like(ref[..., :1, :])], axis=-2)
+    walk = np.sqrt(np.flip(np.cumsum(np.flip(dB ** 2, axis=-2), axis=-2), axis=-2))
+    err = np.abs(got - ref)
+    bound = 2e-2 + 2.0 ** -7 * walk
+    worst, mean = float((err / bound).max()), float((err / bound).mean())
+    print(f"  dg: max-abs {float(err.max()):.3e} mean-abs {float(err.mean()):.3e} "
+          f"err/bound worst {worst:.3f} mean {mean:.3f}")
+    assert worst <= 1.0
+    assert mean <= 0.25
+
+
+def check_grads(got, ref):
+    for name, a, b in zip(("dp1", "dp2", "dI"), got[:3], ref[:3]):
+        check(name, f64(a), b)
+    check_dg(f64(got[3]), ref[3])
+    check_state("dstate_in", f64(got[4]), ref[4])
+
+
+@pytest.mark.parametrize("use_rope", [False, True])
+@pytest.mark.parametrize("T", [1, 17, 128, 129, 300])
+def test_linear_bwd_vs_oracle(T, use_rope):
+    d = make_linear_inputs(2, 2, T, 64, seed=2500 + T, with_dy=True)
+    rope = tables(T) if use_rope else None
+    got = run_bwd(d, rope)
+    ref = oracle_bwd(d, rope)
+    check_grads(got, ref)
+
+
+def test_linear_bwd_with_states_and_extreme_retention():
+    B, H, T = 2, 2, 300
+    d = make_linear_inputs(B, H, T, 64, seed=2600, with_dy=True, resets=True, keep=True)
+    rng = np.random.default_rng(3)
+    C0 = torch.from_numpy(rng.standard_normal((B, H, 64, 64)).astype(np.float32))
+    dCT = torch.from_numpy(rng.standard_normal((B, H, 64, 64)).astype(np.float32))
+    got = run_bwd(d, tables(T), C0, dCT)
+    ref = oracle_bwd(d, tables(T), C0, dCT)
+    check_grads(got, ref)
+
+
+def test_linear_bwd_30m_layer_shape_sampled_heads():
+    """The 30M-class layer (B=32, H=8, T=1024, d_h=64) in the benchmark's
+    launch shape, with RoPE; two heads' gradients from the oracle."""
+    B, H, T = 32, 8, 1024
+    d = make_linear_inputs(B, H, T, 64, seed=42, with_dy=True)
+    rope = tables(T)
+    got = run_bwd(d, rope)
+    for b, h in ((0, 0), (29, 6)):
+        sub = {k: v[b:b + 1, h:h + 1] for k, v in d.items()}
+        ref = oracle_bwd(sub, rope)
+        check_grads([t[b:b + 1, h:h + 1] for t in got], ref)
