@@ -330,9 +330,27 @@ def bench_linear(rel, torch, dev, reps, B=32, H=8, T=1024, D=64, seed=42):
             tf.stop(s0)
     fm = tf.mean_ms()
     nbytes = 12 * D * B * H * T
-    return {"workload": f"linear relation fwd, RoPE, B={B} H={H} T={T} D={D}", "fwd_ms": fm,
-            "tokens_per_s": B * T / (fm * 1e-3), "fwd_GBps": nbytes / (fm * 1e-3) / 1e9,
-            "frac_hbm": nbytes / (fm * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    # backward: reads p1, p2, I, dY (bf16) and g, writes dp1, dp2, dI (bf16)
+    # and dg: 22 D bytes per token and head (the state pass is overhead)
+    dy = torch.randn_like(I)
+    lib = rel.load_library()
+    ws = torch.empty((lib.relation_linear_bwd_workspace_bytes(1, B, H, T, D),), device=dev,
+                     dtype=torch.uint8)
+    tb = EventTimer(torch, stream)
+    for i in range(reps // 2 + 20):
+        s0 = tb.start() if i >= 20 else None
+        rel.relation_linear_bwd(p1, p2, I, g, dy, cs, sn, scale=1 / math.sqrt(D), workspace=ws)
+        if i >= 20:
+            tb.stop(s0)
+    bm = tb.mean_ms()
+    bbytes = 22 * D * B * H * T
+    return {"workload": f"linear relation fwd + bwd, RoPE, B={B} H={H} T={T} D={D}",
+            "fwd_ms": fm, "tokens_per_s": B * T / (fm * 1e-3),
+            "fwd_GBps": nbytes / (fm * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (fm * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "bwd_ms": bm, "bwd_GBps": bbytes / (bm * 1e-3) / 1e9,
+            "bwd_frac_hbm": bbytes / (bm * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "fwdbwd_tokens_per_s": B * T / ((fm + bm) * 1e-3)}
 
 
 def bench_linear_step(rel, torch, dev, reps=200, B=32, H=12, D=64, seed=42):

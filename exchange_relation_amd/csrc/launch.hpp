@@ -77,16 +77,24 @@ hipError_t launch_mhr_post(int dtype, int B, int H, int T, int D, const float* d
 // Linear Relation (linear.hip), bf16, D = 64. g = log retention (fp32, same
 // shape as p1). rope tables [T, D/2] or NULL; state_in / state_out [B, H, D, D]
 // fp32 or NULL; states (or NULL): the state before every chunk of
-// linear_chunk_rows() tokens, [B, H, nchunks, D, D] fp32.
+// linear_chunk_rows() tokens, then the final state, [B, H, nchunks + 1, D, D]
+// fp32.
 int linear_chunk_rows();
 hipError_t launch_linear_fwd(int B, int H, int T, const uint16_t* p1, const uint16_t* p2,
                              const uint16_t* iv, const float* g, const float* rope_cos,
                              const float* rope_sin, const float* state_in, uint16_t* y,
                              float* state_out, float* states, float scale, float tau,
                              hipStream_t stream);
+// The forward's state pass: the state before every chunk, then the final
+// state, into states [B, H, nchunks + 1, D, D] fp32 (no outputs).
+hipError_t launch_linear_fwd_states(int B, int H, int T, const uint16_t* p1, const uint16_t* p2,
+                                    const uint16_t* iv, const float* g, const float* rope_cos,
+                                    const float* rope_sin, const float* state_in, float* states,
+                                    float scale, float tau, hipStream_t stream);
 // Backward: gradients of relation_linear_fwd. ws: linear_bwd_workspace_bytes()
-// (the state before every chunk, then the final state); dstate_out, the
-// gradient of the final state, or NULL; dstate_in (out) or NULL.
+// (the states of the state pass, then the gradient of the state after every
+// chunk); dstate_out, the gradient of the final state, or NULL; dstate_in
+// (out) or NULL.
 size_t linear_bwd_workspace_bytes(int B, int H, int T);
 hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint16_t* p2,
                              const uint16_t* iv, const float* g, const float* rope_cos,

@@ -46,8 +46,9 @@ struct Smem {
 };
 
 // blockIdx.x = head (b * H + h). states (optional): the state before every
-// chunk, [BH][nch][D][D] fp32, for the backward. YOUT false: the state pass
-// alone (no Y; the backward's first pass).
+// chunk and then the final state, [BH][nch + 1][D][D] fp32, for the
+// backward. YOUT false: the state pass alone (no Y; the backward's first
+// pass).
 template <bool ROPE, bool YOUT>
 __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
     const uint16_t* __restrict__ p1, const uint16_t* __restrict__ p2,
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
 
     // ---------------- state update: C = e^{B_L} C + K~^T I (rows 16 rb.., 2 column blocks)
     if (states) {
-      float* st = states + (static_cast<size_t>(head) * nch + n) * D * D;
+      float* st = states + (static_cast<size_t>(head) * (nch + 1) + n) * D * D;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -328,6 +329,13 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
       for (int r = 0; r < 4; ++r)
         cT[static_cast<size_t>(head) * D * D + (16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] =
             cst[i][r];
+  }
+  if (states) {  // the final state after the per-chunk ones
+    float* st = states + (static_cast<size_t>(head) * (nch + 1) + nch) * D * D;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[(16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] = cst[i][r];
   }
 }
 
@@ -391,18 +399,28 @@ hipError_t launch_linear_fwd(int B, int H, int T, const uint16_t* p1, const uint
   using namespace linrel;
   const float sl2 = scale * kLog2e / tau;
   const dim3 grid(static_cast<unsigned>(B) * H);
-  if (rope_cos && y)
+  if (rope_cos)
     hipLaunchKernelGGL((linear_fwd_kernel<true, true>), grid, dim3(NT), 0, stream, p1, p2, iv, g,
                        rope_cos, rope_sin, state_in, y, state_out, states, T, sl2);
-  else if (y)
+  else
     hipLaunchKernelGGL((linear_fwd_kernel<false, true>), grid, dim3(NT), 0, stream, p1, p2, iv, g,
                        nullptr, nullptr, state_in, y, state_out, states, T, sl2);
-  else if (rope_cos)
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_fwd_states(int B, int H, int T, const uint16_t* p1, const uint16_t* p2,
+                                    const uint16_t* iv, const float* g, const float* rope_cos,
+                                    const float* rope_sin, const float* state_in, float* states,
+                                    float scale, float tau, hipStream_t stream) {
+  using namespace linrel;
+  const float sl2 = scale * kLog2e / tau;
+  const dim3 grid(static_cast<unsigned>(B) * H);
+  if (rope_cos)
     hipLaunchKernelGGL((linear_fwd_kernel<true, false>), grid, dim3(NT), 0, stream, p1, p2, iv, g,
-                       rope_cos, rope_sin, state_in, y, state_out, states, T, sl2);
+                       rope_cos, rope_sin, state_in, nullptr, nullptr, states, T, sl2);
   else
     hipLaunchKernelGGL((linear_fwd_kernel<false, false>), grid, dim3(NT), 0, stream, p1, p2, iv,
-                       g, nullptr, nullptr, state_in, y, state_out, states, T, sl2);
+                       g, nullptr, nullptr, state_in, nullptr, nullptr, states, T, sl2);
   return hipGetLastError();
 }
 

@@ -9,26 +9,31 @@
 //   dI_j  = dY_j + sum_{t>j} A_tj dE_t + (k_j e^{B_L - B_j})^T dC
 //   dA_tj = dE_t . I_j,   A_tj = sum_c q_t k_j e^{B_t - B_j}
 //   dC_prev = e^{B_L - B_0} dC + sum_t (q_t e^{B_t - B_0}) dE_t^T
-//   dB_t  = q_t dq_t - k_t dk_t  (+ sum_v dC_T C_T at the last token),
-//   dg_t  = sum_{t' >= t} dB_t'
+//   dg_t  = sum_{t' >= t} (q dq - k dk)_t'  (+ the final state's term),
 // then the chain rule through S = sigmoid(s x1.x2 / tau), the normalisation
 // and RoPE. Every e^{.} factor is split at sub-chunk boundaries into factors
-// <= 1 exactly as in the forward (linear.hip); the diagonal 16 x 16 blocks use
-// the ratio form unless a sub-chunk's retention span is beyond 2^60, where an
+// <= 1 as in the forward (linear.hip); a diagonal 16 x 16 block uses the
+// ratio form unless the sub-chunk's retention span is beyond 2^60, where an
 // exact per-pair path runs instead.
 //
-// One workgroup (8 waves) per head walks the chunks from the last to the
-// first; the state before every chunk comes from the forward's state pass.
-// Wave w owns the 16 rows of sub-chunk w and does, for them, dq against key
-// blocks s' <= w and dk / dI against query blocks w' >= w: nine block pairs on
-// every wave.
+// Three passes: the forward's state pass stores the state before every chunk
+// (and the final state); linear_dstate_kernel walks the chunks backwards and
+// stores dC, the gradient of the state after every chunk; linear_grad_kernel
+// then handles every chunk independently (one workgroup per chunk and head).
+// The reverse sum of dg needs no sequential pass: the sum of (q dq - k dk)
+// over all tokens after chunk n equals sum_v dC[c][v] C[c][v] of the state
+// after chunk n (shifting the log retention of every later token by d only
+// rescales that state by e^d), so each chunk adds it to its own suffix sums.
+// In the gradient kernel wave w owns the 16 rows of sub-chunk w and does, for
+// them, dq against key blocks s' <= w and dk / dI against query blocks
+// w' >= w: nine block pairs on every wave.
 #include "launch.hpp"
 #include "linear_common.hpp"
 
 namespace rel {
 namespace linrel {
 
-struct SmemB {
+struct SmemG {
   uint16_t iv[CH * IS];   // I rows
   uint16_t dy[CH * IS];   // dY rows
   uint16_t qq[CH * IS];   // q e^{B_t - B_start(sub)}
@@ -40,33 +45,46 @@ struct SmemB {
   float stage[NW][16 * KS];  // per-wave layout change (MFMA output -> rows)
   float dec[NW][D];          // e^{L_s[c]}
   float tot[NW][D];          // sum of dB over each sub-chunk
-  float fin[D];              // sum_v dC_T C_T: dB of the last token
-  float carry[2][D];         // sum of dB over the chunks after the current one,
-                             // by chunk parity
+  float carry[D];            // sum of dB over every token after the chunk
+};
+
+struct SmemR {
+  uint16_t dy[CH * IS];
+  uint16_t qq[CH * IS];
+  float dec[NW][D];
 };
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// 8 consecutive fp32 -> bf16 hi / lo into two LDS rows
+__device__ __forceinline__ void put_hilo(uint16_t* hi_row, uint16_t* lo_row, f32x4 a, f32x4 b) {
+  float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  const u32x4 hi = pack8(x);
+  float hx[8], lo[8];
+  unpack8(hi, hx);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) lo[e] = x[e] - hx[e];
+  *reinterpret_cast<u32x4*>(hi_row) = hi;
+  *reinterpret_cast<u32x4*>(lo_row) = pack8(lo);
+}
+
+// dC_T -> dC after every chunk, [BH][nch][D][D]; dc0: the gradient of the
+// initial state (or NULL). One workgroup per head, chunks from the last.
 template <bool ROPE>
-__global__ __launch_bounds__(NT, 1) void linear_bwd_kernel(
+__global__ __launch_bounds__(NT, 1) void linear_dstate_kernel(
     const uint16_t* __restrict__ p1, const uint16_t* __restrict__ p2,
-    const uint16_t* __restrict__ iv, const float* __restrict__ g, const float* __restrict__ rc,
-    const float* __restrict__ rs, const uint16_t* __restrict__ dy,
-    const float* __restrict__ states, const float* __restrict__ cT, const float* __restrict__ dcT,
-    uint16_t* __restrict__ dp1, uint16_t* __restrict__ dp2, uint16_t* __restrict__ dI,
-    float* __restrict__ dg, float* __restrict__ dc0, int T, float sl2, float slope) {
-  __shared__ SmemB sm;
+    const float* __restrict__ g, const float* __restrict__ rc, const float* __restrict__ rs,
+    const uint16_t* __restrict__ dy, const float* __restrict__ dcT, float* __restrict__ dstates,
+    float* __restrict__ dc0, int T, float sl2) {
+  __shared__ SmemR sm;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int head = blockIdx.x;
   const size_t base = static_cast<size_t>(head) * T * D;
   const size_t sbase = static_cast<size_t>(head) * D * D;
   const int nch = (T + CH - 1) / CH;
-
-  // ---- gradient of the state after the current chunk: wave w holds rows
-  // 16 rb .. +15, column blocks cb0, cb0 + 1 (as the forward's state)
   const int rb = w >> 1, cb0 = 2 * (w & 1);
   f32x4 dcs[2];
 #pragma unroll
@@ -74,120 +92,185 @@ __global__ __launch_bounds__(NT, 1) void linear_bwd_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       dcs[i][r] = dcT ? dcT[sbase + (16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] : 0.f;
-  auto put_dstate = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int o = (16 * rb + 4 * grp + r) * IS + 16 * (cb0 + i) + l16;
-        const float x = dcs[i][r];
-        const uint16_t hb = f32_to_bf16_bits(x);
-        sm.dhi[o] = hb;
-        sm.dlo[o] = f32_to_bf16_bits(x - bf16_bits_to_f32(hb));
-      }
-    }
-  };
-  put_dstate();
-  // dB of the last token gains sum_v dC_T[c][v] C_T[c][v]
-  {
-    const int c = tid >> 3, part = tid & 7;
-    float f = 0.f;
-    if (dcT) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const size_t o = sbase + c * D + 8 * part + e;
-        f = fmaf(dcT[o], cT[o], f);
-      }
-    }
-    f += __shfl_xor(f, 1);
-    f += __shfl_xor(f, 2);
-    f += __shfl_xor(f, 4);
-    if (part == 0) sm.fin[c] = f;
-  }
-  if (tid < D) sm.carry[(nch - 1) & 1][tid] = 0.f;
-
-  // prefetch of one chunk: rows, dY rows and the state before it (8
-  // consecutive elements of row c = tid / 8)
   Raw raw;
   u32x4 rdy[2];
-  f32x4 cpre[2];
   auto prefetch = [&](int n) {
     const int t = n * CH + 16 * w + l16;
-    load_raw<ROPE>(raw, p1, p2, iv, g, rc, rs, base, t, T, grp);
+    load_raw<ROPE>(raw, p1, p2, p1, g, rc, rs, base, t, T, grp);
     const size_t row = base + static_cast<size_t>(t < T ? t : T - 1) * D + 8 * grp;
     rdy[0] = *reinterpret_cast<const u32x4*>(dy + row);
     rdy[1] = *reinterpret_cast<const u32x4*>(dy + row + 32);
-    const float* sp = states + (static_cast<size_t>(head) * nch + n) * D * D + 8 * tid;
-    cpre[0] = *reinterpret_cast<const f32x4*>(sp);
-    cpre[1] = *reinterpret_cast<const f32x4*>(sp + 4);
   };
   prefetch(nch - 1);
-
   for (int n = nch - 1; n >= 0; --n) {
-    const int trow = n * CH + 16 * w + l16;
-    // ---------------- row-local recompute
+    // the gradient of the state after chunk n
+    {
+      float* st = dstates + (static_cast<size_t>(head) * nch + n) * D * D;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          st[(16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] = dcs[i][r];
+    }
     RowLocal rl;
     row_local<ROPE>(raw, sl2, lane, rl);
-    const bool ok = raw.ok;
-    const bool safe = rl.safe;
-    {
-      const u32x4 z = {0, 0, 0, 0};
-      rdy[0] = ok ? rdy[0] : z;
-      rdy[1] = ok ? rdy[1] : z;
-    }
-    float qq[16], kk[16], dw[16];
+    const u32x4 z = {0, 0, 0, 0};
+    const u32x4 y0 = raw.ok ? rdy[0] : z, y1 = raw.ok ? rdy[1] : z;
+    float qq[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      qq[i] = rl.q[i] * fast_exp2(rl.b2[i]);
-      kk[i] = rl.k[i] * fast_exp2(rl.lw[i] - rl.b2[i]);
-      dw[i] = fast_exp2(rl.lw[i]);
-    }
-    // the prefix of g waits in this wave's staging area until the row
-    // updates at the end of the chunk (the registers are needed meanwhile)
-    float* st = sm.stage[w];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<f32x4*>(&st[l16 * KS + 32 * s + 8 * grp + 4 * h]) =
-            f32x4{rl.b2[8 * s + 4 * h], rl.b2[8 * s + 4 * h + 1], rl.b2[8 * s + 4 * h + 2],
-                  rl.b2[8 * s + 4 * h + 3]};
-    const bf16x8 bqq[2] = {pack_x8(&qq[0]), pack_x8(&qq[8])};
-    const bf16x8 bdy[2] = {__builtin_bit_cast(bf16x8, rdy[0]), __builtin_bit_cast(bf16x8, rdy[1])};
-    const bf16x8 biv[2] = {__builtin_bit_cast(bf16x8, raw.iv[0]), __builtin_bit_cast(bf16x8, raw.iv[1])};
-    // ---------------- publish
+    for (int i = 0; i < 16; ++i) qq[i] = rl.q[i] * fast_exp2(rl.b2[i]);
     {
       const int o = (16 * w + l16) * IS + 8 * grp;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        *reinterpret_cast<u32x4*>(&sm.iv[o + 32 * s]) = raw.iv[s];
-        *reinterpret_cast<u32x4*>(&sm.dy[o + 32 * s]) = rdy[s];
-        *reinterpret_cast<u32x4*>(&sm.qq[o + 32 * s]) = __builtin_bit_cast(u32x4, bqq[s]);
-        *reinterpret_cast<u32x4*>(&sm.kk[o + 32 * s]) = __builtin_bit_cast(u32x4, pack_x8(&kk[8 * s]));
-      }
+      *reinterpret_cast<u32x4*>(&sm.dy[o]) = y0;
+      *reinterpret_cast<u32x4*>(&sm.dy[o + 32]) = y1;
+      *reinterpret_cast<u32x4*>(&sm.qq[o]) = __builtin_bit_cast(u32x4, pack_x8(&qq[0]));
+      *reinterpret_cast<u32x4*>(&sm.qq[o + 32]) = __builtin_bit_cast(u32x4, pack_x8(&qq[8]));
       if (l16 == 15) {
         float* dr = &sm.dec[w][8 * grp];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          *reinterpret_cast<f32x4*>(dr + 32 * s) = f32x4{dw[8 * s], dw[8 * s + 1], dw[8 * s + 2], dw[8 * s + 3]};
+          *reinterpret_cast<f32x4*>(dr + 32 * s) =
+              f32x4{fast_exp2(rl.lw[8 * s]), fast_exp2(rl.lw[8 * s + 1]), fast_exp2(rl.lw[8 * s + 2]),
+                    fast_exp2(rl.lw[8 * s + 3])};
           *reinterpret_cast<f32x4*>(dr + 32 * s + 4) =
-              f32x4{dw[8 * s + 4], dw[8 * s + 5], dw[8 * s + 6], dw[8 * s + 7]};
+              f32x4{fast_exp2(rl.lw[8 * s + 4]), fast_exp2(rl.lw[8 * s + 5]),
+                    fast_exp2(rl.lw[8 * s + 6]), fast_exp2(rl.lw[8 * s + 7])};
         }
       }
-      // the state before the chunk, hi / lo
-      const int c = tid >> 3, v0 = 8 * (tid & 7);
-      float x[8] = {cpre[0][0], cpre[0][1], cpre[0][2], cpre[0][3],
-                    cpre[1][0], cpre[1][1], cpre[1][2], cpre[1][3]};
-      float lo[8];
-      const u32x4 hi = pack8(x);
-      float hx[8];
-      unpack8(hi, hx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lo[e] = x[e] - hx[e];
-      *reinterpret_cast<u32x4*>(&sm.chi[c * IS + v0]) = hi;
-      *reinterpret_cast<u32x4*>(&sm.clo[c * IS + v0]) = pack8(lo);
     }
-    __syncthreads();  // (1) rows, retentions, C_prev published
+    if (n > 0) prefetch(n - 1);
+    __syncthreads();  // (1) q, dY, retentions of the chunk published
+    // dC_prev = e^{B_L - B_0} dC + sum_t (q_t e^{B_t - B_0}) dE_t^T
+    f32x4 tot4 = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.dec[s][16 * rb + 4 * grp]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tot4[r] *= u[r];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dcs[i][r] *= tot4[r];
+    f32x4 pb = {1.f, 1.f, 1.f, 1.f};  // e^{B_start(s) - B_0} at rows 16 rb + 4 grp + r
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      const int o = (16 * s + 4 * grp + (l16 >> 2)) * IS + 4 * (l16 & 3);
+      // A operand q^T[c = 16 rb + l16][t = 16 s + 4 grp + r], B operand dE[t][v]
+      const s16x4 a = __builtin_bit_cast(s16x4, lds_read_tr16(&sm.qq[o + 16 * rb]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const f32x4 t = mfma16(
+            a, __builtin_bit_cast(s16x4, lds_read_tr16(&sm.dy[o + 16 * (cb0 + i)])),
+            f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dcs[i][r] = fmaf(t[r], pb[r], dcs[i][r]);
+      }
+      const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.dec[s][16 * rb + 4 * grp]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[r] *= u[r];
+    }
+    __syncthreads();  // (2) tiles free for the next chunk
+  }
+  if (dc0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dc0[sbase + (16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] = dcs[i][r];
+  }
+}
+
+// One workgroup per (chunk, head): blockIdx.x = head * nch + n. states:
+// [BH][nch + 1][D][D] (the state before every chunk, then the final state);
+// dstates: [BH][nch][D][D] (the gradient of the state after every chunk).
+template <bool ROPE>
+__global__ __launch_bounds__(NT, 1) void linear_grad_kernel(
+    const uint16_t* __restrict__ p1, const uint16_t* __restrict__ p2,
+    const uint16_t* __restrict__ iv, const float* __restrict__ g, const float* __restrict__ rc,
+    const float* __restrict__ rs, const uint16_t* __restrict__ dy,
+    const float* __restrict__ states, const float* __restrict__ dstates,
+    uint16_t* __restrict__ dp1, uint16_t* __restrict__ dp2, uint16_t* __restrict__ dI,
+    float* __restrict__ dg, int T, float sl2, float slope) {
+  __shared__ SmemG sm;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int nch = (T + CH - 1) / CH;
+  const int head = blockIdx.x / nch, n = blockIdx.x % nch;
+  const size_t base = static_cast<size_t>(head) * T * D;
+  const int trow = n * CH + 16 * w + l16;
+  const float* cprev = states + (static_cast<size_t>(head) * (nch + 1) + n) * D * D;
+  const float* cnext = cprev + D * D;  // the state after the chunk
+  const float* dcn = dstates + (static_cast<size_t>(head) * nch + n) * D * D;
+
+  Raw raw;
+  load_raw<ROPE>(raw, p1, p2, iv, g, rc, rs, base, trow, T, grp);
+  u32x4 rdy[2];
+  {
+    const size_t row = base + static_cast<size_t>(trow < T ? trow : T - 1) * D + 8 * grp;
+    rdy[0] = *reinterpret_cast<const u32x4*>(dy + row);
+    rdy[1] = *reinterpret_cast<const u32x4*>(dy + row + 32);
+  }
+  // the states (8 consecutive elements of row c = tid / 8) and the reverse
+  // sum of dB over the tokens after the chunk
+  {
+    const int c = tid >> 3, v0 = 8 * (tid & 7);
+    const int o = c * D + v0;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(cprev + o);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(cprev + o + 4);
+    const f32x4 d0 = *reinterpret_cast<const f32x4*>(dcn + o);
+    const f32x4 d1 = *reinterpret_cast<const f32x4*>(dcn + o + 4);
+    const f32x4 n0 = *reinterpret_cast<const f32x4*>(cnext + o);
+    const f32x4 n1 = *reinterpret_cast<const f32x4*>(cnext + o + 4);
+    put_hilo(&sm.chi[c * IS + v0], &sm.clo[c * IS + v0], a0, a1);
+    put_hilo(&sm.dhi[c * IS + v0], &sm.dlo[c * IS + v0], d0, d1);
+    float f = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f = fmaf(d0[e], n0[e], fmaf(d1[e], n1[e], f));
+    f += __shfl_xor(f, 1);
+    f += __shfl_xor(f, 2);
+    f += __shfl_xor(f, 4);
+    if ((tid & 7) == 0) sm.carry[c] = f;
+  }
+
+  RowLocal rl;
+  row_local<ROPE>(raw, sl2, lane, rl);
+  const bool ok = raw.ok;
+  const bool safe = rl.safe;
+  {
+    const u32x4 z = {0, 0, 0, 0};
+    rdy[0] = ok ? rdy[0] : z;
+    rdy[1] = ok ? rdy[1] : z;
+  }
+  float qq[16], kk[16], dw[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    qq[i] = rl.q[i] * fast_exp2(rl.b2[i]);
+    kk[i] = rl.k[i] * fast_exp2(rl.lw[i] - rl.b2[i]);
+    dw[i] = fast_exp2(rl.lw[i]);
+  }
+  const bf16x8 bdy[2] = {__builtin_bit_cast(bf16x8, rdy[0]), __builtin_bit_cast(bf16x8, rdy[1])};
+  const bf16x8 biv[2] = {__builtin_bit_cast(bf16x8, raw.iv[0]), __builtin_bit_cast(bf16x8, raw.iv[1])};
+  {
+    const int o = (16 * w + l16) * IS + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      *reinterpret_cast<u32x4*>(&sm.iv[o + 32 * s]) = raw.iv[s];
+      *reinterpret_cast<u32x4*>(&sm.dy[o + 32 * s]) = rdy[s];
+      *reinterpret_cast<u32x4*>(&sm.qq[o + 32 * s]) = __builtin_bit_cast(u32x4, pack_x8(&qq[8 * s]));
+      *reinterpret_cast<u32x4*>(&sm.kk[o + 32 * s]) = __builtin_bit_cast(u32x4, pack_x8(&kk[8 * s]));
+    }
+    if (l16 == 15) {
+      float* dr = &sm.dec[w][8 * grp];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        *reinterpret_cast<f32x4*>(dr + 32 * s) = f32x4{dw[8 * s], dw[8 * s + 1], dw[8 * s + 2], dw[8 * s + 3]};
+        *reinterpret_cast<f32x4*>(dr + 32 * s + 4) =
+            f32x4{dw[8 * s + 4], dw[8 * s + 5], dw[8 * s + 6], dw[8 * s + 7]};
+      }
+    }
+  }
+  __syncthreads();  // (1) rows, retentions and states published
 
     // per-lane column factors read from the sub-chunk retentions:
     // dec of sub-chunk s at the lane's MFMA-output columns 16 cb + l16
@@ -348,55 +431,9 @@ __global__ __launch_bounds__(NT, 1) void linear_bwd_kernel(
         }
       }
     }
-    __syncthreads();  // (2) every wave is done reading C_prev and dC
-
-    // ---- dC_prev = e^{B_L - B_0} dC + sum_t (q_t e^{B_t - B_0}) dE_t^T
-    {
-      f32x4 tot4 = {1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-      for (int s = 0; s < NW; ++s) {
-        const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.dec[s][16 * rb + 4 * grp]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tot4[r] *= u[r];
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dcs[i][r] *= tot4[r];
-      f32x4 pb = {1.f, 1.f, 1.f, 1.f};  // e^{B_start(s) - B_0} at rows 16 rb + 4 grp + r
-#pragma unroll
-      for (int s = 0; s < NW; ++s) {
-        const int o = (16 * s + 4 * grp + (l16 >> 2)) * IS + 4 * (l16 & 3);
-        // A operand q^T[c = 16 rb + l16][t = 16 s + 4 grp + r], B operand dE[t][v]
-        const s16x4 a = __builtin_bit_cast(s16x4, lds_read_tr16(&sm.qq[o + 16 * rb]));
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const f32x4 t = mfma16(
-              a, __builtin_bit_cast(s16x4, lds_read_tr16(&sm.dy[o + 16 * (cb0 + i)])),
-              f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dcs[i][r] = fmaf(t[r], pb[r], dcs[i][r]);
-        }
-        const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.dec[s][16 * rb + 4 * grp]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pb[r] *= u[r];
-      }
-    }
-    put_dstate();
-
-    float b2[16], lw[16];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x4 u = *reinterpret_cast<const f32x4*>(&st[l16 * KS + 32 * s + 8 * grp + 4 * h]);
-        const f32x4 z = *reinterpret_cast<const f32x4*>(&st[15 * KS + 32 * s + 8 * grp + 4 * h]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          b2[8 * s + 4 * h + e] = u[e];
-          lw[8 * s + 4 * h + e] = z[e];
-        }
-      }
+  float* st = sm.stage[w];
+  const float* b2 = rl.b2;
+  const float* lw = rl.lw;
     // ---- exact diagonal block for a sub-chunk with a near-total reset
     float dq_ex[16], dk_ex[16];
 #pragma unroll
@@ -404,7 +441,7 @@ __global__ __launch_bounds__(NT, 1) void linear_bwd_kernel(
       dq_ex[i] = 0.f;
       dk_ex[i] = 0.f;
     }
-    if (!safe) {  // the tiles are still valid: barrier (3) is ahead
+    if (!safe) {  // the tiles are still valid: barrier (2) is ahead
       f32x4 aexact = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
       for (int jj = 0; jj < 16; ++jj) {
@@ -467,16 +504,12 @@ __global__ __launch_bounds__(NT, 1) void linear_bwd_kernel(
     to_rows(dqa, dq);
     to_rows(dka, dk);
     to_rows(dia, di);
-    // the next chunk's rows and state (they land during the rest)
-    if (n > 0) prefetch(n - 1);
-    const bool last = trow == T - 1;
     float dB[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       dq[i] = fmaf(fast_exp2(b2[i]), dq[i], dq_ex[i]);
       dk[i] = fmaf(fast_exp2(lw[i] - b2[i]), dk[i], dk_ex[i]);
-      const int c = 32 * (i >> 3) + 8 * grp + (i & 7);
-      dB[i] = fmaf(rl.q[i], dq[i], -rl.k[i] * dk[i]) + (last ? sm.fin[c] : 0.f);
+      dB[i] = fmaf(rl.q[i], dq[i], -rl.k[i] * dk[i]);
     }
     // dI = dY + the contractions
     {
@@ -551,39 +584,26 @@ __global__ __launch_bounds__(NT, 1) void linear_bwd_kernel(
         *reinterpret_cast<u32x4*>(dI + row + 32 * s) = pack8(*reinterpret_cast<float(*)[8]>(&di[8 * s]));
       }
     }
-    __syncthreads();  // (3) sub-chunk sums of dB published; tiles free for the next chunk
+  __syncthreads();  // (2) sub-chunk sums of dB published
 
-    // dg_t = sum over t' >= t of dB
+  // dg_t = sum over t' >= t of dB: this sub-chunk's suffix, the later
+  // sub-chunks of the chunk and every token after the chunk
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = 32 * (i >> 3) + 8 * grp + (i & 7);
-      float later = 0.f, all = 0.f;
+  for (int i = 0; i < 16; ++i) {
+    const int c = 32 * (i >> 3) + 8 * grp + (i & 7);
+    float later = sm.carry[c];
 #pragma unroll
-      for (int s = 0; s < NW; ++s) {
-        const float v = sm.tot[s][c];
-        later += s > w ? v : 0.f;
-        all += v;
-      }
-      const float cin = sm.carry[n & 1][c];
-      sfx[i] += later + cin;
-      if (w == 0 && l16 == 0) sm.carry[(n & 1) ^ 1][c] = cin + all;
-    }
-    if (ok) {
-      float* gr = dg + base + static_cast<size_t>(trow) * D + 8 * grp;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        *reinterpret_cast<f32x4*>(gr + 32 * s) = f32x4{sfx[8 * s], sfx[8 * s + 1], sfx[8 * s + 2], sfx[8 * s + 3]};
-        *reinterpret_cast<f32x4*>(gr + 32 * s + 4) =
-            f32x4{sfx[8 * s + 4], sfx[8 * s + 5], sfx[8 * s + 6], sfx[8 * s + 7]};
-      }
-    }
+    for (int s = 0; s < NW; ++s) later += s > w ? sm.tot[s][c] : 0.f;
+    sfx[i] += later;
   }
-  if (dc0) {
+  if (ok) {
+    float* gr = dg + base + static_cast<size_t>(trow) * D + 8 * grp;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dc0[sbase + (16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] = dcs[i][r];
+    for (int s = 0; s < 2; ++s) {
+      *reinterpret_cast<f32x4*>(gr + 32 * s) = f32x4{sfx[8 * s], sfx[8 * s + 1], sfx[8 * s + 2], sfx[8 * s + 3]};
+      *reinterpret_cast<f32x4*>(gr + 32 * s + 4) =
+          f32x4{sfx[8 * s + 4], sfx[8 * s + 5], sfx[8 * s + 6], sfx[8 * s + 7]};
+    }
   }
 }
 
@@ -597,29 +617,37 @@ hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint
                              hipStream_t stream) {
   using namespace linrel;
   const int nch = (T + CH - 1) / CH;
-  float* states = ws;
-  float* cT = ws + static_cast<size_t>(B) * H * nch * D * D;
-  // the state before every chunk (and the final state for dC_T's term)
-  hipError_t e = launch_linear_fwd(B, H, T, p1, p2, iv, g, rope_cos, rope_sin, state_in, nullptr,
-                                   dstate_out ? cT : nullptr, states, scale, tau, stream);
+  const size_t BH = static_cast<size_t>(B) * H;
+  float* states = ws;                              // [BH][nch + 1][D][D]
+  float* dstates = ws + BH * (nch + 1) * D * D;    // [BH][nch][D][D]
+  // pass 1: the state before every chunk and the final state
+  hipError_t e = launch_linear_fwd_states(B, H, T, p1, p2, iv, g, rope_cos, rope_sin, state_in,
+                                          states, scale, tau, stream);
   if (e != hipSuccess) return e;
   const float sl2 = scale * kLog2e / tau, slope = scale / tau;
-  const dim3 grid(static_cast<unsigned>(B) * H);
+  const dim3 gh(static_cast<unsigned>(BH)), gc(static_cast<unsigned>(BH * nch));
+  // pass 2: the gradient of the state after every chunk
   if (rope_cos)
-    hipLaunchKernelGGL(linear_bwd_kernel<true>, grid, dim3(NT), 0, stream, p1, p2, iv, g, rope_cos,
-                       rope_sin, dy, states, cT, dstate_out, dp1, dp2, dI, dg, dstate_in, T, sl2,
-                       slope);
+    hipLaunchKernelGGL(linear_dstate_kernel<true>, gh, dim3(NT), 0, stream, p1, p2, g, rope_cos,
+                       rope_sin, dy, dstate_out, dstates, dstate_in, T, sl2);
   else
-    hipLaunchKernelGGL(linear_bwd_kernel<false>, grid, dim3(NT), 0, stream, p1, p2, iv, g, nullptr,
-                       nullptr, dy, states, cT, dstate_out, dp1, dp2, dI, dg, dstate_in, T, sl2,
-                       slope);
+    hipLaunchKernelGGL(linear_dstate_kernel<false>, gh, dim3(NT), 0, stream, p1, p2, g, nullptr,
+                       nullptr, dy, dstate_out, dstates, dstate_in, T, sl2);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // pass 3: every chunk's gradients
+  if (rope_cos)
+    hipLaunchKernelGGL(linear_grad_kernel<true>, gc, dim3(NT), 0, stream, p1, p2, iv, g, rope_cos,
+                       rope_sin, dy, states, dstates, dp1, dp2, dI, dg, T, sl2, slope);
+  else
+    hipLaunchKernelGGL(linear_grad_kernel<false>, gc, dim3(NT), 0, stream, p1, p2, iv, g, nullptr,
+                       nullptr, dy, states, dstates, dp1, dp2, dI, dg, T, sl2, slope);
   return hipGetLastError();
 }
 
 size_t linear_bwd_workspace_bytes(int B, int H, int T) {
   using namespace linrel;
   const size_t nch = (T + CH - 1) / CH;
-  return (static_cast<size_t>(B) * H * (nch + 1) * D * D) * sizeof(float);
+  return static_cast<size_t>(B) * H * (2 * nch + 1) * D * D * sizeof(float);
 }
 
 }  // namespace rel

@@ -302,8 +302,9 @@ relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, i
 /*
  * relation_linear_bwd — gradients of relation_linear_fwd with respect to p1,
  * p2, I, g and state_in, given dy and (optionally) the gradient of the final
- * state. Recomputes the state before every 128-token chunk into the
- * workspace, then walks the chunks from the last to the first.
+ * state. Three passes: the state before every 128-token chunk (forward),
+ * the gradient of the state after every chunk (backward over the chunks),
+ * then every chunk's gradients independently.
  *
  *   p1, p2, I, g, rope_cos/rope_sin, state_in : as relation_linear_fwd
  *   dy               : in  [B, H, T, D] bf16, gradient of y
@@ -314,7 +315,9 @@ relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, i
  *   dstate_in        : out DEVICE fp32 [B, H, D, D] gradient of state_in, or
  *                      NULL
  *   workspace        : relation_linear_bwd_workspace_bytes() bytes, 256-byte
- *                      aligned (B * H * (ceil(T / 128) + 1) * D * D floats)
+ *                      aligned (B * H * (2 ceil(T / 128) + 1) * D * D floats:
+ *                      the state before every chunk and the final state,
+ *                      then the gradient of the state after every chunk)
  */
 size_t relation_linear_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D);
 relation_status relation_linear_bwd(relation_dtype dtype, int B, int H, int T, int D,

@@ -196,7 +196,9 @@ def test_linear_validation(lib):
     assert lfwd(cout=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
 
     need = lib.relation_linear_bwd_workspace_bytes(BF16, 2, 3, 300, 64)
-    assert need == 2 * 3 * (3 + 1) * 64 * 64 * 4  # the state per 128-token chunk + the final one
+    # the state before every 128-token chunk and the final one, then the
+    # gradient of the state after every chunk
+    assert need == 2 * 3 * (2 * 3 + 1) * 64 * 64 * 4
     assert lib.relation_linear_bwd_workspace_bytes(F32, 2, 3, 300, 64) == 0
     assert lib.relation_linear_bwd_workspace_bytes(BF16, 2, 3, 300, 48) == 0
 
