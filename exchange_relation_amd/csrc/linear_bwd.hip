@@ -435,39 +435,18 @@ __global__ __launch_bounds__(NT, 1) void linear_grad_kernel(
   const float* b2 = rl.b2;
   const float* lw = rl.lw;
     // ---- exact diagonal block for a sub-chunk with a near-total reset
-    float dq_ex[16], dk_ex[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dq_ex[i] = 0.f;
-      dk_ex[i] = 0.f;
-    }
-    if (!safe) {  // the tiles are still valid: barrier (2) is ahead
+    // (the tiles are still valid: barrier (2) is ahead). A[jj][j] for dI
+    // here; its dq / dk terms are added to the rows below.
+    if (!safe) {
       f32x4 aexact = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
       for (int jj = 0; jj < 16; ++jj) {
         const int src = (lane & 48) | jj;
-        // dq_t += dA[t][jj] k_jj e^{B_t - B_jj} (t = l16 > jj)
-        float dsel = dat_diag[0];
-#pragma unroll
-        for (int r = 1; r < 4; ++r)
-          if ((jj & 3) == r) dsel = dat_diag[r];
-        const float dAq = __shfl(dsel, l16 + 16 * (jj >> 2));
-        // dk_j += dA[jj][j] q_jj e^{B_jj - B_j} (j = l16 < jj)
-        float esel = da_diag[0];
-#pragma unroll
-        for (int r = 1; r < 4; ++r)
-          if ((jj & 3) == r) esel = da_diag[r];
-        const float dAk = __shfl(esel, l16 + 16 * (jj >> 2));
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float kj = __shfl(rl.k[i], src), qj = __shfl(rl.q[i], src);
-          const float bj = __shfl(b2[i], src);
-          const float eq = fast_exp2(fminf(b2[i] - bj, 0.f));  // t = l16 after jj
-          const float ek = fast_exp2(fminf(bj - b2[i], 0.f));  // jj after j = l16
-          dq_ex[i] = fmaf(jj < l16 ? dAq * kj : 0.f, eq, dq_ex[i]);
-          dk_ex[i] = fmaf(jj > l16 ? dAk * qj : 0.f, ek, dk_ex[i]);
-          part = fmaf(qj * rl.k[i], ek, part);  // A[jj][j = l16]
+          const float qj = __shfl(rl.q[i], src), bj = __shfl(b2[i], src);
+          part = fmaf(qj * rl.k[i], fast_exp2(fminf(bj - b2[i], 0.f)), part);  // A[jj][j = l16]
         }
         part = sum_groups(part);
         if ((jj >> 2) == grp) {
@@ -483,7 +462,6 @@ __global__ __launch_bounds__(NT, 1) void linear_grad_kernel(
         dia[cb] = mfma16(ab, __builtin_bit_cast(s16x4, lds_read_tr16(&sm.dy[o])), dia[cb]);
       }
     }
-
     // ---- this wave's rows: MFMA-output layout -> row layout (wave-private
     // staging; a wave's LDS accesses complete in order)
     auto to_rows = [&](const f32x4 (&acc)[4], float (&out)[16]) {
@@ -507,10 +485,37 @@ __global__ __launch_bounds__(NT, 1) void linear_grad_kernel(
     float dB[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      dq[i] = fmaf(fast_exp2(b2[i]), dq[i], dq_ex[i]);
-      dk[i] = fmaf(fast_exp2(lw[i] - b2[i]), dk[i], dk_ex[i]);
-      dB[i] = fmaf(rl.q[i], dq[i], -rl.k[i] * dk[i]);
+      dq[i] *= fast_exp2(b2[i]);
+      dk[i] *= fast_exp2(lw[i] - b2[i]);
     }
+    if (!safe) {
+      // exact diagonal terms: dq_t += dA[t][jj] k_jj e^{B_t - B_jj} (jj < t),
+      // dk_j += dA[jj][j] q_jj e^{B_jj - B_j} (jj > j); dA from the blocks above
+#pragma unroll 1
+      for (int jj = 0; jj < 16; ++jj) {
+        const int src = (lane & 48) | jj;
+        float dsel = dat_diag[0], esel = da_diag[0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r) {
+          if ((jj & 3) == r) dsel = dat_diag[r];
+          if ((jj & 3) == r) esel = da_diag[r];
+        }
+        // the shuffles run on every lane; the masks are applied after
+        const float vq = __shfl(dsel, l16 + 16 * (jj >> 2));
+        const float vk = __shfl(esel, l16 + 16 * (jj >> 2));
+        const float dAq = jj < l16 ? vq : 0.f;
+        const float dAk = jj > l16 ? vk : 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float kj = __shfl(rl.k[i], src), qj = __shfl(rl.q[i], src);
+          const float bj = __shfl(b2[i], src);
+          dq[i] = fmaf(dAq * kj, fast_exp2(fminf(b2[i] - bj, 0.f)), dq[i]);
+          dk[i] = fmaf(dAk * qj, fast_exp2(fminf(bj - b2[i], 0.f)), dk[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dB[i] = fmaf(rl.q[i], dq[i], -rl.k[i] * dk[i]);
     // dI = dY + the contractions
     {
       const int o = (16 * w + l16) * IS + 8 * grp;
