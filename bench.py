@@ -536,6 +536,15 @@ def main():
         rec["prefill_cache"] = bench_prefill(rel, torch, dev, 10)
         rec["decode_ragged"] = bench_decode_ragged(rel, torch, dev)
         torch.cuda.empty_cache()
+        lin = bench_linear(rel, torch, dev, 20)
+        rec["linear_layer30m"] = lin
+        rec["roofline_linear_fwd"] = {
+            "bound": "hbm", "kernel": "linear_fwd_kernel (one launch per call)",
+            "achieved": lin["fwd_GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": lin["fwd_GBps"] / PEAK_HBM_GBS,
+            "traffic": kernel_traffic("linear_fwd_kernel@linear30m")}
+        rec["linear_decode_step"] = bench_linear_step(rel, torch, dev)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
     print(json.dumps(rec))
