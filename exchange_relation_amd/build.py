@@ -24,6 +24,7 @@ SOURCES = [
     "bwd_common.hip",
     "bwd_f32.hip",
     "bwd_bf16.hip",
+    "bwd80.hip",
     "decode.hip",
     "mhr.hip",
     "linear.hip",

@@ -474,15 +474,20 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
   const float* Dr = reinterpret_cast<const float*>(wsb + w.off_dr);
   const int BH = B * H;
   const int nkb = (T + BK - 1) / BK;
-  if (D == 48)
-    hipLaunchKernelGGL(bwd_bf16_kernel<48>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
-                       stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e, scale,
-                       1.0f / tau, lam, dk32, dv32);
-  else
-    hipLaunchKernelGGL(bwd_bf16_kernel<64>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
-                       stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e, scale,
-                       1.0f / tau, lam, dk32, dv32);
-  e = hipGetLastError();
+  if (D == 80) {  // the wider layout of bwd80.hip
+    e = launch_bwd80_kernel(B, H, T, q, k, v, dy, lse, Dr, dq_acc, dk, dv, scale, tau, lam, stream,
+                            dk32, dv32);
+  } else {
+    if (D == 48)
+      hipLaunchKernelGGL(bwd_bf16_kernel<48>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
+                         stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e,
+                         scale, 1.0f / tau, lam, dk32, dv32);
+    else
+      hipLaunchKernelGGL(bwd_bf16_kernel<64>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
+                         stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e,
+                         scale, 1.0f / tau, lam, dk32, dv32);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   // with fp32 results requested, dq stays in the accumulator (the caller
   // scales it) and only the dL/dlambda reduction runs

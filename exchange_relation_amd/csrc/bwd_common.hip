@@ -142,6 +142,11 @@ hipError_t launch_bwd_pre(int dtype, int B, int H, int T, int D, const void* q, 
                           const void* v, const void* y, const void* dy, const float* lse,
                           float* dlambda, const BwdWorkspace& w, char* ws, float scale, float tau,
                           hipStream_t stream) {
+  if (dtype == 1 && D == 80)
+    return launch_bwd_pre_t<uint16_t, 80>(
+        B, H, T, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(y),
+        static_cast<const uint16_t*>(dy), lse, dlambda, w, ws, scale, tau, true, stream);
   if (dtype == 1 && D == 48)
     return launch_bwd_pre_t<uint16_t, 48>(
         B, H, T, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),

@@ -29,7 +29,8 @@ hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const floa
                           const float* v, const float* y, const float* dy, const float* lse,
                           float* dq, float* dk, float* dv, float* dlambda, void* ws, float scale,
                           float tau, float lam, hipStream_t stream);
-// bf16 D in {48, 64} (48 runs in the 64-wide tiles with zero columns).
+// bf16 D in {48, 64, 80} (48 runs in the 64-wide tiles with zero columns, 80
+// in the wider layout of bwd80.hip).
 // dk32 / dv32 non-NULL: dk (scaled) and dv go there in fp32, and dq is left
 // unscaled in the workspace accumulator (bwd_workspace_layout(...).off_dq).
 hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
@@ -38,6 +39,14 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                            float* dlambda, void* ws, float scale, float tau, float lam,
                            hipStream_t stream, float* dk32 = nullptr,
                            float* dv32 = nullptr);
+
+// The D = 80 backward kernel (bwd80.hip), after the shared preprocess; dq
+// accumulates into dq_acc (fp32, unscaled) as for the other widths.
+hipError_t launch_bwd80_kernel(int B, int H, int T, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const uint16_t* dy, const float* lse,
+                               const float* Dr, float* dq_acc, uint16_t* dk, uint16_t* dv,
+                               float scale, float tau, float lam, hipStream_t stream, float* dk32,
+                               float* dv32);
 
 // Relation Cache prefill (bf16, D in {48, 64, 80}): appends m new tokens per (b, h) at
 // slot n_b (n_hist_dev[b] on the device, or the uniform n_hist when NULL;

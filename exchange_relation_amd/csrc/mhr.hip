@@ -305,6 +305,9 @@ hipError_t launch_mhr_post(int dtype, int B, int H, int T, int D, const float* d
                            const float* rope_cos, const float* rope_sin, const float* theta,
                            int pairing, hipStream_t stream) {
   const Mhr mh{rope_cos, rope_sin, theta, pairing, H};
+  if (dtype == 1 && D == 80)
+    return mhr::run_post<uint16_t, 80>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta,
+                                       part, mh, stream);
   if (dtype == 1 && D == 48)
     return mhr::run_post<uint16_t, 48>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta,
                                        part, mh, stream);

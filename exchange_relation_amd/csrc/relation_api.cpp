@@ -26,8 +26,7 @@ relation_status check_params(float scale, float tau_s, float lambda) {
 
 // Head dimensions built: fp32 (accurate VALU paths) D in {32, 64}; bf16
 // forward, decode and prefill D in {48, 64, 80} (the paper's 10M / 30M /
-// 100M head widths), bf16 backward D in {48, 64} (D = 80 would need more
-// accumulator registers than the backward's one-workgroup-per-CU layout has).
+// 100M head widths), bf16 backward D in {48, 64, 80}.
 relation_status check_dtype_dim(relation_dtype dt, int D) {
   if (dt == REL_F32) return (D == 32 || D == 64) ? REL_OK : REL_ERR_UNSUPPORTED;
   if (dt == REL_BF16) return (D == 48 || D == 64 || D == 80) ? REL_OK : REL_ERR_UNSUPPORTED;
@@ -35,7 +34,7 @@ relation_status check_dtype_dim(relation_dtype dt, int D) {
 }
 relation_status check_dtype_dim_bwd(relation_dtype dt, int D) {
   if (dt == REL_F32) return (D == 32 || D == 64) ? REL_OK : REL_ERR_UNSUPPORTED;
-  if (dt == REL_BF16) return (D == 48 || D == 64) ? REL_OK : REL_ERR_UNSUPPORTED;
+  if (dt == REL_BF16) return (D == 48 || D == 64 || D == 80) ? REL_OK : REL_ERR_UNSUPPORTED;
   return REL_ERR_UNSUPPORTED;
 }
 

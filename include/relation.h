@@ -64,7 +64,7 @@ typedef enum { REL_F32 = 0, REL_BF16 = 1 } relation_dtype;
 
 /* Head dimensions built: REL_F32 forward/backward/decode: D in {32, 64};
  * REL_BF16 forward, decode and prefill: D in {48, 64, 80} (the paper's 10M,
- * 30M and 100M head widths); REL_BF16 backward: D in {48, 64}. Other
+ * 30M and 100M head widths); REL_BF16 backward: D in {48, 64, 80}. Other
  * (dtype, D) pairs -> REL_ERR_UNSUPPORTED. */
 
 /*

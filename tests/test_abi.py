@@ -80,7 +80,8 @@ def test_bwd_validation_and_workspace(lib):
     assert need >= 2 * 3 * 100 * 4 + 2 * 3 * 100 * 64 * 4
     assert lib.relation_bwd_workspace_bytes(F32, 2, 3, 100, 64) < need
     assert lib.relation_bwd_workspace_bytes(BF16, 2, 3, 100, 48) > 0
-    assert lib.relation_bwd_workspace_bytes(BF16, 2, 3, 100, 80) == 0
+    assert lib.relation_bwd_workspace_bytes(BF16, 2, 3, 100, 80) > 0
+    assert lib.relation_bwd_workspace_bytes(BF16, 2, 3, 100, 96) == 0
 
     def bwd(ws=P, wsb=None, dq=P, lse=P, tau=2.0, T=100):
         wsb = need if wsb is None else wsb

@@ -3,9 +3,8 @@
 ragged), prefill and the Multi-Head Relation forward, against the fp64
 oracle. Tolerances as everywhere for bf16: max-abs <= 2e-2 and mean-abs
 <= 3e-3; caches bit for bit. The bf16 backward (plain and Multi-Head
-Relation) also runs at D = 48, checked the same way, with dL/dlambda within
-2e-2 relative plus the bound that the bf16 rounding of the stored Y allows;
-D = 80 must be rejected before anything runs.
+Relation) runs at both widths, checked the same way, with dL/dlambda within
+2e-2 relative plus the bound that the bf16 rounding of the stored Y allows.
 """
 import math
 
@@ -157,11 +156,11 @@ def check_dlam(got, ref, extra):
     assert err <= bound
 
 
+@pytest.mark.parametrize("D", [48, 80])
 @pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 2, 33), (2, 1, 64), (1, 2, 130), (2, 2, 300),
                                    (1, 1, 513)])
-def test_bwd_d48_vs_oracle(B, H, T):
-    D = 48
-    inp = make_inputs(B, H, T, D, "bf16", seed=1400 + T, with_dy=True)
+def test_bwd_head_dims_vs_oracle(B, H, T, D):
+    inp = make_inputs(B, H, T, D, "bf16", seed=1400 + T + D, with_dy=True)
     scale, lam = 1 / math.sqrt(D), inp["lam"]
     q, k, v, dy = (inp[n].to(DEV) for n in ("q", "k", "v", "dy"))
     y, lse, _ = rel.relation_fwd(q, k, v, lam=lam, scale=scale)
@@ -193,9 +192,10 @@ def test_bwd_d48_paper10m_geometry_sampled_heads():
         check(f"dv[{b},{h}]", f64(dv[b:b + 1, h:h + 1]), gv)
 
 
+@pytest.mark.parametrize("D", [48, 80])
 @pytest.mark.parametrize("pairing", [0, 1])
-def test_mhr_bwd_d48(pairing):
-    B, H, T, D = 1, 4, 130, 48
+def test_mhr_bwd_head_dims(pairing, D):
+    B, H, T = 1, 4, 130
     inp = make_inputs(B, H, T, D, "bf16", seed=1500 + pairing, with_dy=True)
     cs, sn, th = make_mhr_maps(T, D, H, 1500)
     scale, lam = 1 / math.sqrt(D), inp["lam"]
@@ -224,10 +224,19 @@ def test_mhr_bwd_d48(pairing):
         assert err <= 2e-2 * max(1.0, abs(rth[p])) + 2.0 ** -7 * mag, (p, err)
 
 
-def test_bwd_d80_rejected():
-    D = 80
-    inp = make_inputs(1, 1, 16, D, "bf16", seed=1, with_dy=True)
+def test_bwd_d80_paper100m_geometry_sampled_head():
+    """The 100M model's layer (B=8, H=8, T=4096, d_h=80) in the benchmark's
+    launch shape; one head's gradients in full from the oracle."""
+    B, H, T, D = 8, 8, 4096, 80
+    inp = make_inputs(B, H, T, D, "bf16", seed=42, with_dy=True)
+    scale, lam = 1 / math.sqrt(D), inp["lam"]
     q, k, v, dy = (inp[n].to(DEV) for n in ("q", "k", "v", "dy"))
-    y, lse, _ = rel.relation_fwd(q, k, v, lam=0.3)
-    with pytest.raises(rel.RelationError):
-        rel.relation_bwd(q, k, v, y, dy, lse, lam=0.3)
+    y, lse, _ = rel.relation_fwd(q, k, v, lam=lam, scale=scale)
+    dq, dk, dv, _ = rel.relation_bwd(q, k, v, y, dy, lse, lam=lam, scale=scale)
+    torch.cuda.synchronize()
+    b, h = 5, 3
+    a = tuple(f64(inp[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v", "dy"))
+    gq, gk, gv, _ = oracle.relation_backward(*a, scale, 2.0, lam)
+    check(f"dq[{b},{h}]", f64(dq[b:b + 1, h:h + 1]), gq)
+    check(f"dk[{b},{h}]", f64(dk[b:b + 1, h:h + 1]), gk)
+    check(f"dv[{b},{h}]", f64(dv[b:b + 1, h:h + 1]), gv)
