@@ -186,12 +186,16 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
       }
     };
     apply(ad, w);
-    // off-diagonal blocks, nearest first: chain = e^{B_start(w) - B_end(s')}
+    // off-diagonal blocks, nearest first: chain = e^{B_start(w) - B_end(s')}.
+    // Unrolled over every possible block with a wave-uniform guard, so the
+    // LDS reads of a block can be issued ahead of the previous block's MFMAs
+    // (a rolled loop measured 9 % slower).
     float chain[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) chain[i] = 1.f;
-#pragma unroll 1
-    for (int sp = w - 1; sp >= 0; --sp) {
+#pragma unroll
+    for (int sp = NW - 2; sp >= 0; --sp) {
+      if (sp >= w) continue;
       const float* kr = &sm.kk[(16 * sp + l16) * KS + 8 * grp];
       float kx[16];
 #pragma unroll
