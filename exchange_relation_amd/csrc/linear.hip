@@ -23,7 +23,7 @@
 //    layout they are already the A operand of the 16x16x16 MFMAs that apply
 //    them to I (no LDS round trip);
 //  * the diagonal 16 x 16 block uses the ratio form (k e^{B_start - B_j} may
-//    exceed 1): exact while a sub-chunk's retention span stays within 2^60;
+//    exceed 1): exact while a sub-chunk's retention span stays within 2^120;
 //    a sub-chunk with a larger span (a near-total reset) takes an exact
 //    per-pair path instead (wave-uniform branch);
 //  * the state (fp32, in registers: 2 blocks of 16 x 16 per wave) feeds the
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
     const int trow = t0 + 16 * w + l16;  // this lane's row
     // ---------------- row-local: coordinates, Self, q, k, prefix of g
     RowLocal rl;
-    row_local<ROPE>(raw, sl2, lane, rl);
+    row_local<ROPE>(raw, sl2, lane, kSafeLog2Fwd, rl);
     const float* q = rl.q;
     const float* k = rl.k;
     const float* b2 = rl.b2;

@@ -15,9 +15,13 @@ constexpr int NT = NW * 64;  // threads
 constexpr int CH = NW * 16;  // tokens per chunk
 constexpr int IS = 72;       // bf16 row stride of the tiles in LDS
 constexpr int KS = 68;       // fp32 row stride of fp32 tiles
-// A sub-chunk whose retention over its 16 tokens is above 2^-60 on every
-// channel uses the ratio form for its diagonal block.
-constexpr float kSafeLog2 = -60.f;
+// A sub-chunk whose retention over its 16 tokens is above 2^kSafeLog2* on
+// every channel uses the ratio form for its diagonal block. The forward's
+// ratio factors stay within 2^+-120 and its largest partial sums (the masked
+// entries, up to 2^120) within fp32; the gradient kernel multiplies its
+// factors by dA = I . dE as well, so it keeps a wider margin.
+constexpr float kSafeLog2Fwd = -120.f;
+constexpr float kSafeLog2Bwd = -60.f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -127,7 +131,8 @@ struct RowLocal {
 };
 
 template <bool ROPE>
-__device__ __forceinline__ void row_local(Raw& raw, float sl2, int lane, RowLocal& o) {
+__device__ __forceinline__ void row_local(Raw& raw, float sl2, int lane, float safe_log2,
+                                          RowLocal& o) {
   const u32x4 z = {0, 0, 0, 0};
   const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -179,7 +184,7 @@ __device__ __forceinline__ void row_local(Raw& raw, float sl2, int lane, RowLoca
     lmin = fminf(lmin, o.lw[i]);
   }
   // every lane holds the wave's minimum; make the branch scalar
-  o.safe = __builtin_amdgcn_readfirstlane(min_groups(lmin) >= kSafeLog2 ? 1 : 0) != 0;
+  o.safe = __builtin_amdgcn_readfirstlane(min_groups(lmin) >= safe_log2 ? 1 : 0) != 0;
 }
 
 }  // namespace linrel

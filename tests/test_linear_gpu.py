@@ -84,11 +84,32 @@ def test_linear_fwd_vs_oracle(T, use_rope):
 
 @pytest.mark.parametrize("resets,keep", [(True, False), (False, True), (True, True)])
 def test_linear_fwd_extreme_retention(resets, keep):
-    """Near-total resets (g = -60 on 1 % of entries: the per-pair path of the
-    diagonal blocks) and channels without loss (g = 0)."""
+    """Near-total resets (g = -60 on 1 % of entries: sub-chunks with two
+    resets on one channel take the per-pair path of the diagonal blocks) and
+    channels without loss (g = 0)."""
     d = make_linear_inputs(2, 3, 400, 64, seed=2100, resets=resets, keep=keep)
     y, c = run_fwd(d)
     r = oracle_fwd(d)
+    check("y", f64(y), r["Y"])
+    check_state("state", f64(c), r["C"])
+
+
+def test_linear_fwd_diagonal_span_limits():
+    """The diagonal block's ratio form is used while a sub-chunk's retention
+    span stays within 2^120 on every channel, the per-pair path beyond it.
+    Sub-chunks with a span just inside (2^-118) and just beyond (2^-122) that
+    limit on one channel, and one with a single token of g = -400, against
+    the oracle."""
+    d = make_linear_inputs(1, 2, 200, 64, seed=2150)
+    g = d["g"].clone()
+    ln2 = math.log(2.0)
+    g[..., 16:32, 5] = -118.0 * ln2 / 16  # sub-chunk 1: ratio form at its limit
+    g[..., 48:64, 40] = -122.0 * ln2 / 16  # sub-chunk 3: per-pair path
+    g[..., 90, 7] = -400.0  # sub-chunk 5: per-pair path
+    g[..., 130:146, :] = -118.0 * ln2 / 16  # a whole chunk-crossing run at the limit
+    d["g"] = g
+    y, c = run_fwd(d, tables(200))
+    r = oracle_fwd(d, tables(200))
     check("y", f64(y), r["Y"])
     check_state("state", f64(c), r["C"])
 
