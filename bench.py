@@ -104,14 +104,23 @@ def bench_fwd(rel, torch, dev, B, H, T, D, reps, rope=False, seed=42):
     lse = torch.empty((B, H, T), device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream(dev)
     t = EventTimer(torch, stream)
-    for i in range(reps + 3):
-        s = t.start() if i >= 3 else None
-        rel.relation_fwd(q, k, v, lam=inp["lam"], scale=1 / math.sqrt(D), y=y, lse=lse)
-        if i >= 3:
-            t.stop(s)
-    ms = t.mean_ms()
+    nws = rel.relation_fwd_workspace_bytes(torch.bfloat16, B, H, T, D)
+    ws = torch.empty((nws,), device=dev, dtype=torch.uint8) if nws else None
+    for _ in range(3):
+        rel.relation_fwd(q, k, v, lam=inp["lam"], scale=1 / math.sqrt(D), y=y, lse=lse,
+                         workspace=ws)
+    torch.cuda.synchronize()
+    # back-to-back calls between one pair of events: a short call (the 10M
+    # layer's is ~20 us) would otherwise also time the host's launch path
+    s = t.start()
+    for _ in range(reps):
+        rel.relation_fwd(q, k, v, lam=inp["lam"], scale=1 / math.sqrt(D), y=y, lse=lse,
+                         workspace=ws)
+    t.stop(s)
+    ms = t.mean_ms() / reps
     tf = fwd_flops(B, H, T, D) / (ms * 1e-3) / 1e12
-    return {"ms": ms, "tflops": tf, "frac_peak": tf / PEAK_BF16_TFLOPS}
+    return {"ms": ms, "tflops": tf, "frac_peak": tf / PEAK_BF16_TFLOPS,
+            "timing": f"{reps} back-to-back calls", "split_over_keys": nws > 0}
 
 
 def bench_fwdbwd_vs_attention(rel, torch, dev, reps, B=8, H=12, T=4096, D=64, seed=42):
@@ -257,12 +266,14 @@ def bench_prefill(rel, torch, dev, reps, B=32, H=12, D=64, m=256, cap=4352, seed
     kc, vc = d["k_cache"].to(dev), d["v_cache"].to(dev)
     nh = torch.tensor(ns, dtype=torch.int32, device=dev)
     y = torch.empty_like(q)
+    nws = rel.relation_prefill_workspace_bytes(torch.bfloat16, B, H, D, m, cap - m, True)
+    ws = torch.empty((nws,), device=dev, dtype=torch.uint8) if nws else None
     stream = torch.cuda.current_stream(dev)
     t = EventTimer(torch, stream)
     for i in range(reps + 3):
         s0 = t.start() if i >= 3 else None
         rel.relation_cache_prefill(q, kn, vn, kc, vc, nh, cap - m, lam=d["lam"],
-                                   scale=1 / math.sqrt(D), y=y)
+                                   scale=1 / math.sqrt(D), y=y, workspace=ws)
         if i >= 3:
             t.stop(s0)
     ms = t.mean_ms()
@@ -270,7 +281,7 @@ def bench_prefill(rel, torch, dev, reps, B=32, H=12, D=64, m=256, cap=4352, seed
     tf = 4 * D * entries / (ms * 1e-3) / 1e12
     return {"workload": f"prefill {m} tokens x {B} sequences x {H} heads, ragged history "
             f"(mean {sum(ns) / B:.0f})", "ms": ms, "tflops": tf,
-            "frac_peak": tf / PEAK_BF16_TFLOPS}
+            "frac_peak": tf / PEAK_BF16_TFLOPS, "split_over_keys": nws > 0}
 
 
 def bench_mhr(rel, torch, dev, reps, B=16, H=8, T=2048, D=64, seed=42):
@@ -521,7 +532,7 @@ def main():
         "fwd_ms": st["fwd_ms"], "bwd_ms": st["bwd_ms"],
     }
     if not args.no_extra:
-        rec["fwd_layer10m"] = bench_fwd(rel, torch, dev, 8, 8, 1024, 64, 20, rope=True)
+        rec["fwd_layer10m"] = bench_fwd(rel, torch, dev, 8, 8, 1024, 64, 50, rope=True)
         rec["fwd_layer100m"] = bench_fwd(rel, torch, dev, 8, 12, 4096, 64, 10)
         rec["layer100m_vs_attention"] = bench_fwdbwd_vs_attention(rel, torch, dev, 5)
         dec = bench_decode(rel, torch, dev)

@@ -19,12 +19,14 @@ __all__ = [
     "lib_path",
     "load_library",
     "relation_fwd",
+    "relation_fwd_workspace_bytes",
     "relation_bwd",
     "relation_bwd_workspace_bytes",
     "relation_cache_decode",
     "relation_decode_workspace_bytes",
     "relation_cache_decode_ragged",
     "relation_cache_prefill",
+    "relation_prefill_workspace_bytes",
     "relation_mhr_fwd",
     "relation_mhr_bwd",
     "relation_linear_fwd",
@@ -40,12 +42,14 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 REL_F32, REL_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
+    "relation_fwd_workspace_bytes",
     "relation_fwd",
     "relation_bwd_workspace_bytes",
     "relation_bwd",
     "relation_decode_workspace_bytes",
     "relation_cache_decode",
     "relation_cache_decode_ragged",
+    "relation_prefill_workspace_bytes",
     "relation_cache_prefill",
     "relation_mhr_fwd_workspace_bytes",
     "relation_mhr_fwd",
@@ -83,9 +87,11 @@ def load_library():
         raise RuntimeError(f"{path} is not built; run `python -m exchange_relation_amd.build`")
     lib = ctypes.CDLL(path)
     c_int, c_float, c_size, vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+    lib.relation_fwd_workspace_bytes.restype = c_size
+    lib.relation_fwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_fwd.restype = c_int
     lib.relation_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
-                                 c_float, c_float, c_float, vp]
+                                 vp, c_size, c_float, c_float, c_float, vp]
     lib.relation_bwd_workspace_bytes.restype = c_size
     lib.relation_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_bwd.restype = c_int
@@ -101,10 +107,13 @@ def load_library():
     lib.relation_cache_decode_ragged.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
                                                  c_int, vp, c_int, vp, vp, vp, c_size, c_float,
                                                  c_float, c_float, vp]
+    lib.relation_prefill_workspace_bytes.restype = c_size
+    lib.relation_prefill_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int,
+                                                     c_int]
     lib.relation_cache_prefill.restype = c_int
     lib.relation_cache_prefill.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
-                                           c_int, vp, c_int, vp, vp, vp, c_float, c_float,
-                                           c_float, vp]
+                                           c_int, vp, c_int, vp, vp, vp, vp, c_size, c_float,
+                                           c_float, c_float, vp]
     lib.relation_mhr_fwd_workspace_bytes.restype = c_size
     lib.relation_mhr_fwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_mhr_fwd.restype = c_int
@@ -156,6 +165,10 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _check(t, name, dtype, shape, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -178,11 +191,27 @@ def _scale(D, scale):
     return 1.0 / math.sqrt(D) if scale is None else float(scale)
 
 
+def relation_fwd_workspace_bytes(dtype, B, H, T, D):
+    code = REL_BF16 if dtype == torch.bfloat16 else REL_F32
+    return int(load_library().relation_fwd_workspace_bytes(code, B, H, T, D))
+
+
+def _workspace(t, need, dev):
+    """The caller's workspace tensor (checked), or a new one when need > 0."""
+    if t is None:
+        return torch.empty((need,), device=dev, dtype=torch.uint8) if need > 0 else None
+    if t.device != dev or not t.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return t
+
+
 def relation_fwd(q, k, v, lam=0.0, scale=None, tau_s=2.0, y=None, lse=None, gate=None,
-                 want_lse=True, want_gate=False, stream=None):
+                 want_lse=True, want_gate=False, workspace=None, split=True, stream=None):
     """Multi-Head Relation forward. q, k, v: [B, H, T, D] on a GPU, float32 or
     bfloat16, contiguous. Returns (y, lse, gate); lse / gate are float32
-    [B, H, T] or None. Outputs may be passed in to avoid allocation."""
+    [B, H, T] or None. Outputs may be passed in to avoid allocation. With
+    split (default) a grid too small to fill the GPU splits its long query
+    blocks over keys, in a workspace allocated here unless one is given."""
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, D]")
@@ -202,9 +231,10 @@ def relation_fwd(q, k, v, lam=0.0, scale=None, tau_s=2.0, y=None, lse=None, gate
     for name, t in (("lse", lse), ("gate", gate)):
         if t is not None:
             _check(t, name, torch.float32, (B, H, T), dev)
+    ws = _workspace(workspace, relation_fwd_workspace_bytes(dt, B, H, T, D), dev) if split else None
     st = lib.relation_fwd(code, B, H, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(lse),
-                          _ptr(gate), _scale(D, scale), float(tau_s), float(lam),
-                          _stream(dev, stream))
+                          _ptr(gate), _ptr(ws), _nbytes(ws), _scale(D, scale), float(tau_s),
+                          float(lam), _stream(dev, stream))
     if st != 0:
         raise RelationError(st, "relation_fwd")
     return y, lse, gate
@@ -322,13 +352,20 @@ def relation_cache_decode_ragged(q, k_new, v_new, k_cache, v_cache, n_hist, max_
     return y, gate
 
 
+def relation_prefill_workspace_bytes(dtype, B, H, D, m, n_hist, per_sequence):
+    code = REL_BF16 if dtype == torch.bfloat16 else REL_F32
+    return int(load_library().relation_prefill_workspace_bytes(code, B, H, D, m, n_hist,
+                                                                1 if per_sequence else 0))
+
+
 def relation_cache_prefill(q, k_new, v_new, k_cache, v_cache, n_hist, max_n_hist=None, lam=0.0,
                            scale=None, tau_s=2.0, y=None, lse=None, gate=None, want_stats=False,
-                           stream=None):
+                           workspace=None, split=True, stream=None):
     """m new tokens per sequence: q, k_new, v_new [B, H, m, D] appended at
     slot n_hist (an int, or a device int32 tensor [B] with max_n_hist its
     bound, default capacity - m) of k_cache, v_cache [B, H, capacity, D].
-    Returns (y, lse, gate); lse and gate only with want_stats."""
+    Returns (y, lse, gate); lse and gate only with want_stats. With split
+    (default) long histories are split over workgroups in a workspace."""
     lib = load_library()
     B, H, m, D = q.shape
     capacity = k_cache.shape[2]
@@ -348,10 +385,15 @@ def relation_cache_prefill(q, k_new, v_new, k_cache, v_cache, n_hist, max_n_hist
     if want_stats:
         lse = torch.empty((B, H, m), device=dev, dtype=torch.float32) if lse is None else lse
         gate = torch.empty((B, H, m), device=dev, dtype=torch.float32) if gate is None else gate
+    ws = None
+    if split and n >= 0:
+        ws = _workspace(workspace, relation_prefill_workspace_bytes(dt, B, H, D, m, n,
+                                                                    nh is not None), dev)
     st = lib.relation_cache_prefill(code, B, H, D, m, _ptr(q), _ptr(k_new), _ptr(v_new),
                                     _ptr(k_cache), _ptr(v_cache), capacity, _ptr(nh), n, _ptr(y),
-                                    _ptr(lse), _ptr(gate), _scale(D, scale), float(tau_s),
-                                    float(lam), _stream(dev, stream))
+                                    _ptr(lse), _ptr(gate), _ptr(ws), _nbytes(ws),
+                                    _scale(D, scale), float(tau_s), float(lam),
+                                    _stream(dev, stream))
     if st != 0:
         raise RelationError(st, "relation_cache_prefill")
     return y, lse, gate

@@ -203,12 +203,29 @@ struct Seg {
   int p0, bound, ld, H;
 };
 
-template <bool MHR, bool OFF, int DR>
+// Split over keys (SPLIT): on a grid too small to fill the chip, a query
+// block's strictly historical tiles are cut into pieces of spl tiles; piece s
+// covers tiles [s spl, min((s + 1) spl, nfull)) and the last piece also the
+// block's own tiles (the diagonal and the Self entry). A block of one piece
+// completes its rows itself; the pieces of a longer block leave their rows'
+// partial scan (acc, m, l and, from the last piece, u'_ii) in `part` for
+// split_combine_kernel, which merges them by App. A.3.2's rule.
+struct Split {
+  float* part;  // [BH][nqb][nsp][BM][D + 4] fp32: acc[D], m, l, u'_ii, unused
+  int spl;      // tiles per piece
+  int nsp;      // pieces per block in the grid (>= the most any block needs)
+};
+struct SplitPlan {
+  int spl, nsp;  // spl = 0: no split
+  size_t bytes;  // workspace for the partial rows
+};
+
+template <bool MHR, bool OFF, int DR, bool SPLIT = false>
 __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ y, float* __restrict__ lse,
     float* __restrict__ gate, int T, int BH, int nqb, float qscale, float inv_tau, float lam,
-    Mhr mh, Seg sg) {
+    Mhr mh, Seg sg, Split sp = Split{}) {
   using Dm = Dims<DR>;
   constexpr int D = Dm::D, NQ = Dm::NQ, ND = Dm::ND, KS = Dm::KS, VS = Dm::VS;
   constexpr int CPR = Dm::CPR, NCH = Dm::NCH;
@@ -222,7 +239,8 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
 
   const int L = blockIdx.x;
   const int head = L % BH;
-  const int qb = nqb - 1 - L / BH;  // longest query blocks first
+  const int qb = nqb - 1 - (L / BH) % nqb;  // longest query blocks first
+  const int piece = SPLIT ? L / (BH * nqb) : 0;
   const size_t base = static_cast<size_t>(head) * T * D;
   const int q0 = qb * BM + wave * 32;
   const int qi = q0 + r;
@@ -234,6 +252,7 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   if (OFF) {
     pos0 = sg.p0s ? sg.p0s[head / sg.H] : sg.p0;
     if (pos0 < 0 || pos0 > sg.bound || pos0 + T > sg.ld) {  // out of range: NaN rows
+      if (piece != 0) return;
       const int r0 = qb * BM, r1 = min(T, r0 + BM);
       for (int e = tid; e < (r1 - r0) * D; e += 256) y[base + static_cast<size_t>(r0) * D + e] = 0x7fc0;
       for (int i = r0 + tid; i < r1; i += 256) {
@@ -292,6 +311,21 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   const int kend = min(Tk, pos0 + (qb + 1) * BM);
   const int ntiles = (kend + BN - 1) / BN;
   const int nfull = (pos0 + qb * BM) / BN;
+  // this workgroup's tiles: historical [kt0, hend), then (last piece) the
+  // block's own up to ntiles; tend bounds the look-ahead (nfull < ntiles, so
+  // a piece that stops at hend < nfull may stage tile hend unused)
+  int kt0 = 0, hend = nfull, tend = ntiles, npc = 1;
+  bool last = true;
+  if (SPLIT) {
+    npc = nfull > 0 ? (nfull + sp.spl - 1) / sp.spl : 1;
+    if (piece >= npc) return;
+    kt0 = piece * sp.spl;
+    last = piece == npc - 1;
+    if (!last) {
+      hend = kt0 + sp.spl;
+      tend = hend + 1;
+    }
+  }
 
   // ---- global -> register prefetch: the tile's 16 B chunks c = tid + 256 i
   // (row c / CPR, column chunk c % CPR; i < NCH), as 32-bit offsets from the
@@ -344,12 +378,12 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   Chunks ck, cv;
   {
     Chunks cn;
-    fetch(kh, 0, ck);
-    fetch(vh, 0, cv);
-    if (ntiles > 1) fetch(kh, 1, cn);
+    fetch(kh, kt0, ck);
+    fetch(vh, kt0, cv);
+    if (kt0 + 1 < tend) fetch(kh, kt0 + 1, cn);
     stash(kp0, ck, KS);
     stash(vbuf[0], cv, VS);
-    if (ntiles > 1) stash(kp1, cn, KS);
+    if (kt0 + 1 < tend) stash(kp1, cn, KS);
   }
   __syncthreads();
 
@@ -357,13 +391,13 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   // MFMAs run under sub-block 0's exponentials, and the next tile's
   // sub-block 0 score under sub-block 1's. No masking.
   f32x16 sa = {0};
-  if (nfull > 0) sa = score<DR>(kp0, 0, qf, r, hf);
-  int kt = 0;
-  for (; kt < nfull; ++kt) {
-    const bool more_k = kt + 2 < ntiles;  // kt + 1 < ntiles always holds here
+  if (kt0 < hend) sa = score<DR>(kp0, 0, qf, r, hf);
+  int kt = kt0;
+  for (; kt < hend; ++kt) {
+    const bool more_k = kt + 2 < tend;  // kt + 1 < tend always holds here
     if (more_k) fetch(kh, kt + 2, ck);
     fetch(vh, kt + 1, cv);
-    const uint16_t* vs = vbuf[kt & 1];
+    const uint16_t* vs = vbuf[(kt - kt0) & 1];
     stabilise<false>(sa, qscale, r, hf, st);
     f32x16 sb = score<DR>(kp0, 1, qf, r, hf);
     accumulate<false, DR>(vs, 0, sa, hf, st);
@@ -371,7 +405,7 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     sa = score<DR>(kp1, 0, qf, r, hf);  // tile kt + 1 <= nfull is resident
     accumulate<false, DR>(vs, 1, sb, hf, st);
     if (more_k) stash(kp2, ck, KS);
-    stash(vbuf[(kt + 1) & 1], cv, VS);
+    stash(vbuf[(kt + 1 - kt0) & 1], cv, VS);
     __syncthreads();
     uint16_t* kt0 = kp0;
     kp0 = kp1;
@@ -381,11 +415,11 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   // ---- the workgroup's own block: per-wave historical / diagonal /
   // beyond. Aligned rows (pos0 = 0) span at most two tiles, both resident;
   // rows at an offset may span three, so K keeps streaming two tiles ahead.
-  for (; kt < ntiles; ++kt) {
+  for (; last && kt < ntiles; ++kt) {
     const bool more_k = kt + 2 < ntiles;
     if (more_k) fetch(kh, kt + 2, ck);
     if (kt + 1 < ntiles) fetch(vh, kt + 1, cv);
-    const uint16_t* vs = vbuf[kt & 1];
+    const uint16_t* vs = vbuf[(kt - kt0) & 1];
     if (wave_live) {
       const int pw = pos0 + q0;  // position of the wave's first query
 #pragma unroll
@@ -403,7 +437,7 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
       }
     }
     if (more_k) stash(kp2, ck, KS);
-    if (kt + 1 < ntiles) stash(vbuf[(kt + 1) & 1], cv, VS);
+    if (kt + 1 < ntiles) stash(vbuf[(kt + 1 - kt0) & 1], cv, VS);
     __syncthreads();
     uint16_t* kt0 = kp0;
     kp0 = kp1;
@@ -418,6 +452,22 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   const float uo = other_half(st.uself);
   const float us = st.has_self ? st.uself : uo;
   if (qi >= T) return;
+  if (SPLIT && npc > 1) {  // partial row for the combine
+    float* pr = sp.part + ((((static_cast<size_t>(head) * nqb + qb) * sp.nsp + piece) * BM) +
+                           wave * 32 + r) * (D + 4);
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + g4 * 8 + hf * 4;
+        if (d0 < DR)
+          *reinterpret_cast<f32x4*>(pr + d0) =
+              f32x4{st.acc[db][g4 * 4], st.acc[db][g4 * 4 + 1], st.acc[db][g4 * 4 + 2],
+                    st.acc[db][g4 * 4 + 3]};
+      }
+    if (hf == 0) *reinterpret_cast<f32x4*>(pr + D) = f32x4{st.m, ltot, us, 0.f};
+    return;
+  }
   const float S = fast_rcp(1.0f + fast_exp2(-us * inv_tau));  // sigmoid(U_ii / tau)
   const float S2 = S * kLog2e;
   float g, lz;
@@ -458,14 +508,133 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
 }  // namespace fwdbf16
 
 namespace fwdbf16 {
+
+// Merge of a split block's pieces and the row completion (App. A.3.5), one
+// thread per (row, 4 value columns). The pieces' scans combine by App.
+// A.3.2's rule: M = max m_s, l = sum l_s 2^(m_s - M), acc likewise; the Self
+// score comes from the last piece. Rows of blocks the forward kernel
+// completed itself (one piece) and rows of out-of-range sequences are left
+// alone.
+template <int DR>
+__global__ __launch_bounds__(256) void split_combine_kernel(
+    const float* __restrict__ part, const uint16_t* __restrict__ v, uint16_t* __restrict__ y,
+    float* __restrict__ lse, float* __restrict__ gate, int T, int BH, int nqb, float inv_tau,
+    float lam, Seg sg, Split sp, bool off) {
+  constexpr int D = DR, CQ = DR / 4, PW = DR + 4;
+  const size_t g = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const size_t row = g / CQ;
+  if (row >= static_cast<size_t>(BH) * T) return;
+  const int quad = static_cast<int>(g % CQ);
+  const int head = static_cast<int>(row / T), qi = static_cast<int>(row % T);
+  int pos0 = 0;
+  size_t kvbase = static_cast<size_t>(head) * T * D;
+  if (off) {
+    pos0 = sg.p0s ? sg.p0s[head / sg.H] : sg.p0;
+    if (pos0 < 0 || pos0 > sg.bound || pos0 + T > sg.ld) return;
+    kvbase = static_cast<size_t>(head) * sg.ld * D;
+  }
+  const int qb = qi / BM;
+  const int nfull = (pos0 + qb * BM) / BN;
+  const int npc = nfull > 0 ? (nfull + sp.spl - 1) / sp.spl : 1;
+  if (npc == 1) return;
+  const float* pr = part + (((static_cast<size_t>(head) * nqb + qb) * sp.nsp) * BM + qi % BM) * PW;
+  const size_t ps = static_cast<size_t>(BM) * PW;  // piece stride
+  float mx = -INFINITY;
+  for (int s = 0; s < npc; ++s) mx = fmaxf(mx, pr[s * ps + D]);
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < npc; ++s) {
+    const f32x4 st = *reinterpret_cast<const f32x4*>(pr + s * ps + D);
+    const float a = fast_exp2(st[0] - mx);
+    l = fmaf(st[1], a, l);
+    const f32x4 u = *reinterpret_cast<const f32x4*>(pr + s * ps + 4 * quad);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(u[e], a, acc[e]);
+  }
+  const float us = pr[(npc - 1) * ps + D + 2];
+  const float S = fast_rcp(1.0f + fast_exp2(-us * inv_tau));
+  const float S2 = S * kLog2e;
+  float gt, lz;
+  if (l > 0.f) {
+    const float A2 = mx + fast_log2(l) - lam * fast_log2(static_cast<float>(pos0 + qi + 1));
+    gt = fast_rcp(1.0f + fast_exp2(S2 - A2));
+    lz = kLn2 * (fmaxf(S2, A2) + fast_log2(1.0f + fast_exp2(-fabsf(S2 - A2))));
+  } else {
+    gt = 0.f;
+    lz = S;
+  }
+  const float gl = l > 0.f ? gt * fast_rcp(l) : 0.f;
+  const float gs = 1.0f - gt;
+  const uint2 vr = *reinterpret_cast<const uint2*>(v + kvbase + static_cast<size_t>(pos0 + qi) * D +
+                                                   4 * quad);
+  const float y0 = fmaf(gs, __uint_as_float(vr.x << 16), gl * acc[0]);
+  const float y1 = fmaf(gs, __uint_as_float(vr.x & 0xffff0000u), gl * acc[1]);
+  const float y2 = fmaf(gs, __uint_as_float(vr.y << 16), gl * acc[2]);
+  const float y3 = fmaf(gs, __uint_as_float(vr.y & 0xffff0000u), gl * acc[3]);
+  *reinterpret_cast<uint2*>(y + row * D + 4 * quad) =
+      make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+  if (quad == 0) {
+    if (lse) lse[row] = lz;
+    if (gate) gate[row] = gt;
+  }
+}
+
+// Split plan for a grid of BH x nqb query blocks whose rows sit at positions
+// up to pbound + [0, T). A grid that already has two workgroups per slot
+// (256 CUs x the workgroups resident per CU) is not split. Otherwise pieces
+// are sized for about 1.5 per slot: the blocks' total tile work (for
+// per-sequence lengths half the bound's, the lengths taken as spread over
+// [0, bound]) over 1.5 x the slots, and at least 16 tiles, since a short
+// workgroup is dominated by its start (the query fragments and first tiles
+// before its first barrier): 6-tile pieces made the 10M-layer forward
+// slower, and 20-23-tile pieces were fastest on the ragged cache prefill.
+SplitPlan plan_split(int BH, int T, int pbound, bool ragged, int DR) {
+  SplitPlan pl{0, 1, 0};
+  const int nqb = (T + BM - 1) / BM;
+  const long long slots = 256LL * (DR <= 64 ? 3 : 2);
+  if (static_cast<long long>(BH) * nqb >= 2 * slots) return pl;
+  long long work = 0;
+  int nfmax = 0;
+  for (int qb = 0; qb < nqb; ++qb) {
+    const int nfull = (pbound + qb * BM) / BN;
+    const int kend = pbound + min(T, (qb + 1) * BM);
+    work += (kend + BN - 1) / BN;
+    nfmax = max(nfmax, nfull);
+  }
+  work *= BH;
+  if (ragged) work /= 2;
+  const int spl = static_cast<int>(max(16LL, (2 * work + 3 * slots - 1) / (3 * slots)));
+  const int nsp = nfmax > 0 ? (nfmax + spl - 1) / spl : 1;
+  if (nsp < 2) return pl;
+  pl.spl = spl;
+  pl.nsp = nsp;
+  pl.bytes = static_cast<size_t>(BH) * nqb * nsp * BM * (DR + 4) * sizeof(float);
+  return pl;
+}
+
 template <int DR>
 hipError_t run_fwd(int BH, int H, int T, const uint16_t* q, const uint16_t* k,
                    const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale, float tau,
-                   float lam, hipStream_t stream, const float* rope_cos, const float* rope_sin) {
+                   float lam, hipStream_t stream, const float* rope_cos, const float* rope_sin,
+                   float* ws, size_t ws_bytes) {
   const int nqb = (T + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(nqb) * BH);
   const Mhr mh{rope_cos, rope_sin, nullptr, 0, H};
   const Seg sg{nullptr, 0, 0, T, H};
+  const SplitPlan pl = ws ? plan_split(BH, T, 0, false, DR) : SplitPlan{0, 1, 0};
+  if (rope_cos == nullptr && pl.spl > 0 && ws_bytes >= pl.bytes) {
+    const Split sp{ws, pl.spl, pl.nsp};
+    hipLaunchKernelGGL((fwd_bf16_kernel<false, false, DR, true>),
+                       dim3(static_cast<unsigned>(nqb) * BH * pl.nsp), dim3(256), 0, stream, q, k,
+                       v, y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg, sp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t threads = static_cast<size_t>(BH) * T * (DR / 4);
+    hipLaunchKernelGGL((split_combine_kernel<DR>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                       dim3(256), 0, stream, ws, v, y, lse, gate, T, BH, nqb, 1.0f / tau, lam, sg,
+                       sp, false);
+    return hipGetLastError();
+  }
   if (rope_cos == nullptr || DR != 64)
     hipLaunchKernelGGL((fwd_bf16_kernel<false, false, DR>), grid, dim3(256), 0, stream, q, k, v,
                        y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
@@ -502,7 +671,8 @@ template <int DR>
 hipError_t run_prefill(int BH, int H, int m, const uint16_t* q, const uint16_t* k_new,
                        const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache, int capacity,
                        const int* n_hist_dev, int n_hist, uint16_t* y, float* lse, float* gate,
-                       float scale, float tau, float lam, hipStream_t stream) {
+                       float scale, float tau, float lam, hipStream_t stream, float* ws,
+                       size_t ws_bytes) {
   const size_t rows = static_cast<size_t>(BH) * m;
   const size_t threads = rows * (DR / 8);
   hipLaunchKernelGGL((append_kernel<DR>), dim3(static_cast<unsigned>((threads + 255) / 256)),
@@ -513,6 +683,22 @@ hipError_t run_prefill(int BH, int H, int m, const uint16_t* q, const uint16_t* 
   const int nqb = (m + BM - 1) / BM;
   const Mhr mh{nullptr, nullptr, nullptr, 0, H};
   const Seg sg{n_hist_dev, n_hist, n_hist, capacity, H};
+  const SplitPlan pl =
+      ws ? plan_split(BH, m, n_hist, n_hist_dev != nullptr, DR) : SplitPlan{0, 1, 0};
+  if (pl.spl > 0 && ws_bytes >= pl.bytes) {
+    const Split sp{ws, pl.spl, pl.nsp};
+    hipLaunchKernelGGL((fwd_bf16_kernel<false, true, DR, true>),
+                       dim3(static_cast<unsigned>(nqb) * BH * pl.nsp), dim3(256), 0, stream, q,
+                       k_cache, v_cache, y, lse, gate, m, BH, nqb, scale * kLog2e, 1.0f / tau, lam,
+                       mh, sg, sp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t threads = static_cast<size_t>(BH) * m * (DR / 4);
+    hipLaunchKernelGGL((split_combine_kernel<DR>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                       dim3(256), 0, stream, ws, v_cache, y, lse, gate, m, BH, nqb, 1.0f / tau,
+                       lam, sg, sp, true);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((fwd_bf16_kernel<false, true, DR>), dim3(static_cast<unsigned>(nqb) * BH),
                      dim3(256), 0, stream, q, k_cache, v_cache, y, lse, gate, m, BH, nqb,
                      scale * kLog2e, 1.0f / tau, lam, mh, sg);
@@ -520,35 +706,46 @@ hipError_t run_prefill(int BH, int H, int m, const uint16_t* q, const uint16_t* 
 }
 }  // namespace fwdbf16
 
+size_t fwd_bf16_workspace_bytes(int B, int H, int T, int D) {
+  return fwdbf16::plan_split(B * H, T, 0, false, D).bytes;
+}
+
+size_t prefill_workspace_bytes(int B, int H, int D, int m, int n_hist, bool per_sequence) {
+  return fwdbf16::plan_split(B * H, m, n_hist, per_sequence, D).bytes;
+}
+
 hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale,
                            float tau, float lam, hipStream_t stream, const float* rope_cos,
-                           const float* rope_sin) {
+                           const float* rope_sin, float* ws, size_t ws_bytes) {
   const int BH = B * H;
   if (D == 48)
     return fwdbf16::run_fwd<48>(BH, H, T, q, k, v, y, lse, gate, scale, tau, lam, stream,
-                                rope_cos, rope_sin);
+                                rope_cos, rope_sin, ws, ws_bytes);
   if (D == 80)
     return fwdbf16::run_fwd<80>(BH, H, T, q, k, v, y, lse, gate, scale, tau, lam, stream,
-                                rope_cos, rope_sin);
+                                rope_cos, rope_sin, ws, ws_bytes);
   return fwdbf16::run_fwd<64>(BH, H, T, q, k, v, y, lse, gate, scale, tau, lam, stream, rope_cos,
-                              rope_sin);
+                              rope_sin, ws, ws_bytes);
 }
 
 hipError_t launch_prefill_bf16(int B, int H, int D, int m, const uint16_t* q,
                                const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
                                uint16_t* v_cache, int capacity, const int* n_hist_dev, int n_hist,
                                uint16_t* y, float* lse, float* gate, float scale, float tau,
-                               float lam, hipStream_t stream) {
+                               float lam, hipStream_t stream, float* ws, size_t ws_bytes) {
   const int BH = B * H;
   if (D == 48)
     return fwdbf16::run_prefill<48>(BH, H, m, q, k_new, v_new, k_cache, v_cache, capacity,
-                                    n_hist_dev, n_hist, y, lse, gate, scale, tau, lam, stream);
+                                    n_hist_dev, n_hist, y, lse, gate, scale, tau, lam, stream, ws,
+                                    ws_bytes);
   if (D == 80)
     return fwdbf16::run_prefill<80>(BH, H, m, q, k_new, v_new, k_cache, v_cache, capacity,
-                                    n_hist_dev, n_hist, y, lse, gate, scale, tau, lam, stream);
+                                    n_hist_dev, n_hist, y, lse, gate, scale, tau, lam, stream, ws,
+                                    ws_bytes);
   return fwdbf16::run_prefill<64>(BH, H, m, q, k_new, v_new, k_cache, v_cache, capacity,
-                                  n_hist_dev, n_hist, y, lse, gate, scale, tau, lam, stream);
+                                  n_hist_dev, n_hist, y, lse, gate, scale, tau, lam, stream, ws,
+                                  ws_bytes);
 }
 
 }  // namespace rel

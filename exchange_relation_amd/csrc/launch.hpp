@@ -18,10 +18,14 @@ hipError_t launch_fwd_f32(int B, int H, int T, int D, const float* q, const floa
 // D in {48, 64, 80}. rope_cos / rope_sin ([T, D/2] fp32, or NULL; D = 64
 // only): RoPE of q fused into the Q fragment load (Multi-Head Relation; k and v come in already rotated /
 // mixed).
+// bf16 forward. ws (optional, fwd_bf16_workspace_bytes) lets a grid too
+// small to fill the chip split its long query blocks over keys.
+size_t fwd_bf16_workspace_bytes(int B, int H, int T, int D);
 hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale,
                            float tau, float lam, hipStream_t stream,
-                           const float* rope_cos = nullptr, const float* rope_sin = nullptr);
+                           const float* rope_cos = nullptr, const float* rope_sin = nullptr,
+                           float* ws = nullptr, size_t ws_bytes = 0);
 
 // Backward. Workspace layout and size are owned by the launcher.
 size_t bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
@@ -52,11 +56,12 @@ hipError_t launch_bwd80_kernel(int B, int H, int T, const uint16_t* q, const uin
 // slot n_b (n_hist_dev[b] on the device, or the uniform n_hist when NULL;
 // with the device array n_hist is their upper bound) and computes their rows
 // against cache rows 0 .. n_b + m - 1.
+size_t prefill_workspace_bytes(int B, int H, int D, int m, int n_hist, bool per_sequence);
 hipError_t launch_prefill_bf16(int B, int H, int D, int m, const uint16_t* q, const uint16_t* k_new,
                                const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache,
                                int capacity, const int* n_hist_dev, int n_hist, uint16_t* y,
                                float* lse, float* gate, float scale, float tau, float lam,
-                               hipStream_t stream);
+                               hipStream_t stream, float* ws = nullptr, size_t ws_bytes = 0);
 
 // Relation Cache decode (one step). dtype 0 = fp32, 1 = bf16. n_hist_dev
 // NULL: every sequence has n_hist slots of history; otherwise sequence b has

@@ -114,9 +114,16 @@ const char* relation_status_string(relation_status s) {
   return "unknown status";
 }
 
+size_t relation_fwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
+  if (dtype != REL_BF16 || check_dtype_dim(dtype, D) != REL_OK || check_shape(B, H, T, D) != REL_OK)
+    return 0;
+  return rel::fwd_bf16_workspace_bytes(B, H, T, D);
+}
+
 relation_status relation_fwd(relation_dtype dtype, int B, int H, int T, int D, const void* q,
                              const void* k, const void* v, void* y, float* lse, float* gate,
-                             float scale, float tau_s, float lambda, void* stream) {
+                             void* workspace, size_t workspace_bytes, float scale, float tau_s,
+                             float lambda, void* stream) {
   if (!q || !k || !v || !y) return REL_ERR_NULL;
   relation_status st = check_dtype_dim(dtype, D);
   if (st != REL_OK) return st;
@@ -125,6 +132,11 @@ relation_status relation_fwd(relation_dtype dtype, int B, int H, int T, int D, c
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
       (lse && !aligned4(lse)) || (gate && !aligned4(gate)))
     return REL_ERR_ALIGN;
+  if (workspace) {
+    if (workspace_bytes < relation_fwd_workspace_bytes(dtype, B, H, T, D))
+      return REL_ERR_WORKSPACE;
+    if (!aligned256(workspace)) return REL_ERR_ALIGN;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == REL_F32)
     return from_hip(rel::launch_fwd_f32(B, H, T, D, static_cast<const float*>(q),
@@ -134,7 +146,9 @@ relation_status relation_fwd(relation_dtype dtype, int B, int H, int T, int D, c
   return from_hip(rel::launch_fwd_bf16(B, H, T, D, static_cast<const uint16_t*>(q),
                                        static_cast<const uint16_t*>(k),
                                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(y),
-                                       lse, gate, scale, tau_s, lambda, s));
+                                       lse, gate, scale, tau_s, lambda, s, nullptr, nullptr,
+                                       static_cast<float*>(workspace),
+                                       workspace ? workspace_bytes : 0));
 }
 
 size_t relation_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
@@ -229,12 +243,20 @@ relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H,
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t relation_prefill_workspace_bytes(relation_dtype dtype, int B, int H, int D, int m,
+                                        int n_hist, int per_sequence) {
+  if (dtype != REL_BF16 || check_dtype_dim(dtype, D) != REL_OK) return 0;
+  if (B < 1 || H < 1 || m < 1 || n_hist < 0) return 0;
+  if (static_cast<long long>(B) * H * ((m + 31) / 32) > 0x7fffffffLL) return 0;
+  return rel::prefill_workspace_bytes(B, H, D, m, n_hist, per_sequence != 0);
+}
+
 relation_status relation_cache_prefill(relation_dtype dtype, int B, int H, int D, int m,
                                        const void* q, const void* k_new, const void* v_new,
                                        void* k_cache, void* v_cache, int capacity,
                                        const int* n_hist_dev, int n_hist, void* y, float* lse,
-                                       float* gate, float scale, float tau_s, float lambda,
-                                       void* stream) {
+                                       float* gate, void* workspace, size_t workspace_bytes,
+                                       float scale, float tau_s, float lambda, void* stream) {
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !y) return REL_ERR_NULL;
   if (dtype != REL_BF16 || check_dtype_dim(dtype, D) != REL_OK) return REL_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || m < 1 || capacity < 1) return REL_ERR_SHAPE;
@@ -247,11 +269,18 @@ relation_status relation_cache_prefill(relation_dtype dtype, int B, int H, int D
       !aligned16(v_cache) || !aligned16(y) || (lse && !aligned4(lse)) ||
       (gate && !aligned4(gate)) || (n_hist_dev && !aligned4(n_hist_dev)))
     return REL_ERR_ALIGN;
+  if (workspace) {
+    if (workspace_bytes <
+        relation_prefill_workspace_bytes(dtype, B, H, D, m, n_hist, n_hist_dev != nullptr))
+      return REL_ERR_WORKSPACE;
+    if (!aligned256(workspace)) return REL_ERR_ALIGN;
+  }
   return from_hip(rel::launch_prefill_bf16(
       B, H, D, m, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
       static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache),
       static_cast<uint16_t*>(v_cache), capacity, n_hist_dev, n_hist, static_cast<uint16_t*>(y),
-      lse, gate, scale, tau_s, lambda, static_cast<hipStream_t>(stream)));
+      lse, gate, scale, tau_s, lambda, static_cast<hipStream_t>(stream),
+      static_cast<float*>(workspace), workspace ? workspace_bytes : 0));
 }
 
 size_t relation_mhr_fwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {

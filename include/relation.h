@@ -77,12 +77,26 @@ typedef enum { REL_F32 = 0, REL_BF16 = 1 } relation_dtype;
  *   lse     : out [B, H, T] float32, LSE_i = ln Z_i; NULL to skip. Needed by
  *             relation_bwd.
  *   gate    : out [B, H, T] float32, the Exchange mass g_i; NULL to skip.
+ *   workspace, workspace_bytes : optional DEVICE scratch, 256-byte aligned,
+ *             of at least relation_fwd_workspace_bytes(...) bytes, owned by
+ *             the caller and free again when the stream has passed the call.
+ *             With it, a grid too small to fill the GPU splits its long
+ *             query blocks over the keys and merges the pieces' (m, l, z)
+ *             in a second kernel by App. A.3.2's rule (the same result up to
+ *             fp32 rounding order). NULL: one workgroup per query block.
+ *             Non-NULL and too small -> REL_ERR_WORKSPACE; misaligned ->
+ *             REL_ERR_ALIGN.
  */
 relation_status relation_fwd(relation_dtype dtype, int B, int H, int T, int D,
                              const void* q, const void* k, const void* v,
                              void* y, float* lse, float* gate,
+                             void* workspace, size_t workspace_bytes,
                              float scale, float tau_s, float lambda,
                              void* stream);
+
+/* Workspace bytes relation_fwd can use at this shape: 0 when the grid is
+ * large enough on its own (and for REL_F32 or an invalid shape). */
+size_t relation_fwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D);
 
 /*
  * relation_bwd — gradients of a scalar loss L through relation_fwd, by
@@ -187,14 +201,26 @@ relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H,
  *   n_hist           : 0 <= n_hist and n_hist + m <= capacity, else
  *                      REL_ERR_CAPACITY.
  *   y                : out [B, H, m, D]; lse, gate: out [B, H, m] fp32 or NULL
+ *   workspace, workspace_bytes : optional DEVICE scratch as for relation_fwd,
+ *                      of relation_prefill_workspace_bytes(...) bytes for the
+ *                      same (B, H, D, m, n_hist) and per_sequence =
+ *                      (n_hist_dev != NULL): splits the rows' long histories
+ *                      over several workgroups. NULL: no split.
  */
 relation_status relation_cache_prefill(relation_dtype dtype, int B, int H, int D, int m,
                                        const void* q, const void* k_new, const void* v_new,
                                        void* k_cache, void* v_cache, int capacity,
                                        const int* n_hist_dev, int n_hist,
                                        void* y, float* lse, float* gate,
+                                       void* workspace, size_t workspace_bytes,
                                        float scale, float tau_s, float lambda,
                                        void* stream);
+
+/* Workspace bytes relation_cache_prefill can use; 0 when it would not split
+ * (or the arguments are invalid). The split assumes per-sequence lengths
+ * spread over [0, n_hist] when per_sequence is non-zero. */
+size_t relation_prefill_workspace_bytes(relation_dtype dtype, int B, int H, int D, int m,
+                                        int n_hist, int per_sequence);
 
 /*
  * relation_mhr_fwd / relation_mhr_bwd — Multi-Head Relation with the two maps

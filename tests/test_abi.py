@@ -53,8 +53,27 @@ def test_status_strings_and_version(lib):
 
 
 def fwd(lib, dtype=BF16, B=1, H=1, T=8, D=64, q=P, k=P, v=P, y=P, lse=NUL, gate=NUL,
-        scale=0.125, tau=2.0, lam=0.5):
-    return lib.relation_fwd(dtype, B, H, T, D, q, k, v, y, lse, gate, scale, tau, lam, None)
+        scale=0.125, tau=2.0, lam=0.5, ws=NUL, wsb=0):
+    return lib.relation_fwd(dtype, B, H, T, D, q, k, v, y, lse, gate, ws, wsb, scale, tau, lam,
+                            None)
+
+
+def test_fwd_split_workspace(lib):
+    # a grid that fills the GPU on its own (30M layer) needs none, nor one
+    # whose blocks have under 17 historical tiles (the 10M layer: pieces of
+    # at least 16 tiles); 4 heads of 8192 tokens split: 64 blocks per head,
+    # pieces of 16 tiles, up to 8 per block (126 historical tiles), 128 rows
+    # x (64 + 4) fp32 per piece and block
+    assert lib.relation_fwd_workspace_bytes(BF16, 16, 8, 2048, 64) == 0
+    assert lib.relation_fwd_workspace_bytes(BF16, 8, 8, 1024, 64) == 0
+    need = lib.relation_fwd_workspace_bytes(BF16, 1, 4, 8192, 64)
+    assert need == 4 * 64 * 8 * 128 * 68 * 4
+    assert lib.relation_fwd_workspace_bytes(F32, 1, 4, 8192, 64) == 0
+    assert lib.relation_fwd_workspace_bytes(BF16, 1, 4, 8192, 96) == 0
+    assert lib.relation_fwd_workspace_bytes(BF16, 0, 4, 8192, 64) == 0
+    assert lib.relation_fwd_workspace_bytes(BF16, 1, 2, 300, 64) == 0
+    assert fwd(lib, B=1, H=4, T=8192, ws=P, wsb=need - 1) == REL_ERR_WORKSPACE
+    assert fwd(lib, B=1, H=4, T=8192, ws=P_MIS, wsb=need) == REL_ERR_ALIGN
 
 
 def test_fwd_validation(lib):
@@ -135,7 +154,23 @@ def test_decode_ragged_validation(lib):
 def test_prefill_validation(lib):
     def pf(m=16, n=10, cap=64, dtype=BF16, D=64, q=P, nh=NUL):
         return lib.relation_cache_prefill(dtype, 2, 3, D, m, q, P, P, P, P, cap, nh, n, P, NUL,
-                                          NUL, 0.125, 2.0, 0.3, None)
+                                          NUL, ws, wsb, 0.125, 2.0, 0.3, None)
+
+    ws, wsb = NUL, 0
+    # the ragged-history workload (32 x 12 heads, 256 new tokens, bound 4096)
+    # splits; a short history does not
+    big = lib.relation_prefill_workspace_bytes(BF16, 32, 12, 64, 256, 4096, 1)
+    assert big > 0 and big % (128 * 68 * 4) == 0
+    assert lib.relation_prefill_workspace_bytes(BF16, 2, 3, 64, 16, 10, 0) == 0
+    assert lib.relation_prefill_workspace_bytes(F32, 32, 12, 64, 256, 4096, 1) == 0
+    assert lib.relation_prefill_workspace_bytes(BF16, 32, 12, 64, 256, -1, 1) == 0
+    need = lib.relation_prefill_workspace_bytes(BF16, 2, 3, 64, 16, 3000, 0)
+    assert need > 0
+    ws, wsb = P, need - 1
+    assert pf(n=3000, cap=4096) == REL_ERR_WORKSPACE
+    ws, wsb = P_MIS, need
+    assert pf(n=3000, cap=4096) == REL_ERR_ALIGN
+    ws, wsb = NUL, 0
 
     assert pf(n=49) == REL_ERR_CAPACITY   # 49 + 16 > 64
     assert pf(n=-1) == REL_ERR_CAPACITY

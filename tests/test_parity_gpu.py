@@ -156,6 +156,48 @@ def test_fwd_bf16_large_scores_rescale():
     check("y", f64(y), Y, "bf16")
 
 
+def close_to_unsplit(name, a, b, vmax):
+    """Split and unsplit runs round every P = exp(E - m) to bf16 against their
+    own stabiliser m (each piece has its own), so single terms differ by up to
+    2^-9 relative and the rows by at most 2^-8 max|v| (y, plus one bf16 unit
+    in the last place of the output) and 2^-8 (lse, gate)."""
+    a, b = a.float(), b.float()
+    d = (a - b).abs()
+    frac = float((d > 0).float().mean())
+    print(f"  {name}: max diff {d.max().item():.3e}, differing {frac:.2e}")
+    if name == "y":
+        bound = 2.0 ** -8 * vmax + torch.clamp(b.abs(), min=2.0 ** -126) * 2.0 ** -7
+    else:
+        bound = torch.full_like(b, 2.0 ** -8)
+    assert bool((d <= bound).all()), name
+    assert frac < 0.05, name
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 2, 1300), (1, 1, 2500), (2, 1, 1800)])
+def test_fwd_bf16_split_over_keys(B, H, T):
+    """A grid too small to fill the GPU splits its long query blocks over the
+    keys; the pieces are merged by App. A.3.2's rule in a second kernel."""
+    assert rel.relation_fwd_workspace_bytes(torch.bfloat16, B, H, T, 64) > 0
+    inp = make_inputs(B, H, T, 64, "bf16", seed=700 + T)
+    scale = 1 / 8
+    y, lse, gate = run_fwd(inp, "bf16", scale)
+    Y, L, G = oracle.relation_forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), scale, 2.0,
+                                      inp["lam"])
+    check("y", f64(y), Y, "bf16")
+    check("lse", f64(lse), L, "bf16")
+    check("gate", f64(gate), G, "bf16")
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    y1, l1, g1 = rel.relation_fwd(q, k, v, lam=inp["lam"], scale=scale, want_gate=True,
+                                  split=False)
+    y2, l2, g2 = run_fwd(inp, "bf16", scale)
+    torch.cuda.synchronize()
+    vmax = float(inp["v"].float().abs().max())
+    close_to_unsplit("y", y, y1, vmax)
+    close_to_unsplit("lse", lse, l1, vmax)
+    close_to_unsplit("gate", gate, g1, vmax)
+    assert torch.equal(y, y2) and torch.equal(lse, l2) and torch.equal(gate, g2)  # deterministic
+
+
 @pytest.mark.parametrize("key,heads", [
     ("layer10m_fwd_bf16", "all"),
     ("layer30m_fwdbwd_bf16", [(0, 0), (3, 5), (9, 2), (15, 7)]),

@@ -39,12 +39,13 @@ def prefill_inputs(B, H, D, m, cap, seed):
     return d, new
 
 
-def run(d, new, n, bound=None):
+def run(d, new, n, bound=None, split=True):
     kc, vc = d["k_cache"].to(DEV), d["v_cache"].to(DEV)
     nh = torch.tensor(n, dtype=torch.int32, device=DEV) if isinstance(n, list) else n
     y, lse, g = rel.relation_cache_prefill(new["q"].to(DEV), new["k_new"].to(DEV),
                                            new["v_new"].to(DEV), kc, vc, nh, max_n_hist=bound,
-                                           lam=d["lam"], scale=1 / 8, want_stats=True)
+                                           lam=d["lam"], scale=1 / 8, want_stats=True,
+                                           split=split)
     torch.cuda.synchronize()
     return y.cpu(), lse.cpu(), g.cpu(), kc.cpu(), vc.cpu()
 
@@ -77,6 +78,34 @@ def test_prefill_ragged_vs_oracle():
     check("y", f64(y), Y)
     check("lse", f64(lse), L)
     assert np.array_equal(f64(kc), KC) and np.array_equal(f64(vc), VC)
+
+
+@pytest.mark.parametrize("ns,bound", [([0, 1, 33, 900, 1700, 2200], 2200), ([2200] * 6, None)])
+def test_prefill_split_over_keys_matches_unsplit(ns, bound):
+    """Long histories split over several workgroups (merged by App. A.3.2's
+    rule) give the unsplit rows up to the bf16 rounding of P = exp(E - m),
+    which each piece takes against its own stabiliser m: y within 2^-8 max|v|
+    plus one bf16 unit in the last place, lse and gate within 2^-8; the
+    cache bit for bit."""
+    B, H, D, m, cap = 6, 2, 64, 100, 2400
+    per_seq = bound is not None
+    n = max(ns) if per_seq else ns[0]
+    assert rel.relation_prefill_workspace_bytes(torch.bfloat16, B, H, D, m, n, per_seq) > 0
+    d, new = prefill_inputs(B, H, D, m, cap, seed=933)
+    arg = ns if per_seq else ns[0]
+    y, lse, g, kc, vc = run(d, new, arg, bound=bound)
+    y1, l1, g1, kc1, vc1 = run(d, new, arg, bound=bound, split=False)
+    vmax = max(float(d["v_cache"].float().abs().max()), float(new["v_new"].float().abs().max()))
+    d_y = (y.float() - y1.float()).abs()
+    bound = 2.0 ** -8 * vmax + torch.clamp(y1.float().abs(), min=2.0 ** -126) * 2.0 ** -7
+    print(f"  y: max diff {d_y.max().item():.3e}, differing {(d_y > 0).float().mean().item():.2e}")
+    assert bool((d_y <= bound).all()) and float((d_y > 0).float().mean()) < 0.05
+    assert bool(((lse - l1).abs() <= 2.0 ** -8).all())
+    assert bool(((g - g1).abs() <= 2.0 ** -8).all())
+    assert torch.equal(kc, kc1) and torch.equal(vc, vc1)
+    Y, L, G, _, _ = oracle_rows(d, new, ns)
+    check("y", f64(y), Y)
+    check("lse", f64(lse), L)
 
 
 def test_prefill_ragged_out_of_range_nan_and_no_write():
