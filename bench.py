@@ -333,13 +333,16 @@ def bench_linear(rel, torch, dev, reps, B=32, H=8, T=1024, D=64, seed=42):
     y = torch.empty_like(I)
     stream = torch.cuda.current_stream(dev)
     tf = EventTimer(torch, stream)
-    warm = 100  # a few ms of work: the clocks ramp under sustained load
-    for i in range(reps + warm):
-        s0 = tf.start() if i >= warm else None
+    for _ in range(100):  # a few ms of work: the clocks ramp under sustained load
         rel.relation_linear_fwd(p1, p2, I, g, cs, sn, scale=1 / math.sqrt(D), y=y)
-        if i >= warm:
-            tf.stop(s0)
-    fm = tf.mean_ms()
+    torch.cuda.synchronize()
+    # back-to-back calls between one pair of events (a ~65 us call would
+    # otherwise also time the host's launch path)
+    s0 = tf.start()
+    for _ in range(reps):
+        rel.relation_linear_fwd(p1, p2, I, g, cs, sn, scale=1 / math.sqrt(D), y=y)
+    tf.stop(s0)
+    fm = tf.mean_ms() / reps
     nbytes = 12 * D * B * H * T
     # backward: reads p1, p2, I, dY (bf16) and g, writes dp1, dp2, dI (bf16)
     # and dg: 22 D bytes per token and head (the state pass is overhead)
@@ -348,12 +351,15 @@ def bench_linear(rel, torch, dev, reps, B=32, H=8, T=1024, D=64, seed=42):
     ws = torch.empty((lib.relation_linear_bwd_workspace_bytes(1, B, H, T, D),), device=dev,
                      dtype=torch.uint8)
     tb = EventTimer(torch, stream)
-    for i in range(reps // 2 + 20):
-        s0 = tb.start() if i >= 20 else None
+    for _ in range(20):
         rel.relation_linear_bwd(p1, p2, I, g, dy, cs, sn, scale=1 / math.sqrt(D), workspace=ws)
-        if i >= 20:
-            tb.stop(s0)
-    bm = tb.mean_ms()
+    torch.cuda.synchronize()
+    nb = max(1, reps // 2)
+    s0 = tb.start()
+    for _ in range(nb):
+        rel.relation_linear_bwd(p1, p2, I, g, dy, cs, sn, scale=1 / math.sqrt(D), workspace=ws)
+    tb.stop(s0)
+    bm = tb.mean_ms() / nb
     bbytes = 22 * D * B * H * T
     return {"workload": f"linear relation fwd + bwd, RoPE, B={B} H={H} T={T} D={D}",
             "fwd_ms": fm, "tokens_per_s": B * T / (fm * 1e-3),
@@ -375,12 +381,16 @@ def bench_linear_step(rel, torch, dev, reps=200, B=32, H=12, D=64, seed=42):
     y = torch.empty_like(I)
     stream = torch.cuda.current_stream(dev)
     t = EventTimer(torch, stream)
-    for i in range(reps + 10):
-        s0 = t.start() if i >= 10 else None
+    for _ in range(10):
         rel.relation_linear_step(p1, p2, I, g, state, scale=1 / math.sqrt(D), y=y)
-        if i >= 10:
-            t.stop(s0)
-    ms = t.mean_ms()
+    torch.cuda.synchronize()
+    # back-to-back steps (each reads and rewrites the state) between one pair
+    # of events: a single ~5 us step is far shorter than the host's launch path
+    s0 = t.start()
+    for _ in range(reps):
+        rel.relation_linear_step(p1, p2, I, g, state, scale=1 / math.sqrt(D), y=y)
+    t.stop(s0)
+    ms = t.mean_ms() / reps
     nbytes = (8 * D * D + 10 * D) * B * H
     return {"workload": f"linear relation decode step, B={B} H={H} D={D}", "ms": ms,
             "GBps": nbytes / (ms * 1e-3) / 1e9}
