@@ -85,7 +85,8 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
     const float* __restrict__ lse, const float* __restrict__ Dr, float* __restrict__ dq_acc,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int T, int BH, float kscale,
-    float scale, float inv_tau, float lam, float* __restrict__ dk32, float* __restrict__ dv32) {
+    float scale, float inv_tau, float lam, float* __restrict__ dk32, float* __restrict__ dv32,
+    const float* __restrict__ rc, const float* __restrict__ rs) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -394,7 +395,42 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
   // ---- dK = scale * dK^T^T, dV = dV^T^T (key kj, d rows of the accumulators)
   if (kj >= T) return;
   const size_t row = base + static_cast<size_t>(kj) * DR;
-  if (dk32) {  // fp32 results for a later pass (Multi-Head Relation's transposes)
+  if (dv32) {  // Multi-Head Relation: dV in fp32 for the Givens transpose pass
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + g4 * 8 + hf * 4;
+        if (d0 >= DR) continue;
+        const f32x16& va = db == 0 ? dv0 : dv1;
+        *reinterpret_cast<f32x4*>(dv32 + row + d0) =
+            f32x4{va[g4 * 4], va[g4 * 4 + 1], va[g4 * 4 + 2], va[g4 * 4 + 3]};
+      }
+    }
+    if constexpr (DR == 64) if (rc) {
+      // dp2 = RoPE^T(scale dK) of this key's position: the rotate-half pairs
+      // (d, d + 32) sit in dk0 / dk1 of one lane. The same fp32 operations as
+      // the separate transpose pass, rounded once.
+      const size_t tr = static_cast<size_t>(kj) * (DR / 2);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = g4 * 8 + hf * 4;
+        const f32x4 c = *reinterpret_cast<const f32x4*>(rc + tr + d0);
+        const f32x4 sn = *reinterpret_cast<const f32x4*>(rs + tr + d0);
+        float lo[4], hi[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = dk0[g4 * 4 + e] * scale, b2 = dk1[g4 * 4 + e] * scale;
+          lo[e] = fmaf(a, c[e], b2 * sn[e]);
+          hi[e] = fmaf(-a, sn[e], b2 * c[e]);
+        }
+        *reinterpret_cast<uint2*>(dk + row + d0) =
+            make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+        *reinterpret_cast<uint2*>(dk + row + d0 + 32) =
+            make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
+      }
+      return;
+    }
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -402,12 +438,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
         const int d0 = db * 32 + g4 * 8 + hf * 4;
         if (d0 >= DR) continue;
         const f32x16& ka = db == 0 ? dk0 : dk1;
-        const f32x16& va = db == 0 ? dv0 : dv1;
         *reinterpret_cast<f32x4*>(dk32 + row + d0) =
             f32x4{ka[g4 * 4] * scale, ka[g4 * 4 + 1] * scale, ka[g4 * 4 + 2] * scale,
                   ka[g4 * 4 + 3] * scale};
-        *reinterpret_cast<f32x4*>(dv32 + row + d0) =
-            f32x4{va[g4 * 4], va[g4 * 4 + 1], va[g4 * 4 + 2], va[g4 * 4 + 3]};
       }
     }
     return;
@@ -444,6 +477,7 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float4* __restri
   if (blockIdx.x == 0 && dlambda) {
     __shared__ float red[256];
     float s = 0.f;
+#pragma unroll 8
     for (int i = threadIdx.x; i < npart; i += 256) s += part[i];
     red[threadIdx.x] = s;
     __syncthreads();
@@ -461,7 +495,8 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                            const uint16_t* v, const uint16_t* y, const uint16_t* dy,
                            const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                            float* dlambda, void* ws, float scale, float tau, float lam,
-                           hipStream_t stream, float* dk32, float* dv32) {
+                           hipStream_t stream, float* dk32, float* dv32, const float* rope_cos,
+                           const float* rope_sin) {
   using namespace bwdbf16;
   const BwdWorkspace w = bwd_workspace_layout(1, B, H, T, D);
   char* wsb = static_cast<char*>(ws);
@@ -481,20 +516,20 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
     if (D == 48)
       hipLaunchKernelGGL(bwd_bf16_kernel<48>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
                          stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e,
-                         scale, 1.0f / tau, lam, dk32, dv32);
+                         scale, 1.0f / tau, lam, dk32, dv32, nullptr, nullptr);
     else
       hipLaunchKernelGGL(bwd_bf16_kernel<64>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
                          stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e,
-                         scale, 1.0f / tau, lam, dk32, dv32);
+                         scale, 1.0f / tau, lam, dk32, dv32, rope_cos, rope_sin);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  // with fp32 results requested, dq stays in the accumulator (the caller
-  // scales it) and only the dL/dlambda reduction runs
-  hipLaunchKernelGGL(dq_finalize_kernel, dim3(dk32 ? 1u : eg), dim3(256), 0, stream,
-                     reinterpret_cast<const float4*>(dq_acc), reinterpret_cast<uint2*>(dq),
-                     dk32 ? size_t{0} : n4, scale,
-                     reinterpret_cast<const float*>(wsb + w.off_part), w.npart, dlambda);
+  // with fp32 results requested (dv32), dq stays in the accumulator and the
+  // caller's transpose pass scales it and reduces the dL/dlambda partials
+  if (dv32) return hipSuccess;
+  hipLaunchKernelGGL(dq_finalize_kernel, dim3(eg), dim3(256), 0, stream,
+                     reinterpret_cast<const float4*>(dq_acc), reinterpret_cast<uint2*>(dq), n4,
+                     scale, reinterpret_cast<const float*>(wsb + w.off_part), w.npart, dlambda);
   return hipGetLastError();
 }
 

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256) void bwd_dlambda_kernel(const float* __restric
                                                           float* __restrict__ out) {
   __shared__ float red[256];
   float s = 0.f;
+#pragma unroll 8
   for (int i = threadIdx.x; i < n; i += 256) s += part[i];
   red[threadIdx.x] = s;
   __syncthreads();

@@ -42,7 +42,8 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                            const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                            float* dlambda, void* ws, float scale, float tau, float lam,
                            hipStream_t stream, float* dk32 = nullptr,
-                           float* dv32 = nullptr);
+                           float* dv32 = nullptr, const float* rope_cos = nullptr,
+                           const float* rope_sin = nullptr);
 
 // The D = 80 backward kernel (bwd80.hip), after the shared preprocess; dq
 // accumulates into dq_acc (fp32, unscaled) as for the other widths.
@@ -82,11 +83,15 @@ hipError_t launch_mhr_prepare(int dtype, int B, int H, int T, int D, const void*
                               const void* p2, const void* vi, void* q, void* k, void* v,
                               const float* rope_cos, const float* rope_sin, const float* theta,
                               int pairing, hipStream_t stream);
+// dk NULL: dp2 is already written (the bf16 backward's fused RoPE^T).
+// dl_part (npart values, or NULL): the backward's dL/dlambda partials, summed
+// in a fixed order into *dlambda by the dq transpose pass.
 hipError_t launch_mhr_post(int dtype, int B, int H, int T, int D, const float* dq, float dq_scale,
                            const float* dk, const float* dv, const void* vmix, void* dp1,
                            void* dp2, void* dI, float* dtheta, float* part,
                            const float* rope_cos, const float* rope_sin, const float* theta,
-                           int pairing, hipStream_t stream);
+                           int pairing, hipStream_t stream, const float* dl_part = nullptr,
+                           int dl_npart = 0, float* dlambda = nullptr);
 
 // Linear Relation (linear.hip), bf16, D = 64. g = log retention (fp32, same
 // shape as p1). rope tables [T, D/2] or NULL; state_in / state_out [B, H, D, D]

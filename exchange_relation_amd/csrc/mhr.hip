@@ -143,7 +143,22 @@ __global__ __launch_bounds__(256) void prepare_kernel(const TE* __restrict__ p1,
 template <typename TE, int D>
 __global__ __launch_bounds__(256) void unrotate_kernel(const float* g, TE* dp, size_t rows, int T,
                                                        float scale, const float* __restrict__ cs,
-                                                       const float* __restrict__ sn) {
+                                                       const float* __restrict__ sn,
+                                                       const float* __restrict__ dl_part,
+                                                       int dl_npart, float* __restrict__ dlambda) {
+  if (blockIdx.x == 0 && dlambda) {  // dL/dlambda: fixed-order sum of the partials
+    __shared__ float red[256];
+    float s = 0.f;
+#pragma unroll 8
+    for (int i = threadIdx.x; i < dl_npart; i += 256) s += dl_part[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) *dlambda = red[0];
+  }
   const Slot sl = slot_of<D>(rows);
   if (!sl.ok) return;
   const int t = static_cast<int>(sl.row % T);
@@ -248,20 +263,26 @@ hipError_t run_prepare(int B, int H, int T, const void* p1, const void* p2, cons
 template <typename TE, int D>
 hipError_t run_post(int B, int H, int T, const float* dq, float dq_scale, const float* dk,
                     const float* dv, const void* vmix, void* dp1, void* dp2, void* dI,
-                    float* dtheta, float* part, const Mhr& mh, hipStream_t stream) {
+                    float* dtheta, float* part, const Mhr& mh, hipStream_t stream,
+                    const float* dl_part, int dl_npart, float* dlambda) {
   const size_t rows = static_cast<size_t>(B) * H * T;
   const unsigned nb = static_cast<unsigned>((rows * (D / 16) + 255) / 256);
   hipLaunchKernelGGL((unrotate_kernel<TE, D>), dim3(nb), dim3(256), 0, stream, dq,
-                     static_cast<TE*>(dp1), rows, T, dq_scale, mh.cos, mh.sin);
+                     static_cast<TE*>(dp1), rows, T, dq_scale, mh.cos, mh.sin, dl_part, dl_npart,
+                     dl_part ? dlambda : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((unrotate_kernel<TE, D>), dim3(nb), dim3(256), 0, stream, dk,
-                     static_cast<TE*>(dp2), rows, T, 1.0f, mh.cos, mh.sin);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (dk) {  // else the backward wrote dp2 itself
+    hipLaunchKernelGGL((unrotate_kernel<TE, D>), dim3(nb), dim3(256), 0, stream, dk,
+                       static_cast<TE*>(dp2), rows, T, 1.0f, mh.cos, mh.sin, nullptr, 0,
+                       nullptr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (mh.theta == nullptr) {  // no mixing: dI = dv (a plain copy / rounding)
     hipLaunchKernelGGL((unrotate_kernel<TE, D>), dim3(nb), dim3(256), 0, stream, dv,
-                       static_cast<TE*>(dI), rows, T, 1.0f, nullptr, nullptr);
+                       static_cast<TE*>(dI), rows, T, 1.0f, nullptr, nullptr, nullptr, 0,
+                       nullptr);
     return hipGetLastError();
   }
   const unsigned nx = static_cast<unsigned>((static_cast<size_t>(T) * (D / 16) + 255) / 256);
@@ -303,22 +324,23 @@ hipError_t launch_mhr_post(int dtype, int B, int H, int T, int D, const float* d
                            const float* dk, const float* dv, const void* vmix, void* dp1,
                            void* dp2, void* dI, float* dtheta, float* part,
                            const float* rope_cos, const float* rope_sin, const float* theta,
-                           int pairing, hipStream_t stream) {
+                           int pairing, hipStream_t stream, const float* dl_part, int dl_npart,
+                           float* dlambda) {
   const Mhr mh{rope_cos, rope_sin, theta, pairing, H};
   if (dtype == 1 && D == 80)
     return mhr::run_post<uint16_t, 80>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta,
-                                       part, mh, stream);
+                                       part, mh, stream, dl_part, dl_npart, dlambda);
   if (dtype == 1 && D == 48)
     return mhr::run_post<uint16_t, 48>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta,
-                                       part, mh, stream);
+                                       part, mh, stream, dl_part, dl_npart, dlambda);
   if (dtype == 1)
     return mhr::run_post<uint16_t, 64>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta,
-                                       part, mh, stream);
+                                       part, mh, stream, dl_part, dl_npart, dlambda);
   if (D == 64)
     return mhr::run_post<float, 64>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta,
-                                    part, mh, stream);
+                                    part, mh, stream, dl_part, dl_npart, dlambda);
   return mhr::run_post<float, 32>(B, H, T, dq, dq_scale, dk, dv, vmix, dp1, dp2, dI, dtheta, part,
-                                  mh, stream);
+                                  mh, stream, dl_part, dl_npart, dlambda);
 }
 
 }  // namespace rel

@@ -385,19 +385,26 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                                          static_cast<const float*>(dI), v, dp1, dp2, dI, dth,
                                          part, rope_cos, rope_sin, th, pairing, s));
   }
-  float* dk32 = reinterpret_cast<float*>(w + L.dk32);
+  // At D = 64 the backward applies RoPE^T to dK itself and writes dp2; dV
+  // (Givens pairs span two heads) and dQ (an accumulator until the end) stay
+  // fp32 for the transpose passes, which also reduce dL/dlambda.
+  const bool fuse_dk = D == 64 && rope_cos != nullptr;
+  float* dk32 = fuse_dk ? nullptr : reinterpret_cast<float*>(w + L.dk32);
   float* dv32 = reinterpret_cast<float*>(w + L.dv32);
   if (rel::launch_bwd_bf16(B, H, T, D, static_cast<const uint16_t*>(q),
                            static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                            static_cast<const uint16_t*>(y), static_cast<const uint16_t*>(dy), lse,
                            static_cast<uint16_t*>(dp1), static_cast<uint16_t*>(dp2),
                            static_cast<uint16_t*>(dI), dlambda, w + L.bwd, scale, tau_s, lambda,
-                           s, dk32, dv32) != hipSuccess)
+                           s, dk32, dv32, fuse_dk ? rope_cos : nullptr,
+                           fuse_dk ? rope_sin : nullptr) != hipSuccess)
     return REL_ERR_HIP;
-  const float* dq_acc =
-      reinterpret_cast<const float*>(w + L.bwd + rel::bwd_workspace_layout(1, B, H, T, D).off_dq);
+  const rel::BwdWorkspace bl = rel::bwd_workspace_layout(1, B, H, T, D);
+  const float* dq_acc = reinterpret_cast<const float*>(w + L.bwd + bl.off_dq);
+  const float* dl_part = reinterpret_cast<const float*>(w + L.bwd + bl.off_part);
   return from_hip(rel::launch_mhr_post(1, B, H, T, D, dq_acc, scale, dk32, dv32, v, dp1, dp2, dI,
-                                       dth, part, rope_cos, rope_sin, th, pairing, s));
+                                       dth, part, rope_cos, rope_sin, th, pairing, s,
+                                       dlambda ? dl_part : nullptr, bl.npart, dlambda));
 }
 
 relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, int D,
