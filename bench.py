@@ -288,7 +288,9 @@ def bench_mhr(rel, torch, dev, reps, B=16, H=8, T=2048, D=64, seed=42):
     """Multi-Head Relation with its upstream maps (RoPE of p1 / p2 from
     [T, D/2] tables, Givens mixing of I, pairing M_B) on the 30M layer shape:
     forward and forward+backward, next to the plain operator on the same
-    tensors. Flops are the operator's (the maps are O(T D) per head)."""
+    tensors. Flops are the operator's (the maps are O(T D) per head). The
+    backward reads the forward's rotated keys and mixed values from its
+    workspace, as a training step that keeps the forward's buffers does."""
     from workloads import make_inputs, make_mhr_maps
     inp = make_inputs(B, H, T, D, "bf16", seed=seed, with_dy=True)
     p1, p2, I, dy = (inp[n].to(dev) for n in ("q", "k", "v", "dy"))
@@ -311,12 +313,13 @@ def bench_mhr(rel, torch, dev, reps, B=16, H=8, T=2048, D=64, seed=42):
             tf.stop(s0)
         s1 = tb.start() if i >= 3 else None
         rel.relation_mhr_bwd(p1, p2, I, y, dy, lse, cs, sn, th, 1, lam=lam, scale=scale,
-                             workspace=wsb)
+                             workspace=wsb, fwd_workspace=wsf)
         if i >= 3:
             tb.stop(s1)
     f = fwd_flops(B, H, T, D)
     fm, bm = tf.mean_ms(), tb.mean_ms()
-    return {"workload": "layer30m MHR (RoPE + Givens M_B)", "fwd_ms": fm, "bwd_ms": bm,
+    return {"workload": "layer30m MHR (RoPE + Givens M_B), backward reusing the forward's maps",
+            "fwd_ms": fm, "bwd_ms": bm,
             "fwd_tflops": f / (fm * 1e-3) / 1e12,
             "fwdbwd_tflops": 3.5 * f / ((fm + bm) * 1e-3) / 1e12}
 

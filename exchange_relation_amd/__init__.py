@@ -123,8 +123,8 @@ def load_library():
     lib.relation_mhr_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_mhr_bwd.restype = c_int
     lib.relation_mhr_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
-                                     c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size, c_float,
-                                     c_float, c_float, vp]
+                                     c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size,
+                                     c_float, c_float, c_float, vp]
     lib.relation_linear_fwd.restype = c_int
     lib.relation_linear_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, c_float, c_float, vp]
@@ -443,9 +443,11 @@ def relation_mhr_fwd(p1, p2, I, rope_cos=None, rope_sin=None, theta=None, pairin
 
 def relation_mhr_bwd(p1, p2, I, y, dy, lse, rope_cos=None, rope_sin=None, theta=None, pairing=0,
                      lam=0.0, scale=None, tau_s=2.0, dp1=None, dp2=None, dI=None, dlambda=None,
-                     dtheta=None, workspace=None, stream=None):
+                     dtheta=None, workspace=None, fwd_workspace=None, stream=None):
     """Gradients of relation_mhr_fwd. Returns (dp1, dp2, dI, dlambda [1],
-    dtheta [H/2] or None)."""
+    dtheta [H/2] or None). fwd_workspace: the workspace tensor the forward
+    used (unchanged since), whose rotated keys and mixed values are then
+    reused instead of formed again."""
     lib = load_library()
     B, H, T, D = p1.shape
     dev, dt = p1.device, p1.dtype
@@ -466,7 +468,7 @@ def relation_mhr_bwd(p1, p2, I, y, dy, lse, rope_cos=None, rope_sin=None, theta=
     st = lib.relation_mhr_bwd(code, B, H, T, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(rope_cos),
                               _ptr(rope_sin), _ptr(theta), int(pairing), _ptr(y), _ptr(dy),
                               _ptr(lse), _ptr(dp1), _ptr(dp2), _ptr(dI), _ptr(dlambda),
-                              _ptr(dtheta), _ptr(workspace),
+                              _ptr(dtheta), _ptr(fwd_workspace), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _scale(D, scale),
                               float(tau_s), float(lam), _stream(dev, stream))
     if st != 0:

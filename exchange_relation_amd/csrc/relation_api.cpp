@@ -340,8 +340,9 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                                  const float* rope_sin, const float* theta, int pairing,
                                  const void* y, const void* dy, const float* lse, void* dp1,
                                  void* dp2, void* dI, float* dlambda, float* dtheta,
-                                 void* workspace, size_t workspace_bytes, float scale,
-                                 float tau_s, float lambda, void* stream) {
+                                 const void* fwd_workspace, void* workspace,
+                                 size_t workspace_bytes, float scale, float tau_s, float lambda,
+                                 void* stream) {
   if (!p1 || !p2 || !I || !y || !dy || !lse || !dp1 || !dp2 || !dI) return REL_ERR_NULL;
   relation_status st = check_dtype_dim_bwd(dtype, D);
   if (st != REL_OK) return st;
@@ -354,18 +355,28 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
     return REL_ERR_ALIGN;
   const MhrLayout L = mhr_layout(true, dtype, B, H, T, D);
   if (!workspace || workspace_bytes < L.total) return REL_ERR_WORKSPACE;
-  if (!aligned256(workspace)) return REL_ERR_ALIGN;
+  if (!aligned256(workspace) || (fwd_workspace && !aligned256(fwd_workspace))) return REL_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(workspace);
-  void* q = rope_cos ? w + L.q : nullptr;
-  void* k = rope_cos ? w + L.k : nullptr;
-  void* v = theta ? w + L.v : nullptr;
+  // the maps' outputs: formed here, or read from the forward's workspace
+  // (which holds k and v, and q too where the forward does not rotate its
+  // queries in registers)
+  const MhrLayout F = mhr_layout(false, dtype, B, H, T, D);
+  const char* fw = static_cast<const char*>(fwd_workspace);
+  const bool fwd_q = fw && (dtype == REL_F32 || D != 64);
+  void* q = rope_cos ? (fwd_q ? const_cast<char*>(fw) + F.q : w + L.q) : nullptr;
+  void* k = rope_cos ? (fw ? const_cast<char*>(fw) + F.k : w + L.k) : nullptr;
+  void* v = theta ? (fw ? const_cast<char*>(fw) + F.v : w + L.v) : nullptr;
   float* part = reinterpret_cast<float*>(w + L.part);
   const float* th = theta;
   float* dth = theta ? dtheta : nullptr;
   const int dcode = dtype == REL_BF16 ? 1 : 0;
-  if ((q || v) && rel::launch_mhr_prepare(dcode, B, H, T, D, p1, p2, I, q, k, v, rope_cos,
-                                          rope_sin, th, pairing, s) != hipSuccess)
+  void* q_out = fwd_q ? nullptr : q;
+  void* k_out = fw ? nullptr : k;
+  void* v_out = fw ? nullptr : v;
+  if ((q_out || k_out || v_out) &&
+      rel::launch_mhr_prepare(dcode, B, H, T, D, p1, p2, I, q_out, k_out, v_out, rope_cos,
+                              rope_sin, th, pairing, s) != hipSuccess)
     return REL_ERR_HIP;
   if (!q) q = const_cast<void*>(p1);
   if (!k) k = const_cast<void*>(p2);

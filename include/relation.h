@@ -264,6 +264,14 @@ size_t relation_prefill_workspace_bytes(relation_dtype dtype, int B, int H, int 
  *   dlambda          : out DEVICE float32 scalar (NULL to skip)
  *   dtheta           : out DEVICE float32 [H/2] (NULL to skip; ignored
  *                      without theta)
+ *   fwd_workspace    : optional: the workspace of the relation_mhr_fwd call
+ *                      that produced y and lse, unchanged since (same inputs,
+ *                      tables, theta, pairing). The rotated keys and mixed
+ *                      values (and, where the forward stored them, the
+ *                      rotated queries) are then read from it instead of
+ *                      being formed again. NULL: formed here. A workspace
+ *                      that does not hold that forward's values gives wrong
+ *                      gradients (it cannot be checked).
  *   workspace        : relation_mhr_bwd_workspace_bytes() bytes, 256-byte
  *                      aligned; contents on entry are ignored.
  *   Other arguments as relation_bwd; y and lse are the forward's outputs.
@@ -288,6 +296,7 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                                  const void* y, const void* dy, const float* lse,
                                  void* dp1, void* dp2, void* dI,
                                  float* dlambda, float* dtheta,
+                                 const void* fwd_workspace,
                                  void* workspace, size_t workspace_bytes,
                                  float scale, float tau_s, float lambda,
                                  void* stream);

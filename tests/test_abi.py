@@ -202,13 +202,14 @@ def test_mhr_validation(lib):
     assert fwd(cs=P_MIS) == REL_ERR_ALIGN
     assert fwd() == REL_ERR_WORKSPACE                # keys / values go through a workspace
 
-    def bwd(ws=P, wsb=None):
+    def bwd(ws=P, wsb=None, fws=NUL):
         wsb = need if wsb is None else wsb
         return lib.relation_mhr_bwd(BF16, 2, 4, 128, 64, P, P, P, P, P, P, 0, P, P, P, P, P, P,
-                                    NUL, NUL, ws, wsb, 0.125, 2.0, 0.3, None)
+                                    NUL, NUL, fws, ws, wsb, 0.125, 2.0, 0.3, None)
 
     assert bwd(wsb=need - 256) == REL_ERR_WORKSPACE
     assert bwd(ws=NUL) == REL_ERR_WORKSPACE
+    assert bwd(fws=P_MIS) == REL_ERR_ALIGN  # the forward's workspace, when given
 
 
 def test_linear_validation(lib):

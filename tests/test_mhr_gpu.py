@@ -159,6 +159,30 @@ def test_mhr_bwd_vs_oracle(dtype, pairing, T):
             check_rel(f"dtheta[{p}]", float(dtheta[p].item()), rth[p], 2e-2, 2.0 ** -7 * mag)
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 48), ("f32", 64)])
+@pytest.mark.parametrize("use_rope,use_mix", [(True, True), (True, False), (False, True)])
+def test_mhr_bwd_reuses_forward_workspace(dtype, D, use_rope, use_mix):
+    """Gradients computed with the forward's workspace (its rotated keys and
+    mixed values, and its rotated queries where it stores them) equal those
+    that form them again, bit for bit."""
+    B, H, T = 1, 4, 200
+    inp = make_inputs(B, H, T, D, dtype, seed=760 + D, with_dy=True)
+    cs, sn, th = to_dev(*maps(T, D, H, 760, use_rope, use_mix))
+    p1, p2, I, dy = (inp[n].to(DEV) for n in ("q", "k", "v", "dy"))
+    lib = rel.load_library()
+    code = rel.REL_BF16 if dtype == "bf16" else rel.REL_F32
+    fws = torch.empty((lib.relation_mhr_fwd_workspace_bytes(code, B, H, T, D),), device=DEV,
+                      dtype=torch.uint8)
+    y, lse, _ = rel.relation_mhr_fwd(p1, p2, I, cs, sn, th, 1, lam=inp["lam"], scale=0.125,
+                                     workspace=fws)
+    a = rel.relation_mhr_bwd(p1, p2, I, y, dy, lse, cs, sn, th, 1, lam=inp["lam"], scale=0.125)
+    b = rel.relation_mhr_bwd(p1, p2, I, y, dy, lse, cs, sn, th, 1, lam=inp["lam"], scale=0.125,
+                             fwd_workspace=fws)
+    torch.cuda.synchronize()
+    for x, x1 in zip(a, b):
+        assert (x is None and x1 is None) or torch.equal(x, x1)
+
+
 def test_mhr_layer30m_shape_sampled_pairs():
     """The 30M layer's head geometry (H=8, D=64) at T=2048 with both maps; one
     sequence, every head computed by the oracle for the forward and two head
