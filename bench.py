@@ -7,10 +7,14 @@ TFLOP/s (fwd = 2*B*H*T^2*D flops, bwd = 2.5x fwd). The same run also measures
 the forward alone on the 10M / 30M / 100M layer shapes, forward+backward on
 the 100M shape beside torch's causal scaled-dot-product attention of the same
 shape, and 256 Relation Cache decode steps (B=32, H=12, D=64, history 4096) in
-GB/s, plus the fp64 CPU oracle on a bounded sample (cpu_baseline).
+GB/s, plus the fp64 CPU oracle on a bounded sample (cpu_baseline). The extra
+lines cover ragged decode, chunked prefill, Multi-Head Relation and Linear
+Relation (forward, backward, decode step); `roofline*` objects price the
+dominant kernel of each against MI355X's published peaks.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extra] [--only {step,fwd,decode}]
+                       [--no-extra] [--only {step,fwd,decode,ragged,mhr,prefill,
+                       attn,linear,copy}]
 """
 import argparse
 import json

@@ -47,6 +47,10 @@
 //     and bf16.
 //   * The row sum l accumulates the bf16-rounded P (v_dot2 with ones), the
 //     same values the P V contraction consumes.
+//   * SPLIT (a grid too small to fill the chip, with a caller workspace):
+//     long query blocks are cut over their historical key tiles into pieces
+//     of at least 16 tiles; the pieces' (acc, m, l) rows are merged by
+//     split_combine_kernel (see struct Split and plan_split).
 #include <math.h>
 
 #include "common.hpp"
