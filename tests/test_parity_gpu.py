@@ -173,13 +173,15 @@ def close_to_unsplit(name, a, b, vmax):
     assert frac < 0.05, name
 
 
-@pytest.mark.parametrize("B,H,T", [(1, 2, 1300), (1, 1, 2500), (2, 1, 1800)])
-def test_fwd_bf16_split_over_keys(B, H, T):
+@pytest.mark.parametrize("B,H,T,D", [(1, 2, 1300, 64), (1, 1, 2500, 64), (2, 1, 1800, 64),
+                                     (1, 1, 2100, 48), (1, 1, 2100, 80)])
+def test_fwd_bf16_split_over_keys(B, H, T, D):
     """A grid too small to fill the GPU splits its long query blocks over the
-    keys; the pieces are merged by App. A.3.2's rule in a second kernel."""
-    assert rel.relation_fwd_workspace_bytes(torch.bfloat16, B, H, T, 64) > 0
-    inp = make_inputs(B, H, T, 64, "bf16", seed=700 + T)
-    scale = 1 / 8
+    keys; the pieces are merged by App. A.3.2's rule in a second kernel (at
+    every head width: the partial rows are D + 4 floats)."""
+    assert rel.relation_fwd_workspace_bytes(torch.bfloat16, B, H, T, D) > 0
+    inp = make_inputs(B, H, T, D, "bf16", seed=700 + T)
+    scale = 1 / math.sqrt(D)
     y, lse, gate = run_fwd(inp, "bf16", scale)
     Y, L, G = oracle.relation_forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), scale, 2.0,
                                       inp["lam"])
