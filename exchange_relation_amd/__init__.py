@@ -36,6 +36,8 @@ __all__ = [
     "relation_version",
     "RelationFunction",
     "relation",
+    "MultiHeadRelationFunction",
+    "mhr_relation",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -568,13 +570,13 @@ def relation_linear_step(p1, p2, I, g, state, rope_cos=None, rope_sin=None, scal
 
 class RelationFunction(torch.autograd.Function):
     """autograd wrapper: y = Relation(q, k, v; lambda) with gradients for q,
-    k, v and the layer's lambda (a 1-element tensor)."""
+    k, v and the layer's lambda (a one-element tensor)."""
 
     @staticmethod
     def forward(ctx, q, k, v, lam, scale, tau_s):
         y, lse, _ = relation_fwd(q, k, v, lam=float(lam), scale=scale, tau_s=tau_s)
         ctx.save_for_backward(q, k, v, y, lse)
-        ctx.lam, ctx.scale, ctx.tau_s = float(lam), scale, tau_s
+        ctx.lam, ctx.scale, ctx.tau_s, ctx.lam_shape = float(lam), scale, tau_s, lam.shape
         return y
 
     @staticmethod
@@ -582,9 +584,44 @@ class RelationFunction(torch.autograd.Function):
         q, k, v, y, lse = ctx.saved_tensors
         dq, dk, dv, dlam = relation_bwd(q, k, v, y, dy.contiguous(), lse, lam=ctx.lam,
                                         scale=ctx.scale, tau_s=ctx.tau_s)
-        return dq, dk, dv, dlam.reshape(()), None, None
+        return dq, dk, dv, dlam.reshape(ctx.lam_shape), None, None
 
 
 def relation(q, k, v, lam, scale=None, tau_s=2.0):
     """Differentiable Multi-Head Relation; lam is a scalar tensor (learnable)."""
     return RelationFunction.apply(q, k, v, lam, scale, tau_s)
+
+
+class MultiHeadRelationFunction(torch.autograd.Function):
+    """autograd wrapper of relation_mhr_fwd / relation_mhr_bwd: gradients for
+    p1, p2, I, lambda and the Givens angles theta. The forward's workspace
+    (rotated keys, mixed values) is kept for the backward, which reads it
+    instead of forming the maps again."""
+
+    @staticmethod
+    def forward(ctx, p1, p2, I, lam, theta, rope_cos, rope_sin, pairing, scale, tau_s):
+        B, H, T, D = p1.shape
+        need = int(load_library().relation_mhr_fwd_workspace_bytes(_dtype_code(p1), B, H, T, D))
+        ws = torch.empty((need,), device=p1.device, dtype=torch.uint8) if need else None
+        y, lse, _ = relation_mhr_fwd(p1, p2, I, rope_cos, rope_sin, theta, pairing,
+                                     lam=float(lam), scale=scale, tau_s=tau_s, workspace=ws)
+        ctx.save_for_backward(p1, p2, I, y, lse, theta, rope_cos, rope_sin, ws)
+        ctx.lam, ctx.scale, ctx.tau_s, ctx.pairing = float(lam), scale, tau_s, pairing
+        ctx.lam_shape = lam.shape
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        p1, p2, I, y, lse, theta, rope_cos, rope_sin, ws = ctx.saved_tensors
+        dp1, dp2, dI, dlam, dth = relation_mhr_bwd(
+            p1, p2, I, y, dy.contiguous(), lse, rope_cos, rope_sin, theta, ctx.pairing,
+            lam=ctx.lam, scale=ctx.scale, tau_s=ctx.tau_s, fwd_workspace=ws)
+        return (dp1, dp2, dI, dlam.reshape(ctx.lam_shape), dth, None, None, None, None, None)
+
+
+def mhr_relation(p1, p2, I, lam, theta=None, rope_cos=None, rope_sin=None, pairing=0, scale=None,
+                 tau_s=2.0):
+    """Differentiable Multi-Head Relation with RoPE tables [T, D/2] and
+    Givens angles theta [H/2] (learnable); lam is a scalar tensor."""
+    return MultiHeadRelationFunction.apply(p1, p2, I, lam, theta, rope_cos, rope_sin, pairing,
+                                           scale, tau_s)

@@ -1,0 +1,68 @@
+"""The autograd wrappers (exchange_relation_amd.relation, .mhr_relation):
+forward and backward through torch.autograd give the direct C-ABI calls'
+results (y, lse-based gradients) bit for bit, except dq / dp1, which the
+backward accumulates with fp32 atomics in an unspecified order and which is
+therefore compared within the bf16 tolerance (max-abs 2e-2, mean-abs 3e-3)
+against the direct call and the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exchange_relation_amd as rel
+import oracle
+from workloads import make_inputs, make_mhr_maps
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def close(a, b):
+    d = (a.float() - b.float()).abs()
+    assert float(d.max()) <= 2e-2 and float(d.mean()) <= 3e-3
+
+
+def test_relation_autograd_matches_direct_calls_and_oracle():
+    B, H, T, D = 1, 2, 300, 64
+    inp = make_inputs(B, H, T, D, "bf16", seed=1200, with_dy=True)
+    q, k, v, dy = (inp[n].to(DEV) for n in ("q", "k", "v", "dy"))
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    lam = torch.tensor([inp["lam"]], device=DEV, requires_grad=True)
+    y = rel.relation(qa, ka, va, lam, scale=1 / 8)
+    y.backward(dy)
+    y0, lse0, _ = rel.relation_fwd(q, k, v, lam=inp["lam"], scale=1 / 8)
+    dq0, dk0, dv0, dl0 = rel.relation_bwd(q, k, v, y0, dy, lse0, lam=inp["lam"], scale=1 / 8)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    assert torch.equal(ka.grad, dk0) and torch.equal(va.grad, dv0)
+    assert lam.grad.shape == lam.shape and torch.equal(lam.grad, dl0.reshape(lam.shape))
+    close(qa.grad, dq0)
+    gq = oracle.relation_backward(*(inp[n].double().numpy() for n in ("q", "k", "v", "dy")),
+                                  1 / 8, 2.0, inp["lam"])[0]
+    err = np.abs(qa.grad.detach().cpu().double().numpy() - gq)
+    assert err.max() <= 2e-2 and err.mean() <= 3e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mhr_relation_autograd_matches_direct_calls(dtype):
+    B, H, T, D = 1, 4, 200, 64
+    inp = make_inputs(B, H, T, D, dtype, seed=1210, with_dy=True)
+    cs, sn, th = (t.to(DEV) for t in make_mhr_maps(T, D, H, 1210))
+    p1, p2, I, dy = (inp[n].to(DEV) for n in ("q", "k", "v", "dy"))
+    pa, pb, ia = (x.clone().requires_grad_(True) for x in (p1, p2, I))
+    tha = th.clone().requires_grad_(True)
+    lam = torch.tensor(inp["lam"], device=DEV, requires_grad=True)
+    scale = 1 / math.sqrt(D)
+    y = rel.mhr_relation(pa, pb, ia, lam, tha, cs, sn, 1, scale=scale)
+    y.backward(dy)
+    y0, lse0, _ = rel.relation_mhr_fwd(p1, p2, I, cs, sn, th, 1, lam=inp["lam"], scale=scale)
+    g0 = rel.relation_mhr_bwd(p1, p2, I, y0, dy, lse0, cs, sn, th, 1, lam=inp["lam"], scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    assert torch.equal(pb.grad, g0[1]) and torch.equal(ia.grad, g0[2])
+    assert torch.equal(lam.grad, g0[3].reshape(())) and torch.equal(tha.grad, g0[4])
+    if dtype == "f32":  # the fp32 path has no atomics
+        assert torch.equal(pa.grad, g0[0])
+    else:
+        close(pa.grad, g0[0])
