@@ -86,7 +86,8 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     const float* __restrict__ lse, const float* __restrict__ Dr, float* __restrict__ dq_acc,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int T, int BH, float kscale,
     float scale, float inv_tau, float lam, float* __restrict__ dk32, float* __restrict__ dv32,
-    const float* __restrict__ rc, const float* __restrict__ rs) {
+    const float* __restrict__ rc, const float* __restrict__ rs, float* __restrict__ part,
+    int nbt) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -144,6 +145,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
   }
 
   f32x16 dv0 = {0}, dv1 = {0}, dk0 = {0}, dk1 = {0};  // dV^T, dK^T: key r, d rows
+  float dl_acc = 0.f;  // this lane's dL/dlambda term (its Self entry, diagonal sub-tile)
 
   // ---- query tile prefetch: q and dY rows, 16 B chunks (2 per thread with 4
   // waves, 1 with 8; chunk c: row c >> 3, d chunk c & 7)
@@ -264,6 +266,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
         const float S = fast_rcp(1.0f + fast_exp2(-us_ * kscale * inv_tau));
         fself = fast_exp2(S * kLog2e - ll);
         uself = fself * dps * S * (1.0f - S) * inv_tau;
+        // dL/dlambda = sum_i ln(i) dR_ii with dR_ii = F_ii (dP_ii - Dr_i); the
+        // row is kw0 + r (this sub-tile's queries start at the wave's keys)
+        if (mine) dl_acc += logf(static_cast<float>(kw0 + r + 1)) * fself * dps;
       }
 
       uint32_t fw[8], uw[8];
@@ -392,6 +397,14 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     buf = buf == 2 ? 0 : buf + 1;
   }
 
+  // ---- the dL/dlambda terms of this wave's 32 rows: part[head][kw0 / 32]
+  if (part) {
+    float sdl = dl_acc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sdl += __shfl_xor(sdl, o);
+    if (lane == 0 && kw0 < T) part[static_cast<size_t>(head) * nbt + kw0 / 32] = sdl;
+  }
+
   // ---- dK = scale * dK^T^T, dV = dV^T^T (key kj, d rows of the accumulators)
   if (kj >= T) return;
   const size_t row = base + static_cast<size_t>(kj) * DR;
@@ -507,6 +520,7 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                                 stream);
   if (e != hipSuccess) return e;
   const float* Dr = reinterpret_cast<const float*>(wsb + w.off_dr);
+  float* part = reinterpret_cast<float*>(wsb + w.off_part);  // dL/dlambda terms
   const int BH = B * H;
   const int nkb = (T + BK - 1) / BK;
   if (D == 80) {  // the wider layout of bwd80.hip
@@ -516,11 +530,13 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
     if (D == 48)
       hipLaunchKernelGGL(bwd_bf16_kernel<48>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
                          stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e,
-                         scale, 1.0f / tau, lam, dk32, dv32, nullptr, nullptr);
+                         scale, 1.0f / tau, lam, dk32, dv32, nullptr, nullptr, part,
+                         (T + 31) / 32);
     else
       hipLaunchKernelGGL(bwd_bf16_kernel<64>, dim3(static_cast<unsigned>(nkb) * BH), dim3(NT), 0,
                          stream, q, k, v, dy, lse, Dr, dq_acc, dk, dv, T, BH, scale * kLog2e,
-                         scale, 1.0f / tau, lam, dk32, dv32, rope_cos, rope_sin);
+                         scale, 1.0f / tau, lam, dk32, dv32, rope_cos, rope_sin, part,
+                         (T + 31) / 32);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
