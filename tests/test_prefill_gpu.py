@@ -108,6 +108,23 @@ def test_prefill_split_over_keys_matches_unsplit(ns, bound):
     check("lse", f64(lse), L)
 
 
+def test_prefill_split_with_out_of_range_sequence():
+    """Split over keys with a sequence whose length is above the bound: its
+    rows are NaN and its cache rows untouched; the others match the oracle."""
+    B, H, D, m, cap = 3, 2, 64, 100, 2400
+    ns = [500, 2290, 2200]  # bound 2200: sequence 1 is above it
+    assert rel.relation_prefill_workspace_bytes(torch.bfloat16, B, H, D, m, 2200, True) > 0
+    d, new = prefill_inputs(B, H, D, m, cap, seed=939)
+    y, lse, g, kc, vc = run(d, new, ns, bound=2200)
+    assert np.isnan(f64(y[1])).all() and np.isnan(f64(lse[1])).all()
+    assert torch.equal(kc[1], d["k_cache"][1]) and torch.equal(vc[1], d["v_cache"][1])
+    Y, L, _, _, _ = oracle_rows(
+        {**d, "k_cache": d["k_cache"][[0, 2]], "v_cache": d["v_cache"][[0, 2]]},
+        {k: t[[0, 2]] for k, t in new.items()}, [500, 2200])
+    check("valid rows", f64(y[[0, 2]]), Y)
+    check("valid lse", f64(lse[[0, 2]]), L)
+
+
 def test_prefill_ragged_out_of_range_nan_and_no_write():
     B, H, D, m, cap = 3, 2, 64, 16, 96
     ns = [10, 90, 20]  # bound 40: sequence 1 is above it (and would not fit)
