@@ -360,6 +360,19 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
       c.a[i] = *reinterpret_cast<const u32x4*>(src + (r0 * D + ccol[i] * 8));
     }
   };
+  // a tile wholly inside the keys: no clamp, no zero-fill
+  auto fetch_full = [&](const uint16_t* __restrict__ src, int kt, Chunks& c) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const uint32_t r0 = static_cast<uint32_t>(kt * BN + crow[i]);
+      c.a[i] = *reinterpret_cast<const u32x4*>(src + (r0 * D + ccol[i] * 8));
+    }
+  };
+  auto stash_full = [&](uint16_t* dst, const Chunks& c, int stride) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (cin[i]) *reinterpret_cast<u32x4*>(&dst[crow[i] * stride + ccol[i] * 8]) = c.a[i];
+  };
   auto stash = [&](uint16_t* dst, const Chunks& c, int stride) {
     const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
@@ -399,8 +412,13 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   int kt = kt0;
   for (; kt < hend; ++kt) {
     const bool more_k = kt + 2 < tend;  // kt + 1 < tend always holds here
-    if (more_k) fetch(kh, kt + 2, ck);
-    fetch(vh, kt + 1, cv);
+    const bool kfull = (kt + 3) * BN <= Tk, vfull = (kt + 2) * BN <= Tk;
+    if (more_k) {
+      if (kfull) fetch_full(kh, kt + 2, ck);
+      else fetch(kh, kt + 2, ck);
+    }
+    if (vfull) fetch_full(vh, kt + 1, cv);
+    else fetch(vh, kt + 1, cv);
     const uint16_t* vs = vbuf[(kt - kt0) & 1];
     stabilise<false>(sa, qscale, r, hf, st);
     f32x16 sb = score<DR>(kp0, 1, qf, r, hf);
@@ -408,8 +426,12 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     stabilise<false>(sb, qscale, r, hf, st);
     sa = score<DR>(kp1, 0, qf, r, hf);  // tile kt + 1 <= nfull is resident
     accumulate<false, DR>(vs, 1, sb, hf, st);
-    if (more_k) stash(kp2, ck, KS);
-    stash(vbuf[(kt + 1 - kt0) & 1], cv, VS);
+    if (more_k) {
+      if (kfull) stash_full(kp2, ck, KS);
+      else stash(kp2, ck, KS);
+    }
+    if (vfull) stash_full(vbuf[(kt + 1 - kt0) & 1], cv, VS);
+    else stash(vbuf[(kt + 1 - kt0) & 1], cv, VS);
     __syncthreads();
     uint16_t* kt0 = kp0;
     kp0 = kp1;
