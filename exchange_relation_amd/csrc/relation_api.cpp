@@ -38,10 +38,15 @@ relation_status check_dtype_dim_bwd(relation_dtype dt, int D) {
   return REL_ERR_UNSUPPORTED;
 }
 
+// The kernels index inside one head (rows x D, or capacity x D) with 32-bit
+// offsets from the head's base.
+constexpr long long kMaxHeadElems = 0x7fffffffLL;
+
 relation_status check_shape(int B, int H, int T, int D) {
   if (B < 1 || H < 1 || T < 1 || D < 1) return REL_ERR_SHAPE;
   const long long n = static_cast<long long>(B) * H * T;
   if (n * D > kMaxElems) return REL_ERR_SHAPE;
+  if (static_cast<long long>(T) * D > kMaxHeadElems) return REL_ERR_SHAPE;
   // one workgroup per 32..128 rows: keep the 1-D grid within 2^31 - 1
   if (static_cast<long long>(B) * H * ((T + 31) / 32) > 0x7fffffffLL) return REL_ERR_SHAPE;
   return REL_OK;
@@ -202,7 +207,9 @@ relation_status relation_cache_decode(relation_dtype dtype, int B, int H, int D,
   relation_status st = check_dtype_dim(dtype, D);
   if (st != REL_OK) return st;
   if (B < 1 || H < 1 || capacity < 1) return REL_ERR_SHAPE;
-  if (static_cast<long long>(B) * H * capacity * D > kMaxElems) return REL_ERR_SHAPE;
+  if (static_cast<long long>(B) * H * capacity * D > kMaxElems ||
+      static_cast<long long>(capacity) * D > kMaxHeadElems)
+    return REL_ERR_SHAPE;
   if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
   if (n_hist < 0 || n_hist >= capacity) return REL_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
@@ -228,7 +235,9 @@ relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H,
   relation_status st = check_dtype_dim(dtype, D);
   if (st != REL_OK) return st;
   if (B < 1 || H < 1 || capacity < 1) return REL_ERR_SHAPE;
-  if (static_cast<long long>(B) * H * capacity * D > kMaxElems) return REL_ERR_SHAPE;
+  if (static_cast<long long>(B) * H * capacity * D > kMaxElems ||
+      static_cast<long long>(capacity) * D > kMaxHeadElems)
+    return REL_ERR_SHAPE;
   if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
   if (max_n_hist < 0 || max_n_hist >= capacity) return REL_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
@@ -260,7 +269,9 @@ relation_status relation_cache_prefill(relation_dtype dtype, int B, int H, int D
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !y) return REL_ERR_NULL;
   if (dtype != REL_BF16 || check_dtype_dim(dtype, D) != REL_OK) return REL_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || m < 1 || capacity < 1) return REL_ERR_SHAPE;
-  if (static_cast<long long>(B) * H * capacity * D > kMaxElems) return REL_ERR_SHAPE;
+  if (static_cast<long long>(B) * H * capacity * D > kMaxElems ||
+      static_cast<long long>(capacity) * D > kMaxHeadElems)
+    return REL_ERR_SHAPE;
   if (static_cast<long long>(B) * H * ((m + 31) / 32) > 0x7fffffffLL) return REL_ERR_SHAPE;
   relation_status st = check_params(scale, tau_s, lambda);
   if (st != REL_OK) return st;

@@ -51,7 +51,9 @@ extern "C" {
 typedef enum {
   REL_OK = 0,
   REL_ERR_NULL = 1,        /* a required pointer is NULL                      */
-  REL_ERR_SHAPE = 2,       /* B, H, T < 1, or sizes overflow the index range  */
+  REL_ERR_SHAPE = 2,       /* B, H, T < 1, or sizes overflow the index range  *
+                            * (one head's T * D or capacity * D must be below *
+                            * 2^31 elements; all heads below 2^40)             */
   REL_ERR_UNSUPPORTED = 3, /* dtype / head dimension not built                */
   REL_ERR_PARAM = 4,       /* scale or lambda not finite, tau_s <= 0          */
   REL_ERR_CAPACITY = 5,    /* decode: n_hist < 0 or n_hist + 1 > capacity     */

@@ -81,6 +81,9 @@ def test_fwd_validation(lib):
     assert fwd(lib, y=NUL) == REL_ERR_NULL
     assert fwd(lib, T=0) == REL_ERR_SHAPE
     assert fwd(lib, B=-1) == REL_ERR_SHAPE
+    # one head's rows are indexed with 32-bit offsets: T * D < 2^31
+    assert fwd(lib, T=(1 << 25), D=64) == REL_ERR_SHAPE
+    assert fwd(lib, T=(1 << 25) - 1, D=64, q=NUL) == REL_ERR_NULL  # the shape itself passes
     assert fwd(lib, dtype=F32, D=48) == REL_ERR_UNSUPPORTED
     assert fwd(lib, dtype=BF16, D=32) == REL_ERR_UNSUPPORTED
     assert fwd(lib, dtype=BF16, D=96) == REL_ERR_UNSUPPORTED
@@ -132,6 +135,7 @@ def test_decode_validation(lib):
     assert dec(wsb=need - 4) == REL_ERR_WORKSPACE
     assert dec(D=32) == REL_ERR_UNSUPPORTED
     assert dec(cap=0, n=0) == REL_ERR_SHAPE
+    assert dec(cap=(1 << 25), n=10) == REL_ERR_SHAPE  # capacity * D >= 2^31
     assert dec(q=P_MIS) == REL_ERR_ALIGN
 
 
