@@ -433,10 +433,10 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     if (vfull) stash_full(vbuf[(kt + 1 - kt0) & 1], cv, VS);
     else stash(vbuf[(kt + 1 - kt0) & 1], cv, VS);
     __syncthreads();
-    uint16_t* kt0 = kp0;
+    uint16_t* kfree = kp0;
     kp0 = kp1;
     kp1 = kp2;
-    kp2 = kt0;
+    kp2 = kfree;
   }
   // ---- the workgroup's own block: per-wave historical / diagonal /
   // beyond. Aligned rows (pos0 = 0) span at most two tiles, both resident;
@@ -465,10 +465,10 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     if (more_k) stash(kp2, ck, KS);
     if (kt + 1 < ntiles) stash(vbuf[(kt + 1 - kt0) & 1], cv, VS);
     __syncthreads();
-    uint16_t* kt0 = kp0;
+    uint16_t* kfree = kp0;
     kp0 = kp1;
     kp1 = kp2;
-    kp2 = kt0;
+    kp2 = kfree;
   }
 
   if (!wave_live) return;
