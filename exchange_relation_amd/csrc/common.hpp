@@ -86,52 +86,72 @@ template <> struct Elem<uint16_t> {
   __device__ __forceinline__ static void store(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
 };
 
-// One lane's D/8 consecutive elements of a row, widened to fp32, with one
-// vector load (bf16 D=64: 16 B; fp32 D=64: 32 B; fp32 D=32: 16 B).
-template <typename TE, int D>
-__device__ __forceinline__ void load_row_piece(const TE* p, float* x);
+// A vector (or scalar) load. NT: a streaming load (the non-temporal hint), for
+// data read once per call, so that it does not displace what the caches hold.
+template <bool NT, typename V>
+__device__ __forceinline__ V vload(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
 
-template <>
-__device__ __forceinline__ void load_row_piece<uint16_t, 64>(const uint16_t* p, float* x) {
-  const uint4 w = *reinterpret_cast<const uint4*>(p);
-  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+// One lane's D/8 consecutive elements of a row, widened to fp32, with one
+// vector load (bf16 D=64: 16 B; fp32 D=64: 32 B; fp32 D=32: 16 B). bf16 rows
+// of 48 or 80 elements: a lane's piece (6 or 10 elements) starts only 4-byte
+// aligned, so it is read as 32-bit words.
+template <typename TE, int D, bool NT>
+struct RowPiece;
+
+template <bool NT>
+struct RowPiece<uint16_t, 64, NT> {
+  __device__ __forceinline__ static void load(const uint16_t* p, float* x) {
+    const u32x4 w = vload<NT>(reinterpret_cast<const u32x4*>(p));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(a[i] << 16);
-    x[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
   }
-}
-template <>
-__device__ __forceinline__ void load_row_piece<float, 64>(const float* p, float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-// bf16 rows of 48 or 80 elements: a lane's piece (6 or 10 elements) starts
-// only 4-byte aligned, so it is read as 32-bit words.
-template <int E>
-__device__ __forceinline__ void load_bf16_words(const uint16_t* p, float* x) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+};
+template <bool NT>
+struct RowPiece<float, 64, NT> {
+  __device__ __forceinline__ static void load(const float* p, float* x) {
+    const f32x4 a = vload<NT>(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = vload<NT>(reinterpret_cast<const f32x4*>(p + 4));
 #pragma unroll
-  for (int i = 0; i < E / 2; ++i) {
-    const uint32_t a = w[i];
-    x[2 * i] = __uint_as_float(a << 16);
-    x[2 * i + 1] = __uint_as_float(a & 0xffff0000u);
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
   }
-}
-template <>
-__device__ __forceinline__ void load_row_piece<uint16_t, 48>(const uint16_t* p, float* x) {
-  load_bf16_words<6>(p, x);
-}
-template <>
-__device__ __forceinline__ void load_row_piece<uint16_t, 80>(const uint16_t* p, float* x) {
-  load_bf16_words<10>(p, x);
-}
-template <>
-__device__ __forceinline__ void load_row_piece<float, 32>(const float* p, float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+};
+template <bool NT>
+struct RowPiece<float, 32, NT> {
+  __device__ __forceinline__ static void load(const float* p, float* x) {
+    const f32x4 a = vload<NT>(reinterpret_cast<const f32x4*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = a[i];
+  }
+};
+template <int E, bool NT>
+struct Bf16Words {
+  __device__ __forceinline__ static void load(const uint16_t* p, float* x) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      const uint32_t a = vload<NT>(w + i);
+      x[2 * i] = __uint_as_float(a << 16);
+      x[2 * i + 1] = __uint_as_float(a & 0xffff0000u);
+    }
+  }
+};
+template <bool NT>
+struct RowPiece<uint16_t, 48, NT> : Bf16Words<6, NT> {};
+template <bool NT>
+struct RowPiece<uint16_t, 80, NT> : Bf16Words<10, NT> {};
+
+template <typename TE, int D, bool NT = false>
+__device__ __forceinline__ void load_row_piece(const TE* p, float* x) {
+  RowPiece<TE, D, NT>::load(p, x);
 }
 
 // 8 bf16 <-> 8 fp32
