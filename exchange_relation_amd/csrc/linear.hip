@@ -57,7 +57,12 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
     float* __restrict__ cT, float* __restrict__ states, int T, float sl2) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  // Wave (tid >> 6) owns sub-chunk w = (tid >> 6) ^ 4. Waves 0-3 and 4-7 pair
+  // up on the four SIMDs, and timestamps show waves 0-3 getting through the
+  // row-local phase about 1.5x faster than their partners; giving them the
+  // sub-chunks with the most blocks below the diagonal (4-7) is 1.8 % faster
+  // than the identity mapping.
+  const int w = (tid >> 6) ^ 4, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int head = blockIdx.x;
   const size_t base = static_cast<size_t>(head) * T * D;
   const int nch = (T + CH - 1) / CH;
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(NT, 1) void linear_fwd_kernel(
     const int trow = t0 + 16 * w + l16;  // this lane's row
     // ---------------- row-local: coordinates, Self, q, k, prefix of g
     RowLocal rl;
-    row_local<ROPE>(raw, sl2, lane, kSafeLog2Fwd, rl);
+    row_local<ROPE>(raw, sl2, kSafeLog2Fwd, rl);
     const float* q = rl.q;
     const float* k = rl.k;
     const float* b2 = rl.b2;

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NT, 1) void linear_dstate_kernel(
           st[(16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] = dcs[i][r];
     }
     RowLocal rl;
-    row_local<ROPE>(raw, sl2, lane, kSafeLog2Bwd, rl);
+    row_local<ROPE>(raw, sl2, kSafeLog2Bwd, rl);
     const u32x4 z = {0, 0, 0, 0};
     const u32x4 y0 = raw.ok ? rdy[0] : z, y1 = raw.ok ? rdy[1] : z;
     float qq[16];
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(NT, 1) void linear_grad_kernel(
   }
 
   RowLocal rl;
-  row_local<ROPE>(raw, sl2, lane, kSafeLog2Bwd, rl);
+  row_local<ROPE>(raw, sl2, kSafeLog2Bwd, rl);
   const bool ok = raw.ok;
   const bool safe = rl.safe;
   {

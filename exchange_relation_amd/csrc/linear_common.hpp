@@ -59,12 +59,20 @@ __device__ __forceinline__ float row_prefix(float x) {
   return x;
 }
 // sum over the four 16-lane groups (the four channel groups of a row)
+// lane 15 of each 16-lane row, broadcast over the row (DPP row_newbcast)
+__device__ __forceinline__ float row_bcast15(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xF, 0xF, false));
+}
+// The exchanges between 16-lane rows use v_permlane16_swap / v_permlane32_swap
+// (register moves, no LDS round trip).
 __device__ __forceinline__ float sum_groups(float x) {
-  x += __shfl_xor(x, 16);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
   return sum_across_halves(x);
 }
 __device__ __forceinline__ float min_groups(float x) {
-  x = fminf(x, __shfl_xor(x, 16));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fminf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
@@ -131,7 +139,7 @@ struct RowLocal {
 };
 
 template <bool ROPE>
-__device__ __forceinline__ void row_local(Raw& raw, float sl2, int lane, float safe_log2,
+__device__ __forceinline__ void row_local(Raw& raw, float sl2, float safe_log2,
                                           RowLocal& o) {
   const u32x4 z = {0, 0, 0, 0};
   const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
@@ -180,7 +188,7 @@ __device__ __forceinline__ void row_local(Raw& raw, float sl2, int lane, float s
     o.q[i] = o.x1[i] * r1;
     o.k[i] = o.x2[i] * r2;
     o.b2[i] = row_prefix(raw.gg[i >> 2][i & 3] * kLog2e);
-    o.lw[i] = __shfl(o.b2[i], (lane & 48) | 15);
+    o.lw[i] = row_bcast15(o.b2[i]);
     lmin = fminf(lmin, o.lw[i]);
   }
   // every lane holds the wave's minimum; make the branch scalar
