@@ -199,12 +199,19 @@ __device__ __forceinline__ void accumulate(const uint16_t* vs, int sb, const f32
 
 // Rows at an offset (OFF: prefill into a Relation Cache): the T query rows
 // of every head (q, y: [BH, T, D]) sit at positions pos0 .. pos0 + T - 1 of
-// their sequence, pos0 = p0s[b] (device lengths) or p0 (uniform); keys and
-// values are the cache's rows 0 .. pos0 + T - 1 (head stride ld rows).
-// Sequences with pos0 < 0, pos0 > bound or pos0 + T > ld get NaN rows.
+// their sequence, pos0 = p0s[b] (device lengths) or p0 (uniform). Keys and
+// values at positions 0 .. pos0 - 1 are the cache's rows (head stride ld
+// rows); those at pos0 .. pos0 + T - 1 are the new rows kn / vn ([BH, T, D]),
+// which piece 0 of each query block also copies into the cache (no workgroup
+// of the launch reads them there). Sequences with pos0 < 0, pos0 > bound or
+// pos0 + T > ld get NaN rows and no copy.
 struct Seg {
   const int* p0s;
   int p0, bound, ld, H;
+  const uint16_t* kn = nullptr;
+  const uint16_t* vn = nullptr;
+  uint16_t* kc = nullptr;  // the caches, written only at rows pos0 ..
+  uint16_t* vc = nullptr;
 };
 
 // Split over keys (SPLIT): on a grid too small to fill the chip, a query
@@ -338,6 +345,20 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   // select turns the loads into generic ones.
   const uint16_t* __restrict__ kh = k + kvbase;
   const uint16_t* __restrict__ vh = v + kvbase;
+  // OFF: rows at or after pos0 come from the new rows instead of the cache
+  const uint16_t* __restrict__ knh = OFF ? sg.kn + base : kh;
+  const uint16_t* __restrict__ vnh = OFF ? sg.vn + base : vh;
+  auto rowp = [&](const uint16_t* src, const uint16_t* srcn, uint32_t r0, int col) {
+    if constexpr (OFF) {
+      const uint32_t p = static_cast<uint32_t>(pos0);
+      return r0 < p ? src + (r0 * D + col) : srcn + ((r0 - p) * D + col);
+    } else {
+      return src + (r0 * D + col);
+    }
+  };
+  // OFF: tile kt lies wholly in the cache (a wave-uniform test), so its rows
+  // need no per-row source select
+  auto in_cache = [&](int kt) { return !OFF || (kt + 1) * BN <= pos0; };
   int crow[NCH], ccol[NCH];
   bool cin[NCH];  // chunk exists (BN * CPR need not be a multiple of 256)
 #pragma unroll
@@ -351,21 +372,31 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     u32x4 a[NCH];
     bool ok[NCH];
   };
-  auto fetch = [&](const uint16_t* __restrict__ src, int kt, Chunks& c) {
+  auto fetch = [&](const uint16_t* __restrict__ src, const uint16_t* __restrict__ srcn, int kt,
+                   Chunks& c) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int key = kt * BN + crow[i];
       c.ok[i] = cin[i] && key < Tk;
       const uint32_t r0 = static_cast<uint32_t>(key < Tk ? key : Tk - 1);
-      c.a[i] = *reinterpret_cast<const u32x4*>(src + (r0 * D + ccol[i] * 8));
+      c.a[i] = *reinterpret_cast<const u32x4*>(rowp(src, srcn, r0, ccol[i] * 8));
     }
   };
   // a tile wholly inside the keys: no clamp, no zero-fill
-  auto fetch_full = [&](const uint16_t* __restrict__ src, int kt, Chunks& c) {
+  auto fetch_full = [&](const uint16_t* __restrict__ src, const uint16_t* __restrict__ srcn,
+                        int kt, Chunks& c) {
+    if (in_cache(kt)) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const uint32_t r0 = static_cast<uint32_t>(kt * BN + crow[i]);
-      c.a[i] = *reinterpret_cast<const u32x4*>(src + (r0 * D + ccol[i] * 8));
+      for (int i = 0; i < NCH; ++i) {
+        const uint32_t r0 = static_cast<uint32_t>(kt * BN + crow[i]);
+        c.a[i] = *reinterpret_cast<const u32x4*>(src + (r0 * D + ccol[i] * 8));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const uint32_t r0 = static_cast<uint32_t>(kt * BN + crow[i]);
+        c.a[i] = *reinterpret_cast<const u32x4*>(rowp(src, srcn, r0, ccol[i] * 8));
+      }
     }
   };
   auto stash_full = [&](uint16_t* dst, const Chunks& c, int stride) {
@@ -395,9 +426,9 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   Chunks ck, cv;
   {
     Chunks cn;
-    fetch(kh, kt0, ck);
-    fetch(vh, kt0, cv);
-    if (kt0 + 1 < tend) fetch(kh, kt0 + 1, cn);
+    fetch(kh, knh, kt0, ck);
+    fetch(vh, vnh, kt0, cv);
+    if (kt0 + 1 < tend) fetch(kh, knh, kt0 + 1, cn);
     stash(kp0, ck, KS);
     stash(vbuf[0], cv, VS);
     if (kt0 + 1 < tend) stash(kp1, cn, KS);
@@ -414,11 +445,11 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     const bool more_k = kt + 2 < tend;  // kt + 1 < tend always holds here
     const bool kfull = (kt + 3) * BN <= Tk, vfull = (kt + 2) * BN <= Tk;
     if (more_k) {
-      if (kfull) fetch_full(kh, kt + 2, ck);
-      else fetch(kh, kt + 2, ck);
+      if (kfull) fetch_full(kh, knh, kt + 2, ck);
+      else fetch(kh, knh, kt + 2, ck);
     }
-    if (vfull) fetch_full(vh, kt + 1, cv);
-    else fetch(vh, kt + 1, cv);
+    if (vfull) fetch_full(vh, vnh, kt + 1, cv);
+    else fetch(vh, vnh, kt + 1, cv);
     const uint16_t* vs = vbuf[(kt - kt0) & 1];
     stabilise<false>(sa, qscale, r, hf, st);
     f32x16 sb = score<DR>(kp0, 1, qf, r, hf);
@@ -443,8 +474,8 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   // rows at an offset may span three, so K keeps streaming two tiles ahead.
   for (; last && kt < ntiles; ++kt) {
     const bool more_k = kt + 2 < ntiles;
-    if (more_k) fetch(kh, kt + 2, ck);
-    if (kt + 1 < ntiles) fetch(vh, kt + 1, cv);
+    if (more_k) fetch(kh, knh, kt + 2, ck);
+    if (kt + 1 < ntiles) fetch(vh, vnh, kt + 1, cv);
     const uint16_t* vs = vbuf[(kt - kt0) & 1];
     if (wave_live) {
       const int pw = pos0 + q0;  // position of the wave's first query
@@ -471,6 +502,22 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     kp2 = kfree;
   }
 
+  // OFF: piece 0 appends its query block's new rows to the cache, after its
+  // scan so that the copies of the grid's first wave spread out under the
+  // compute of the others (all threads of the workgroup are still here)
+  if constexpr (OFF) {
+    if (piece == 0) {
+      const int r0 = qb * BM, r1 = min(T, r0 + BM);
+      constexpr int CPR16 = D / 8;  // 16-byte chunks per row
+      for (int e = tid; e < (r1 - r0) * CPR16; e += 256) {
+        const int rr = r0 + e / CPR16, cc = e % CPR16;
+        const size_t from = base + static_cast<size_t>(rr) * D + cc * 8;
+        const size_t to = kvbase + static_cast<size_t>(pos0 + rr) * D + cc * 8;
+        *reinterpret_cast<u32x4*>(sg.kc + to) = *reinterpret_cast<const u32x4*>(sg.kn + from);
+        *reinterpret_cast<u32x4*>(sg.vc + to) = *reinterpret_cast<const u32x4*>(sg.vn + from);
+      }
+    }
+  }
   if (!wave_live) return;
   // ---- row completion (App. A.3.5), base-2 domain
   // cross-lane exchanges first, with every lane active, then select
@@ -508,14 +555,16 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   const float gl = (ltot > 0.f) ? g * fast_rcp(ltot) : 0.f;
   const float gs = 1.0f - g;
   const size_t row = base + static_cast<size_t>(qi) * D;
-  const size_t vrow = kvbase + static_cast<size_t>(pos0 + qi) * D;  // I_i, the row's own value
+  // I_i, the row's own value (OFF: the new row, not yet in the cache)
+  const uint16_t* vown = OFF ? sg.vn + base + static_cast<size_t>(qi) * D
+                             : v + kvbase + static_cast<size_t>(pos0 + qi) * D;
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d0 = db * 32 + g4 * 8 + hf * 4;
       if (d0 >= DR) continue;  // padding columns
-      const uint2 vr = *reinterpret_cast<const uint2*>(v + vrow + d0);
+      const uint2 vr = *reinterpret_cast<const uint2*>(vown + d0);
       const f32x16& acc = st.acc[db];
       const float y0 = fmaf(gs, __uint_as_float(vr.x << 16), gl * acc[g4 * 4 + 0]);
       const float y1 = fmaf(gs, __uint_as_float(vr.x & 0xffff0000u), gl * acc[g4 * 4 + 1]);
@@ -591,8 +640,8 @@ __global__ __launch_bounds__(256) void split_combine_kernel(
   }
   const float gl = l > 0.f ? gt * fast_rcp(l) : 0.f;
   const float gs = 1.0f - gt;
-  const uint2 vr = *reinterpret_cast<const uint2*>(v + kvbase + static_cast<size_t>(pos0 + qi) * D +
-                                                   4 * quad);
+  const uint16_t* vo = off ? sg.vn + row * D : v + kvbase + static_cast<size_t>(pos0 + qi) * D;
+  const uint2 vr = *reinterpret_cast<const uint2*>(vo + 4 * quad);
   const float y0 = fmaf(gs, __uint_as_float(vr.x << 16), gl * acc[0]);
   const float y1 = fmaf(gs, __uint_as_float(vr.x & 0xffff0000u), gl * acc[1]);
   const float y2 = fmaf(gs, __uint_as_float(vr.y << 16), gl * acc[2]);
@@ -673,42 +722,16 @@ hipError_t run_fwd(int BH, int H, int T, const uint16_t* q, const uint16_t* k,
 // Appends the m new tokens of every (b, h) to cache slots n_b .. n_b + m - 1
 // (an exact 16-bit copy); sequences out of range are left untouched.
 template <int DR>
-__global__ __launch_bounds__(256) void append_kernel(const uint16_t* __restrict__ kn,
-                                                     const uint16_t* __restrict__ vn,
-                                                     uint16_t* __restrict__ kc,
-                                                     uint16_t* __restrict__ vc, size_t rows, int m,
-                                                     int H, int cap, const int* __restrict__ nh,
-                                                     int n, int bound) {
-  constexpr int CPR = DR / 8;
-  const size_t g = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const size_t row = g / CPR;  // (head, t) of the new tokens
-  if (row >= rows) return;
-  const int c = static_cast<int>(g % CPR);
-  const size_t head = row / m;
-  const int t = static_cast<int>(row % m);
-  const int p0 = nh ? nh[head / H] : n;
-  if (p0 < 0 || p0 > bound || p0 + m > cap) return;
-  const size_t dst = (head * cap + p0 + t) * DR + c * 8;
-  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(kn + row * DR + c * 8);
-  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(vn + row * DR + c * 8);
-}
-
-template <int DR>
 hipError_t run_prefill(int BH, int H, int m, const uint16_t* q, const uint16_t* k_new,
                        const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache, int capacity,
                        const int* n_hist_dev, int n_hist, uint16_t* y, float* lse, float* gate,
                        float scale, float tau, float lam, hipStream_t stream, float* ws,
                        size_t ws_bytes) {
-  const size_t rows = static_cast<size_t>(BH) * m;
-  const size_t threads = rows * (DR / 8);
-  hipLaunchKernelGGL((append_kernel<DR>), dim3(static_cast<unsigned>((threads + 255) / 256)),
-                     dim3(256), 0, stream, k_new, v_new, k_cache, v_cache, rows, m, H, capacity,
-                     n_hist_dev, n_hist, n_hist);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int nqb = (m + BM - 1) / BM;
   const Mhr mh{nullptr, nullptr, nullptr, 0, H};
-  const Seg sg{n_hist_dev, n_hist, n_hist, capacity, H};
+  // the kernel reads the new rows from k_new / v_new and appends them itself
+  const Seg sg{n_hist_dev, n_hist, n_hist, capacity, H, k_new, v_new, k_cache, v_cache};
+  hipError_t e;
   const SplitPlan pl =
       ws ? plan_split(BH, m, n_hist, n_hist_dev != nullptr, DR) : SplitPlan{0, 1, 0};
   if (pl.spl > 0 && ws_bytes >= pl.bytes) {
