@@ -210,7 +210,8 @@ struct Seg {
   int p0, bound, ld, H;
   const uint16_t* kn = nullptr;
   const uint16_t* vn = nullptr;
-  uint16_t* kc = nullptr;  // the caches, written only at rows pos0 ..
+  uint16_t* kc = nullptr;  // the caches (the same buffers as k, v), written
+                           // only at rows pos0 .. pos0 + T - 1
   uint16_t* vc = nullptr;
 };
 
