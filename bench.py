@@ -368,13 +368,35 @@ def bench_linear(rel, torch, dev, reps, B=32, H=8, T=1024, D=64, seed=42):
     tb.stop(s0)
     bm = tb.mean_ms() / nb
     bbytes = 22 * D * B * H * T
+    # a training step: the forward stores the state before every chunk and the
+    # backward reuses them instead of running its own state pass
+    states = torch.empty(rel.linear_states_shape(B, H, T, D), device=dev, dtype=torch.float32)
+    t1, t2 = EventTimer(torch, stream), EventTimer(torch, stream)
+    for _ in range(10):
+        rel.relation_linear_fwd(p1, p2, I, g, cs, sn, scale=1 / math.sqrt(D), y=y, states=states)
+        rel.relation_linear_bwd(p1, p2, I, g, dy, cs, sn, scale=1 / math.sqrt(D), workspace=ws,
+                                fwd_states=states)
+    torch.cuda.synchronize()
+    s1 = t1.start()
+    for _ in range(nb):
+        rel.relation_linear_fwd(p1, p2, I, g, cs, sn, scale=1 / math.sqrt(D), y=y, states=states)
+    t1.stop(s1)
+    s2 = t2.start()
+    for _ in range(nb):
+        rel.relation_linear_bwd(p1, p2, I, g, dy, cs, sn, scale=1 / math.sqrt(D), workspace=ws,
+                                fwd_states=states)
+    t2.stop(s2)
+    tfm, tbm = t1.mean_ms() / nb, t2.mean_ms() / nb
     return {"workload": f"linear relation fwd + bwd, RoPE, B={B} H={H} T={T} D={D}",
             "fwd_ms": fm, "tokens_per_s": B * T / (fm * 1e-3),
             "fwd_GBps": nbytes / (fm * 1e-3) / 1e9,
             "frac_hbm": nbytes / (fm * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "bwd_ms": bm, "bwd_GBps": bbytes / (bm * 1e-3) / 1e9,
             "bwd_frac_hbm": bbytes / (bm * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "fwdbwd_tokens_per_s": B * T / ((fm + bm) * 1e-3)}
+            "fwdbwd_tokens_per_s": B * T / ((fm + bm) * 1e-3),
+            "train_fwd_ms": tfm, "train_bwd_ms": tbm,
+            "train_fwdbwd_tokens_per_s": B * T / ((tfm + tbm) * 1e-3),
+            "train_note": "forward stores the per-chunk states, backward reuses them"}
 
 
 def bench_linear_step(rel, torch, dev, reps=200, B=32, H=12, D=64, seed=42):

@@ -31,6 +31,7 @@ __all__ = [
     "relation_mhr_bwd",
     "relation_linear_fwd",
     "relation_linear_bwd",
+    "linear_states_shape",
     "relation_linear_step",
     "relation_status_string",
     "relation_version",
@@ -129,12 +130,12 @@ def load_library():
                                      c_float, c_float, c_float, vp]
     lib.relation_linear_fwd.restype = c_int
     lib.relation_linear_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
-                                        vp, vp, vp, c_float, c_float, vp]
+                                        vp, vp, vp, vp, c_float, c_float, vp]
     lib.relation_linear_bwd_workspace_bytes.restype = c_size
     lib.relation_linear_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_linear_bwd.restype = c_int
     lib.relation_linear_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
-                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size, c_float,
+                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size, c_float,
                                         c_float, vp]
     lib.relation_linear_step.restype = c_int
     lib.relation_linear_step.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, vp,
@@ -480,10 +481,13 @@ def relation_mhr_bwd(p1, p2, I, y, dy, lse, rope_cos=None, rope_sin=None, theta=
 
 def relation_linear_fwd(p1, p2, I, g, rope_cos=None, rope_sin=None, state_in=None,
                         want_state=False, scale=None, tau_s=2.0, y=None, state_out=None,
-                        stream=None):
+                        states=None, stream=None):
     """Linear Relation forward (bf16 p1, p2, I [B, H, T, 64]; fp32 log
     retention g of the same shape). Optional RoPE tables [T, 32] and initial
-    state [B, H, 64, 64] fp32. Returns (y, state_out or None)."""
+    state [B, H, 64, 64] fp32. `states` (optional, fp32
+    [B, H, ceil(T / 128) + 1, 64, 64]) receives the state before every chunk
+    and the final state, for relation_linear_bwd(fwd_states=...). Returns
+    (y, state_out or None)."""
     lib = load_library()
     B, H, T, D = p1.shape
     dev, dt = p1.device, p1.dtype
@@ -499,20 +503,29 @@ def relation_linear_fwd(p1, p2, I, g, rope_cos=None, rope_sin=None, state_in=Non
         state_out = torch.empty((B, H, D, D), device=dev, dtype=torch.float32)
     if state_out is not None:
         _check(state_out, "state_out", torch.float32, (B, H, D, D), dev)
+    if states is not None:
+        _check(states, "states", torch.float32, linear_states_shape(B, H, T, D), dev)
     st = lib.relation_linear_fwd(_dtype_code(p1), B, H, T, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(g),
                                  _ptr(rope_cos), _ptr(rope_sin), _ptr(state_in), _ptr(y),
-                                 _ptr(state_out), _scale(D, scale), float(tau_s),
+                                 _ptr(state_out), _ptr(states), _scale(D, scale), float(tau_s),
                                  _stream(dev, stream))
     if st != 0:
         raise RelationError(st, "relation_linear_fwd")
     return y, state_out
 
 
+def linear_states_shape(B, H, T, D=64):
+    """Shape of the per-chunk states relation_linear_fwd can store: the state
+    before every 128-token chunk, then the final state."""
+    return (B, H, (T + 127) // 128 + 1, D, D)
+
+
 def relation_linear_bwd(p1, p2, I, g, dy, rope_cos=None, rope_sin=None, state_in=None,
                         dstate_out=None, want_dstate_in=False, scale=None, tau_s=2.0,
-                        workspace=None, stream=None):
+                        workspace=None, fwd_states=None, stream=None):
     """Gradients of relation_linear_fwd. Returns (dp1, dp2, dI, dg,
-    dstate_in or None); dg is fp32 like g."""
+    dstate_in or None); dg is fp32 like g. fwd_states: the `states` the
+    forward stored for these same inputs (skips the backward's state pass)."""
     lib = load_library()
     B, H, T, D = p1.shape
     dev, dt = p1.device, p1.dtype
@@ -523,6 +536,8 @@ def relation_linear_bwd(p1, p2, I, g, dy, rope_cos=None, rope_sin=None, state_in
     for name, t in (("state_in", state_in), ("dstate_out", dstate_out)):
         if t is not None:
             _check(t, name, torch.float32, (B, H, D, D), dev)
+    if fwd_states is not None:
+        _check(fwd_states, "fwd_states", torch.float32, linear_states_shape(B, H, T, D), dev)
     dp1, dp2, dI = torch.empty_like(p1), torch.empty_like(p2), torch.empty_like(I)
     dg = torch.empty_like(g)
     dstate_in = (torch.empty((B, H, D, D), device=dev, dtype=torch.float32)
@@ -533,7 +548,7 @@ def relation_linear_bwd(p1, p2, I, g, dy, rope_cos=None, rope_sin=None, state_in
     st = lib.relation_linear_bwd(_dtype_code(p1), B, H, T, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(g),
                                  _ptr(rope_cos), _ptr(rope_sin), _ptr(state_in), _ptr(dy),
                                  _ptr(dstate_out), _ptr(dp1), _ptr(dp2), _ptr(dI), _ptr(dg),
-                                 _ptr(dstate_in), _ptr(workspace),
+                                 _ptr(dstate_in), _ptr(fwd_states), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _scale(D, scale),
                                  float(tau_s), _stream(dev, stream))
     if st != 0:

@@ -119,8 +119,8 @@ hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint
                              const uint16_t* iv, const float* g, const float* rope_cos,
                              const float* rope_sin, const float* state_in, const uint16_t* dy,
                              const float* dstate_out, uint16_t* dp1, uint16_t* dp2, uint16_t* dI,
-                             float* dg, float* dstate_in, float* ws, float scale, float tau,
-                             hipStream_t stream);
+                             float* dg, float* dstate_in, const float* fwd_states, float* ws,
+                             float scale, float tau, hipStream_t stream);
 // One token per head; state [B, H, D, D] fp32 updated in place; rope tables
 // are the [D/2] rows of the token's position, or NULL.
 hipError_t launch_linear_step(int B, int H, const uint16_t* p1, const uint16_t* p2,

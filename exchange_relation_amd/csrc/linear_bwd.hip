@@ -618,17 +618,22 @@ hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint
                              const uint16_t* iv, const float* g, const float* rope_cos,
                              const float* rope_sin, const float* state_in, const uint16_t* dy,
                              const float* dstate_out, uint16_t* dp1, uint16_t* dp2, uint16_t* dI,
-                             float* dg, float* dstate_in, float* ws, float scale, float tau,
-                             hipStream_t stream) {
+                             float* dg, float* dstate_in, const float* fwd_states, float* ws,
+                             float scale, float tau, hipStream_t stream) {
   using namespace linrel;
   const int nch = (T + CH - 1) / CH;
   const size_t BH = static_cast<size_t>(B) * H;
-  float* states = ws;                              // [BH][nch + 1][D][D]
   float* dstates = ws + BH * (nch + 1) * D * D;    // [BH][nch][D][D]
-  // pass 1: the state before every chunk and the final state
-  hipError_t e = launch_linear_fwd_states(B, H, T, p1, p2, iv, g, rope_cos, rope_sin, state_in,
-                                          states, scale, tau, stream);
-  if (e != hipSuccess) return e;
+  // pass 1: the state before every chunk and the final state ([BH][nch + 1][D][D]),
+  // unless the forward stored them
+  const float* states = fwd_states;
+  hipError_t e = hipSuccess;
+  if (!states) {
+    e = launch_linear_fwd_states(B, H, T, p1, p2, iv, g, rope_cos, rope_sin, state_in, ws, scale,
+                                 tau, stream);
+    if (e != hipSuccess) return e;
+    states = ws;
+  }
   const float sl2 = scale * kLog2e / tau, slope = scale / tau;
   const dim3 gh(static_cast<unsigned>(BH)), gc(static_cast<unsigned>(BH * nch));
   // pass 2: the gradient of the state after every chunk

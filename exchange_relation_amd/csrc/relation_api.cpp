@@ -432,8 +432,8 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
 relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, int D,
                                     const void* p1, const void* p2, const void* I,
                                     const float* g, const float* rope_cos, const float* rope_sin,
-                                    const float* state_in, void* y, float* state_out, float scale,
-                                    float tau_s, void* stream) {
+                                    const float* state_in, void* y, float* state_out,
+                                    float* states, float scale, float tau_s, void* stream) {
   if (!p1 || !p2 || !I || !g || !y) return REL_ERR_NULL;
   if (!rope_cos != !rope_sin) return REL_ERR_NULL;
   if (dtype != REL_BF16 || D != 64) return REL_ERR_UNSUPPORTED;
@@ -442,12 +442,13 @@ relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, i
   if ((st = check_params(scale, tau_s, 0.f)) != REL_OK) return st;
   if (!aligned16(p1) || !aligned16(p2) || !aligned16(I) || !aligned16(g) || !aligned16(y) ||
       (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) ||
-      (state_in && !aligned4(state_in)) || (state_out && !aligned4(state_out)))
+      (state_in && !aligned4(state_in)) || (state_out && !aligned4(state_out)) ||
+      (states && !aligned4(states)))
     return REL_ERR_ALIGN;
   return from_hip(rel::launch_linear_fwd(
       B, H, T, static_cast<const uint16_t*>(p1), static_cast<const uint16_t*>(p2),
       static_cast<const uint16_t*>(I), g, rope_cos, rope_sin, state_in, static_cast<uint16_t*>(y),
-      state_out, nullptr, scale, tau_s, static_cast<hipStream_t>(stream)));
+      state_out, states, scale, tau_s, static_cast<hipStream_t>(stream)));
 }
 
 size_t relation_linear_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
@@ -460,9 +461,9 @@ relation_status relation_linear_bwd(relation_dtype dtype, int B, int H, int T, i
                                     const float* g, const float* rope_cos, const float* rope_sin,
                                     const float* state_in, const void* dy,
                                     const float* dstate_out, void* dp1, void* dp2, void* dI,
-                                    float* dg, float* dstate_in, void* workspace,
-                                    size_t workspace_bytes, float scale, float tau_s,
-                                    void* stream) {
+                                    float* dg, float* dstate_in, const float* fwd_states,
+                                    void* workspace, size_t workspace_bytes, float scale,
+                                    float tau_s, void* stream) {
   if (!p1 || !p2 || !I || !g || !dy || !dp1 || !dp2 || !dI || !dg) return REL_ERR_NULL;
   if (!rope_cos != !rope_sin) return REL_ERR_NULL;
   if (dtype != REL_BF16 || D != 64) return REL_ERR_UNSUPPORTED;
@@ -473,7 +474,7 @@ relation_status relation_linear_bwd(relation_dtype dtype, int B, int H, int T, i
       !aligned16(dp1) || !aligned16(dp2) || !aligned16(dI) || !aligned16(dg) ||
       (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) ||
       (state_in && !aligned4(state_in)) || (dstate_out && !aligned4(dstate_out)) ||
-      (dstate_in && !aligned4(dstate_in)))
+      (dstate_in && !aligned4(dstate_in)) || (fwd_states && !aligned4(fwd_states)))
     return REL_ERR_ALIGN;
   const size_t need = rel::linear_bwd_workspace_bytes(B, H, T);
   if (!workspace || workspace_bytes < need) return REL_ERR_WORKSPACE;
@@ -482,7 +483,7 @@ relation_status relation_linear_bwd(relation_dtype dtype, int B, int H, int T, i
       B, H, T, static_cast<const uint16_t*>(p1), static_cast<const uint16_t*>(p2),
       static_cast<const uint16_t*>(I), g, rope_cos, rope_sin, state_in,
       static_cast<const uint16_t*>(dy), dstate_out, static_cast<uint16_t*>(dp1),
-      static_cast<uint16_t*>(dp2), static_cast<uint16_t*>(dI), dg, dstate_in,
+      static_cast<uint16_t*>(dp2), static_cast<uint16_t*>(dI), dg, dstate_in, fwd_states,
       static_cast<float*>(workspace), scale, tau_s, static_cast<hipStream_t>(stream)));
 }
 

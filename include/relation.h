@@ -327,13 +327,18 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
  *   y                : out [B, H, T, D] bf16
  *   state_out        : out DEVICE fp32 [B, H, D, D] the state after the last
  *                      token, or NULL (a later call continues from it)
+ *   states           : out DEVICE fp32 [B, H, ceil(T / 128) + 1, D, D], 4-byte
+ *                      aligned, or NULL: the state before every 128-token
+ *                      chunk, then the final state. A training step passes
+ *                      it to relation_linear_bwd as fwd_states, which then
+ *                      skips its own state pass.
  *   scale, tau_s     : finite scale, tau_s > 0 (else REL_ERR_PARAM)
  */
 relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, int D,
                                     const void* p1, const void* p2, const void* I,
                                     const float* g, const float* rope_cos,
                                     const float* rope_sin, const float* state_in,
-                                    void* y, float* state_out,
+                                    void* y, float* state_out, float* states,
                                     float scale, float tau_s, void* stream);
 
 /*
@@ -351,6 +356,12 @@ relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, i
  *   dg               : out [B, H, T, D] fp32, gradient of the log retention
  *   dstate_in        : out DEVICE fp32 [B, H, D, D] gradient of state_in, or
  *                      NULL
+ *   fwd_states       : in  DEVICE fp32, 4-byte aligned, or NULL: the states
+ *                      relation_linear_fwd stored for these same inputs
+ *                      (its `states` output). Given, the first pass is
+ *                      skipped and its region of the workspace is unused;
+ *                      states of other inputs give wrong gradients, with no
+ *                      error.
  *   workspace        : relation_linear_bwd_workspace_bytes() bytes, 256-byte
  *                      aligned (B * H * (2 ceil(T / 128) + 1) * D * D floats:
  *                      the state before every chunk and the final state,
@@ -363,9 +374,9 @@ relation_status relation_linear_bwd(relation_dtype dtype, int B, int H, int T, i
                                     const float* rope_sin, const float* state_in,
                                     const void* dy, const float* dstate_out,
                                     void* dp1, void* dp2, void* dI, float* dg,
-                                    float* dstate_in, void* workspace,
-                                    size_t workspace_bytes, float scale, float tau_s,
-                                    void* stream);
+                                    float* dstate_in, const float* fwd_states,
+                                    void* workspace, size_t workspace_bytes, float scale,
+                                    float tau_s, void* stream);
 
 /*
  * relation_linear_step — one decode step of Linear Relation (the recurrent

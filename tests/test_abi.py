@@ -218,9 +218,9 @@ def test_mhr_validation(lib):
 
 def test_linear_validation(lib):
     def lfwd(dtype=BF16, B=1, H=1, T=8, D=64, p1=P, g=P, y=P, rc=NUL, rs=NUL, cin=NUL,
-             cout=NUL, scale=0.125, tau=2.0):
+             cout=NUL, states=NUL, scale=0.125, tau=2.0):
         return lib.relation_linear_fwd(dtype, B, H, T, D, p1, P, P, g, rc, rs, cin, y, cout,
-                                       scale, tau, None)
+                                       states, scale, tau, None)
 
     assert lfwd(p1=NUL) == REL_ERR_NULL
     assert lfwd(g=NUL) == REL_ERR_NULL
@@ -235,6 +235,7 @@ def test_linear_validation(lib):
     assert lfwd(g=P_MIS) == REL_ERR_ALIGN
     assert lfwd(rc=P_MIS, rs=P) == REL_ERR_ALIGN
     assert lfwd(cout=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+    assert lfwd(states=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
 
     need = lib.relation_linear_bwd_workspace_bytes(BF16, 2, 3, 300, 64)
     # the state before every 128-token chunk and the final one, then the
@@ -243,9 +244,9 @@ def test_linear_validation(lib):
     assert lib.relation_linear_bwd_workspace_bytes(F32, 2, 3, 300, 64) == 0
     assert lib.relation_linear_bwd_workspace_bytes(BF16, 2, 3, 300, 48) == 0
 
-    def lbwd(dtype=BF16, D=64, dy=P, dg=P, ws=P, wsb=need, dsin=NUL, tau=2.0):
+    def lbwd(dtype=BF16, D=64, dy=P, dg=P, ws=P, wsb=need, dsin=NUL, fst=NUL, tau=2.0):
         return lib.relation_linear_bwd(dtype, 2, 3, 300, D, P, P, P, P, NUL, NUL, NUL, dy, NUL,
-                                       P, P, P, dg, dsin, ws, wsb, 0.125, tau, None)
+                                       P, P, P, dg, dsin, fst, ws, wsb, 0.125, tau, None)
 
     assert lbwd(dy=NUL) == REL_ERR_NULL
     assert lbwd(dg=NUL) == REL_ERR_NULL
@@ -257,6 +258,7 @@ def test_linear_validation(lib):
     assert lbwd(ws=ctypes.c_void_p(0x7F0000000010)) == REL_ERR_ALIGN
     assert lbwd(dg=P_MIS) == REL_ERR_ALIGN
     assert lbwd(dsin=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+    assert lbwd(fst=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN  # the forward's states
 
     def lstep(dtype=BF16, B=1, H=1, D=64, st=P, y=P, tau=2.0):
         return lib.relation_linear_step(dtype, B, H, D, P, P, P, P, NUL, NUL, st, y, 0.125, tau,

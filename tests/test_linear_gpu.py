@@ -195,6 +195,35 @@ def run_bwd(d, rope=None, C0=None, dCT=None):
     return [t.cpu() for t in out]
 
 
+def test_linear_bwd_reuses_forward_states():
+    """The forward can store the state before every chunk (and the final
+    state); the backward given them skips its own state pass. y and the final
+    state are unchanged bit for bit, the last stored state is state_out, and
+    every gradient equals the three-pass backward's bit for bit (both sides
+    run the same state recurrence)."""
+    B, H, T = 2, 3, 300
+    d = make_linear_inputs(B, H, T, 64, seed=77, with_dy=True)
+    cs, sn = (t.to(DEV) for t in tables(T))
+    C0 = (0.1 * torch.randn(B, H, 64, 64, generator=torch.Generator().manual_seed(5))).to(DEV)
+    dCT = torch.randn(B, H, 64, 64, generator=torch.Generator().manual_seed(6)).to(DEV)
+    p1, p2, I, g, dy = (d[n].to(DEV) for n in ("p1", "p2", "I", "g", "dy"))
+    kw = dict(rope_cos=cs, rope_sin=sn, state_in=C0, scale=SCALE, tau_s=TAU)
+    states = torch.full(rel.linear_states_shape(B, H, T), float("nan"), device=DEV)
+    assert states.shape[2] == 4  # ceil(300 / 128) chunks, then the final state
+    y0, c0 = rel.relation_linear_fwd(p1, p2, I, g, want_state=True, **kw)
+    y1, c1 = rel.relation_linear_fwd(p1, p2, I, g, want_state=True, states=states, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(c0, c1)
+    assert torch.equal(states[:, :, -1], c1)
+    assert torch.equal(states[:, :, 0], C0)  # the state before the first chunk
+    ref = rel.relation_linear_bwd(p1, p2, I, g, dy, dstate_out=dCT, want_dstate_in=True, **kw)
+    got = rel.relation_linear_bwd(p1, p2, I, g, dy, dstate_out=dCT, want_dstate_in=True,
+                                  fwd_states=states, **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dp1", "dp2", "dI", "dg", "dstate_in"), got, ref):
+        assert torch.equal(a, b), name
+
+
 def oracle_bwd(d, rope=None, C0=None, dCT=None):
     cs, sn = (None, None) if rope is None else (f64(rope[0]), f64(rope[1]))
     return oracle.linear_relation_backward(
