@@ -32,6 +32,8 @@ __all__ = [
     "relation_linear_fwd",
     "relation_linear_bwd",
     "linear_states_shape",
+    "LinearRelationFunction",
+    "linear_relation",
     "relation_linear_step",
     "relation_status_string",
     "relation_version",
@@ -632,6 +634,45 @@ class MultiHeadRelationFunction(torch.autograd.Function):
             p1, p2, I, y, dy.contiguous(), lse, rope_cos, rope_sin, theta, ctx.pairing,
             lam=ctx.lam, scale=ctx.scale, tau_s=ctx.tau_s, fwd_workspace=ws)
         return (dp1, dp2, dI, dlam.reshape(ctx.lam_shape), dth, None, None, None, None, None)
+
+
+class LinearRelationFunction(torch.autograd.Function):
+    """autograd wrapper of relation_linear_fwd / relation_linear_bwd:
+    gradients for p1, p2, I, the log retention g and the initial state. The
+    forward stores the state before every chunk, and the backward reads them
+    instead of running its own state pass."""
+
+    @staticmethod
+    def forward(ctx, p1, p2, I, g, state_in, rope_cos, rope_sin, scale, tau_s):
+        B, H, T, D = p1.shape
+        states = torch.empty(linear_states_shape(B, H, T, D), device=p1.device,
+                             dtype=torch.float32)
+        y, state_out = relation_linear_fwd(p1, p2, I, g, rope_cos, rope_sin, state_in,
+                                           want_state=True, scale=scale, tau_s=tau_s,
+                                           states=states)
+        ctx.save_for_backward(p1, p2, I, g, state_in, rope_cos, rope_sin, states)
+        ctx.scale, ctx.tau_s = scale, tau_s
+        ctx.set_materialize_grads(False)
+        return y, state_out
+
+    @staticmethod
+    def backward(ctx, dy, dstate_out):
+        p1, p2, I, g, state_in, rope_cos, rope_sin, states = ctx.saved_tensors
+        if dy is None:
+            dy = torch.zeros_like(I)
+        want_dsin = state_in is not None and ctx.needs_input_grad[4]
+        dp1, dp2, dI, dg, dsin = relation_linear_bwd(
+            p1, p2, I, g, dy.contiguous(), rope_cos, rope_sin, state_in,
+            dstate_out=None if dstate_out is None else dstate_out.contiguous(),
+            want_dstate_in=want_dsin, scale=ctx.scale, tau_s=ctx.tau_s, fwd_states=states)
+        return dp1, dp2, dI, dg, dsin, None, None, None, None
+
+
+def linear_relation(p1, p2, I, g, state_in=None, rope_cos=None, rope_sin=None, scale=None,
+                    tau_s=2.0):
+    """Differentiable Linear Relation: returns (y, state_out), both with
+    gradients (state_out continues into a later call)."""
+    return LinearRelationFunction.apply(p1, p2, I, g, state_in, rope_cos, rope_sin, scale, tau_s)
 
 
 def mhr_relation(p1, p2, I, lam, theta=None, rope_cos=None, rope_sin=None, pairing=0, scale=None,

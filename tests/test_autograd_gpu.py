@@ -66,3 +66,37 @@ def test_mhr_relation_autograd_matches_direct_calls(dtype):
         assert torch.equal(pa.grad, g0[0])
     else:
         close(pa.grad, g0[0])
+
+
+def test_linear_relation_autograd_matches_direct_calls_and_oracle():
+    """exchange_relation_amd.linear_relation: y and the final state from the
+    forward, and through autograd (with gradients on both outputs) the same
+    gradients as the direct three-pass relation_linear_bwd, bit for bit (the
+    wrapper's backward reuses the forward's per-chunk states); dp1 also
+    against the fp64 oracle."""
+    from workloads import make_linear_inputs
+    B, H, T, D = 2, 2, 260, 64
+    d = make_linear_inputs(B, H, T, D, seed=1300, with_dy=True)
+    p1, p2, I, g, dy = (d[n].to(DEV) for n in ("p1", "p2", "I", "g", "dy"))
+    cs, sn, _ = (t.to(DEV) for t in make_mhr_maps(T, D, 2, 1300))
+    gen = torch.Generator().manual_seed(1301)
+    C0 = (0.1 * torch.randn(B, H, D, D, generator=gen)).to(DEV)
+    dCT = torch.randn(B, H, D, D, generator=gen).to(DEV)
+    scale = 1 / math.sqrt(D)
+    leaves = [x.clone().requires_grad_(True) for x in (p1, p2, I, g, C0)]
+    y, cT = rel.linear_relation(*leaves, rope_cos=cs, rope_sin=sn, scale=scale)
+    ((y.float() * dy.float()).sum() + (cT * dCT).sum()).backward()
+    y0, c0 = rel.relation_linear_fwd(p1, p2, I, g, cs, sn, C0, want_state=True, scale=scale)
+    ref = rel.relation_linear_bwd(p1, p2, I, g, dy, cs, sn, C0, dstate_out=dCT,
+                                  want_dstate_in=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach(), y0) and torch.equal(cT.detach(), c0)
+    for name, leaf, r in zip(("dp1", "dp2", "dI", "dg", "dstate_in"), leaves, ref):
+        assert torch.equal(leaf.grad, r), name
+    o = oracle.linear_relation_backward(
+        *(d[n].double().numpy() for n in ("p1", "p2", "I", "g", "dy")), scale, 2.0,
+        cs.cpu().double().numpy(), sn.cpu().double().numpy(), C0=C0.cpu().double().numpy(),
+        dC_T=dCT.cpu().double().numpy())
+    ref_dp1 = o["dp1"] if isinstance(o, dict) else o[0]
+    err = np.abs(leaves[0].grad.cpu().double().numpy() - ref_dp1)
+    assert float(err.max()) <= 2e-2 * max(1.0, float(np.abs(ref_dp1).max()) / 4)
