@@ -7,14 +7,20 @@ TFLOP/s (fwd = 2*B*H*T^2*D flops, bwd = 2.5x fwd). The same run also measures
 the forward alone on the 10M / 30M / 100M layer shapes, forward+backward on
 the 100M shape beside torch's causal scaled-dot-product attention of the same
 shape, and 256 Relation Cache decode steps (B=32, H=12, D=64, history 4096) in
-GB/s, plus the fp64 CPU oracle on a bounded sample (cpu_baseline). The extra
+GB/s, plus the fp64 CPU oracle on a bounded sample of every workload
+(cpu_baseline). Before the W warm-up steps, untimed steps run for
+--prewarm-ms of wall time so that the timed window starts at steady clocks
+(reported as prewarm_ms / prewarm_steps). The extra
 lines cover ragged decode, chunked prefill, Multi-Head Relation and Linear
 Relation (forward, backward, decode step); `roofline*` objects price the
 dominant kernel of each against MI355X's published peaks.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extra] [--only {step,fwd,decode,ragged,mhr,prefill,
-                       attn,linear,copy}]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-ms MS]
+                       [--no-cpu-baseline] [--no-extra]
+                       [--only {step,fwd,fwd10m,fwd100m,decode,ragged,mhr,prefill,
+                                attn,linear,copy,cpu}]
+--only runs one workload and prints its raw numbers (one workload per run, so
+that a profile of it holds that workload alone).
 """
 import argparse
 import json
@@ -63,7 +69,22 @@ class EventTimer:
         return sum(v) / len(v) if v else float("nan")
 
 
-def bench_step(rel, torch, dev, steps, warmup, B=16, H=8, T=2048, D=64, seed=42):
+def prewarm(torch, fn, ms):
+    """Clock ramp: call fn() back to back until `ms` milliseconds of wall time
+    have passed (synchronising every few calls), so that the timed window
+    starts at the GPU's steady clocks whatever the untimed step count is.
+    Returns (wall ms spent, calls)."""
+    t0, n = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3, n
+
+
+def bench_step(rel, torch, dev, steps, warmup, B=16, H=8, T=2048, D=64, seed=42,
+               prewarm_ms=0.0):
     from workloads import make_inputs
     inp = make_inputs(B, H, T, D, "bf16", seed=seed, with_dy=True)
     lam, scale = inp["lam"], 1.0 / math.sqrt(D)
@@ -88,6 +109,7 @@ def bench_step(rel, torch, dev, steps, warmup, B=16, H=8, T=2048, D=64, seed=42)
         if timed:
             tb.stop(s)
 
+    pw_ms, pw_n = prewarm(torch, lambda: step(False), prewarm_ms)
     for _ in range(warmup):
         step(False)
     torch.cuda.synchronize()
@@ -97,10 +119,11 @@ def bench_step(rel, torch, dev, steps, warmup, B=16, H=8, T=2048, D=64, seed=42)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return {"ms_per_step": (t1 - t0) * 1e3 / steps, "fwd_ms": tf.mean_ms(),
-            "bwd_ms": tb.mean_ms(), "flops_fwd": fwd_flops(B, H, T, D)}
+            "bwd_ms": tb.mean_ms(), "flops_fwd": fwd_flops(B, H, T, D),
+            "prewarm_ms": pw_ms, "prewarm_steps": pw_n}
 
 
-def bench_fwd(rel, torch, dev, B, H, T, D, reps, rope=False, seed=42):
+def bench_fwd(rel, torch, dev, B, H, T, D, reps, rope=False, seed=42, prewarm_ms=100.0):
     from workloads import make_inputs
     inp = make_inputs(B, H, T, D, "bf16", seed=seed, rope=rope)
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
@@ -110,10 +133,8 @@ def bench_fwd(rel, torch, dev, B, H, T, D, reps, rope=False, seed=42):
     t = EventTimer(torch, stream)
     nws = rel.relation_fwd_workspace_bytes(torch.bfloat16, B, H, T, D)
     ws = torch.empty((nws,), device=dev, dtype=torch.uint8) if nws else None
-    for _ in range(3):
-        rel.relation_fwd(q, k, v, lam=inp["lam"], scale=1 / math.sqrt(D), y=y, lse=lse,
-                         workspace=ws)
-    torch.cuda.synchronize()
+    prewarm(torch, lambda: rel.relation_fwd(q, k, v, lam=inp["lam"], scale=1 / math.sqrt(D),
+                                            y=y, lse=lse, workspace=ws), prewarm_ms)
     # back-to-back calls between one pair of events: a short call (the 10M
     # layer's is ~20 us) would otherwise also time the host's launch path
     s = t.start()
@@ -127,7 +148,8 @@ def bench_fwd(rel, torch, dev, B, H, T, D, reps, rope=False, seed=42):
             "timing": f"{reps} back-to-back calls", "split_over_keys": nws > 0}
 
 
-def bench_fwdbwd_vs_attention(rel, torch, dev, reps, B=8, H=12, T=4096, D=64, seed=42):
+def bench_fwdbwd_vs_attention(rel, torch, dev, reps, B=8, H=12, T=4096, D=64, seed=42,
+                              prewarm_ms=200.0):
     from workloads import make_inputs
     inp = make_inputs(B, H, T, D, "bf16", seed=seed, with_dy=True)
     q, k, v, dy = (inp[n].to(dev) for n in ("q", "k", "v", "dy"))
@@ -140,6 +162,12 @@ def bench_fwdbwd_vs_attention(rel, torch, dev, reps, B=8, H=12, T=4096, D=64, se
                      device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev)
     tf_, tfb = EventTimer(torch, stream), EventTimer(torch, stream)
+
+    def rel_step():
+        rel.relation_fwd(q, k, v, lam=lam, scale=scale, y=y, lse=lse)
+        rel.relation_bwd(q, k, v, y, dy, lse, lam=lam, scale=scale, dq=dq, dk=dk, dv=dv,
+                         dlambda=dl, workspace=ws)
+    prewarm(torch, rel_step, prewarm_ms)
     for i in range(reps + 2):
         s = tf_.start() if i >= 2 else None
         rel.relation_fwd(q, k, v, lam=lam, scale=scale, y=y, lse=lse)
@@ -160,6 +188,11 @@ def bench_fwdbwd_vs_attention(rel, torch, dev, reps, B=8, H=12, T=4096, D=64, se
         import torch.nn.functional as Fn
         qa, ka, va = (x.detach().clone().requires_grad_(True) for x in (q, k, v))
         ta, tab = EventTimer(torch, stream), EventTimer(torch, stream)
+
+        def attn_step():
+            Fn.scaled_dot_product_attention(qa, ka, va, is_causal=True, scale=scale).backward(dy)
+            qa.grad = ka.grad = va.grad = None
+        prewarm(torch, attn_step, prewarm_ms)
         for i in range(reps + 2):
             s = ta.start() if i >= 2 else None
             o = Fn.scaled_dot_product_attention(qa, ka, va, is_causal=True, scale=scale)
@@ -182,7 +215,8 @@ def bench_fwdbwd_vs_attention(rel, torch, dev, reps, B=8, H=12, T=4096, D=64, se
     return out
 
 
-def bench_decode(rel, torch, dev, B=32, H=12, D=64, n0=4096, steps=256, cap=4352, seed=42):
+def bench_decode(rel, torch, dev, B=32, H=12, D=64, n0=4096, steps=256, cap=4352, seed=42,
+                 prewarm_ms=200.0):
     from workloads import make_decode_inputs
     d = make_decode_inputs(B, H, D, n0, steps, cap, "bf16", seed=seed)
     kc, vc = d["k_cache"].to(dev), d["v_cache"].to(dev)
@@ -192,7 +226,10 @@ def bench_decode(rel, torch, dev, B=32, H=12, D=64, n0=4096, steps=256, cap=4352
                      device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev)
     kc0, vc0 = kc.clone(), vc.clone()
-    # warm-up pass over a copy of the cache, then restore
+    # warm-up (clock ramp) on the first steps' slots, then restore the cache
+    prewarm(torch, lambda: rel.relation_cache_decode(qs[0], kn[0], vn[0], kc, vc, n0,
+                                                     lam=d["lam"], scale=1 / math.sqrt(D), y=y,
+                                                     workspace=ws), prewarm_ms)
     for s in range(4):
         rel.relation_cache_decode(qs[s], kn[s], vn[s], kc, vc, n0 + s, lam=d["lam"],
                                   scale=1 / math.sqrt(D), y=y, workspace=ws)
@@ -461,44 +498,113 @@ def kernel_traffic(name):
         return None
 
 
-def cpu_baseline(budget_s=15.0, max_heads=32):
-    """The fp64 oracle, as it stands, on a bounded sample of the step's
-    workload: whole heads of the 30M layer (T=2048, D=64), forward + backward
-    (materialised), run until about budget_s seconds are spent; scaled to
-    TFLOP/s with the same algorithmic count as the GPU."""
-    import oracle
-    from workloads import make_inputs
+def _oracle_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    inp = make_inputs(1, max_heads, 2048, 64, "bf16", seed=42, with_dy=True)
-    f64 = {n: inp[n][0].double().numpy() for n in ("q", "k", "v", "dy")}
-    heads, t0 = 0, time.perf_counter()
-    while heads < max_heads and (time.perf_counter() - t0) < budget_s:
-        oracle.relation_backward_head(f64["q"][heads], f64["k"][heads], f64["v"][heads],
-                                      f64["dy"][heads], 1 / 8, 2.0, inp["lam"])
-        heads += 1
-    dt = time.perf_counter() - t0
-    flops = 3.5 * fwd_flops(1, heads, 2048, 64)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} whole heads (of 128) of the B=16,H=8,T=2048,D=64 layer, "
-                      f"fwd+bwd, materialised fp64 numpy, {dt:.1f} s; "
-                      f"host cpu_count={os.cpu_count()}"}
+        return len(os.sched_getaffinity(0))
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline():
+    """The fp64 oracle, as it stands, timed on this host on a bounded sample
+    of every workload (about 20 s of CPU work in all), each scaled to the
+    workload's unit with the same algorithmic count as the GPU lines:
+      * single Multi-Head Relation forward, fp32, B=1 H=2 T=128 D=32: whole;
+      * 10M layer forward (B=8 H=8 T=1024 D=64, RoPE'd q / k): 8 of 64 heads;
+      * 30M layer (B=16 H=8 T=2048 D=64): forward on 4 heads, forward +
+        backward on 8 heads (of 128);
+      * 100M layer (B=8 H=12 T=4096 D=64): forward on 1 head, forward +
+        backward on 1 head (of 96);
+      * Relation Cache decode (B=32 H=12 D=64, history 4096): the first 2 of
+        the 256 steps, whole batch, in GB/s of the step's algorithmic bytes.
+    Heads are whole (each head's rows are independent of the others), so
+    the per-head time scales exactly to the full workload's count.
+    `value` is the 30M layer's forward + backward (the step's metric)."""
+    import oracle
+    from workloads import make_decode_inputs, make_inputs
+
+    def f64(t):
+        return t.double().numpy()
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    per = {}
+
+    def heads_run(key, B, H, T, D, dtype, nh, kind, rope=False):
+        inp = make_inputs(B, H, T, D, dtype, seed=42, rope=rope, with_dy=(kind == "fwdbwd"))
+        a = {n: f64(inp[n].reshape(B * H, T, D)[:nh]) for n in inp if n != "lam"}
+        s = 1 / math.sqrt(D)
+        if kind == "fwd":
+            dt = timed(lambda: [oracle.relation_forward_head(a["q"][i], a["k"][i], a["v"][i], s,
+                                                             2.0, inp["lam"]) for i in range(nh)])
+            fl = fwd_flops(1, nh, T, D)
+        else:
+            dt = timed(lambda: [oracle.relation_backward_head(a["q"][i], a["k"][i], a["v"][i],
+                                                              a["dy"][i], s, 2.0, inp["lam"])
+                                for i in range(nh)])
+            fl = 3.5 * fwd_flops(1, nh, T, D)
+        per[key] = {"kind": kind, "sample": f"{nh} of {B * H} heads", "seconds": dt,
+                    "value": fl / dt / 1e12, "unit": "TFLOP/s",
+                    "full_workload_seconds_est": dt * B * H / nh}
+
+    heads_run("mhr_fwd_f32", 1, 2, 128, 32, "f32", 2, "fwd")
+    heads_run("layer10m_fwd_bf16", 8, 8, 1024, 64, "bf16", 8, "fwd", rope=True)
+    heads_run("layer30m_fwd_bf16", 16, 8, 2048, 64, "bf16", 4, "fwd")
+    heads_run("layer30m_fwdbwd_bf16", 16, 8, 2048, 64, "bf16", 8, "fwdbwd")
+    heads_run("layer100m_fwd_bf16", 8, 12, 4096, 64, "bf16", 1, "fwd")
+    heads_run("layer100m_fwdbwd_bf16", 8, 12, 4096, 64, "bf16", 1, "fwdbwd")
+    B, H, D, n0, cap, nst = 32, 12, 64, 4096, 4352, 2
+    d = make_decode_inputs(B, H, D, n0, nst, cap, "bf16", seed=42)
+    kc, vc = f64(d["k_cache"]), f64(d["v_cache"])
+    dt = 0.0
+    for st in range(nst):
+        t0 = time.perf_counter()
+        _, _, kc, vc = oracle.relation_decode_step(f64(d["q"][st]), f64(d["k_new"][st]),
+                                                   f64(d["v_new"][st]), kc, vc, n0 + st,
+                                                   1 / math.sqrt(D), 2.0, d["lam"])
+        dt += time.perf_counter() - t0
+    byts = sum(decode_bytes(B, H, D, n0 + st) for st in range(nst))
+    per["cache_decode_bf16"] = {"kind": "decode", "sample": f"steps 0..{nst - 1} of 256, whole "
+                                "batch", "seconds": dt, "value": byts / dt / 1e9, "unit": "GB/s",
+                                "full_workload_seconds_est": dt * 256 / nst}
+    head = per["layer30m_fwdbwd_bf16"]
+    return {"value": head["value"], "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "kind": "oracle",
+            "sample": "30M layer (B=16,H=8,T=2048,D=64) fwd+bwd on 8 whole heads of 128, "
+                      f"materialised fp64 numpy, {head['seconds']:.1f} s; per_config holds "
+                      "every workload's sample",
+            "host": {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+                     "cpu_model": _cpu_model()},
+            "per_config": per}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the GPU's clocks take on the order of 0.1 s of sustained work to ramp;
-    # 200 untimed steps of the 30M-layer step are about that
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU's clocks take on the order of 0.1 s of sustained work to ramp:
+    # a time-based phase of untimed steps comes before the W warm-up steps
+    ap.add_argument("--prewarm-ms", type=float, default=500.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["step", "fwd", "decode", "ragged", "mhr", "prefill", "attn",
-                             "linear", "copy"],
+    ap.add_argument("--only", choices=["step", "fwd", "fwd10m", "fwd100m", "decode", "ragged",
+                                       "mhr", "prefill", "attn", "linear", "copy", "cpu"],
                     default=None,
                     help="run one measurement and print its raw numbers ('copy': a plain "
                          "device copy of known size, the HBM-counter calibration)")
@@ -520,11 +626,24 @@ def main():
     if args.only == "copy":
         print(json.dumps(bench_copy(torch, dev)))
         return
+    if args.only == "cpu":
+        print(json.dumps(cpu_baseline()))
+        return
     if args.only == "step":
-        print(json.dumps(bench_step(rel, torch, dev, args.steps, args.warmup)))
+        print(json.dumps(bench_step(rel, torch, dev, args.steps, args.warmup,
+                                    prewarm_ms=args.prewarm_ms)))
         return
     if args.only == "fwd":
-        print(json.dumps(bench_fwd(rel, torch, dev, 16, 8, 2048, 64, args.steps)))
+        print(json.dumps(bench_fwd(rel, torch, dev, 16, 8, 2048, 64, args.steps,
+                                   prewarm_ms=args.prewarm_ms)))
+        return
+    if args.only == "fwd10m":
+        print(json.dumps(bench_fwd(rel, torch, dev, 8, 8, 1024, 64, args.steps, rope=True,
+                                   prewarm_ms=args.prewarm_ms)))
+        return
+    if args.only == "fwd100m":
+        print(json.dumps(bench_fwd(rel, torch, dev, 8, 12, 4096, 64, args.steps,
+                                   prewarm_ms=args.prewarm_ms)))
         return
     if args.only == "decode":
         print(json.dumps(bench_decode(rel, torch, dev)))
@@ -546,7 +665,7 @@ def main():
         print(json.dumps(bench_fwdbwd_vs_attention(rel, torch, dev, args.steps)))
         return
 
-    st = bench_step(rel, torch, dev, args.steps, args.warmup)
+    st = bench_step(rel, torch, dev, args.steps, args.warmup, prewarm_ms=args.prewarm_ms)
     f = st["flops_fwd"]
     value = 3.5 * f / (st["ms_per_step"] * 1e-3) / 1e12
     bwd_tf = 2.5 * f / (st["bwd_ms"] * 1e-3) / 1e12
@@ -554,6 +673,7 @@ def main():
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": st["ms_per_step"],
+        "prewarm_ms": round(st["prewarm_ms"], 1), "prewarm_steps": st["prewarm_steps"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Gaussian q, k, v, dY; no dataset)",
         "config": {"workload": "layer30m_fwdbwd_bf16", "B": 16, "H": 8, "T": 2048, "D": 64,

@@ -61,7 +61,9 @@ EXPORTED_SYMBOLS = (
     "relation_mhr_bwd_workspace_bytes",
     "relation_mhr_bwd",
     "relation_linear_fwd",
+    "relation_linear_states_bytes",
     "relation_linear_bwd_workspace_bytes",
+    "relation_linear_bwd_reuse_workspace_bytes",
     "relation_linear_bwd",
     "relation_linear_step",
     "relation_status_string",
@@ -133,8 +135,10 @@ def load_library():
     lib.relation_linear_fwd.restype = c_int
     lib.relation_linear_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp, c_float, c_float, vp]
-    lib.relation_linear_bwd_workspace_bytes.restype = c_size
-    lib.relation_linear_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    for fn in ("relation_linear_states_bytes", "relation_linear_bwd_workspace_bytes",
+               "relation_linear_bwd_reuse_workspace_bytes"):
+        getattr(lib, fn).restype = c_size
+        getattr(lib, fn).argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_linear_bwd.restype = c_int
     lib.relation_linear_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size, c_float,
@@ -518,8 +522,12 @@ def relation_linear_fwd(p1, p2, I, g, rope_cos=None, rope_sin=None, state_in=Non
 
 def linear_states_shape(B, H, T, D=64):
     """Shape of the per-chunk states relation_linear_fwd can store: the state
-    before every 128-token chunk, then the final state."""
-    return (B, H, (T + 127) // 128 + 1, D, D)
+    before every chunk, then the final state ([B, H, nchunks + 1, D, D] fp32;
+    the library's relation_linear_states_bytes gives the size)."""
+    n = int(load_library().relation_linear_states_bytes(REL_BF16, B, H, T, D))
+    if n == 0:
+        raise ValueError(f"no Linear Relation states for B={B} H={H} T={T} D={D}")
+    return (B, H, n // (B * H * D * D * 4), D, D)
 
 
 def relation_linear_bwd(p1, p2, I, g, dy, rope_cos=None, rope_sin=None, state_in=None,
@@ -544,7 +552,9 @@ def relation_linear_bwd(p1, p2, I, g, dy, rope_cos=None, rope_sin=None, state_in
     dg = torch.empty_like(g)
     dstate_in = (torch.empty((B, H, D, D), device=dev, dtype=torch.float32)
                  if want_dstate_in else None)
-    need = int(lib.relation_linear_bwd_workspace_bytes(_dtype_code(p1), B, H, T, D))
+    query = (lib.relation_linear_bwd_workspace_bytes if fwd_states is None
+             else lib.relation_linear_bwd_reuse_workspace_bytes)
+    need = int(query(_dtype_code(p1), B, H, T, D))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), device=dev, dtype=torch.uint8)
     st = lib.relation_linear_bwd(_dtype_code(p1), B, H, T, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(g),

@@ -112,9 +112,11 @@ hipError_t launch_linear_fwd_states(int B, int H, int T, const uint16_t* p1, con
                                     float scale, float tau, hipStream_t stream);
 // Backward: gradients of relation_linear_fwd. ws: linear_bwd_workspace_bytes()
 // (the states of the state pass, then the gradient of the state after every
-// chunk); dstate_out, the gradient of the final state, or NULL; dstate_in
-// (out) or NULL.
-size_t linear_bwd_workspace_bytes(int B, int H, int T);
+// chunk; with fwd_states, only the state gradients); dstate_out, the gradient
+// of the final state, or NULL; dstate_in (out) or NULL.
+size_t linear_bwd_workspace_bytes(int B, int H, int T, bool with_fwd_states);
+// Bytes of the per-chunk states ([B, H, nchunks + 1, D, D] fp32).
+size_t linear_states_bytes(int B, int H, int T);
 hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint16_t* p2,
                              const uint16_t* iv, const float* g, const float* rope_cos,
                              const float* rope_sin, const float* state_in, const uint16_t* dy,

@@ -623,7 +623,9 @@ hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint
   using namespace linrel;
   const int nch = (T + CH - 1) / CH;
   const size_t BH = static_cast<size_t>(B) * H;
-  float* dstates = ws + BH * (nch + 1) * D * D;    // [BH][nch][D][D]
+  // [BH][nch][D][D], after the state pass's region unless the forward's
+  // states are given (then the workspace holds only the state gradients)
+  float* dstates = fwd_states ? ws : ws + BH * (nch + 1) * D * D;
   // pass 1: the state before every chunk and the final state ([BH][nch + 1][D][D]),
   // unless the forward stored them
   const float* states = fwd_states;
@@ -654,10 +656,17 @@ hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint
   return hipGetLastError();
 }
 
-size_t linear_bwd_workspace_bytes(int B, int H, int T) {
+size_t linear_bwd_workspace_bytes(int B, int H, int T, bool with_fwd_states) {
   using namespace linrel;
   const size_t nch = (T + CH - 1) / CH;
-  return static_cast<size_t>(B) * H * (2 * nch + 1) * D * D * sizeof(float);
+  return static_cast<size_t>(B) * H * ((with_fwd_states ? 0 : nch + 1) + nch) * D * D *
+         sizeof(float);
+}
+
+size_t linear_states_bytes(int B, int H, int T) {
+  using namespace linrel;
+  const size_t nch = (T + CH - 1) / CH;
+  return static_cast<size_t>(B) * H * (nch + 1) * D * D * sizeof(float);
 }
 
 }  // namespace rel

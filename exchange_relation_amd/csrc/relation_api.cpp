@@ -443,7 +443,7 @@ relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, i
   if (!aligned16(p1) || !aligned16(p2) || !aligned16(I) || !aligned16(g) || !aligned16(y) ||
       (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) ||
       (state_in && !aligned4(state_in)) || (state_out && !aligned4(state_out)) ||
-      (states && !aligned4(states)))
+      (states && !aligned16(states)))
     return REL_ERR_ALIGN;
   return from_hip(rel::launch_linear_fwd(
       B, H, T, static_cast<const uint16_t*>(p1), static_cast<const uint16_t*>(p2),
@@ -451,9 +451,20 @@ relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, i
       state_out, states, scale, tau_s, static_cast<hipStream_t>(stream)));
 }
 
+size_t relation_linear_states_bytes(relation_dtype dtype, int B, int H, int T, int D) {
+  if (dtype != REL_BF16 || D != 64 || check_shape(B, H, T, D) != REL_OK) return 0;
+  return rel::linear_states_bytes(B, H, T);
+}
+
 size_t relation_linear_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
   if (dtype != REL_BF16 || D != 64 || check_shape(B, H, T, D) != REL_OK) return 0;
-  return rel::linear_bwd_workspace_bytes(B, H, T);
+  return rel::linear_bwd_workspace_bytes(B, H, T, false);
+}
+
+size_t relation_linear_bwd_reuse_workspace_bytes(relation_dtype dtype, int B, int H, int T,
+                                                 int D) {
+  if (dtype != REL_BF16 || D != 64 || check_shape(B, H, T, D) != REL_OK) return 0;
+  return rel::linear_bwd_workspace_bytes(B, H, T, true);
 }
 
 relation_status relation_linear_bwd(relation_dtype dtype, int B, int H, int T, int D,
@@ -474,9 +485,9 @@ relation_status relation_linear_bwd(relation_dtype dtype, int B, int H, int T, i
       !aligned16(dp1) || !aligned16(dp2) || !aligned16(dI) || !aligned16(dg) ||
       (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) ||
       (state_in && !aligned4(state_in)) || (dstate_out && !aligned4(dstate_out)) ||
-      (dstate_in && !aligned4(dstate_in)) || (fwd_states && !aligned4(fwd_states)))
+      (dstate_in && !aligned4(dstate_in)) || (fwd_states && !aligned16(fwd_states)))
     return REL_ERR_ALIGN;
-  const size_t need = rel::linear_bwd_workspace_bytes(B, H, T);
+  const size_t need = rel::linear_bwd_workspace_bytes(B, H, T, fwd_states != nullptr);
   if (!workspace || workspace_bytes < need) return REL_ERR_WORKSPACE;
   if (!aligned256(workspace)) return REL_ERR_ALIGN;
   return from_hip(rel::launch_linear_bwd(

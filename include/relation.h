@@ -142,7 +142,8 @@ relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D,
  *   gate             : out [B, H] float32 Exchange mass g; NULL to skip
  *   workspace        : device scratch of at least
  *                      relation_decode_workspace_bytes() bytes (256-byte
- *                      aligned); contents on entry are ignored.
+ *                      aligned); contents on entry are ignored. Calls that
+ *                      run at the same time must not share it.
  */
 size_t relation_decode_workspace_bytes(relation_dtype dtype, int B, int H, int D, int capacity);
 
@@ -327,7 +328,8 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
  *   y                : out [B, H, T, D] bf16
  *   state_out        : out DEVICE fp32 [B, H, D, D] the state after the last
  *                      token, or NULL (a later call continues from it)
- *   states           : out DEVICE fp32 [B, H, ceil(T / 128) + 1, D, D], 4-byte
+ *   states           : out DEVICE fp32 [B, H, ceil(T / 128) + 1, D, D]
+ *                      (relation_linear_states_bytes() bytes), 16-byte
  *                      aligned, or NULL: the state before every 128-token
  *                      chunk, then the final state. A training step passes
  *                      it to relation_linear_bwd as fwd_states, which then
@@ -356,18 +358,26 @@ relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, i
  *   dg               : out [B, H, T, D] fp32, gradient of the log retention
  *   dstate_in        : out DEVICE fp32 [B, H, D, D] gradient of state_in, or
  *                      NULL
- *   fwd_states       : in  DEVICE fp32, 4-byte aligned, or NULL: the states
+ *   fwd_states       : in  DEVICE fp32, 16-byte aligned (the kernels read it
+ *                      with 16-byte vector loads), or NULL: the states
  *                      relation_linear_fwd stored for these same inputs
  *                      (its `states` output). Given, the first pass is
- *                      skipped and its region of the workspace is unused;
- *                      states of other inputs give wrong gradients, with no
- *                      error.
- *   workspace        : relation_linear_bwd_workspace_bytes() bytes, 256-byte
- *                      aligned (B * H * (2 ceil(T / 128) + 1) * D * D floats:
- *                      the state before every chunk and the final state,
- *                      then the gradient of the state after every chunk)
+ *                      skipped; states of other inputs give wrong gradients,
+ *                      with no error.
+ *   workspace        : 256-byte aligned. Without fwd_states:
+ *                      relation_linear_bwd_workspace_bytes() bytes
+ *                      (B * H * (2 ceil(T / 128) + 1) * D * D floats: the
+ *                      state before every chunk and the final state, then
+ *                      the gradient of the state after every chunk). With
+ *                      fwd_states: relation_linear_bwd_reuse_workspace_bytes()
+ *                      bytes (B * H * ceil(T / 128) * D * D floats, the state
+ *                      gradients only). Smaller: REL_ERR_WORKSPACE.
+ * The three size queries return 0 for unsupported (dtype, D) or bad shapes.
  */
+size_t relation_linear_states_bytes(relation_dtype dtype, int B, int H, int T, int D);
 size_t relation_linear_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D);
+size_t relation_linear_bwd_reuse_workspace_bytes(relation_dtype dtype, int B, int H, int T,
+                                                 int D);
 relation_status relation_linear_bwd(relation_dtype dtype, int B, int H, int T, int D,
                                     const void* p1, const void* p2, const void* I,
                                     const float* g, const float* rope_cos,

@@ -121,7 +121,8 @@ def test_bwd_validation_and_workspace(lib):
 
 def test_decode_validation(lib):
     need = lib.relation_decode_workspace_bytes(BF16, 2, 3, 64, 4352)
-    assert need > 0
+    # one partial (m, l, z[64]) per chunk of about 512 slots (9 for 4352) and head
+    assert need == 2 * 3 * 9 * 66 * 4
 
     def dec(n=10, cap=4352, ws=P, wsb=None, q=P, D=64, dtype=BF16):
         wsb = need if wsb is None else wsb
@@ -236,6 +237,7 @@ def test_linear_validation(lib):
     assert lfwd(rc=P_MIS, rs=P) == REL_ERR_ALIGN
     assert lfwd(cout=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
     assert lfwd(states=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+    assert lfwd(states=P_MIS) == REL_ERR_ALIGN  # read back with 16-byte loads
 
     need = lib.relation_linear_bwd_workspace_bytes(BF16, 2, 3, 300, 64)
     # the state before every 128-token chunk and the final one, then the
@@ -243,6 +245,16 @@ def test_linear_validation(lib):
     assert need == 2 * 3 * (2 * 3 + 1) * 64 * 64 * 4
     assert lib.relation_linear_bwd_workspace_bytes(F32, 2, 3, 300, 64) == 0
     assert lib.relation_linear_bwd_workspace_bytes(BF16, 2, 3, 300, 48) == 0
+    # with the forward's states: the state gradients only
+    need_r = lib.relation_linear_bwd_reuse_workspace_bytes(BF16, 2, 3, 300, 64)
+    assert need_r == 2 * 3 * 3 * 64 * 64 * 4
+    assert lib.relation_linear_bwd_reuse_workspace_bytes(F32, 2, 3, 300, 64) == 0
+    # the states the forward stores: before each of the 3 chunks, then the final one
+    assert lib.relation_linear_states_bytes(BF16, 2, 3, 300, 64) == 2 * 3 * 4 * 64 * 64 * 4
+    assert lib.relation_linear_states_bytes(BF16, 2, 3, 256, 64) == 2 * 3 * 3 * 64 * 64 * 4
+    assert lib.relation_linear_states_bytes(BF16, 2, 3, 0, 64) == 0
+    assert lib.relation_linear_states_bytes(BF16, 2, 3, 300, 80) == 0
+    assert rel.linear_states_shape(2, 3, 300) == (2, 3, 4, 64, 64)
 
     def lbwd(dtype=BF16, D=64, dy=P, dg=P, ws=P, wsb=need, dsin=NUL, fst=NUL, tau=2.0):
         return lib.relation_linear_bwd(dtype, 2, 3, 300, D, P, P, P, P, NUL, NUL, NUL, dy, NUL,
@@ -259,6 +271,10 @@ def test_linear_validation(lib):
     assert lbwd(dg=P_MIS) == REL_ERR_ALIGN
     assert lbwd(dsin=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
     assert lbwd(fst=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN  # the forward's states
+    assert lbwd(fst=P_MIS) == REL_ERR_ALIGN  # read with 16-byte vector loads
+    # with the forward's states the smaller workspace suffices, one byte less does not
+    assert lbwd(fst=P, ws=P, wsb=need_r - 1) == REL_ERR_WORKSPACE
+    assert lbwd(fst=P, ws=ctypes.c_void_p(0x7F0000000010), wsb=need_r) == REL_ERR_ALIGN
 
     def lstep(dtype=BF16, B=1, H=1, D=64, st=P, y=P, tau=2.0):
         return lib.relation_linear_step(dtype, B, H, D, P, P, P, P, NUL, NUL, st, y, 0.125, tau,

@@ -217,8 +217,13 @@ def test_linear_bwd_reuses_forward_states():
     assert torch.equal(states[:, :, -1], c1)
     assert torch.equal(states[:, :, 0], C0)  # the state before the first chunk
     ref = rel.relation_linear_bwd(p1, p2, I, g, dy, dstate_out=dCT, want_dstate_in=True, **kw)
+    # with the forward's states the workspace holds only the state gradients:
+    # exactly the size the library asks for, filled with NaN bytes first
+    need = rel.load_library().relation_linear_bwd_reuse_workspace_bytes(1, B, H, T, 64)
+    assert need == B * H * 3 * 64 * 64 * 4
+    ws = torch.full((need,), 0xFF, device=DEV, dtype=torch.uint8)
     got = rel.relation_linear_bwd(p1, p2, I, g, dy, dstate_out=dCT, want_dstate_in=True,
-                                  fwd_states=states, **kw)
+                                  fwd_states=states, workspace=ws, **kw)
     torch.cuda.synchronize()
     for name, a, b in zip(("dp1", "dp2", "dI", "dg", "dstate_in"), got, ref):
         assert torch.equal(a, b), name
