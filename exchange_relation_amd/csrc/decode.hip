@@ -23,6 +23,18 @@
 // 64 e) merges the chunk partials
 // (every partial load issued up front), adds Self and writes y / gate.
 //
+// Whole-history mode (WHOLE, uniform lengths): when the batch has enough
+// heads to fill the chip on its own (B * H >= kWholeHeads), every (b, h)
+// gets ONE workgroup that scans its whole history, merges its 32 group
+// states in LDS and completes the row itself (Self, A, g, y; App. A.3.5),
+// with the append; no partials and no second launch (cache workload: 60.7
+// us per step against 62.6 + 4.2 split and combine). Every workgroup streams
+// at the same rate (their loads in flight are alike and HBM is the shared
+// bound), so the workgroups that share a CU do not set the time. Ragged
+// batches keep the split: there one workgroup per head would leave the
+// longest histories to a few slow workgroups (measured 51 against 40 us per
+// step at lengths uniform in [0, 4096]).
+//
 // Ragged batches: each sequence b has its own history length n_b (a device
 // int array). The launch is sized for an upper bound of the lengths; a split
 // workgroup whose chunk lies past its sequence's n_b exits at once, and the
@@ -46,6 +58,7 @@ constexpr int kChunk = REL_DECODE_CHUNK;    // target slots per split workgroup
 constexpr int kGroups = 32;                 // 8-lane groups per 256-lane workgroup
 constexpr int kUnroll = REL_DECODE_UNROLL;  // slots per group per iteration (loads in flight)
 constexpr int kBatch = 8;                   // partials loaded at once by the combine
+constexpr int kWholeHeads = 256;            // heads from which one workgroup per head fills the chip
 
 __host__ __device__ inline int num_splits(int n) { return (n + kChunk - 1) / kChunk; }
 
@@ -65,11 +78,13 @@ __host__ __device__ inline SplitPlan split_plan(int n) {
 // Uniform batches pass the common length in n (and nh = NULL); ragged ones
 // pass the per-sequence lengths nh[B], the heads per sequence H and the
 // length bound n (the grid has nsplit = num_splits(bound) chunks per head).
-template <typename TE, int D, bool RAGGED>
+template <typename TE, int D, bool RAGGED, bool WHOLE = false>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const TE* __restrict__ q, const TE* __restrict__ kn, const TE* __restrict__ vn,
     TE* __restrict__ kc, TE* __restrict__ vc, float* __restrict__ part, int capacity, int n,
-    const int* __restrict__ nh, int H, int nsplit, int chunk, float qscale) {
+    const int* __restrict__ nh, int H, int nsplit, int chunk, float qscale,
+    TE* __restrict__ y = nullptr, float* __restrict__ gate = nullptr, float inv_tau = 0.f,
+    float lam = 0.f) {
   constexpr int E = D / 8;
   __shared__ float s_m[kGroups], s_l[kGroups];
   __shared__ float s_z[kGroups][D + 1];
@@ -77,9 +92,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int tid = threadIdx.x;
   const int grp = tid >> 3;
   const int sub = tid & 7;
-  const int split = blockIdx.x % nsplit;
-  const int head = blockIdx.x / nsplit;
+  const int split = WHOLE ? 0 : blockIdx.x % nsplit;
+  const int head = WHOLE ? blockIdx.x : blockIdx.x / nsplit;
   const size_t cbase = static_cast<size_t>(head) * capacity * D;
+  const size_t hv = static_cast<size_t>(head) * D;
+  static_assert(!(RAGGED && WHOLE), "the whole-history mode is for uniform lengths");
   if (RAGGED) {
     const int bound = n;
     n = nh[head / H];
@@ -88,18 +105,29 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     if (split >= sp.nsplit) return;
     chunk = sp.chunk;
   }
+  if (WHOLE) chunk = n;
   const int c0 = split * chunk;
   const int c1 = min(n, c0 + chunk);
   if (!RAGGED && split == 0 && tid < D) {  // append: exact copy of the new token into slot n
     const size_t slot = cbase + static_cast<size_t>(n) * D + tid;
-    kc[slot] = kn[static_cast<size_t>(head) * D + tid];
-    vc[slot] = vn[static_cast<size_t>(head) * D + tid];
+    kc[slot] = kn[hv + tid];
+    vc[slot] = vn[hv + tid];
   }
 
   float qv[E];
-  load_row_piece<TE, D>(q + static_cast<size_t>(head) * D + sub * E, qv);
+  load_row_piece<TE, D>(q + hv + sub * E, qv);
 #pragma unroll
   for (int e = 0; e < E; ++e) qv[e] *= qscale;
+  float us = 0.f;  // WHOLE: u'_ii = scale*log2(e) * q . k_new, in every lane of each group
+  if (WHOLE) {
+    float kx[E];
+    load_row_piece<TE, D>(kn + hv + sub * E, kx);
+#pragma unroll
+    for (int e = 0; e < E; ++e) us = fmaf(qv[e], kx[e], us);
+    us += __shfl_xor(us, 1, 8);
+    us += __shfl_xor(us, 2, 8);
+    us += __shfl_xor(us, 4, 8);
+  }
 
   float m = -INFINITY, l = 0.f, z[E];
 #pragma unroll
@@ -154,7 +182,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
   for (int e = 0; e < E; ++e) s_z[grp][sub * E + e] = z[e];
   __syncthreads();
-  float* out = part + (static_cast<size_t>(head) * nsplit + split) * (D + 2);
   if (tid < D) {
     float M = -INFINITY;
     for (int g2 = 0; g2 < kGroups; ++g2) M = fmaxf(M, s_m[g2]);
@@ -166,10 +193,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         Ls = fmaf(w, s_l[g2], Ls);
       }
     }
-    out[2 + tid] = Z;
-    if (tid == 0) {
-      out[0] = M;
-      out[1] = Ls;
+    if (WHOLE) {  // row completion (App. A.3.5), base-2 domain
+      const float S = fast_rcp(1.0f + fast_exp2(-us * inv_tau));  // sigmoid(U_ii / tau)
+      float g = 0.f;
+      if (Ls > 0.f) {
+        const float A2 = M + fast_log2(Ls) - lam * fast_log2(static_cast<float>(n + 1));
+        g = fast_rcp(1.0f + fast_exp2(S * kLog2e - A2));
+      }
+      const float gl = (Ls > 0.f) ? g * fast_rcp(Ls) : 0.f;
+      Elem<TE>::store(y + hv + tid, (1.0f - g) * Elem<TE>::load(vn + hv + tid) + gl * Z);
+      if (tid == 0 && gate) gate[head] = g;
+    } else {
+      float* out = part + (static_cast<size_t>(head) * nsplit + split) * (D + 2);
+      out[2 + tid] = Z;
+      if (tid == 0) {
+        out[0] = M;
+        out[1] = Ls;
+      }
     }
   }
 }
@@ -290,6 +330,12 @@ hipError_t run(int BH, int H, const void* q, const void* k_new, const void* v_ne
   TE* kct = static_cast<TE*>(k_cache);
   TE* vct = static_cast<TE*>(v_cache);
   int nsplit = 0;
+  if (nh == nullptr && BH >= kWholeHeads && n > 0) {  // one workgroup per head completes its row
+    hipLaunchKernelGGL((decode_split_kernel<TE, D, false, true>), dim3(BH), dim3(256), 0, stream,
+                       qt, knt, vnt, kct, vct, part, capacity, n, nullptr, H, 1, 0, qscale,
+                       static_cast<TE*>(y), gate, 1.0f / tau, lam);
+    return hipGetLastError();
+  }
   if (nh == nullptr) {
     if (n > 0) {
       const SplitPlan sp = split_plan(n);

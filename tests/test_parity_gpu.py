@@ -398,6 +398,29 @@ def test_decode_full_size_cache_workload():
         check(f"gate step {s}", np.stack([f64(gs[s][b, h]) for b, h in heads]), G, "bf16")
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 48), ("bf16", 80), ("f32", 64),
+                                     ("f32", 32)])
+@pytest.mark.parametrize("n0", [1, 33, 700])
+def test_decode_whole_history_mode(dtype, D, n0):
+    """B * H >= 256: one workgroup per head scans the whole history and
+    completes the row in the same launch. Every head against the oracle over
+    two steps, and the cache bit for bit."""
+    B, H, steps = 32, 8, 2
+    d = make_decode_inputs(B, H, D, n0, steps, n0 + steps + 3, dtype, seed=350 + n0 + D)
+    scale = 1 / math.sqrt(D)
+    ys, gs, kc, vc = run_decode_steps(d, n0, steps, scale)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    kfull, vfull = d["k_cache"].clone(), d["v_cache"].clone()
+    for s in range(steps):
+        dd = dict(d, k_cache=kfull, v_cache=vfull)
+        Y, G = oracle_decode_rows(dd, s, n0 + s, heads, scale, d["lam"])
+        check(f"y step {s}", np.stack([f64(ys[s][b, h]) for b, h in heads]), Y, dtype)
+        check(f"gate step {s}", np.stack([f64(gs[s][b, h]) for b, h in heads]), G, dtype)
+        kfull[:, :, n0 + s] = d["k_new"][s]
+        vfull[:, :, n0 + s] = d["v_new"][s]
+    assert torch.equal(kc, kfull) and torch.equal(vc, vfull)
+
+
 # ------------------------------------------------------------ ragged decode
 def ragged_lengths_inputs(B, H, D, lengths, capacity, steps, dtype, seed):
     """Decode inputs with every cache slot filled (so untouched slots can be
@@ -472,6 +495,37 @@ def test_decode_ragged_out_of_range_lengths_give_nan_and_no_write():
             f64(d["k_cache"][b:b + 1]), f64(d["v_cache"][b:b + 1]), [n], 1 / 8, 2.0, d["lam"])
         check(f"valid row {b}", y[b:b + 1], Y, "bf16")
         assert torch.equal(kc[b, :, n], d["k_new"][0, b])
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 80), ("f32", 32)])
+def test_decode_ragged_many_heads(dtype, D):
+    """Ragged lengths on a batch of B * H >= 256 heads (where uniform
+    batches take the one-workgroup-per-head mode; ragged ones keep the
+    split): lengths 0, 1, 31, 512, 513, 700 and two out of range (above the
+    bound, negative); valid rows against the oracle, invalid rows NaN with
+    their cache rows untouched, appends bit for bit."""
+    base = [0, 1, 31, 512, 513, 700, 900, -3]  # bound 720: 900 above it, -3 negative
+    lengths = base * 4
+    B, H, cap = len(lengths), 8, 730
+    d, nh = ragged_lengths_inputs(B, H, D, lengths, cap, 1, dtype, seed=470 + D)
+    scale = 1 / math.sqrt(D)
+    ys, gs, kc, vc = run_ragged_steps(d, nh, 1, scale, 720)
+    y, g = f64(ys[0]), f64(gs[0])
+    ok = [b for b, n in enumerate(lengths) if 0 <= n <= 720]
+    bad = [b for b in range(B) if b not in ok]
+    assert np.isnan(y[bad]).all() and np.isnan(g[bad]).all()
+    for b in bad:
+        assert torch.equal(kc[b], d["k_cache"][b]) and torch.equal(vc[b], d["v_cache"][b])
+    Y, G, kexp, vexp = oracle.relation_decode_step_ragged(
+        f64(d["q"][0, ok]), f64(d["k_new"][0, ok]), f64(d["v_new"][0, ok]),
+        f64(d["k_cache"][ok]), f64(d["v_cache"][ok]), [lengths[b] for b in ok], scale, 2.0,
+        d["lam"])
+    check("ragged whole y", y[ok], Y, dtype)
+    check("ragged whole gate", g[ok], G, dtype)
+    for b in ok:
+        n = lengths[b]
+        assert torch.equal(kc[b, :, n], d["k_new"][0, b])
+        assert torch.equal(vc[b, :, n], d["v_new"][0, b])
 
 
 def test_decode_ragged_full_size_workload():
