@@ -23,6 +23,7 @@ __all__ = [
     "relation_bwd",
     "relation_bwd_workspace_bytes",
     "relation_cache_decode",
+    "relation_cache_decode_noalloc",
     "relation_decode_workspace_bytes",
     "relation_cache_decode_ragged",
     "relation_cache_prefill",
@@ -53,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "relation_bwd",
     "relation_decode_workspace_bytes",
     "relation_cache_decode",
+    "relation_cache_decode_noalloc",
     "relation_cache_decode_ragged",
     "relation_prefill_workspace_bytes",
     "relation_cache_prefill",
@@ -110,6 +112,10 @@ def load_library():
     lib.relation_cache_decode.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, c_int,
                                           c_int, vp, vp, vp, c_size, c_float, c_float, c_float,
                                           vp]
+    lib.relation_cache_decode_noalloc.restype = c_int
+    lib.relation_cache_decode_noalloc.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
+                                                  c_int, c_int, vp, vp, c_float, c_float,
+                                                  c_float, vp]
     lib.relation_cache_decode_ragged.restype = c_int
     lib.relation_cache_decode_ragged.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
                                                  c_int, vp, c_int, vp, vp, vp, c_size, c_float,
@@ -320,6 +326,31 @@ def relation_cache_decode(q, k_new, v_new, k_cache, v_cache, n_hist, lam=0.0, sc
                                    _stream(dev, stream))
     if st != 0:
         raise RelationError(st, "relation_cache_decode")
+    return y, gate
+
+
+def relation_cache_decode_noalloc(q, k_new, v_new, k_cache, v_cache, n_hist, y, lam=0.0,
+                                  scale=None, tau_s=2.0, gate=None, stream=None):
+    """relation_cache_decode without a workspace: the library's static
+    per-GPU scratch serves instead, and nothing is allocated (y and gate are
+    the caller's). Calls that overlap in time on one GPU race. Returns
+    (y, gate)."""
+    lib = load_library()
+    B, H, D = q.shape
+    capacity = k_cache.shape[2]
+    dev, dt = q.device, q.dtype
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("y", y)):
+        _check(t, name, dt, (B, H, D), dev)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, name, dt, (B, H, capacity, D), dev)
+    if gate is not None:
+        _check(gate, "gate", torch.float32, (B, H), dev)
+    st = lib.relation_cache_decode_noalloc(_dtype_code(q), B, H, D, _ptr(q), _ptr(k_new),
+                                           _ptr(v_new), _ptr(k_cache), _ptr(v_cache), capacity,
+                                           int(n_hist), _ptr(y), _ptr(gate), _scale(D, scale),
+                                           float(tau_s), float(lam), _stream(dev, stream))
+    if st != 0:
+        raise RelationError(st, "relation_cache_decode_noalloc")
     return y, gate
 
 

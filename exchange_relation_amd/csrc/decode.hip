@@ -42,6 +42,8 @@
 // above the bound, or without a free slot) gets NaN outputs and no append.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -366,6 +368,62 @@ hipError_t run(int BH, int H, const void* q, const void* k_new, const void* v_ne
 }
 
 }  // namespace dec
+
+// ---- allocation-free decode: the workspace lives in a static device array.
+// Each GPU the library runs on holds its own copy of `scratch` until the
+// process ends; the host uses the address hipGetSymbolAddress returns for
+// the current device (the array's name is only a host-side stand-in). The
+// decode kernels write every partial they read within the call, so nothing
+// in it has to start at zero; it keeps the last call's partials.
+namespace dec {
+constexpr size_t kScratchBytes = 8u << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace dec
+
+static __device__ __align__(256) unsigned char scratch[dec::kScratchBytes];
+
+namespace dec {
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address, looked up at the first call on the device
+// (with that device current) and kept.
+hipError_t scratch_for_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if ((e = hipStreamGetDevice(stream, &sdev)) != hipSuccess) return e;
+    if (sdev != dev) return hipErrorInvalidDevice;  // the stream must be the current device's
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+}  // namespace dec
+
+size_t decode_scratch_bytes() { return dec::kScratchBytes; }
+
+hipError_t launch_decode_noalloc(int dtype, int B, int H, int D, const void* q,
+                                 const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, int capacity, int n_hist, void* y, float* gate,
+                                 float scale, float tau, float lam, hipStream_t stream) {
+  void* ws = nullptr;
+  hipError_t e = dec::scratch_for_device(stream, &ws);
+  if (e != hipSuccess) return e;
+  return launch_decode(dtype, B, H, D, q, k_new, v_new, k_cache, v_cache, capacity, n_hist,
+                       nullptr, y, gate, ws, scale, tau, lam, stream);
+}
 
 size_t decode_workspace_bytes(int dtype, int B, int H, int D, int capacity) {
   (void)dtype;

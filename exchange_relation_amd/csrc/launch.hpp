@@ -73,6 +73,15 @@ hipError_t launch_decode(int dtype, int B, int H, int D, const void* q, const vo
                          int n_hist, const int* n_hist_dev, void* y, float* gate, void* ws,
                          float scale, float tau, float lam, hipStream_t stream);
 
+// The same uniform decode step with its workspace in the library's static
+// per-device array of decode_scratch_bytes() bytes (callers check the size
+// first); allocates nothing.
+size_t decode_scratch_bytes();
+hipError_t launch_decode_noalloc(int dtype, int B, int H, int D, const void* q,
+                                 const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, int capacity, int n_hist, void* y, float* gate,
+                                 float scale, float tau, float lam, hipStream_t stream);
+
 // Multi-Head Relation passes (mhr.hip): RoPE of p1 / p2 into q / k and the
 // Givens mixing of vi into v (an output pointer NULL: not produced); and the
 // transposes of both on fp32 gradients (dq scaled by dq_scale), rounded once

@@ -115,6 +115,7 @@ const char* relation_status_string(relation_status s) {
     case REL_ERR_ALIGN: return "pointer not aligned (16 B tensors, 256 B workspace)";
     case REL_ERR_WORKSPACE: return "workspace missing or too small";
     case REL_ERR_HIP: return "HIP runtime error";
+    case REL_ERR_SCRATCH: return "call needs more than the library's static scratch (8 MiB)";
   }
   return "unknown status";
 }
@@ -222,6 +223,32 @@ relation_status relation_cache_decode(relation_dtype dtype, int B, int H, int D,
                                      k_cache, v_cache, capacity, n_hist, nullptr, y, gate,
                                      workspace, scale, tau_s, lambda,
                                      static_cast<hipStream_t>(stream)));
+}
+
+relation_status relation_cache_decode_noalloc(relation_dtype dtype, int B, int H, int D,
+                                              const void* q, const void* k_new,
+                                              const void* v_new, void* k_cache, void* v_cache,
+                                              int capacity, int n_hist, void* y, float* gate,
+                                              float scale, float tau_s, float lambda,
+                                              void* stream) {
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !y) return REL_ERR_NULL;
+  relation_status st = check_dtype_dim(dtype, D);
+  if (st != REL_OK) return st;
+  if (B < 1 || H < 1 || capacity < 1) return REL_ERR_SHAPE;
+  if (static_cast<long long>(B) * H * capacity * D > kMaxElems ||
+      static_cast<long long>(capacity) * D > kMaxHeadElems)
+    return REL_ERR_SHAPE;
+  if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
+  if (n_hist < 0 || n_hist >= capacity) return REL_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(y) || (gate && !aligned4(gate)))
+    return REL_ERR_ALIGN;
+  if (rel::decode_workspace_bytes(dtype == REL_BF16 ? 1 : 0, B, H, D, capacity) >
+      rel::decode_scratch_bytes())
+    return REL_ERR_SCRATCH;
+  return from_hip(rel::launch_decode_noalloc(dtype == REL_BF16 ? 1 : 0, B, H, D, q, k_new, v_new,
+                                             k_cache, v_cache, capacity, n_hist, y, gate, scale,
+                                             tau_s, lambda, static_cast<hipStream_t>(stream)));
 }
 
 relation_status relation_cache_decode_ragged(relation_dtype dtype, int B, int H, int D,

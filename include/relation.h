@@ -59,7 +59,8 @@ typedef enum {
   REL_ERR_CAPACITY = 5,    /* decode: n_hist < 0 or n_hist + 1 > capacity     */
   REL_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned                */
   REL_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the queried size */
-  REL_ERR_HIP = 8          /* the HIP runtime reported an error               */
+  REL_ERR_HIP = 8,         /* the HIP runtime reported an error               */
+  REL_ERR_SCRATCH = 9      /* more scratch than the static buffer holds       */
 } relation_status;
 
 typedef enum { REL_F32 = 0, REL_BF16 = 1 } relation_dtype;
@@ -155,6 +156,32 @@ relation_status relation_cache_decode(relation_dtype dtype, int B, int H, int D,
                                       void* workspace, size_t workspace_bytes,
                                       float scale, float tau_s, float lambda,
                                       void* stream);
+
+/*
+ * relation_cache_decode_noalloc — relation_cache_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same step and the same
+ * kernels, with the workspace taken from a static device array of the
+ * library (8 MiB per GPU, held until the process ends) instead of an
+ * argument. It calls no allocator.
+ *
+ *   Arguments as for relation_cache_decode, without the workspace. The
+ *   stream must belong to the current device (else REL_ERR_HIP).
+ *   A call whose relation_decode_workspace_bytes() exceeds 8 MiB returns
+ *   REL_ERR_SCRATCH and does nothing (at D = 64 and a capacity of 4352,
+ *   up to about 3900 heads B * H).
+ *   The first call on a device looks up that device's copy of the array.
+ *   Every call on one GPU shares it and it keeps the last call's contents
+ *   (nothing in it needs to start at zero), so calls that overlap in time
+ *   on one GPU (other streams, other threads) race and give wrong results;
+ *   calls ordered on one stream are safe.
+ */
+relation_status relation_cache_decode_noalloc(relation_dtype dtype, int B, int H, int D,
+                                              const void* q, const void* k_new,
+                                              const void* v_new, void* k_cache, void* v_cache,
+                                              int capacity, int n_hist, void* y, float* gate,
+                                              float scale, float tau_s, float lambda,
+                                              void* stream);
 
 /*
  * relation_cache_decode_ragged — the same step as relation_cache_decode for a

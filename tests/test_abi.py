@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "relation.h")
 
 REL_OK, REL_ERR_NULL, REL_ERR_SHAPE, REL_ERR_UNSUPPORTED, REL_ERR_PARAM = 0, 1, 2, 3, 4
-REL_ERR_CAPACITY, REL_ERR_ALIGN, REL_ERR_WORKSPACE, REL_ERR_HIP = 5, 6, 7, 8
+REL_ERR_CAPACITY, REL_ERR_ALIGN, REL_ERR_WORKSPACE, REL_ERR_HIP, REL_ERR_SCRATCH = 5, 6, 7, 8, 9
 F32, BF16 = 0, 1
 
 # Fake device addresses: validation never dereferences them, and every call
@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(9):
+    for s in range(10):
         assert rel.relation_status_string(s)
     assert rel.relation_status_string(99) == "unknown status"
     assert rel.relation_version() == 100
@@ -138,6 +138,26 @@ def test_decode_validation(lib):
     assert dec(cap=0, n=0) == REL_ERR_SHAPE
     assert dec(cap=(1 << 25), n=10) == REL_ERR_SHAPE  # capacity * D >= 2^31
     assert dec(q=P_MIS) == REL_ERR_ALIGN
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode validates like relation_cache_decode and
+    rejects a call whose workspace would exceed its 8 MiB static scratch (all
+    on the host: nothing is launched)."""
+    def dec(B=2, H=3, n=10, cap=4352, q=P, D=64, dtype=BF16, y=P):
+        return lib.relation_cache_decode_noalloc(dtype, B, H, D, q, P, P, P, P, cap, n, y, NUL,
+                                                 0.125, 2.0, 0.3, None)
+
+    assert dec(n=4352) == REL_ERR_CAPACITY
+    assert dec(n=-1) == REL_ERR_CAPACITY
+    assert dec(q=NUL) == REL_ERR_NULL
+    assert dec(y=NUL) == REL_ERR_NULL
+    assert dec(D=32) == REL_ERR_UNSUPPORTED
+    assert dec(q=P_MIS) == REL_ERR_ALIGN
+    # 32 x 128 heads at capacity 4352: 4096 * 9 * 66 * 4 B = 9.3 MiB > 8 MiB
+    assert lib.relation_decode_workspace_bytes(BF16, 32, 128, 64, 4352) > 8 << 20
+    assert dec(B=32, H=128) == REL_ERR_SCRATCH
+    assert "scratch" in rel.relation_status_string(REL_ERR_SCRATCH)
 
 
 def test_decode_ragged_validation(lib):
