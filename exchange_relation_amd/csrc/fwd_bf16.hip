@@ -361,6 +361,7 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   // need no per-row source select
   auto in_cache = [&](int kt) { return !OFF || (kt + 1) * BN <= pos0; };
   int crow[NCH], ccol[NCH];
+  uint32_t toff[NCH];  // element offset of the chunk within a tile
   bool cin[NCH];  // chunk exists (BN * CPR need not be a multiple of 256)
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -368,6 +369,7 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     cin[i] = c < BN * CPR;
     crow[i] = cin[i] ? c / CPR : 0;
     ccol[i] = cin[i] ? c % CPR : 0;
+    toff[i] = static_cast<uint32_t>(crow[i] * D + ccol[i] * 8);
   }
   struct Chunks {
     u32x4 a[NCH];
@@ -387,11 +389,11 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   auto fetch_full = [&](const uint16_t* __restrict__ src, const uint16_t* __restrict__ srcn,
                         int kt, Chunks& c) {
     if (in_cache(kt)) {
+      // uniform tile base (scalar registers) plus a per-thread offset fixed
+      // for the whole loop: no per-tile vector address arithmetic (1-2 %)
+      const uint16_t* tb = src + static_cast<uint32_t>(kt * BN * D);
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const uint32_t r0 = static_cast<uint32_t>(kt * BN + crow[i]);
-        c.a[i] = *reinterpret_cast<const u32x4*>(src + (r0 * D + ccol[i] * 8));
-      }
+      for (int i = 0; i < NCH; ++i) c.a[i] = *reinterpret_cast<const u32x4*>(tb + toff[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
