@@ -657,7 +657,7 @@ def main():
                                    prewarm_ms=args.prewarm_ms)))
         return
     if args.only == "decode":
-        print(json.dumps(bench_decode(rel, torch, dev)))
+        print(json.dumps(bench_decode(rel, torch, dev, prewarm_ms=args.prewarm_ms)))
         return
     if args.only == "ragged":
         print(json.dumps(bench_decode_ragged(rel, torch, dev)))
@@ -673,7 +673,8 @@ def main():
                           "step": bench_linear_step(rel, torch, dev)}))
         return
     if args.only == "attn":
-        print(json.dumps(bench_fwdbwd_vs_attention(rel, torch, dev, args.steps)))
+        print(json.dumps(bench_fwdbwd_vs_attention(rel, torch, dev, args.steps,
+                                                   prewarm_ms=args.prewarm_ms)))
         return
 
     st = bench_step(rel, torch, dev, args.steps, args.warmup, prewarm_ms=args.prewarm_ms)
