@@ -100,12 +100,12 @@ def load_library():
     lib.relation_fwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_fwd.restype = c_int
     lib.relation_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
-                                 vp, c_size, c_float, c_float, c_float, vp]
+                                 vp, c_size, c_float, c_float, c_float, vp, vp]
     lib.relation_bwd_workspace_bytes.restype = c_size
     lib.relation_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_bwd.restype = c_int
     lib.relation_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
-                                 vp, vp, vp, vp, vp, c_size, c_float, c_float, c_float, vp]
+                                 vp, vp, vp, vp, vp, c_size, c_float, c_float, c_float, vp, vp]
     lib.relation_decode_workspace_bytes.restype = c_size
     lib.relation_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_cache_decode.restype = c_int
@@ -131,13 +131,14 @@ def load_library():
     lib.relation_mhr_fwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_mhr_fwd.restype = c_int
     lib.relation_mhr_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
-                                     c_int, vp, vp, vp, vp, c_size, c_float, c_float, c_float, vp]
+                                     c_int, vp, vp, vp, vp, c_size, c_float, c_float, c_float, vp,
+                                     vp]
     lib.relation_mhr_bwd_workspace_bytes.restype = c_size
     lib.relation_mhr_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_mhr_bwd.restype = c_int
     lib.relation_mhr_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                      c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size,
-                                     c_float, c_float, c_float, vp]
+                                     c_float, c_float, c_float, vp, vp]
     lib.relation_linear_fwd.restype = c_int
     lib.relation_linear_fwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp, c_float, c_float, vp]
@@ -206,6 +207,19 @@ def _scale(D, scale):
     return 1.0 / math.sqrt(D) if scale is None else float(scale)
 
 
+def _lam(lam, dev):
+    """lambda as (value, device pointer): a number is passed by value; a
+    one-element float32 tensor on the inputs' device is read by the kernels
+    when they run (no host synchronisation)."""
+    if isinstance(lam, torch.Tensor):
+        if lam.device != dev or lam.dtype != torch.float32 or lam.numel() != 1:
+            raise ValueError("a tensor lambda must be one float32 element on the inputs' device")
+        if not lam.is_contiguous():
+            raise ValueError("lambda tensor must be contiguous")
+        return 0.0, _ptr(lam)
+    return float(lam), None
+
+
 def relation_fwd_workspace_bytes(dtype, B, H, T, D):
     code = REL_BF16 if dtype == torch.bfloat16 else REL_F32
     return int(load_library().relation_fwd_workspace_bytes(code, B, H, T, D))
@@ -247,9 +261,10 @@ def relation_fwd(q, k, v, lam=0.0, scale=None, tau_s=2.0, y=None, lse=None, gate
         if t is not None:
             _check(t, name, torch.float32, (B, H, T), dev)
     ws = _workspace(workspace, relation_fwd_workspace_bytes(dt, B, H, T, D), dev) if split else None
+    lv, lp = _lam(lam, dev)
     st = lib.relation_fwd(code, B, H, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(lse),
                           _ptr(gate), _ptr(ws), _nbytes(ws), _scale(D, scale), float(tau_s),
-                          float(lam), _stream(dev, stream))
+                          lv, lp, _stream(dev, stream))
     if st != 0:
         raise RelationError(st, "relation_fwd")
     return y, lse, gate
@@ -281,10 +296,11 @@ def relation_bwd(q, k, v, y, dy, lse, lam=0.0, scale=None, tau_s=2.0, dq=None, d
     need = int(lib.relation_bwd_workspace_bytes(code, B, H, T, D))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), device=dev, dtype=torch.uint8)
+    lv, lp = _lam(lam, dev)
     st = lib.relation_bwd(code, B, H, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy),
                           _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlambda),
                           _ptr(workspace), workspace.numel() * workspace.element_size(),
-                          _scale(D, scale), float(tau_s), float(lam), _stream(dev, stream))
+                          _scale(D, scale), float(tau_s), lv, lp, _stream(dev, stream))
     if st != 0:
         raise RelationError(st, "relation_bwd")
     return dq, dk, dv, dlambda
@@ -475,7 +491,7 @@ def relation_mhr_fwd(p1, p2, I, rope_cos=None, rope_sin=None, theta=None, pairin
     st = lib.relation_mhr_fwd(code, B, H, T, D, _ptr(p1), _ptr(p2), _ptr(I), _ptr(rope_cos),
                               _ptr(rope_sin), _ptr(theta), int(pairing), _ptr(y), _ptr(lse),
                               _ptr(gate), _ptr(workspace), wsb, _scale(D, scale), float(tau_s),
-                              float(lam), _stream(dev, stream))
+                              *_lam(lam, dev), _stream(dev, stream))
     if st != 0:
         raise RelationError(st, "relation_mhr_fwd")
     return y, lse, gate
@@ -510,7 +526,7 @@ def relation_mhr_bwd(p1, p2, I, y, dy, lse, rope_cos=None, rope_sin=None, theta=
                               _ptr(lse), _ptr(dp1), _ptr(dp2), _ptr(dI), _ptr(dlambda),
                               _ptr(dtheta), _ptr(fwd_workspace), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _scale(D, scale),
-                              float(tau_s), float(lam), _stream(dev, stream))
+                              float(tau_s), *_lam(lam, dev), _stream(dev, stream))
     if st != 0:
         raise RelationError(st, "relation_mhr_bwd")
     return dp1, dp2, dI, dlambda, dtheta
@@ -626,21 +642,32 @@ def relation_linear_step(p1, p2, I, g, state, rope_cos=None, rope_sin=None, scal
     return y
 
 
+def _lam_tensor(lam, dev):
+    """The learnable lambda as a one-element float32 tensor on `dev` (a copy
+    only when its dtype, device or layout differ; no host round trip)."""
+    t = lam.detach().reshape(1)
+    if t.device != dev or t.dtype != torch.float32:
+        t = t.to(device=dev, dtype=torch.float32)
+    return t.contiguous()
+
+
 class RelationFunction(torch.autograd.Function):
     """autograd wrapper: y = Relation(q, k, v; lambda) with gradients for q,
     k, v and the layer's lambda (a one-element tensor)."""
 
     @staticmethod
     def forward(ctx, q, k, v, lam, scale, tau_s):
-        y, lse, _ = relation_fwd(q, k, v, lam=float(lam), scale=scale, tau_s=tau_s)
-        ctx.save_for_backward(q, k, v, y, lse)
-        ctx.lam, ctx.scale, ctx.tau_s, ctx.lam_shape = float(lam), scale, tau_s, lam.shape
+        # lambda stays on the device: the kernels read it when they run
+        lam_d = _lam_tensor(lam, q.device)
+        y, lse, _ = relation_fwd(q, k, v, lam=lam_d, scale=scale, tau_s=tau_s)
+        ctx.save_for_backward(q, k, v, y, lse, lam_d)
+        ctx.scale, ctx.tau_s, ctx.lam_shape = scale, tau_s, lam.shape
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        q, k, v, y, lse = ctx.saved_tensors
-        dq, dk, dv, dlam = relation_bwd(q, k, v, y, dy.contiguous(), lse, lam=ctx.lam,
+        q, k, v, y, lse, lam_d = ctx.saved_tensors
+        dq, dk, dv, dlam = relation_bwd(q, k, v, y, dy.contiguous(), lse, lam=lam_d,
                                         scale=ctx.scale, tau_s=ctx.tau_s)
         return dq, dk, dv, dlam.reshape(ctx.lam_shape), None, None
 
@@ -661,19 +688,20 @@ class MultiHeadRelationFunction(torch.autograd.Function):
         B, H, T, D = p1.shape
         need = int(load_library().relation_mhr_fwd_workspace_bytes(_dtype_code(p1), B, H, T, D))
         ws = torch.empty((need,), device=p1.device, dtype=torch.uint8) if need else None
+        lam_d = _lam_tensor(lam, p1.device)
         y, lse, _ = relation_mhr_fwd(p1, p2, I, rope_cos, rope_sin, theta, pairing,
-                                     lam=float(lam), scale=scale, tau_s=tau_s, workspace=ws)
-        ctx.save_for_backward(p1, p2, I, y, lse, theta, rope_cos, rope_sin, ws)
-        ctx.lam, ctx.scale, ctx.tau_s, ctx.pairing = float(lam), scale, tau_s, pairing
+                                     lam=lam_d, scale=scale, tau_s=tau_s, workspace=ws)
+        ctx.save_for_backward(p1, p2, I, y, lse, theta, rope_cos, rope_sin, ws, lam_d)
+        ctx.scale, ctx.tau_s, ctx.pairing = scale, tau_s, pairing
         ctx.lam_shape = lam.shape
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        p1, p2, I, y, lse, theta, rope_cos, rope_sin, ws = ctx.saved_tensors
+        p1, p2, I, y, lse, theta, rope_cos, rope_sin, ws, lam_d = ctx.saved_tensors
         dp1, dp2, dI, dlam, dth = relation_mhr_bwd(
             p1, p2, I, y, dy.contiguous(), lse, rope_cos, rope_sin, theta, ctx.pairing,
-            lam=ctx.lam, scale=ctx.scale, tau_s=ctx.tau_s, fwd_workspace=ws)
+            lam=lam_d, scale=ctx.scale, tau_s=ctx.tau_s, fwd_workspace=ws)
         return (dp1, dp2, dI, dlam.reshape(ctx.lam_shape), dth, None, None, None, None, None)
 
 

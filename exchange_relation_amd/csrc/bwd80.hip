@@ -57,7 +57,8 @@ __global__ __launch_bounds__(NT, 1) void bwd80_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
     const float* __restrict__ lse, const float* __restrict__ Dr, float* __restrict__ dq_acc,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int T, int BH, float kscale,
-    float scale, float inv_tau, float lam, float* __restrict__ dk32, float* __restrict__ dv32) {
+    float scale, float inv_tau, Lam lamp, float* __restrict__ dk32, float* __restrict__ dv32) {
+  const float lam = lamp.get();
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(NT, 1) void bwd80_kernel(
 hipError_t launch_bwd80_kernel(int B, int H, int T, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const uint16_t* dy, const float* lse,
                                const float* Dr, float* dq_acc, uint16_t* dk, uint16_t* dv,
-                               float scale, float tau, float lam, hipStream_t stream, float* dk32,
+                               float scale, float tau, Lam lam, hipStream_t stream, float* dk32,
                                float* dv32) {
   using namespace bwd80;
   const int BH = B * H;

@@ -85,10 +85,11 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
     const float* __restrict__ lse, const float* __restrict__ Dr, float* __restrict__ dq_acc,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int T, int BH, float kscale,
-    float scale, float inv_tau, float lam, float* __restrict__ dk32, float* __restrict__ dv32,
+    float scale, float inv_tau, Lam lamp, float* __restrict__ dk32, float* __restrict__ dv32,
     const float* __restrict__ rc, const float* __restrict__ rs, float* __restrict__ part,
     int nbt) {
   __shared__ Smem sm;
+  const float lam = lamp.get();
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float4* __restri
 hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const uint16_t* y, const uint16_t* dy,
                            const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                           float* dlambda, void* ws, float scale, float tau, float lam,
+                           float* dlambda, void* ws, float scale, float tau, Lam lam,
                            hipStream_t stream, float* dk32, float* dv32, const float* rope_cos,
                            const float* rope_sin) {
   using namespace bwdbf16;

@@ -39,7 +39,8 @@ template <int D>
 __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ dy, const float* __restrict__ lse, const float* __restrict__ Dr,
-    float* __restrict__ dq, int T, int nblk, float scale, float tau, float lam) {
+    float* __restrict__ dq, int T, int nblk, float scale, float tau, Lam lamp) {
+  const float lam = lamp.get();
   __shared__ float Qo[64][D + 1], Go[64][D + 1];  // own q_i, dY_i
   __shared__ float Ks[64][D + 1], Vs[64][D + 1];
   const int lane = threadIdx.x;
@@ -90,7 +91,8 @@ __global__ __launch_bounds__(64) void bwd_f32_dkdv_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ dy, const float* __restrict__ lse, const float* __restrict__ Dr,
     float* __restrict__ dk, float* __restrict__ dv, int T, int nblk, float scale, float tau,
-    float lam) {
+    Lam lamp) {
+  const float lam = lamp.get();
   __shared__ float Ko[64][D + 1], Vo[64][D + 1];  // own k_j, v_j
   __shared__ float Qs[64][D + 1], Gs[64][D + 1];  // scanned q_i, dY_i
   __shared__ float Ls[64], Rs[64], Cs[64];
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dkdv_kernel(
 hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const float* k,
                           const float* v, const float* y, const float* dy, const float* lse,
                           float* dq, float* dk, float* dv, float* dlambda, void* ws, float scale,
-                          float tau, float lam, hipStream_t stream) {
+                          float tau, Lam lam, hipStream_t stream) {
   const BwdWorkspace w = bwd_workspace_layout(0, B, H, T, D);
   char* wsb = static_cast<char*>(ws);
   hipError_t e = launch_bwd_pre(0, B, H, T, D, q, k, v, y, dy, lse, dlambda, w, wsb, scale, tau,

@@ -236,7 +236,7 @@ template <bool MHR, bool OFF, int DR, bool SPLIT = false>
 __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ y, float* __restrict__ lse,
-    float* __restrict__ gate, int T, int BH, int nqb, float qscale, float inv_tau, float lam,
+    float* __restrict__ gate, int T, int BH, int nqb, float qscale, float inv_tau, Lam lam,
     Mhr mh, Seg sg, Split sp = Split{}) {
   using Dm = Dims<DR>;
   constexpr int D = Dm::D, NQ = Dm::NQ, ND = Dm::ND, KS = Dm::KS, VS = Dm::VS;
@@ -548,7 +548,7 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   const float S2 = S * kLog2e;
   float g, lz;
   if (ltot > 0.f) {
-    const float A2 = st.m + fast_log2(ltot) - lam * fast_log2(static_cast<float>(pos0 + qi + 1));
+    const float A2 = st.m + fast_log2(ltot) - lam.get() * fast_log2(static_cast<float>(pos0 + qi + 1));
     g = fast_rcp(1.0f + fast_exp2(S2 - A2));
     lz = kLn2 * (fmaxf(S2, A2) + fast_log2(1.0f + fast_exp2(-fabsf(S2 - A2))));
   } else {  // row 1: empty history, A = -inf
@@ -597,7 +597,7 @@ template <int DR>
 __global__ __launch_bounds__(256) void split_combine_kernel(
     const float* __restrict__ part, const uint16_t* __restrict__ v, uint16_t* __restrict__ y,
     float* __restrict__ lse, float* __restrict__ gate, int T, int BH, int nqb, float inv_tau,
-    float lam, Seg sg, Split sp, bool off) {
+    Lam lam, Seg sg, Split sp, bool off) {
   constexpr int D = DR, CQ = DR / 4, PW = DR + 4;
   const size_t g = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   const size_t row = g / CQ;
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(256) void split_combine_kernel(
   const float S2 = S * kLog2e;
   float gt, lz;
   if (l > 0.f) {
-    const float A2 = mx + fast_log2(l) - lam * fast_log2(static_cast<float>(pos0 + qi + 1));
+    const float A2 = mx + fast_log2(l) - lam.get() * fast_log2(static_cast<float>(pos0 + qi + 1));
     gt = fast_rcp(1.0f + fast_exp2(S2 - A2));
     lz = kLn2 * (fmaxf(S2, A2) + fast_log2(1.0f + fast_exp2(-fabsf(S2 - A2))));
   } else {
@@ -693,7 +693,7 @@ SplitPlan plan_split(int BH, int T, int pbound, bool ragged, int DR) {
 template <int DR>
 hipError_t run_fwd(int BH, int H, int T, const uint16_t* q, const uint16_t* k,
                    const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale, float tau,
-                   float lam, hipStream_t stream, const float* rope_cos, const float* rope_sin,
+                   Lam lam, hipStream_t stream, const float* rope_cos, const float* rope_sin,
                    float* ws, size_t ws_bytes) {
   const int nqb = (T + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(nqb) * BH);
@@ -768,7 +768,7 @@ size_t prefill_workspace_bytes(int B, int H, int D, int m, int n_hist, bool per_
 
 hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale,
-                           float tau, float lam, hipStream_t stream, const float* rope_cos,
+                           float tau, Lam lam, hipStream_t stream, const float* rope_cos,
                            const float* rope_sin, float* ws, size_t ws_bytes) {
   const int BH = B * H;
   if (D == 48)

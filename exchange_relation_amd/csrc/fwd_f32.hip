@@ -22,7 +22,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
                                                      float* __restrict__ y,
                                                      float* __restrict__ lse,
                                                      float* __restrict__ gate, int T, int nblk,
-                                                     float scale, float tau, float lam) {
+                                                     float scale, float tau, Lam lam) {
   __shared__ float Ks[64][D + 1];
   __shared__ float Vs[64][D + 1];
   const int lane = threadIdx.x;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
   const size_t row = base + static_cast<size_t>(t) * D;
   float g, lz;
   if (l > 0.f) {
-    const float A = m + logf(l) - lam * logf(static_cast<float>(t + 1));
+    const float A = m + logf(l) - lam.get() * logf(static_cast<float>(t + 1));
     g = 1.f / (1.f + expf(S - A));
     lz = fmaxf(S, A) + log1pf(expf(-fabsf(S - A)));
   } else {  // empty history: A = -inf
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
 
 hipError_t launch_fwd_f32(int B, int H, int T, int D, const float* q, const float* k,
                           const float* v, float* y, float* lse, float* gate, float scale,
-                          float tau, float lam, hipStream_t stream) {
+                          float tau, Lam lam, hipStream_t stream) {
   const int nblk = (T + 63) / 64;
   const dim3 grid(static_cast<unsigned>(nblk) * B * H);
   if (D == 32) {

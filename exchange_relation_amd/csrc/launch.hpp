@@ -9,10 +9,20 @@
 
 namespace rel {
 
+// The count correction's lambda (Sec. 3.1): a value, or a device fp32 scalar
+// read by the kernels at run time (p non-NULL; v is then unused), so that a
+// learnable lambda kept on the device needs no host synchronisation.
+struct Lam {
+  float v;
+  const float* p;
+  __host__ __device__ Lam(float x = 0.f, const float* ptr = nullptr) : v(x), p(ptr) {}
+  __device__ __forceinline__ float get() const { return p ? *p : v; }
+};
+
 // Forward, fp32 storage and arithmetic (VALU), D in {32, 64}.
 hipError_t launch_fwd_f32(int B, int H, int T, int D, const float* q, const float* k,
                           const float* v, float* y, float* lse, float* gate, float scale,
-                          float tau, float lam, hipStream_t stream);
+                          float tau, Lam lam, hipStream_t stream);
 
 // Forward, bf16 storage, bf16 MFMA contractions with fp32 accumulation,
 // D in {48, 64, 80}. rope_cos / rope_sin ([T, D/2] fp32, or NULL; D = 64
@@ -23,7 +33,7 @@ hipError_t launch_fwd_f32(int B, int H, int T, int D, const float* q, const floa
 size_t fwd_bf16_workspace_bytes(int B, int H, int T, int D);
 hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, uint16_t* y, float* lse, float* gate, float scale,
-                           float tau, float lam, hipStream_t stream,
+                           float tau, Lam lam, hipStream_t stream,
                            const float* rope_cos = nullptr, const float* rope_sin = nullptr,
                            float* ws = nullptr, size_t ws_bytes = 0);
 
@@ -32,7 +42,7 @@ size_t bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
 hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const float* k,
                           const float* v, const float* y, const float* dy, const float* lse,
                           float* dq, float* dk, float* dv, float* dlambda, void* ws, float scale,
-                          float tau, float lam, hipStream_t stream);
+                          float tau, Lam lam, hipStream_t stream);
 // bf16 D in {48, 64, 80} (48 runs in the 64-wide tiles with zero columns, 80
 // in the wider layout of bwd80.hip).
 // dk32 / dv32 non-NULL: dk (scaled) and dv go there in fp32, and dq is left
@@ -40,7 +50,7 @@ hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const floa
 hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const uint16_t* y, const uint16_t* dy,
                            const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                           float* dlambda, void* ws, float scale, float tau, float lam,
+                           float* dlambda, void* ws, float scale, float tau, Lam lam,
                            hipStream_t stream, float* dk32 = nullptr,
                            float* dv32 = nullptr, const float* rope_cos = nullptr,
                            const float* rope_sin = nullptr);
@@ -50,7 +60,7 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
 hipError_t launch_bwd80_kernel(int B, int H, int T, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const uint16_t* dy, const float* lse,
                                const float* Dr, float* dq_acc, uint16_t* dk, uint16_t* dv,
-                               float scale, float tau, float lam, hipStream_t stream, float* dk32,
+                               float scale, float tau, Lam lam, hipStream_t stream, float* dk32,
                                float* dv32);
 
 // Relation Cache prefill (bf16, D in {48, 64, 80}): appends m new tokens per (b, h) at

@@ -129,15 +129,17 @@ size_t relation_fwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, i
 relation_status relation_fwd(relation_dtype dtype, int B, int H, int T, int D, const void* q,
                              const void* k, const void* v, void* y, float* lse, float* gate,
                              void* workspace, size_t workspace_bytes, float scale, float tau_s,
-                             float lambda, void* stream) {
+                             float lambda, const float* lambda_dev, void* stream) {
   if (!q || !k || !v || !y) return REL_ERR_NULL;
   relation_status st = check_dtype_dim(dtype, D);
   if (st != REL_OK) return st;
   if ((st = check_shape(B, H, T, D)) != REL_OK) return st;
   if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
-      (lse && !aligned4(lse)) || (gate && !aligned4(gate)))
+      (lse && !aligned4(lse)) || (gate && !aligned4(gate)) ||
+      (lambda_dev && !aligned4(lambda_dev)))
     return REL_ERR_ALIGN;
+  const rel::Lam lam(lambda, lambda_dev);
   if (workspace) {
     if (workspace_bytes < relation_fwd_workspace_bytes(dtype, B, H, T, D))
       return REL_ERR_WORKSPACE;
@@ -148,11 +150,11 @@ relation_status relation_fwd(relation_dtype dtype, int B, int H, int T, int D, c
     return from_hip(rel::launch_fwd_f32(B, H, T, D, static_cast<const float*>(q),
                                         static_cast<const float*>(k),
                                         static_cast<const float*>(v), static_cast<float*>(y), lse,
-                                        gate, scale, tau_s, lambda, s));
+                                        gate, scale, tau_s, lam, s));
   return from_hip(rel::launch_fwd_bf16(B, H, T, D, static_cast<const uint16_t*>(q),
                                        static_cast<const uint16_t*>(k),
                                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(y),
-                                       lse, gate, scale, tau_s, lambda, s, nullptr, nullptr,
+                                       lse, gate, scale, tau_s, lam, s, nullptr, nullptr,
                                        static_cast<float*>(workspace),
                                        workspace ? workspace_bytes : 0));
 }
@@ -166,7 +168,7 @@ relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D, c
                              const void* k, const void* v, const void* y, const void* dy,
                              const float* lse, void* dq, void* dk, void* dv, float* dlambda,
                              void* workspace, size_t workspace_bytes, float scale, float tau_s,
-                             float lambda, void* stream) {
+                             float lambda, const float* lambda_dev, void* stream) {
   if (!q || !k || !v || !y || !dy || !lse || !dq || !dk || !dv) return REL_ERR_NULL;
   relation_status st = check_dtype_dim_bwd(dtype, D);
   if (st != REL_OK) return st;
@@ -174,8 +176,9 @@ relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D, c
   if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) || !aligned16(dy) ||
       !aligned4(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
-      (dlambda && !aligned4(dlambda)))
+      (dlambda && !aligned4(dlambda)) || (lambda_dev && !aligned4(lambda_dev)))
     return REL_ERR_ALIGN;
+  const rel::Lam lam(lambda, lambda_dev);
   const size_t need = rel::bwd_workspace_bytes(dtype == REL_BF16 ? 1 : 0, B, H, T, D);
   if (!workspace || workspace_bytes < need) return REL_ERR_WORKSPACE;
   if (!aligned256(workspace)) return REL_ERR_ALIGN;
@@ -185,13 +188,13 @@ relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D, c
         B, H, T, D, static_cast<const float*>(q), static_cast<const float*>(k),
         static_cast<const float*>(v), static_cast<const float*>(y), static_cast<const float*>(dy),
         lse, static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), dlambda,
-        workspace, scale, tau_s, lambda, s));
+        workspace, scale, tau_s, lam, s));
   return from_hip(rel::launch_bwd_bf16(
       B, H, T, D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(y),
       static_cast<const uint16_t*>(dy), lse, static_cast<uint16_t*>(dq),
       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dlambda, workspace, scale, tau_s,
-      lambda, s));
+      lam, s));
 }
 
 size_t relation_decode_workspace_bytes(relation_dtype dtype, int B, int H, int D, int capacity) {
@@ -330,7 +333,8 @@ relation_status relation_mhr_fwd(relation_dtype dtype, int B, int H, int T, int 
                                  const void* p2, const void* I, const float* rope_cos,
                                  const float* rope_sin, const float* theta, int pairing, void* y,
                                  float* lse, float* gate, void* workspace, size_t workspace_bytes,
-                                 float scale, float tau_s, float lambda, void* stream) {
+                                 float scale, float tau_s, float lambda, const float* lambda_dev,
+                                 void* stream) {
   if (!p1 || !p2 || !I || !y) return REL_ERR_NULL;
   relation_status st = check_dtype_dim(dtype, D);
   if (st != REL_OK) return st;
@@ -338,8 +342,10 @@ relation_status relation_mhr_fwd(relation_dtype dtype, int B, int H, int T, int 
   if ((st = check_params(scale, tau_s, lambda)) != REL_OK) return st;
   if ((st = check_mhr(H, rope_cos, rope_sin, theta, pairing)) != REL_OK) return st;
   if (!aligned16(p1) || !aligned16(p2) || !aligned16(I) || !aligned16(y) ||
-      (lse && !aligned4(lse)) || (gate && !aligned4(gate)))
+      (lse && !aligned4(lse)) || (gate && !aligned4(gate)) ||
+      (lambda_dev && !aligned4(lambda_dev)))
     return REL_ERR_ALIGN;
+  const rel::Lam lam(lambda, lambda_dev);
   const MhrLayout L = mhr_layout(false, dtype, B, H, T, D);
   if (!workspace || workspace_bytes < L.total) return REL_ERR_WORKSPACE;
   if (!aligned256(workspace)) return REL_ERR_ALIGN;
@@ -362,10 +368,10 @@ relation_status relation_mhr_fwd(relation_dtype dtype, int B, int H, int T, int 
     return from_hip(rel::launch_fwd_bf16(
         B, H, T, D, static_cast<const uint16_t*>(qe), static_cast<const uint16_t*>(ke),
         static_cast<const uint16_t*>(ve), static_cast<uint16_t*>(y), lse, gate, scale, tau_s,
-        lambda, s, q ? nullptr : rope_cos, q ? nullptr : rope_sin));
+        lam, s, q ? nullptr : rope_cos, q ? nullptr : rope_sin));
   return from_hip(rel::launch_fwd_f32(B, H, T, D, static_cast<const float*>(qe),
                                       static_cast<const float*>(ke), static_cast<const float*>(ve),
-                                      static_cast<float*>(y), lse, gate, scale, tau_s, lambda, s));
+                                      static_cast<float*>(y), lse, gate, scale, tau_s, lam, s));
 }
 
 size_t relation_mhr_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D) {
@@ -380,7 +386,7 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                                  void* dp2, void* dI, float* dlambda, float* dtheta,
                                  const void* fwd_workspace, void* workspace,
                                  size_t workspace_bytes, float scale, float tau_s, float lambda,
-                                 void* stream) {
+                                 const float* lambda_dev, void* stream) {
   if (!p1 || !p2 || !I || !y || !dy || !lse || !dp1 || !dp2 || !dI) return REL_ERR_NULL;
   relation_status st = check_dtype_dim_bwd(dtype, D);
   if (st != REL_OK) return st;
@@ -389,8 +395,10 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
   if ((st = check_mhr(H, rope_cos, rope_sin, theta, pairing)) != REL_OK) return st;
   if (!aligned16(p1) || !aligned16(p2) || !aligned16(I) || !aligned16(y) || !aligned16(dy) ||
       !aligned4(lse) || !aligned16(dp1) || !aligned16(dp2) || !aligned16(dI) ||
-      (dlambda && !aligned4(dlambda)) || (dtheta && !aligned4(dtheta)))
+      (dlambda && !aligned4(dlambda)) || (dtheta && !aligned4(dtheta)) ||
+      (lambda_dev && !aligned4(lambda_dev)))
     return REL_ERR_ALIGN;
+  const rel::Lam lam(lambda, lambda_dev);
   const MhrLayout L = mhr_layout(true, dtype, B, H, T, D);
   if (!workspace || workspace_bytes < L.total) return REL_ERR_WORKSPACE;
   if (!aligned256(workspace) || (fwd_workspace && !aligned256(fwd_workspace))) return REL_ERR_ALIGN;
@@ -426,7 +434,7 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                             static_cast<const float*>(k), static_cast<const float*>(v),
                             static_cast<const float*>(y), static_cast<const float*>(dy), lse,
                             static_cast<float*>(dp1), static_cast<float*>(dp2),
-                            static_cast<float*>(dI), dlambda, w + L.bwd, scale, tau_s, lambda,
+                            static_cast<float*>(dI), dlambda, w + L.bwd, scale, tau_s, lam,
                             s) != hipSuccess)
       return REL_ERR_HIP;
     return from_hip(rel::launch_mhr_post(0, B, H, T, D, static_cast<const float*>(dp1), 1.0f,
@@ -444,7 +452,7 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                            static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                            static_cast<const uint16_t*>(y), static_cast<const uint16_t*>(dy), lse,
                            static_cast<uint16_t*>(dp1), static_cast<uint16_t*>(dp2),
-                           static_cast<uint16_t*>(dI), dlambda, w + L.bwd, scale, tau_s, lambda,
+                           static_cast<uint16_t*>(dI), dlambda, w + L.bwd, scale, tau_s, lam,
                            s, dk32, dv32, fuse_dk ? rope_cos : nullptr,
                            fuse_dk ? rope_sin : nullptr) != hipSuccess)
     return REL_ERR_HIP;

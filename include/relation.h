@@ -27,9 +27,10 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
  *    call only enqueues work on that stream and returns; the caller
  *    synchronises. Call order on one stream defines the data flow.
- *  - The library allocates no device memory, keeps no state between calls,
- *    never frees or retains caller memory, and is safe to call from several
- *    host threads. Outputs must not alias inputs.
+ *  - The library allocates no device memory, keeps no state between calls
+ *    (save the static scratch of relation_cache_decode_noalloc), never frees
+ *    or retains caller memory, and is safe to call from several host
+ *    threads. Outputs must not alias inputs.
  *  - Validation is synchronous, on the host, before anything is enqueued; on
  *    any error nothing is written. Errors reported by the HIP runtime at
  *    launch map to REL_ERR_HIP; faults inside kernels surface at the caller's
@@ -38,6 +39,12 @@
  *    so callers normally pass 1/sqrt(D). Any finite value is accepted.
  *  - tau_s > 0 (the pages fix tau_s = 2); lambda: any finite value (the
  *    pages' learnable layer-wise count correction, Sec. 3.1).
+ *  - lambda_dev (relation_fwd, relation_bwd, relation_mhr_fwd,
+ *    relation_mhr_bwd): NULL, or a DEVICE float32 scalar, 4-byte aligned,
+ *    that the kernels read when they run; `lambda` is then unused (still
+ *    checked to be finite: pass 0). A learnable lambda kept on the device
+ *    thus needs no host synchronisation per call. Its value is not checked:
+ *    a non-finite one gives non-finite outputs.
  */
 #ifndef LIBRELATION_RELATION_H
 #define LIBRELATION_RELATION_H
@@ -95,7 +102,7 @@ relation_status relation_fwd(relation_dtype dtype, int B, int H, int T, int D,
                              void* y, float* lse, float* gate,
                              void* workspace, size_t workspace_bytes,
                              float scale, float tau_s, float lambda,
-                             void* stream);
+                             const float* lambda_dev, void* stream);
 
 /* Workspace bytes relation_fwd can use at this shape: 0 when the grid is
  * large enough on its own (and for REL_F32 or an invalid shape). */
@@ -125,7 +132,7 @@ relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D,
                              void* dq, void* dk, void* dv, float* dlambda,
                              void* workspace, size_t workspace_bytes,
                              float scale, float tau_s, float lambda,
-                             void* stream);
+                             const float* lambda_dev, void* stream);
 
 /*
  * relation_cache_decode — one autoregressive step over the KV-style Relation
@@ -315,7 +322,7 @@ relation_status relation_mhr_fwd(relation_dtype dtype, int B, int H, int T, int 
                                  void* y, float* lse, float* gate,
                                  void* workspace, size_t workspace_bytes,
                                  float scale, float tau_s, float lambda,
-                                 void* stream);
+                                 const float* lambda_dev, void* stream);
 
 size_t relation_mhr_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, int D);
 
@@ -329,7 +336,7 @@ relation_status relation_mhr_bwd(relation_dtype dtype, int B, int H, int T, int 
                                  const void* fwd_workspace,
                                  void* workspace, size_t workspace_bytes,
                                  float scale, float tau_s, float lambda,
-                                 void* stream);
+                                 const float* lambda_dev, void* stream);
 
 /*
  * relation_linear_fwd — Linear Relation (Sec. 5.2; App. A.4): historical

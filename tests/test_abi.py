@@ -53,9 +53,9 @@ def test_status_strings_and_version(lib):
 
 
 def fwd(lib, dtype=BF16, B=1, H=1, T=8, D=64, q=P, k=P, v=P, y=P, lse=NUL, gate=NUL,
-        scale=0.125, tau=2.0, lam=0.5, ws=NUL, wsb=0):
+        scale=0.125, tau=2.0, lam=0.5, ws=NUL, wsb=0, lam_dev=NUL):
     return lib.relation_fwd(dtype, B, H, T, D, q, k, v, y, lse, gate, ws, wsb, scale, tau, lam,
-                            None)
+                            lam_dev, None)
 
 
 def test_fwd_split_workspace(lib):
@@ -94,6 +94,8 @@ def test_fwd_validation(lib):
     assert fwd(lib, scale=float("inf")) == REL_ERR_PARAM
     assert fwd(lib, q=P_MIS) == REL_ERR_ALIGN
     assert fwd(lib, lse=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
+    assert fwd(lib, lam_dev=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN  # device lambda
+    assert fwd(lib, lam=float("nan"), lam_dev=P) == REL_ERR_PARAM  # still checked when unused
 
 
 def test_bwd_validation_and_workspace(lib):
@@ -105,10 +107,12 @@ def test_bwd_validation_and_workspace(lib):
     assert lib.relation_bwd_workspace_bytes(BF16, 2, 3, 100, 80) > 0
     assert lib.relation_bwd_workspace_bytes(BF16, 2, 3, 100, 96) == 0
 
-    def bwd(ws=P, wsb=None, dq=P, lse=P, tau=2.0, T=100):
+    def bwd(ws=P, wsb=None, dq=P, lse=P, tau=2.0, T=100, lam_dev=NUL):
         wsb = need if wsb is None else wsb
         return lib.relation_bwd(BF16, 2, 3, T, 64, P, P, P, P, P, lse, dq, P, P, NUL, ws, wsb,
-                                0.125, tau, 0.3, None)
+                                0.125, tau, 0.3, lam_dev, None)
+
+    assert bwd(lam_dev=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN  # device lambda
 
     assert bwd(dq=NUL) == REL_ERR_NULL
     assert bwd(lse=NUL) == REL_ERR_NULL
@@ -216,9 +220,11 @@ def test_mhr_validation(lib):
     need = lib.relation_mhr_bwd_workspace_bytes(BF16, 2, 4, 128, 64)
     assert need > lib.relation_bwd_workspace_bytes(BF16, 2, 4, 128, 64)
 
-    def fwd(H=4, cs=P, sn=P, th=P, pairing=0, dtype=BF16, ws=NUL, wsb=0):
+    def fwd(H=4, cs=P, sn=P, th=P, pairing=0, dtype=BF16, ws=NUL, wsb=0, lam_dev=NUL):
         return lib.relation_mhr_fwd(dtype, 2, H, 128, 64, P, P, P, cs, sn, th, pairing, P, NUL,
-                                    NUL, ws, wsb, 0.125, 2.0, 0.3, None)
+                                    NUL, ws, wsb, 0.125, 2.0, 0.3, lam_dev, None)
+
+    assert fwd(lam_dev=ctypes.c_void_p(0x7F0000000002)) == REL_ERR_ALIGN
 
     assert fwd(cs=NUL) == REL_ERR_NULL               # tables go together
     assert fwd(H=5) == REL_ERR_SHAPE                 # Givens pairs need even H
@@ -230,7 +236,7 @@ def test_mhr_validation(lib):
     def bwd(ws=P, wsb=None, fws=NUL):
         wsb = need if wsb is None else wsb
         return lib.relation_mhr_bwd(BF16, 2, 4, 128, 64, P, P, P, P, P, P, 0, P, P, P, P, P, P,
-                                    NUL, NUL, fws, ws, wsb, 0.125, 2.0, 0.3, None)
+                                    NUL, NUL, fws, ws, wsb, 0.125, 2.0, 0.3, NUL, None)
 
     assert bwd(wsb=need - 256) == REL_ERR_WORKSPACE
     assert bwd(ws=NUL) == REL_ERR_WORKSPACE
