@@ -385,13 +385,26 @@ __global__ __launch_bounds__(NT, 8 / NW) void bwd_bf16_kernel(
       // queries past T
       float* __restrict__ dqh = dq_acc + base;
       const bool full = qt0 + BQ <= T;
+      if (dw * 16 < DR) {
+        if (full) {  // straight-line: no per-lane test
 #pragma unroll
-      for (int b = 0; b < QBW; ++b) {
+          for (int b = 0; b < QBW; ++b) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = qt0 + (qw + b) * 16 + g16 * 4 + j;
-          if ((full || i < T) && dw * 16 < DR)
-            unsafeAtomicAdd(dqh + static_cast<uint32_t>(i * DR + dw * 16 + l16), aq[b][j]);
+            for (int j = 0; j < 4; ++j) {
+              const int i = qt0 + (qw + b) * 16 + g16 * 4 + j;
+              unsafeAtomicAdd(dqh + static_cast<uint32_t>(i * DR + dw * 16 + l16), aq[b][j]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < QBW; ++b) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = qt0 + (qw + b) * 16 + g16 * 4 + j;
+              if (i < T)
+                unsafeAtomicAdd(dqh + static_cast<uint32_t>(i * DR + dw * 16 + l16), aq[b][j]);
+            }
+          }
         }
       }
     }

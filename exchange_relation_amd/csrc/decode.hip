@@ -38,7 +38,10 @@
 // Ragged batches: each sequence b has its own history length n_b (a device
 // int array). The launch is sized for an upper bound of the lengths; a split
 // workgroup whose chunk lies past its sequence's n_b exits at once, and the
-// combine does the append. A sequence whose n_b is out of range (negative,
+// combine does the append. The ragged grid is split-major (chunk s of every
+// head before chunk s + 1 of any), so the chunks that hold work are spread
+// over the whole launch rather than bunched by sequence: 45.9 -> 34.3 us per
+// step at lengths uniform in [0, 4096] (32 x 12 heads). A sequence whose n_b is out of range (negative,
 // above the bound, or without a free slot) gets NaN outputs and no append.
 #include <math.h>
 
@@ -51,12 +54,13 @@ namespace rel {
 namespace dec {
 
 #ifndef REL_DECODE_CHUNK
-#define REL_DECODE_CHUNK 512
+#define REL_DECODE_CHUNK 256
 #endif
 #ifndef REL_DECODE_UNROLL
 #define REL_DECODE_UNROLL 8
 #endif
-constexpr int kChunk = REL_DECODE_CHUNK;    // target slots per split workgroup
+// target slots per split workgroup: one pass of the 32 groups x 8 slots
+constexpr int kChunk = REL_DECODE_CHUNK;
 constexpr int kGroups = 32;                 // 8-lane groups per 256-lane workgroup
 constexpr int kUnroll = REL_DECODE_UNROLL;  // slots per group per iteration (loads in flight)
 constexpr int kBatch = 8;                   // partials loaded at once by the combine
@@ -94,8 +98,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int tid = threadIdx.x;
   const int grp = tid >> 3;
   const int sub = tid & 7;
-  const int split = WHOLE ? 0 : blockIdx.x % nsplit;
-  const int head = WHOLE ? blockIdx.x : blockIdx.x / nsplit;
+  // ragged: split-major grid (every head's first chunk is dispatched first)
+  const int bhg = gridDim.x / nsplit;
+  const int split = WHOLE ? 0 : RAGGED ? blockIdx.x / bhg : blockIdx.x % nsplit;
+  const int head = WHOLE ? blockIdx.x : RAGGED ? blockIdx.x % bhg : blockIdx.x / nsplit;
   const size_t cbase = static_cast<size_t>(head) * capacity * D;
   const size_t hv = static_cast<size_t>(head) * D;
   static_assert(!(RAGGED && WHOLE), "the whole-history mode is for uniform lengths");
@@ -232,78 +238,95 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   bool act[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) act[e] = tid + 64 * e < D;
-  if (RAGGED) {
-    const int bound = n;
-    n = nh[head / H];
-    if (n < 0 || n > bound || n >= capacity) {  // out of range: NaN outputs, no append
-#pragma unroll
-      for (int e = 0; e < EL; ++e)
-        if (act[e]) Elem<TE>::store(y + hv + tid + 64 * e, NAN);
-      if (tid == 0 && gate) gate[head] = NAN;
-      return;
-    }
-    nsplit = n > 0 ? split_plan(n).nsplit : 0;
-  }
+  // Every load that does not depend on the sequence's length is issued
+  // first: the new token's q / k / v and, for a ragged batch, every partial
+  // slot of the head (the grid's pstride chunks; slots past the sequence's
+  // own chunks hold stale values and are dropped by selects below).
+  const int bound = n;
+  if (RAGGED) n = nh[head / H];
   float qd[EL], kd[EL], vd[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) {
-    const int d = tid + 64 * e;
-    qd[e] = act[e] ? Elem<TE>::load(q + hv + d) : 0.f;
-    kd[e] = act[e] ? Elem<TE>::load(kn + hv + d) : 0.f;
-    vd[e] = act[e] ? Elem<TE>::load(vn + hv + d) : 0.f;
+    const int d = act[e] ? tid + 64 * e : 0;
+    qd[e] = Elem<TE>::load(q + hv + d);
+    kd[e] = Elem<TE>::load(kn + hv + d);
+    vd[e] = Elem<TE>::load(vn + hv + d);
   }
-  if (RAGGED || nsplit == 0) {  // the append was not done by a split kernel
-#pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      if (!act[e]) continue;
-      const int d = tid + 64 * e;
-      const size_t slot = (static_cast<size_t>(head) * capacity + n) * D + d;
-      kc[slot] = kn[hv + d];
-      vc[slot] = vn[hv + d];
-    }
-  }
-
-  // Self: u'_ii = scale*log2(e) * q . k_new
-  float us = 0.f;
-#pragma unroll
-  for (int e = 0; e < EL; ++e) us = fmaf(qd[e], kd[e], us);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) us += __shfl_xor(us, o);
-  us *= qscale;
-
-  // merge the chunk partials (App. A.3.2), kBatch partials per round with
-  // all their loads issued before any is used
+  const float* ph = part + static_cast<size_t>(head) * (RAGGED ? pstride : nsplit) * (D + 2);
   float M = -INFINITY, Ls = 0.f, Z[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) Z[e] = 0.f;
-  const float* ph = part + static_cast<size_t>(head) * (RAGGED ? pstride : nsplit) * (D + 2);
-  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
-    float pm[kBatch], pl[kBatch], pz[kBatch][EL];
+  // merge the chunk partials (App. A.3.2), kBatch partials per round with
+  // all their loads issued before any is used
+  auto merge = [&](int s0, int ns, int nvalid) {
+    constexpr int KB = RAGGED ? 2 * kBatch : kBatch;
+    float pm[KB], pl[KB], pz[KB][EL];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const bool ok = s0 + b < nsplit;
-      const float* pr = ph + static_cast<size_t>(ok ? s0 + b : 0) * (D + 2);
-      pm[b] = ok ? pr[0] : -INFINITY;
-      pl[b] = ok ? pr[1] : 0.f;
+    for (int b = 0; b < KB; ++b) {
+      const bool in = s0 + b < ns;
+      const float* pr = ph + static_cast<size_t>(in ? s0 + b : 0) * (D + 2);
+      pm[b] = pr[0];
+      pl[b] = pr[1];
 #pragma unroll
-      for (int e = 0; e < EL; ++e) pz[b][e] = (ok && act[e]) ? pr[2 + tid + 64 * e] : 0.f;
+      for (int e = 0; e < EL; ++e) pz[b][e] = pr[2 + (act[e] ? tid + 64 * e : 0)];
+    }
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      const bool ok = s0 + b < nvalid;
+      pm[b] = ok ? pm[b] : -INFINITY;
+      pl[b] = ok ? pl[b] : 0.f;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) pz[b][e] = (ok && act[e]) ? pz[b][e] : 0.f;
     }
     float Mn = M;
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) Mn = fmaxf(Mn, pm[b]);
-    if (Mn == -INFINITY) continue;  // nothing yet
+    for (int b = 0; b < KB; ++b) Mn = fmaxf(Mn, pm[b]);
+    if (Mn == -INFINITY) return;  // nothing yet
     const float a = fast_exp2(M - Mn);  // M = -inf -> 0
     Ls *= a;
 #pragma unroll
     for (int e = 0; e < EL; ++e) Z[e] *= a;
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
+    for (int b = 0; b < KB; ++b) {
       const float w = fast_exp2(pm[b] - Mn);  // -inf -> 0
       Ls = fmaf(w, pl[b], Ls);
 #pragma unroll
       for (int e = 0; e < EL; ++e) Z[e] = fmaf(w, pz[b][e], Z[e]);
     }
     M = Mn;
+  };
+  if (RAGGED) {
+    const bool bad = n < 0 || n > bound || n >= capacity;
+    if (bad) {  // out of range: NaN outputs, no append
+#pragma unroll
+      for (int e = 0; e < EL; ++e)
+        if (act[e]) Elem<TE>::store(y + hv + tid + 64 * e, NAN);
+      if (tid == 0 && gate) gate[head] = NAN;
+      return;
+    }
+  }
+  if (RAGGED || nsplit == 0) {  // the append was not done by a split kernel
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      if (!act[e]) continue;
+      const size_t slot = (static_cast<size_t>(head) * capacity + n) * D + tid + 64 * e;
+      kc[slot] = kn[hv + tid + 64 * e];
+      vc[slot] = vn[hv + tid + 64 * e];
+    }
+  }
+  // Self: u'_ii = scale*log2(e) * q . k_new
+  float us = 0.f;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) us = act[e] ? fmaf(qd[e], kd[e], us) : us;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) us += __shfl_xor(us, o);
+  us *= qscale;
+
+  if (RAGGED) {
+    const int nvalid = n > 0 ? split_plan(n).nsplit : 0;
+    for (int s0 = 0; s0 < pstride; s0 += 2 * kBatch) merge(s0, pstride, nvalid);
+  } else {
+    for (int s0 = 0; s0 < nsplit; s0 += kBatch) merge(s0, nsplit, nsplit);
   }
   const float S = fast_rcp(1.0f + fast_exp2(-us * inv_tau));  // sigmoid(U_ii / tau)
   float g = 0.f;
@@ -423,6 +446,12 @@ hipError_t launch_decode_noalloc(int dtype, int B, int H, int D, const void* q,
   if (e != hipSuccess) return e;
   return launch_decode(dtype, B, H, D, q, k_new, v_new, k_cache, v_cache, capacity, n_hist,
                        nullptr, y, gate, ws, scale, tau, lam, stream);
+}
+
+size_t decode_uniform_need_bytes(int B, int H, int D, int n_hist) {
+  const long long bh = static_cast<long long>(B) * H;
+  if (n_hist <= 0 || bh >= dec::kWholeHeads) return 0;  // no partials: combine only, or WHOLE
+  return static_cast<size_t>(bh) * dec::split_plan(n_hist).nsplit * (D + 2) * sizeof(float);
 }
 
 size_t decode_workspace_bytes(int dtype, int B, int H, int D, int capacity) {

@@ -83,9 +83,12 @@ hipError_t launch_decode(int dtype, int B, int H, int D, const void* q, const vo
                          int n_hist, const int* n_hist_dev, void* y, float* gate, void* ws,
                          float scale, float tau, float lam, hipStream_t stream);
 
+// Workspace bytes the uniform step actually uses at history n_hist (0 when
+// it needs none: n_hist = 0, or one workgroup per head).
+size_t decode_uniform_need_bytes(int B, int H, int D, int n_hist);
 // The same uniform decode step with its workspace in the library's static
-// per-device array of decode_scratch_bytes() bytes (callers check the size
-// first); allocates nothing.
+// per-device array of decode_scratch_bytes() bytes (callers check
+// decode_uniform_need_bytes against it first); allocates nothing.
 size_t decode_scratch_bytes();
 hipError_t launch_decode_noalloc(int dtype, int B, int H, int D, const void* q,
                                  const void* k_new, const void* v_new, void* k_cache,

@@ -246,8 +246,7 @@ relation_status relation_cache_decode_noalloc(relation_dtype dtype, int B, int H
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
       !aligned16(v_cache) || !aligned16(y) || (gate && !aligned4(gate)))
     return REL_ERR_ALIGN;
-  if (rel::decode_workspace_bytes(dtype == REL_BF16 ? 1 : 0, B, H, D, capacity) >
-      rel::decode_scratch_bytes())
+  if (rel::decode_uniform_need_bytes(B, H, D, n_hist) > rel::decode_scratch_bytes())
     return REL_ERR_SCRATCH;
   return from_hip(rel::launch_decode_noalloc(dtype == REL_BF16 ? 1 : 0, B, H, D, q, k_new, v_new,
                                              k_cache, v_cache, capacity, n_hist, y, gate, scale,

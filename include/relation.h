@@ -174,9 +174,12 @@ relation_status relation_cache_decode(relation_dtype dtype, int B, int H, int D,
  *
  *   Arguments as for relation_cache_decode, without the workspace. The
  *   stream must belong to the current device (else REL_ERR_HIP).
- *   A call whose relation_decode_workspace_bytes() exceeds 8 MiB returns
- *   REL_ERR_SCRATCH and does nothing (at D = 64 and a capacity of 4352,
- *   up to about 3900 heads B * H).
+ *   The step uses scratch only when B * H < 256 and n_hist > 0: one fp32
+ *   partial of D + 2 values per head and chunk of about 256 history slots,
+ *   B * H * ceil(n_hist / 256) * (D + 2) * 4 bytes. A call that needs more
+ *   than 8 MiB returns REL_ERR_SCRATCH and does nothing (at D = 64 that is
+ *   beyond about 7.8 M slots of history summed over the heads; batches of
+ *   256 heads or more need none).
  *   The first call on a device looks up that device's copy of the array.
  *   Every call on one GPU shares it and it keeps the last call's contents
  *   (nothing in it needs to start at zero), so calls that overlap in time

@@ -125,8 +125,8 @@ def test_bwd_validation_and_workspace(lib):
 
 def test_decode_validation(lib):
     need = lib.relation_decode_workspace_bytes(BF16, 2, 3, 64, 4352)
-    # one partial (m, l, z[64]) per chunk of about 512 slots (9 for 4352) and head
-    assert need == 2 * 3 * 9 * 66 * 4
+    # one partial (m, l, z[64]) per chunk of about 256 slots (17 for 4352) and head
+    assert need == 2 * 3 * 17 * 66 * 4
 
     def dec(n=10, cap=4352, ws=P, wsb=None, q=P, D=64, dtype=BF16):
         wsb = need if wsb is None else wsb
@@ -158,9 +158,11 @@ def test_decode_noalloc_validation(lib):
     assert dec(y=NUL) == REL_ERR_NULL
     assert dec(D=32) == REL_ERR_UNSUPPORTED
     assert dec(q=P_MIS) == REL_ERR_ALIGN
-    # 32 x 128 heads at capacity 4352: 4096 * 9 * 66 * 4 B = 9.3 MiB > 8 MiB
-    assert lib.relation_decode_workspace_bytes(BF16, 32, 128, 64, 4352) > 8 << 20
-    assert dec(B=32, H=128) == REL_ERR_SCRATCH
+    # the scratch holds what the step uses: one partial per head and 256-slot
+    # chunk below 256 heads. 1 x 100 heads at history 199999: 782 chunks,
+    # 100 * 782 * 66 * 4 B = 19.7 MiB > 8 MiB (rejected before any launch)
+    assert dec(B=1, H=100, n=199999, cap=200000) == REL_ERR_SCRATCH
+    assert dec(B=1, H=100, n=199999, cap=200000, q=NUL) == REL_ERR_NULL
     assert "scratch" in rel.relation_status_string(REL_ERR_SCRATCH)
 
 

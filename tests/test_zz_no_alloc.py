@@ -48,3 +48,31 @@ def test_noalloc_decode_fp32_and_widths():
     one_pair(1, 4, 32, 700, 720, "f32", seed=9)
     one_pair(3, 2, 80, 999, 1024, "bf16", seed=10)
     one_pair(3, 2, 48, 513, 520, "bf16", seed=11)
+
+
+def test_noalloc_many_heads_need_no_scratch():
+    """From 256 heads on, the uniform step runs one workgroup per head and
+    uses no scratch, so a batch whose capacity-sized workspace is larger
+    than the 8 MiB array (4096 heads at capacity 2048) is still served, bit
+    for bit equal to relation_cache_decode; then a small split call reuses
+    the scratch."""
+    B, H, D, n, cap = 32, 128, 64, 1000, 2048
+    assert rel.relation_decode_workspace_bytes(torch.bfloat16, B, H, D, cap) > 8 << 20
+    g = torch.Generator(device=DEV).manual_seed(5)
+
+    def rnd(*shape):
+        return torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16)
+    q, kn, vn = rnd(B, H, D), rnd(B, H, D), rnd(B, H, D)
+    kc1, vc1 = rnd(B, H, cap, D), rnd(B, H, cap, D)
+    kc2, vc2 = kc1.clone(), vc1.clone()
+    scale = 1 / math.sqrt(D)
+    y1, g1 = rel.relation_cache_decode(q, kn, vn, kc1, vc1, n, lam=0.3, scale=scale,
+                                       want_gate=True)
+    y2 = torch.full_like(q, float("nan"))
+    g2 = torch.full((B, H), float("nan"), device=DEV)
+    rel.relation_cache_decode_noalloc(q, kn, vn, kc2, vc2, n, y2, lam=0.3, scale=scale, gate=g2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(g1, g2)
+    assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2)
+    del kc1, vc1, kc2, vc2
+    one_pair(2, 3, 64, 1500, 1600, "bf16", seed=12)
