@@ -97,6 +97,27 @@ struct RowState {
 // Element vi of the result is key k0 + (vi>>2)*8 + hf*4 + (vi&3), query
 // q0 + r (raw q . k).
 template <int DR>
+struct KFrag {
+  bf16x8 k[Dims<DR>::NQ];
+};
+template <int DR>
+__device__ __forceinline__ KFrag<DR> load_kfrag(const uint16_t* ks, int sb, int r, int hf) {
+  constexpr int NQ = Dims<DR>::NQ, KS = Dims<DR>::KS;
+  KFrag<DR> f;
+#pragma unroll
+  for (int c = 0; c < NQ; ++c)
+    f.k[c] = as_bf16x8(*reinterpret_cast<const uint4*>(&ks[(sb * 32 + r) * KS + hf * 8 + 16 * c]));
+  return f;
+}
+template <int DR>
+__device__ __forceinline__ f32x16 score_from(const KFrag<DR>& f, const bf16x8 (&qf)[Dims<DR>::NQ]) {
+  f32x16 s = {0};
+#pragma unroll
+  for (int c = 0; c < Dims<DR>::NQ; ++c)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.k[c], qf[c], s, 0, 0, 0);
+  return s;
+}
+template <int DR>
 __device__ __forceinline__ f32x16 score(const uint16_t* ks, int sb,
                                         const bf16x8 (&qf)[Dims<DR>::NQ], int r, int hf) {
   constexpr int NQ = Dims<DR>::NQ, KS = Dims<DR>::KS;
@@ -159,6 +180,19 @@ template <bool DIAG, int DR>
 __device__ __forceinline__ void accumulate(const uint16_t* vs, int sb, const f32x16& s, int hf,
                                            RowState<Dims<DR>::ND>& st) {
   constexpr int ND = Dims<DR>::ND, VS = Dims<DR>::VS;
+  // V^T operands first: their LDS latency runs under the exponentials
+  const int l16 = threadIdx.x & 15;
+  const int dcol = 16 * ((threadIdx.x >> 4) & 1) + 4 * (l16 & 3);
+  uint2 vt[2][ND][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int o = (sb * 32 + c * 16 + hf * 4 + (l16 >> 2)) * VS + dcol;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      vt[c][db][0] = lds_read_tr16(&vs[o + 32 * db]);
+      vt[c][db][1] = lds_read_tr16(&vs[o + 8 * VS + 32 * db]);
+    }
+  }
   uint32_t pw[8];
   const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
@@ -181,16 +215,12 @@ __device__ __forceinline__ void accumulate(const uint16_t* vs, int sb, const f32
   // key row k0 + (l16>>2), columns d0 + 4*(l16&3), so lane i gets keys
   // k0..k0+3 of column d0 + i; d0 = 32*db + 16*((lane>>4)&1) makes the
   // column 32*db + (lane&31).
-  const int l16 = threadIdx.x & 15;
-  const int dcol = 16 * ((threadIdx.x >> 4) & 1) + 4 * (l16 & 3);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const bf16x8 pb = as_bf16x8(make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
-    const int o = (sb * 32 + c * 16 + hf * 4 + (l16 >> 2)) * VS + dcol;
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
-      const uint2 al = lds_read_tr16(&vs[o + 32 * db]);
-      const uint2 ah = lds_read_tr16(&vs[o + 8 * VS + 32 * db]);
+      const uint2 al = vt[c][db][0], ah = vt[c][db][1];
       st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           as_bf16x8(make_uint4(al.x, al.y, ah.x, ah.y)), pb, st.acc[db], 0, 0, 0);
     }
@@ -444,6 +474,8 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   f32x16 sa = {0};
   if (kt0 < hend) sa = score<DR>(kp0, 0, qf, r, hf);
   int kt = kt0;
+  KFrag<DR> kn;
+  if (kt0 < hend) kn = load_kfrag<DR>(kp0, 1, r, hf);
   for (; kt < hend; ++kt) {
     const bool more_k = kt + 2 < tend;  // kt + 1 < tend always holds here
     const bool kfull = (kt + 3) * BN <= Tk, vfull = (kt + 2) * BN <= Tk;
@@ -455,10 +487,12 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     else fetch(vh, vnh, kt + 1, cv);
     const uint16_t* vs = vbuf[(kt - kt0) & 1];
     stabilise<false>(sa, qscale, r, hf, st);
-    f32x16 sb = score<DR>(kp0, 1, qf, r, hf);
+    f32x16 sb = score_from<DR>(kn, qf);
+    kn = load_kfrag<DR>(kp1, 0, r, hf);  // tile kt + 1 <= nfull is resident
     accumulate<false, DR>(vs, 0, sa, hf, st);
     stabilise<false>(sb, qscale, r, hf, st);
-    sa = score<DR>(kp1, 0, qf, r, hf);  // tile kt + 1 <= nfull is resident
+    sa = score_from<DR>(kn, qf);
+    kn = load_kfrag<DR>(kp1, 1, r, hf);
     accumulate<false, DR>(vs, 1, sb, hf, st);
     if (more_k) {
       if (kfull) stash_full(kp2, ck, KS);
