@@ -322,7 +322,8 @@ def bench_decode_ragged(rel, torch, dev, B=32, H=12, D=64, nmax=4096, steps=64, 
             "bytes": byts}
 
 
-def bench_prefill(rel, torch, dev, reps, B=32, H=12, D=64, m=256, cap=4352, seed=42):
+def bench_prefill(rel, torch, dev, reps, B=32, H=12, D=64, m=256, cap=4352, seed=42,
+                  prewarm_ms=200.0):
     """Chunked prefill into the Relation Cache on the decode workload's cache
     shape: m new tokens per sequence at ragged history lengths (uniform in
     [0, cap - m], seeded). Flops count the causal entries of the new rows,
@@ -337,14 +338,17 @@ def bench_prefill(rel, torch, dev, reps, B=32, H=12, D=64, m=256, cap=4352, seed
     nws = rel.relation_prefill_workspace_bytes(torch.bfloat16, B, H, D, m, cap - m, True)
     ws = torch.empty((nws,), device=dev, dtype=torch.uint8) if nws else None
     stream = torch.cuda.current_stream(dev)
-    t = EventTimer(torch, stream)
-    for i in range(reps + 3):
-        s0 = t.start() if i >= 3 else None
+
+    def call():  # the same new rows at the same slots every call
         rel.relation_cache_prefill(q, kn, vn, kc, vc, nh, cap - m, lam=d["lam"],
                                    scale=1 / math.sqrt(D), y=y, workspace=ws)
-        if i >= 3:
-            t.stop(s0)
-    ms = t.mean_ms()
+    prewarm(torch, call, prewarm_ms)
+    t = EventTimer(torch, stream)
+    s0 = t.start()  # back-to-back calls between one pair of events
+    for _ in range(reps):
+        call()
+    t.stop(s0)
+    ms = t.mean_ms() / reps
     entries = sum(m * n + m * (m + 1) / 2 for n in ns) * H
     tf = 4 * D * entries / (ms * 1e-3) / 1e12
     return {"workload": f"prefill {m} tokens x {B} sequences x {H} heads, ragged history "
@@ -352,7 +356,7 @@ def bench_prefill(rel, torch, dev, reps, B=32, H=12, D=64, m=256, cap=4352, seed
             "frac_peak": tf / PEAK_BF16_TFLOPS, "split_over_keys": nws > 0}
 
 
-def bench_mhr(rel, torch, dev, reps, B=16, H=8, T=2048, D=64, seed=42):
+def bench_mhr(rel, torch, dev, reps, B=16, H=8, T=2048, D=64, seed=42, prewarm_ms=200.0):
     """Multi-Head Relation with its upstream maps (RoPE of p1 / p2 from
     [T, D/2] tables, Givens mixing of I, pairing M_B) on the 30M layer shape:
     forward and forward+backward, next to the plain operator on the same
@@ -372,27 +376,33 @@ def bench_mhr(rel, torch, dev, reps, B=16, H=8, T=2048, D=64, seed=42):
     y = torch.empty_like(I)
     lse = torch.empty((B, H, T), device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream(dev)
-    tf, tb = EventTimer(torch, stream), EventTimer(torch, stream)
-    for i in range(reps + 3):
-        s0 = tf.start() if i >= 3 else None
+
+    def fwd():
         rel.relation_mhr_fwd(p1, p2, I, cs, sn, th, 1, lam=lam, scale=scale, y=y, lse=lse,
                              workspace=wsf)
-        if i >= 3:
-            tf.stop(s0)
-        s1 = tb.start() if i >= 3 else None
+
+    def bwd():
         rel.relation_mhr_bwd(p1, p2, I, y, dy, lse, cs, sn, th, 1, lam=lam, scale=scale,
                              workspace=wsb, fwd_workspace=wsf)
-        if i >= 3:
-            tb.stop(s1)
+    prewarm(torch, lambda: (fwd(), bwd()), prewarm_ms)
+    tf, tb = EventTimer(torch, stream), EventTimer(torch, stream)
+    s0 = tf.start()  # back-to-back calls between one pair of events
+    for _ in range(reps):
+        fwd()
+    tf.stop(s0)
+    s1 = tb.start()  # the backward reads the last forward's y, lse and maps
+    for _ in range(reps):
+        bwd()
+    tb.stop(s1)
     f = fwd_flops(B, H, T, D)
-    fm, bm = tf.mean_ms(), tb.mean_ms()
+    fm, bm = tf.mean_ms() / reps, tb.mean_ms() / reps
     return {"workload": "layer30m MHR (RoPE + Givens M_B), backward reusing the forward's maps",
             "fwd_ms": fm, "bwd_ms": bm,
             "fwd_tflops": f / (fm * 1e-3) / 1e12,
             "fwdbwd_tflops": 3.5 * f / ((fm + bm) * 1e-3) / 1e12}
 
 
-def bench_linear(rel, torch, dev, reps, B=32, H=8, T=1024, D=64, seed=42):
+def bench_linear(rel, torch, dev, reps, B=32, H=8, T=1024, D=64, seed=42, prewarm_ms=200.0):
     """Linear Relation forward with RoPE on the 30M-class layer at the pages'
     steady-state micro-batch (B=32, H=8, T=1024, d_h=64; App. H, Table 16).
     Algorithmic HBM bytes per token and head: p1, p2, I, y in bf16 and the
@@ -404,9 +414,8 @@ def bench_linear(rel, torch, dev, reps, B=32, H=8, T=1024, D=64, seed=42):
     y = torch.empty_like(I)
     stream = torch.cuda.current_stream(dev)
     tf = EventTimer(torch, stream)
-    for _ in range(100):  # a few ms of work: the clocks ramp under sustained load
-        rel.relation_linear_fwd(p1, p2, I, g, cs, sn, scale=1 / math.sqrt(D), y=y)
-    torch.cuda.synchronize()
+    prewarm(torch, lambda: rel.relation_linear_fwd(p1, p2, I, g, cs, sn, scale=1 / math.sqrt(D),
+                                                   y=y), prewarm_ms)
     # back-to-back calls between one pair of events (a ~65 us call would
     # otherwise also time the host's launch path)
     s0 = tf.start()
@@ -679,13 +688,14 @@ def main():
         print(json.dumps(bench_decode_ragged(rel, torch, dev, prewarm_ms=args.prewarm_ms)))
         return
     if args.only == "mhr":
-        print(json.dumps(bench_mhr(rel, torch, dev, args.steps)))
+        print(json.dumps(bench_mhr(rel, torch, dev, args.steps, prewarm_ms=args.prewarm_ms)))
         return
     if args.only == "prefill":
-        print(json.dumps(bench_prefill(rel, torch, dev, args.steps)))
+        print(json.dumps(bench_prefill(rel, torch, dev, args.steps, prewarm_ms=args.prewarm_ms)))
         return
     if args.only == "linear":
-        print(json.dumps({"fwd": bench_linear(rel, torch, dev, args.steps),
+        print(json.dumps({"fwd": bench_linear(rel, torch, dev, args.steps,
+                                              prewarm_ms=args.prewarm_ms),
                           "step": bench_linear_step(rel, torch, dev)}))
         return
     if args.only == "attn":
