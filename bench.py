@@ -118,9 +118,32 @@ def bench_step(rel, torch, dev, steps, warmup, B=16, H=8, T=2048, D=64, seed=42,
         step(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # The same step captured once as a HIP graph and replayed: the launch path
+    # of a training loop whose shapes do not change. Reported beside the
+    # value, which is the eager step above.
+    graph = {}
+    try:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(False)
+        stream.wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(False)
+        for _ in range(max(warmup, 3)):
+            g.replay()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph = {"ms_per_step": (time.perf_counter() - t2) * 1e3 / steps}
+    except RuntimeError as e:  # reported, never fatal to the value
+        graph = {"error": str(e)[:200]}
     return {"ms_per_step": (t1 - t0) * 1e3 / steps, "fwd_ms": tf.mean_ms(),
             "bwd_ms": tb.mean_ms(), "flops_fwd": fwd_flops(B, H, T, D),
-            "prewarm_ms": pw_ms, "prewarm_steps": pw_n}
+            "prewarm_ms": pw_ms, "prewarm_steps": pw_n, "graph": graph}
 
 
 def bench_fwd(rel, torch, dev, B, H, T, D, reps, rope=False, seed=42, prewarm_ms=100.0):
@@ -727,6 +750,9 @@ def main():
                          "frac": fwd_tf / PEAK_BF16_TFLOPS,
                          "traffic": kernel_traffic("fwd_bf16_kernel@layer30m")},
         "fwd_ms": st["fwd_ms"], "bwd_ms": st["bwd_ms"],
+        "step_graph_replay": dict(st["graph"], **({"tflops": 3.5 * f / (st["graph"]["ms_per_step"]
+                                                                       * 1e-3) / 1e12}
+                                                  if "ms_per_step" in st["graph"] else {})),
     }
     if not args.no_extra:
         rec["fwd_layer10m"] = bench_fwd(rel, torch, dev, 8, 8, 1024, 64, 50, rope=True)
