@@ -17,8 +17,10 @@
 //
 // RoPE pairs element d with d + D/2 and reads the caller's tables cos, sin
 // [T, D/2] (fp32) at the row's position. Thread layout of every pass: one
-// thread per (row, 8 pairs) - the chunk j of elements d = 8j..8j+7 and the
-// matching chunk of d + D/2 - so D/16 threads per row.
+// thread per (row, 4 pairs) - the chunk j of elements d = 4j..4j+3 and the
+// matching chunk of d + D/2 - so D/8 threads per row, each half of a row read
+// by consecutive threads as one contiguous run (8 pairs per thread, with two
+// strided 16-byte pieces per half, ran the dI and dp1 passes 15-18 % slower).
 #include <math.h>
 
 #include "common.hpp"
@@ -27,27 +29,32 @@
 namespace rel {
 namespace mhr {
 
+// Pairs per thread: 4, so that the 8 threads of a 64-wide row read each half
+// of it as one contiguous run (16-byte fp32 / 8-byte bf16 pieces).
+constexpr int NP = 4;
 template <typename TE> struct Io;
-template <> struct Io<uint16_t> {  // 8 bf16 per chunk
-  __device__ static void load(const uint16_t* p, float (&x)[8]) {
-    unpack8(*reinterpret_cast<const u32x4*>(p), x);
+template <> struct Io<uint16_t> {  // NP bf16 per chunk
+  __device__ static void load(const uint16_t* p, float (&x)[NP]) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
   }
-  __device__ static void store(uint16_t* p, const float (&x)[8]) {
-    *reinterpret_cast<u32x4*>(p) = pack8(x);
+  __device__ static void store(uint16_t* p, const float (&x)[NP]) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
   }
 };
-template <> struct Io<float> {  // 8 floats per chunk
-  __device__ static void load(const float* p, float (&x)[8]) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+template <> struct Io<float> {  // NP floats per chunk
+  __device__ static void load(const float* p, float (&x)[NP]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
     x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
-    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
   }
-  __device__ static void store(float* p, const float (&x)[8]) {
+  __device__ static void store(float* p, const float (&x)[NP]) {
     *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
   }
 };
-__device__ __forceinline__ void load8f(const float* p, float (&x)[8]) { Io<float>::load(p, x); }
+__device__ __forceinline__ void loadf(const float* p, float (&x)[NP]) { Io<float>::load(p, x); }
 
 // Thread -> (row of [B*H*T], chunk j) for a tensor of D-wide rows.
 struct Slot {
@@ -57,25 +64,25 @@ struct Slot {
 };
 template <int D>
 __device__ __forceinline__ Slot slot_of(size_t rows) {
-  constexpr int CPR = D / 16;  // chunks of 8 pairs per row
+  constexpr int CPR = D / (2 * NP);  // chunks of NP pairs per row
   const size_t g = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   return {g / CPR, static_cast<int>(g % CPR), g / CPR < rows};
 }
 
 // The same arithmetic as rope8 / the fused forward's mixing, on fp32 lanes.
-__device__ __forceinline__ void rope_pairs(float (&a)[8], float (&b)[8], const float (&c)[8],
-                                           const float (&s)[8]) {
+__device__ __forceinline__ void rope_pairs(float (&a)[NP], float (&b)[NP], const float (&c)[NP],
+                                           const float (&s)[NP]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < NP; ++e) {
     const float a2 = fmaf(a[e], c[e], -b[e] * s[e]);
     b[e] = fmaf(a[e], s[e], b[e] * c[e]);
     a[e] = a2;
   }
 }
-__device__ __forceinline__ void rope_pairs_t(float (&a)[8], float (&b)[8], const float (&c)[8],
-                                             const float (&s)[8]) {
+__device__ __forceinline__ void rope_pairs_t(float (&a)[NP], float (&b)[NP], const float (&c)[NP],
+                                             const float (&s)[NP]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < NP; ++e) {
     const float a2 = fmaf(a[e], c[e], b[e] * s[e]);
     b[e] = fmaf(-a[e], s[e], b[e] * c[e]);
     a[e] = a2;
@@ -93,12 +100,12 @@ __global__ __launch_bounds__(256) void prepare_kernel(const TE* __restrict__ p1,
   const Slot sl = slot_of<D>(rows);
   if (!sl.ok) return;
   const int t = static_cast<int>(sl.row % T);
-  const size_t o = sl.row * D + sl.j * 8;
-  float a[8], b[8];
+  const size_t o = sl.row * D + sl.j * NP;
+  float a[NP], b[NP];
   if (q || k) {  // RoPE tables of the row (requested only with RoPE)
-    float c[8], s[8];
-    load8f(mh.cos + static_cast<size_t>(t) * (D / 2) + sl.j * 8, c);
-    load8f(mh.sin + static_cast<size_t>(t) * (D / 2) + sl.j * 8, s);
+    float c[NP], s[NP];
+    loadf(mh.cos + static_cast<size_t>(t) * (D / 2) + sl.j * NP, c);
+    loadf(mh.sin + static_cast<size_t>(t) * (D / 2) + sl.j * NP, s);
     if (q) {
       Io<TE>::load(p1 + o, a);
       Io<TE>::load(p1 + o + D / 2, b);
@@ -125,11 +132,11 @@ __global__ __launch_bounds__(256) void prepare_kernel(const TE* __restrict__ p1,
     givens_role(h, mh.H, mh.pairing, pair, partner, sgn);
     const float mixc = cosf(mh.theta[pair]), mixs = sgn * sinf(mh.theta[pair]);
     const size_t po = o + (static_cast<size_t>(partner) - h) * T * D;
-    float pa[8], pb[8];
+    float pa[NP], pb[NP];
     Io<TE>::load(vi + po, pa);
     Io<TE>::load(vi + po + D / 2, pb);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NP; ++e) {
       a[e] = fmaf(mixc, a[e], mixs * pa[e]);
       b[e] = fmaf(mixc, b[e], mixs * pb[e]);
     }
@@ -162,19 +169,19 @@ __global__ __launch_bounds__(256) void unrotate_kernel(const float* g, TE* dp, s
   const Slot sl = slot_of<D>(rows);
   if (!sl.ok) return;
   const int t = static_cast<int>(sl.row % T);
-  const size_t o = sl.row * D + sl.j * 8;
-  float a[8], b[8];
-  load8f(g + o, a);
-  load8f(g + o + D / 2, b);
+  const size_t o = sl.row * D + sl.j * NP;
+  float a[NP], b[NP];
+  loadf(g + o, a);
+  loadf(g + o + D / 2, b);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < NP; ++e) {
     a[e] *= scale;
     b[e] *= scale;
   }
   if (cs) {
-    float c[8], s[8];
-    load8f(cs + static_cast<size_t>(t) * (D / 2) + sl.j * 8, c);
-    load8f(sn + static_cast<size_t>(t) * (D / 2) + sl.j * 8, s);
+    float c[NP], s[NP];
+    loadf(cs + static_cast<size_t>(t) * (D / 2) + sl.j * NP, c);
+    loadf(sn + static_cast<size_t>(t) * (D / 2) + sl.j * NP, s);
     rope_pairs_t(a, b, c, s);
   }
   Io<TE>::store(dp + o, a);
@@ -189,8 +196,8 @@ template <typename TE, int D>
 __global__ __launch_bounds__(256) void unmix_kernel(const float* dv, TE* dI,
                                                     const TE* __restrict__ v, int B, int T,
                                                     Mhr mh, float* __restrict__ part) {
-  __shared__ float red[256];
-  constexpr int CPR = D / 16;
+  __shared__ float red[4];
+  constexpr int CPR = D / (2 * NP);
   const int p = blockIdx.y / B, b = blockIdx.y % B;
   const size_t g = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   const size_t t = g / CPR;
@@ -201,19 +208,19 @@ __global__ __launch_bounds__(256) void unmix_kernel(const float* dv, TE* dI,
     const int ha = mh.pairing == 0 ? 2 * p : 2 * p + 1;
     const int hb = mh.pairing == 0 ? 2 * p + 1 : (2 * p + 2) % mh.H;
     const float c = cosf(mh.theta[p]), s = sinf(mh.theta[p]);
-    const size_t oa = ((static_cast<size_t>(b) * mh.H + ha) * T + t) * D + j * 8;
-    const size_t ob = ((static_cast<size_t>(b) * mh.H + hb) * T + t) * D + j * 8;
+    const size_t oa = ((static_cast<size_t>(b) * mh.H + ha) * T + t) * D + j * NP;
+    const size_t ob = ((static_cast<size_t>(b) * mh.H + hb) * T + t) * D + j * NP;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const size_t xa = oa + half * (D / 2), xb = ob + half * (D / 2);
-      float ga[8], gb[8], va[8], vb[8];
-      load8f(dv + xa, ga);
-      load8f(dv + xb, gb);
+      float ga[NP], gb[NP], va[NP], vb[NP];
+      loadf(dv + xa, ga);
+      loadf(dv + xb, gb);
       Io<TE>::load(v + xa, va);
       Io<TE>::load(v + xb, vb);
-      float ia[8], ib[8];
+      float ia[NP], ib[NP];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < NP; ++e) {
         acc = fmaf(ga[e], vb[e], acc);
         acc = fmaf(-gb[e], va[e], acc);
         ia[e] = fmaf(c, ga[e], -s * gb[e]);
@@ -223,13 +230,14 @@ __global__ __launch_bounds__(256) void unmix_kernel(const float* dv, TE* dI,
       Io<TE>::store(dI + xb, ib);
     }
   }
-  red[threadIdx.x] = acc;
+  // the workgroup's partial: each wave by lane exchanges, then the 4 waves
+  // in a fixed order
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) part[static_cast<size_t>(blockIdx.y) * gridDim.x + blockIdx.x] = red[0];
+  if (threadIdx.x == 0)
+    part[static_cast<size_t>(blockIdx.y) * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 // dtheta[p] = sum of pair p's partials, in a fixed order (deterministic).
@@ -252,7 +260,7 @@ template <typename TE, int D>
 hipError_t run_prepare(int B, int H, int T, const void* p1, const void* p2, const void* vi,
                        void* q, void* k, void* v, const Mhr& mh, hipStream_t stream) {
   const size_t rows = static_cast<size_t>(B) * H * T;
-  const size_t threads = rows * (D / 16);
+  const size_t threads = rows * (D / (2 * NP));
   hipLaunchKernelGGL((prepare_kernel<TE, D>), dim3(static_cast<unsigned>((threads + 255) / 256)),
                      dim3(256), 0, stream, static_cast<const TE*>(p1), static_cast<const TE*>(p2),
                      static_cast<const TE*>(vi), static_cast<TE*>(q), static_cast<TE*>(k),
@@ -266,7 +274,7 @@ hipError_t run_post(int B, int H, int T, const float* dq, float dq_scale, const 
                     float* dtheta, float* part, const Mhr& mh, hipStream_t stream,
                     const float* dl_part, int dl_npart, float* dlambda) {
   const size_t rows = static_cast<size_t>(B) * H * T;
-  const unsigned nb = static_cast<unsigned>((rows * (D / 16) + 255) / 256);
+  const unsigned nb = static_cast<unsigned>((rows * (D / (2 * NP)) + 255) / 256);
   hipLaunchKernelGGL((unrotate_kernel<TE, D>), dim3(nb), dim3(256), 0, stream, dq,
                      static_cast<TE*>(dp1), rows, T, dq_scale, mh.cos, mh.sin, dl_part, dl_npart,
                      dl_part ? dlambda : nullptr);
@@ -285,7 +293,7 @@ hipError_t run_post(int B, int H, int T, const float* dq, float dq_scale, const 
                        nullptr);
     return hipGetLastError();
   }
-  const unsigned nx = static_cast<unsigned>((static_cast<size_t>(T) * (D / 16) + 255) / 256);
+  const unsigned nx = static_cast<unsigned>((static_cast<size_t>(T) * (D / (2 * NP)) + 255) / 256);
   hipLaunchKernelGGL((unmix_kernel<TE, D>), dim3(nx, static_cast<unsigned>(H / 2 * B)), dim3(256),
                      0, stream, dv, static_cast<TE*>(dI), static_cast<const TE*>(vmix), B, T, mh,
                      part);
@@ -302,7 +310,7 @@ hipError_t run_post(int B, int H, int T, const float* dq, float dq_scale, const 
 }  // namespace mhr
 
 size_t mhr_part_floats(int B, int H, int T, int D) {
-  const size_t nx = (static_cast<size_t>(T) * (D / 16) + 255) / 256;
+  const size_t nx = (static_cast<size_t>(T) * (D / (2 * mhr::NP)) + 255) / 256;
   return nx * static_cast<size_t>(B) * (H / 2 > 0 ? H / 2 : 1);
 }
 
