@@ -114,10 +114,13 @@ def bench_step(rel, torch, dev, steps, warmup, B=16, H=8, T=2048, D=64, seed=42,
         step(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step(True)
+    for _ in range(steps):  # the timed steps: nothing but the two calls
+        step(False)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    for _ in range(steps):  # the same steps again with events around each call
+        step(True)
+    torch.cuda.synchronize()
     # The same step captured once as a HIP graph and replayed: the launch path
     # of a training loop whose shapes do not change. Reported beside the
     # value, which is the eager step above.
