@@ -40,11 +40,18 @@ CFLAGS = [
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# Per-source scheduler choice: the forward kernels take the compiler's
+# iterative ILP scheduler (164 VGPRs for the plain D = 64 kernel,
+# still three waves per SIMD; 30M-layer forward 2 % faster in interleaved
+# timing, outputs bit-identical).
+SOURCE_FLAGS = {
+    "fwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS]
+    cmd = [HIPCC, *CFLAGS, *SOURCE_FLAGS.get(src, [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
