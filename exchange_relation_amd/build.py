@@ -40,12 +40,15 @@ CFLAGS = [
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-# Per-source scheduler choice: the forward kernels take the compiler's
-# iterative ILP scheduler (164 VGPRs for the plain D = 64 kernel,
-# still three waves per SIMD; 30M-layer forward 2 % faster in interleaved
-# timing, outputs bit-identical).
+# Per-source scheduler choices, each measured by interleaved timing with
+# bit-identical outputs and unchanged occupancy: the forward kernels and the
+# Linear Relation forward take the compiler's iterative ILP scheduler (30M
+# forward -2 %, Linear forward -3.7 %), the Linear Relation backward the
+# memory-clause one (-2 %).
 SOURCE_FLAGS = {
     "fwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "linear.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "linear_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
 }
 
 
