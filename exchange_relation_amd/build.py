@@ -41,14 +41,20 @@ CFLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 # Per-source scheduler choices, each measured by interleaved timing with
-# bit-identical outputs and unchanged occupancy: the forward kernels and the
-# Linear Relation forward take the compiler's iterative ILP scheduler (30M
-# forward -2 %, Linear forward -3.7 %), the Linear Relation backward the
-# memory-clause one (-2 %).
+# unchanged occupancy and no spills: the forward kernels, the Linear Relation
+# forward, the D = 80 backward (one wave per SIMD, so its own instruction
+# order is all the latency hiding it has) and the decode kernels take the
+# compiler's iterative ILP scheduler (30M forward -2 %, Linear forward
+# -3.7 %, D = 80 backward -7.3 %, ragged decode -2.4 %, uniform decode at
+# the cache workload unchanged); the Linear Relation backward the
+# memory-clause one (-2 %). Outputs are bit-identical except the atomically
+# accumulated dq, whose addition order varies from run to run anyway.
 SOURCE_FLAGS = {
     "fwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "linear.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "linear_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+    "bwd80.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "decode.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 
