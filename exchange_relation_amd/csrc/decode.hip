@@ -256,8 +256,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   float M = -INFINITY, Ls = 0.f, Z[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) Z[e] = 0.f;
-  // merge the chunk partials (App. A.3.2), kBatch partials per round with
-  // all their loads issued before any is used
+  // merge the chunk partials (App. A.3.2), kBatch partials per round (2 kBatch
+  // for a ragged batch) with all their loads issued before any is used
   auto merge = [&](int s0, int ns, int nvalid) {
     constexpr int KB = RAGGED ? 2 * kBatch : kBatch;
     float pm[KB], pl[KB], pz[KB][EL];
