@@ -14,7 +14,8 @@
 // Work decomposition
 //   * A workgroup of 4 waves owns a block of 128 query rows of one (b, h);
 //     each wave owns 32 rows. Workgroups are dispatched longest-first (the
-//     last query blocks of every head first) and the linear block id keeps all
+//     last query blocks of every head first; a grid of at most two per CU
+//     pairs each long block with a short one on a CU) and the linear block id keeps all
 //     query blocks of a head on the same XCD (ids differ by a multiple of the
 //     head count), so K / V of a head are shared through one L2.
 //   * Key / value tiles of 64 rows are staged row-major in LDS from
@@ -281,7 +282,15 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
 
   const int L = blockIdx.x;
   const int head = L % BH;
-  const int qb = nqb - 1 - (L / BH) % nqb;  // longest query blocks first
+  // Longest query blocks first. A grid of at most two workgroups per CU
+  // (<= 512) runs in one wave, with workgroups L and L + 256 on one CU; the
+  // older of the two issues first, so two long blocks on a CU leave the
+  // younger at half speed. There the second half of the grid takes the
+  // blocks shortest first, pairing every long block with a short one.
+  const int qj = (L / BH) % nqb;
+  const int qb = (!SPLIT && !OFF && BH * nqb <= 512 && nqb % 2 == 0 && qj >= nqb / 2)
+                     ? qj - nqb / 2
+                     : nqb - 1 - qj;
   const int piece = SPLIT ? L / (BH * nqb) : 0;
   const size_t base = static_cast<size_t>(head) * T * D;
   const int q0 = qb * BM + wave * 32;
