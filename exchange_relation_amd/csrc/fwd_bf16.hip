@@ -48,6 +48,9 @@
 //     and bf16.
 //   * The row sum l accumulates the bf16-rounded P (v_dot2 with ones), the
 //     same values the P V contraction consumes.
+//   * SK (a grid of at most one wave even at 64 rows per workgroup): 64-row
+//     blocks whose two 32-row groups each split every key tile between two
+//     waves, merged before the row completion.
 //   * SPLIT (a grid too small to fill the chip, with a caller workspace):
 //     long query blocks are cut over their historical key tiles into pieces
 //     of at least 16 tiles; the pieces' (acc, m, l) rows are merged by
@@ -263,7 +266,7 @@ struct SplitPlan {
   size_t bytes;  // workspace for the partial rows
 };
 
-template <bool MHR, bool OFF, int DR, bool SPLIT = false>
+template <bool MHR, bool OFF, int DR, bool SPLIT = false, bool SK = false>
 __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ y, float* __restrict__ lse,
@@ -279,6 +282,15 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   const int lane = tid & 63;
   const int r = lane & 31;   // query within the wave's 32 rows / key row in A operands
   const int hf = lane >> 5;  // which half of the K dimension this lane feeds
+  // SK (a grid that fits the GPU in one wave even at half the rows per
+  // workgroup): blocks of 64 query rows; wave w owns row group w & 1 and, of
+  // every key tile, the 32-key sub-block w >> 1, so a block's chain of tiles
+  // takes half as long. The two waves of a row group merge their scans
+  // before the row completion.
+  static_assert(!SK || (!MHR && !OFF && !SPLIT), "SK is a mode of the plain forward");
+  constexpr int BMW = SK ? 64 : BM;  // query rows per workgroup
+  const int rgrp = SK ? (wave & 1) : wave;
+  const int khalf = SK ? (wave >> 1) : 0;
 
   const int L = blockIdx.x;
   const int head = L % BH;
@@ -293,7 +305,7 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
                      : nqb - 1 - qj;
   const int piece = SPLIT ? L / (BH * nqb) : 0;
   const size_t base = static_cast<size_t>(head) * T * D;
-  const int q0 = qb * BM + wave * 32;
+  const int q0 = qb * BMW + rgrp * 32;
   const int qi = q0 + r;
   const bool wave_live = q0 < T;
   // keys / values: this head's T rows, or (OFF) the cache's rows
@@ -359,9 +371,9 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
 
   // tiles of keys before the block's first query position are history for
   // every row of the block
-  const int kend = min(Tk, pos0 + (qb + 1) * BM);
+  const int kend = min(Tk, pos0 + (qb + 1) * BMW);
   const int ntiles = (kend + BN - 1) / BN;
-  const int nfull = (pos0 + qb * BM) / BN;
+  const int nfull = (pos0 + qb * BMW) / BN;
   // this workgroup's tiles: historical [kt0, hend), then (last piece) the
   // block's own up to ntiles; tend bounds the look-ahead (nfull < ntiles, so
   // a piece that stops at hend < nfull may stage tile hend unused)
@@ -479,12 +491,13 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
 
   // ---- strictly historical tiles, software-pipelined: sub-block 1's score
   // MFMAs run under sub-block 0's exponentials, and the next tile's
-  // sub-block 0 score under sub-block 1's. No masking.
+  // sub-block 0 score under sub-block 1's (SK: the wave's one sub-block of
+  // the next tile under this tile's). No masking.
   f32x16 sa = {0};
-  if (kt0 < hend) sa = score<DR>(kp0, 0, qf, r, hf);
+  if (kt0 < hend) sa = score<DR>(kp0, khalf, qf, r, hf);
   int kt = kt0;
   KFrag<DR> kn;
-  if (kt0 < hend) kn = load_kfrag<DR>(kp0, 1, r, hf);
+  if (!SK && kt0 < hend) kn = load_kfrag<DR>(kp0, 1, r, hf);
   for (; kt < hend; ++kt) {
     const bool more_k = kt + 2 < tend;  // kt + 1 < tend always holds here
     const bool kfull = (kt + 3) * BN <= Tk, vfull = (kt + 2) * BN <= Tk;
@@ -495,14 +508,21 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
     if (vfull) fetch_full(vh, vnh, kt + 1, cv);
     else fetch(vh, vnh, kt + 1, cv);
     const uint16_t* vs = vbuf[(kt - kt0) & 1];
-    stabilise<false>(sa, qscale, r, hf, st);
-    f32x16 sb = score_from<DR>(kn, qf);
-    kn = load_kfrag<DR>(kp1, 0, r, hf);  // tile kt + 1 <= nfull is resident
-    accumulate<false, DR>(vs, 0, sa, hf, st);
-    stabilise<false>(sb, qscale, r, hf, st);
-    sa = score_from<DR>(kn, qf);
-    kn = load_kfrag<DR>(kp1, 1, r, hf);
-    accumulate<false, DR>(vs, 1, sb, hf, st);
+    if constexpr (SK) {
+      stabilise<false>(sa, qscale, r, hf, st);
+      const f32x16 sn = score<DR>(kp1, khalf, qf, r, hf);  // tile kt + 1 <= nfull is resident
+      accumulate<false, DR>(vs, khalf, sa, hf, st);
+      sa = sn;
+    } else {
+      stabilise<false>(sa, qscale, r, hf, st);
+      f32x16 sb = score_from<DR>(kn, qf);
+      kn = load_kfrag<DR>(kp1, 0, r, hf);  // tile kt + 1 <= nfull is resident
+      accumulate<false, DR>(vs, 0, sa, hf, st);
+      stabilise<false>(sb, qscale, r, hf, st);
+      sa = score_from<DR>(kn, qf);
+      kn = load_kfrag<DR>(kp1, 1, r, hf);
+      accumulate<false, DR>(vs, 1, sb, hf, st);
+    }
     if (more_k) {
       if (kfull) stash_full(kp2, ck, KS);
       else stash(kp2, ck, KS);
@@ -527,6 +547,7 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
       const int pw = pos0 + q0;  // position of the wave's first query
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
+        if (SK && sb != khalf) continue;
         const int k0 = kt * BN + sb * 32;
         if (k0 + 31 < pw) {  // history for every row of the wave
           f32x16 s = score<DR>(kp0, sb, qf, r, hf);
@@ -562,6 +583,40 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
         *reinterpret_cast<u32x4*>(sg.kc + to) = *reinterpret_cast<const u32x4*>(sg.kn + from);
         *reinterpret_cast<u32x4*>(sg.vc + to) = *reinterpret_cast<const u32x4*>(sg.vn + from);
       }
+    }
+  }
+  if constexpr (SK) {
+    // Each row group's second key half hands its (acc, m, l, u'_ii) to the
+    // first through LDS (the K ring is free after the loops' last barrier);
+    // the first merges them by App. A.3.2's rule and completes the rows.
+    constexpr int SW = ND * 16 + 4;  // floats per lane: acc, m, l, u'_ii, has_self
+    static_assert(128 * SW * sizeof(float) <= sizeof(kbuf), "merge area");
+    float* xs = reinterpret_cast<float*>(&kbuf[0][0]) + (rgrp * 64 + lane) * SW;
+    if (khalf == 1) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int vi = 0; vi < 16; ++vi) xs[db * 16 + vi] = st.acc[db][vi];
+      xs[ND * 16 + 0] = st.m;
+      xs[ND * 16 + 1] = st.lsum;
+      xs[ND * 16 + 2] = st.uself;
+      xs[ND * 16 + 3] = st.has_self ? 1.f : 0.f;
+    }
+    __syncthreads();
+    if (khalf == 1) return;
+    const float m1 = xs[ND * 16 + 0];
+    const float mx = fmaxf(st.m, m1);  // both bounds start at 0 and only grow
+    const float a0 = fast_exp2(st.m - mx), a1 = fast_exp2(m1 - mx);
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int vi = 0; vi < 16; ++vi)
+        st.acc[db][vi] = fmaf(st.acc[db][vi], a0, xs[db * 16 + vi] * a1);
+    st.lsum = fmaf(st.lsum, a0, xs[ND * 16 + 1] * a1);
+    st.m = mx;
+    if (xs[ND * 16 + 3] != 0.f) {  // the diagonal sat in the second half
+      st.uself = xs[ND * 16 + 2];
+      st.has_self = true;
     }
   }
   if (!wave_live) return;
@@ -756,7 +811,16 @@ hipError_t run_fwd(int BH, int H, int T, const uint16_t* q, const uint16_t* k,
                        sp, false);
     return hipGetLastError();
   }
-  if (rope_cos == nullptr || DR != 64)
+  // A grid whose 64-row blocks still fit the GPU in one wave (256 CUs x the
+  // workgroups resident per CU) takes the SK mode: half the rows per
+  // workgroup, twice the workgroups, each block's chain of tiles halved.
+  const long long nqb64 = (T + 63) / 64;
+  if (rope_cos == nullptr && nqb64 * BH <= 256LL * (DR <= 64 ? 3 : 2)) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<false, false, DR, false, true>),
+                       dim3(static_cast<unsigned>(nqb64 * BH)), dim3(256), 0, stream, q, k, v, y,
+                       lse, gate, T, BH, static_cast<int>(nqb64), scale * kLog2e, 1.0f / tau, lam,
+                       mh, sg);
+  } else if (rope_cos == nullptr || DR != 64)
     hipLaunchKernelGGL((fwd_bf16_kernel<false, false, DR>), grid, dim3(256), 0, stream, q, k, v,
                        y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
   else

@@ -134,6 +134,41 @@ def test_fwd_bf16_shapes(B, H, T):
     check("gate", f64(gate), G, "bf16")
 
 
+@pytest.mark.parametrize("T", [1, 65, 129])
+def test_fwd_bf16_many_heads_short_rows(T):
+    """Short rows on 1024 heads: a grid too large for the 64-row split-key
+    blocks, so the 128-row blocks run their ragged and single-row cases
+    (small grids take the split-key blocks); sampled heads vs the oracle."""
+    B, H, scale = 16, 64, 1 / 8
+    inp = make_inputs(B, H, T, 64, "bf16", seed=700 + T)
+    y, lse, gate = run_fwd(inp, "bf16", scale)
+    heads = [(b, h) for b in range(0, B, 5) for h in range(0, H, 13)]
+    refs = oracle_heads(inp, heads, scale, 2.0, inp["lam"])
+    check("y", np.stack([f64(y[b, h]) for b, h in heads]), np.stack([r["Y"] for r in refs]), "bf16")
+    check("lse", np.stack([f64(lse[b, h]) for b, h in heads]), np.stack([r["LSE"] for r in refs]),
+          "bf16")
+    check("gate", np.stack([f64(gate[b, h]) for b, h in heads]), np.stack([r["g"] for r in refs]),
+          "bf16")
+
+
+@pytest.mark.parametrize("D", [48, 64, 80])
+def test_fwd_bf16_split_key_blocks_match_full_blocks(D):
+    """The same heads through both block shapes: inside a 1024-head call
+    (128-row blocks) and as a 2-head call (64-row blocks whose key tiles two
+    waves split, merged before the completion). Each wave rounds P against
+    its own stabiliser, so the two agree to the split-over-keys bound."""
+    B, H, T = 16, 64, 300
+    inp = make_inputs(B, H, T, D, "bf16", seed=800 + D)
+    scale = 1 / math.sqrt(D)
+    y, lse, gate = run_fwd(inp, "bf16", scale)
+    sub = {n: inp[n][3:4, 10:12].contiguous() for n in ("q", "k", "v")}
+    y2, l2, g2 = run_fwd({**inp, **sub}, "bf16", scale)
+    vmax = float(sub["v"].float().abs().max())
+    close_to_unsplit("y", y2, y[3:4, 10:12], vmax)
+    close_to_unsplit("lse", l2, lse[3:4, 10:12], vmax)
+    close_to_unsplit("gate", g2, gate[3:4, 10:12], vmax)
+
+
 @pytest.mark.parametrize("lam", [0.0, 1.0, -0.5, 4.0])
 @pytest.mark.parametrize("scale", [1 / 8, 1 / 64, 0.5])
 def test_fwd_bf16_params(lam, scale):

@@ -139,7 +139,9 @@ def test_prefill_ragged_out_of_range_nan_and_no_write():
 
 
 def test_prefill_from_empty_history_is_the_forward_bit_exact():
-    B, H, T, D = 2, 2, 300, 64
+    # 192 heads: the forward runs 128-row blocks, as the prefill always does
+    # (a small grid would take its 64-row split-key blocks instead)
+    B, H, T, D = 4, 48, 300, 64
     inp = make_inputs(B, H, T, D, "bf16", seed=941)
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     yf, lf, gf = rel.relation_fwd(q, k, v, lam=inp["lam"], scale=1 / 8, want_gate=True)
