@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   // every key tile, the 32-key sub-block w >> 1, so a block's chain of tiles
   // takes half as long. The two waves of a row group merge their scans
   // before the row completion.
-  static_assert(!SK || (!MHR && !OFF && !SPLIT), "SK is a mode of the plain forward");
+  static_assert(!SK || (!OFF && !SPLIT), "SK is a mode of the aligned, unsplit forward");
   constexpr int BMW = SK ? 64 : BM;  // query rows per workgroup
   const int rgrp = SK ? (wave & 1) : wave;
   const int khalf = SK ? (wave >> 1) : 0;
@@ -814,13 +814,21 @@ hipError_t run_fwd(int BH, int H, int T, const uint16_t* q, const uint16_t* k,
   // A grid whose 64-row blocks still fit the GPU in one wave (256 CUs x the
   // workgroups resident per CU) takes the SK mode: half the rows per
   // workgroup, twice the workgroups, each block's chain of tiles halved.
+  // (Query RoPE is fused into the fragment load at D = 64 only; at 48 / 80
+  // the Multi-Head Relation pre-pass has rotated q already.)
   const long long nqb64 = (T + 63) / 64;
-  if (rope_cos == nullptr && nqb64 * BH <= 256LL * (DR <= 64 ? 3 : 2)) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<false, false, DR, false, true>),
-                       dim3(static_cast<unsigned>(nqb64 * BH)), dim3(256), 0, stream, q, k, v, y,
-                       lse, gate, T, BH, static_cast<int>(nqb64), scale * kLog2e, 1.0f / tau, lam,
-                       mh, sg);
-  } else if (rope_cos == nullptr || DR != 64)
+  const bool qrope = rope_cos != nullptr && DR == 64;
+  if (nqb64 * BH <= 256LL * (DR <= 64 ? 3 : 2)) {
+    const dim3 g64(static_cast<unsigned>(nqb64 * BH));
+    if (qrope)
+      hipLaunchKernelGGL((fwd_bf16_kernel<true, false, DR, false, true>), g64, dim3(256), 0,
+                         stream, q, k, v, y, lse, gate, T, BH, static_cast<int>(nqb64),
+                         scale * kLog2e, 1.0f / tau, lam, mh, sg);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<false, false, DR, false, true>), g64, dim3(256), 0,
+                         stream, q, k, v, y, lse, gate, T, BH, static_cast<int>(nqb64),
+                         scale * kLog2e, 1.0f / tau, lam, mh, sg);
+  } else if (!qrope)
     hipLaunchKernelGGL((fwd_bf16_kernel<false, false, DR>), grid, dim3(256), 0, stream, q, k, v,
                        y, lse, gate, T, BH, nqb, scale * kLog2e, 1.0f / tau, lam, mh, sg);
   else
