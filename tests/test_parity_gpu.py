@@ -118,8 +118,9 @@ def test_fwd_f32_shapes_params(D, T, lam, scale_kind):
     check("gate", f64(gate), G, "f32")
 
 
-BF16_SHAPES = [(1, 1, 1), (1, 2, 2), (2, 1, 31), (1, 2, 32), (1, 1, 33), (2, 2, 127),
-               (1, 2, 128), (1, 1, 129), (1, 3, 300), (1, 1, 513)]
+BF16_SHAPES = [(1, 1, 1), (1, 2, 2), (2, 1, 31), (1, 2, 32), (1, 1, 33), (1, 2, 63), (2, 1, 64),
+               (1, 1, 65), (2, 2, 127), (1, 2, 128), (1, 1, 129), (1, 2, 191), (1, 1, 192),
+               (2, 1, 193), (1, 3, 300), (1, 1, 513)]
 
 
 @pytest.mark.parametrize("B,H,T", BF16_SHAPES)
@@ -180,11 +181,13 @@ def test_fwd_bf16_params(lam, scale):
     check("lse", f64(lse), L, "bf16")
 
 
-def test_fwd_bf16_large_scores_rescale():
+@pytest.mark.parametrize("D", [48, 64, 80])
+def test_fwd_bf16_large_scores_rescale(D):
     """Scores far above the lazy-rescale slack force the running stabiliser
-    to move several times inside a row."""
-    inp = make_inputs(1, 2, 384, 64, "bf16", seed=9)
-    scale = 2.0  # U std ~ 16
+    to move several times inside a row (a small grid: the split-key blocks,
+    whose two key halves then merge scans with different stabilisers)."""
+    inp = make_inputs(1, 2, 384, D, "bf16", seed=9)
+    scale = 2.0 * 8 / math.sqrt(D)  # U std ~ 16
     y, lse, gate = run_fwd(inp, "bf16", scale)
     Y, L, G = oracle.relation_forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), scale, 2.0,
                                       inp["lam"])
