@@ -37,7 +37,7 @@ ARCH = "gfx950"
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
+    "-munsafe-fp-atomics", "-Wall", "-Wextra", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 # Per-source scheduler choices, each measured by interleaved timing with

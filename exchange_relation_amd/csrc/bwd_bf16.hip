@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float4* __restri
     for (int i = threadIdx.x; i < npart; i += 256) s += part[i];
     red[threadIdx.x] = s;
     __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
+    for (unsigned w = 128; w > 0; w >>= 1) {
       if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
       __syncthreads();
     }
@@ -530,7 +530,7 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
   float* dq_acc = reinterpret_cast<float*>(wsb + w.off_dq);
   const size_t n4 = static_cast<size_t>(B) * H * T * D / 4;
   const unsigned eg = static_cast<unsigned>(n4 < 4096 * 256 ? (n4 + 255) / 256 : 4096);
-  hipError_t e = launch_bwd_pre(1, B, H, T, D, q, k, v, y, dy, lse, nullptr, w, wsb, scale, tau,
+  hipError_t e = launch_bwd_pre(1, T, D, q, k, v, y, dy, lse, nullptr, w, wsb, scale, tau,
                                 stream);
   if (e != hipSuccess) return e;
   const float* Dr = reinterpret_cast<const float*>(wsb + w.off_dr);

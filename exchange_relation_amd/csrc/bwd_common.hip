@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void bwd_dlambda_kernel(const float* __restric
   for (int i = threadIdx.x; i < n; i += 256) s += part[i];
   red[threadIdx.x] = s;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (unsigned w = 128; w > 0; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
@@ -131,7 +131,7 @@ size_t bwd_workspace_bytes(int dtype, int B, int H, int T, int D) {
 }
 
 template <typename TE, int D>
-hipError_t launch_bwd_pre_t(int B, int H, int T, const TE* q, const TE* k, const TE* v,
+hipError_t launch_bwd_pre_t(int T, const TE* q, const TE* k, const TE* v,
                             const TE* y, const TE* dy, const float* lse, float* dlambda,
                             const BwdWorkspace& w, char* ws, float scale, float tau,
                             bool zero_dq, bool with_dl, hipStream_t stream) {
@@ -146,7 +146,7 @@ hipError_t launch_bwd_pre_t(int B, int H, int T, const TE* q, const TE* k, const
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_pre(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+hipError_t launch_bwd_pre(int dtype, int T, int D, const void* q, const void* k,
                           const void* v, const void* y, const void* dy, const float* lse,
                           float* dlambda, const BwdWorkspace& w, char* ws, float scale, float tau,
                           hipStream_t stream) {
@@ -154,18 +154,18 @@ hipError_t launch_bwd_pre(int dtype, int B, int H, int T, int D, const void* q, 
   const auto b16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
   const auto f32 = [](const void* p) { return static_cast<const float*>(p); };
   if (dtype == 1 && D == 80)
-    return launch_bwd_pre_t<uint16_t, 80>(B, H, T, b16(q), b16(k), b16(v), b16(y), b16(dy), lse,
+    return launch_bwd_pre_t<uint16_t, 80>(T, b16(q), b16(k), b16(v), b16(y), b16(dy), lse,
                                           dlambda, w, ws, scale, tau, true, true, stream);
   if (dtype == 1 && D == 48)
-    return launch_bwd_pre_t<uint16_t, 48>(B, H, T, b16(q), b16(k), b16(v), b16(y), b16(dy), lse,
+    return launch_bwd_pre_t<uint16_t, 48>(T, b16(q), b16(k), b16(v), b16(y), b16(dy), lse,
                                           dlambda, w, ws, scale, tau, true, false, stream);
   if (dtype == 1)
-    return launch_bwd_pre_t<uint16_t, 64>(B, H, T, b16(q), b16(k), b16(v), b16(y), b16(dy), lse,
+    return launch_bwd_pre_t<uint16_t, 64>(T, b16(q), b16(k), b16(v), b16(y), b16(dy), lse,
                                           dlambda, w, ws, scale, tau, true, false, stream);
   if (D == 64)
-    return launch_bwd_pre_t<float, 64>(B, H, T, f32(q), f32(k), f32(v), f32(y), f32(dy), lse,
+    return launch_bwd_pre_t<float, 64>(T, f32(q), f32(k), f32(v), f32(y), f32(dy), lse,
                                        dlambda, w, ws, scale, tau, false, true, stream);
-  return launch_bwd_pre_t<float, 32>(B, H, T, f32(q), f32(k), f32(v), f32(y), f32(dy), lse,
+  return launch_bwd_pre_t<float, 32>(T, f32(q), f32(k), f32(v), f32(y), f32(dy), lse,
                                      dlambda, w, ws, scale, tau, false, true, stream);
 }
 

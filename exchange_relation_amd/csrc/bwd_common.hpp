@@ -19,7 +19,7 @@ BwdWorkspace bwd_workspace_layout(int dtype, int B, int H, int T, int D);
 // Dr rows and the dL/dlambda partials; also reduces the partials into
 // *dlambda when dlambda != NULL (else the caller reduces them). dtype 0 =
 // fp32, 1 = bf16.
-hipError_t launch_bwd_pre(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+hipError_t launch_bwd_pre(int dtype, int T, int D, const void* q, const void* k,
                           const void* v, const void* y, const void* dy, const float* lse,
                           float* dlambda, const BwdWorkspace& w, char* ws, float scale, float tau,
                           hipStream_t stream);

@@ -152,7 +152,7 @@ hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const floa
                           float tau, Lam lam, hipStream_t stream) {
   const BwdWorkspace w = bwd_workspace_layout(0, B, H, T, D);
   char* wsb = static_cast<char*>(ws);
-  hipError_t e = launch_bwd_pre(0, B, H, T, D, q, k, v, y, dy, lse, dlambda, w, wsb, scale, tau,
+  hipError_t e = launch_bwd_pre(0, T, D, q, k, v, y, dy, lse, dlambda, w, wsb, scale, tau,
                                 stream);
   if (e != hipSuccess) return e;
   const float* Dr = reinterpret_cast<const float*>(wsb + w.off_dr);

@@ -357,7 +357,6 @@ __global__ __launch_bounds__(256) void linear_step_kernel(
     const float* __restrict__ rs, float* __restrict__ state, uint16_t* __restrict__ y,
     float sl2) {
   __shared__ float h1[D], h2[D], al[D], part[4][D];
-  __shared__ float sS;
   const int tid = threadIdx.x, v = tid & 63, kg = tid >> 6;
   const size_t head = blockIdx.x;
   const size_t ro = head * D;

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void unrotate_kernel(const float* g, TE* dp, s
     for (int i = threadIdx.x; i < dl_npart; i += 256) s += dl_part[i];
     red[threadIdx.x] = s;
     __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
+    for (unsigned w = 128; w > 0; w >>= 1) {
       if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
       __syncthreads();
     }
