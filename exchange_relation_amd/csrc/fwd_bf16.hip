@@ -656,9 +656,13 @@ __global__ __launch_bounds__(256, DR <= 64 ? 3 : 2) void fwd_bf16_kernel(
   const float gl = (ltot > 0.f) ? g * fast_rcp(ltot) : 0.f;
   const float gs = 1.0f - g;
   const size_t row = base + static_cast<size_t>(qi) * D;
-  // I_i, the row's own value (OFF: the new row, not yet in the cache)
+  // I_i, the row's own value. Aligned rows read it from the block's own V
+  // tile, still resident in LDS after the loops (tile t sits in
+  // vbuf[(t - kt0) & 1] and nothing restages it); OFF reads the new row from
+  // HBM, since rows at an offset may span a third tile that the ring no
+  // longer holds.
   const uint16_t* vown = OFF ? sg.vn + base + static_cast<size_t>(qi) * D
-                             : v + kvbase + static_cast<size_t>(pos0 + qi) * D;
+                             : &vbuf[(qi / BN - kt0) & 1][(qi % BN) * VS];
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
 #pragma unroll
