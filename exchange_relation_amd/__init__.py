@@ -52,6 +52,7 @@ EXPORTED_SYMBOLS = (
     "relation_fwd",
     "relation_bwd_workspace_bytes",
     "relation_bwd",
+    "relation_bwd_events",
     "relation_decode_workspace_bytes",
     "relation_cache_decode",
     "relation_cache_decode_noalloc",
@@ -106,6 +107,8 @@ def load_library():
     lib.relation_bwd.restype = c_int
     lib.relation_bwd.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                  vp, vp, vp, vp, vp, c_size, c_float, c_float, c_float, vp, vp]
+    lib.relation_bwd_events.restype = c_int
+    lib.relation_bwd_events.argtypes = lib.relation_bwd.argtypes + [vp, vp]
     lib.relation_decode_workspace_bytes.restype = c_size
     lib.relation_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.relation_cache_decode.restype = c_int
@@ -276,9 +279,12 @@ def relation_bwd_workspace_bytes(dtype, B, H, T, D):
 
 
 def relation_bwd(q, k, v, y, dy, lse, lam=0.0, scale=None, tau_s=2.0, dq=None, dk=None, dv=None,
-                 dlambda=None, workspace=None, want_dlambda=True, stream=None):
+                 dlambda=None, workspace=None, want_dlambda=True, stream=None, main_events=None):
     """Backward of relation_fwd. Returns (dq, dk, dv, dlambda) where dlambda is
-    a float32 device tensor of shape [1] (or None)."""
+    a float32 device tensor of shape [1] (or None). main_events: an optional
+    pair of torch.cuda.Event(enable_timing=True) that the library records on
+    its stream right before and after the main backward kernel(s)
+    (relation_bwd_events), for timing that part alone."""
     lib = load_library()
     B, H, T, D = q.shape
     dev, dt = q.device, q.dtype
@@ -297,10 +303,19 @@ def relation_bwd(q, k, v, y, dy, lse, lam=0.0, scale=None, tau_s=2.0, dq=None, d
     if workspace is None:
         workspace = torch.empty((max(need, 1),), device=dev, dtype=torch.uint8)
     lv, lp = _lam(lam, dev)
-    st = lib.relation_bwd(code, B, H, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy),
-                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlambda),
-                          _ptr(workspace), workspace.numel() * workspace.element_size(),
-                          _scale(D, scale), float(tau_s), lv, lp, _stream(dev, stream))
+    args = (code, B, H, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(lse), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dlambda), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _scale(D, scale), float(tau_s), lv, lp,
+            _stream(dev, stream))
+    if main_events is None:
+        st = lib.relation_bwd(*args)
+    else:
+        handles = []
+        for e in main_events:
+            if e.cuda_event == 0:  # torch creates the HIP event at its first record
+                e.record(torch.cuda.current_stream(dev))
+            handles.append(ctypes.c_void_p(e.cuda_event))
+        st = lib.relation_bwd_events(*args, *handles)
     if st != 0:
         raise RelationError(st, "relation_bwd")
     return dq, dk, dv, dlambda

@@ -523,7 +523,7 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                            const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                            float* dlambda, void* ws, float scale, float tau, Lam lam,
                            hipStream_t stream, float* dk32, float* dv32, const float* rope_cos,
-                           const float* rope_sin) {
+                           const float* rope_sin, hipEvent_t ev0, hipEvent_t ev1) {
   using namespace bwdbf16;
   const BwdWorkspace w = bwd_workspace_layout(1, B, H, T, D);
   char* wsb = static_cast<char*>(ws);
@@ -537,6 +537,7 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
   float* part = reinterpret_cast<float*>(wsb + w.off_part);  // dL/dlambda terms
   const int BH = B * H;
   const int nkb = (T + BK - 1) / BK;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   if (D == 80) {  // the wider layout of bwd80.hip
     e = launch_bwd80_kernel(B, H, T, q, k, v, dy, lse, Dr, dq_acc, dk, dv, scale, tau, lam, stream,
                             dk32, dv32);
@@ -554,6 +555,7 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   // with fp32 results requested (dv32), dq stays in the accumulator and the
   // caller's transpose pass scales it and reduces the dL/dlambda partials
   if (dv32) return hipSuccess;

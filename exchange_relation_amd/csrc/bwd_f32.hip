@@ -149,7 +149,8 @@ __global__ __launch_bounds__(64) void bwd_f32_dkdv_kernel(
 hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const float* k,
                           const float* v, const float* y, const float* dy, const float* lse,
                           float* dq, float* dk, float* dv, float* dlambda, void* ws, float scale,
-                          float tau, Lam lam, hipStream_t stream) {
+                          float tau, Lam lam, hipStream_t stream, hipEvent_t ev0,
+                          hipEvent_t ev1) {
   const BwdWorkspace w = bwd_workspace_layout(0, B, H, T, D);
   char* wsb = static_cast<char*>(ws);
   hipError_t e = launch_bwd_pre(0, T, D, q, k, v, y, dy, lse, dlambda, w, wsb, scale, tau,
@@ -158,6 +159,7 @@ hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const floa
   const float* Dr = reinterpret_cast<const float*>(wsb + w.off_dr);
   const int nblk = (T + 63) / 64;
   const dim3 grid(static_cast<unsigned>(nblk) * B * H);
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   if (D == 32) {
     hipLaunchKernelGGL(bwd_f32_dq_kernel<32>, grid, dim3(64), 0, stream, q, k, v, dy, lse, Dr, dq,
                        T, nblk, scale, tau, lam);
@@ -169,7 +171,8 @@ hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const floa
     hipLaunchKernelGGL(bwd_f32_dkdv_kernel<64>, grid, dim3(64), 0, stream, q, k, v, dy, lse, Dr,
                        dk, dv, T, nblk, scale, tau, lam);
   }
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return ev1 ? hipEventRecord(ev1, stream) : hipSuccess;
 }
 
 }  // namespace rel

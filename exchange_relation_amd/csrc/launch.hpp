@@ -37,12 +37,16 @@ hipError_t launch_fwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                            const float* rope_cos = nullptr, const float* rope_sin = nullptr,
                            float* ws = nullptr, size_t ws_bytes = 0);
 
-// Backward. Workspace layout and size are owned by the launcher.
+// Backward. Workspace layout and size are owned by the launcher. ev0 / ev1
+// (either may be null) are recorded on the stream right before and right
+// after the main backward kernel(s), without the preprocess and the dq
+// finalize, so that a caller can time that part alone.
 size_t bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
 hipError_t launch_bwd_f32(int B, int H, int T, int D, const float* q, const float* k,
                           const float* v, const float* y, const float* dy, const float* lse,
                           float* dq, float* dk, float* dv, float* dlambda, void* ws, float scale,
-                          float tau, Lam lam, hipStream_t stream);
+                          float tau, Lam lam, hipStream_t stream, hipEvent_t ev0 = nullptr,
+                          hipEvent_t ev1 = nullptr);
 // bf16 D in {48, 64, 80} (48 runs in the 64-wide tiles with zero columns, 80
 // in the wider layout of bwd80.hip).
 // dk32 / dv32 non-NULL: dk (scaled) and dv go there in fp32, and dq is left
@@ -53,7 +57,8 @@ hipError_t launch_bwd_bf16(int B, int H, int T, int D, const uint16_t* q, const 
                            float* dlambda, void* ws, float scale, float tau, Lam lam,
                            hipStream_t stream, float* dk32 = nullptr,
                            float* dv32 = nullptr, const float* rope_cos = nullptr,
-                           const float* rope_sin = nullptr);
+                           const float* rope_sin = nullptr, hipEvent_t ev0 = nullptr,
+                           hipEvent_t ev1 = nullptr);
 
 // The D = 80 backward kernel (bwd80.hip), after the shared preprocess; dq
 // accumulates into dq_acc (fp32, unscaled) as for the other widths.

@@ -164,11 +164,12 @@ size_t relation_bwd_workspace_bytes(relation_dtype dtype, int B, int H, int T, i
   return rel::bwd_workspace_bytes(dtype == REL_BF16 ? 1 : 0, B, H, T, D);
 }
 
-relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D, const void* q,
-                             const void* k, const void* v, const void* y, const void* dy,
-                             const float* lse, void* dq, void* dk, void* dv, float* dlambda,
-                             void* workspace, size_t workspace_bytes, float scale, float tau_s,
-                             float lambda, const float* lambda_dev, void* stream) {
+static relation_status bwd_impl(relation_dtype dtype, int B, int H, int T, int D, const void* q,
+                                const void* k, const void* v, const void* y, const void* dy,
+                                const float* lse, void* dq, void* dk, void* dv, float* dlambda,
+                                void* workspace, size_t workspace_bytes, float scale, float tau_s,
+                                float lambda, const float* lambda_dev, void* stream,
+                                hipEvent_t ev0, hipEvent_t ev1) {
   if (!q || !k || !v || !y || !dy || !lse || !dq || !dk || !dv) return REL_ERR_NULL;
   relation_status st = check_dtype_dim_bwd(dtype, D);
   if (st != REL_OK) return st;
@@ -188,13 +189,34 @@ relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D, c
         B, H, T, D, static_cast<const float*>(q), static_cast<const float*>(k),
         static_cast<const float*>(v), static_cast<const float*>(y), static_cast<const float*>(dy),
         lse, static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), dlambda,
-        workspace, scale, tau_s, lam, s));
+        workspace, scale, tau_s, lam, s, ev0, ev1));
   return from_hip(rel::launch_bwd_bf16(
       B, H, T, D, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(y),
       static_cast<const uint16_t*>(dy), lse, static_cast<uint16_t*>(dq),
       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dlambda, workspace, scale, tau_s,
-      lam, s));
+      lam, s, nullptr, nullptr, nullptr, nullptr, ev0, ev1));
+}
+
+relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D, const void* q,
+                             const void* k, const void* v, const void* y, const void* dy,
+                             const float* lse, void* dq, void* dk, void* dv, float* dlambda,
+                             void* workspace, size_t workspace_bytes, float scale, float tau_s,
+                             float lambda, const float* lambda_dev, void* stream) {
+  return bwd_impl(dtype, B, H, T, D, q, k, v, y, dy, lse, dq, dk, dv, dlambda, workspace,
+                  workspace_bytes, scale, tau_s, lambda, lambda_dev, stream, nullptr, nullptr);
+}
+
+relation_status relation_bwd_events(relation_dtype dtype, int B, int H, int T, int D,
+                                    const void* q, const void* k, const void* v, const void* y,
+                                    const void* dy, const float* lse, void* dq, void* dk,
+                                    void* dv, float* dlambda, void* workspace,
+                                    size_t workspace_bytes, float scale, float tau_s,
+                                    float lambda, const float* lambda_dev, void* stream,
+                                    void* ev_main_begin, void* ev_main_end) {
+  return bwd_impl(dtype, B, H, T, D, q, k, v, y, dy, lse, dq, dk, dv, dlambda, workspace,
+                  workspace_bytes, scale, tau_s, lambda, lambda_dev, stream,
+                  static_cast<hipEvent_t>(ev_main_begin), static_cast<hipEvent_t>(ev_main_end));
 }
 
 size_t relation_decode_workspace_bytes(relation_dtype dtype, int B, int H, int D, int capacity) {

@@ -135,6 +135,28 @@ relation_status relation_bwd(relation_dtype dtype, int B, int H, int T, int D,
                              const float* lambda_dev, void* stream);
 
 /*
+ * relation_bwd_events — relation_bwd (same operation, App. A.1.7; same
+ * arguments, results and errors) that also records two caller-created HIP
+ * events on `stream`. ev_main_begin is recorded right before the main
+ * backward kernel(s) and ev_main_end right after them. Neither covers the
+ * preprocess (row terms, accumulator clear) or the dq finalize. With
+ * hipEventElapsedTime, a caller can time the main kernel alone, for example
+ * to compare with a profiler's per-kernel durations.
+ *   ev_main_begin, ev_main_end : hipEvent_t as void*, owned by the caller;
+ *                                either may be NULL (then not recorded).
+ * A failed record returns REL_ERR_HIP with the same meaning as a failed
+ * launch.
+ */
+relation_status relation_bwd_events(relation_dtype dtype, int B, int H, int T, int D,
+                                    const void* q, const void* k, const void* v,
+                                    const void* y, const void* dy, const float* lse,
+                                    void* dq, void* dk, void* dv, float* dlambda,
+                                    void* workspace, size_t workspace_bytes,
+                                    float scale, float tau_s, float lambda,
+                                    const float* lambda_dev, void* stream,
+                                    void* ev_main_begin, void* ev_main_end);
+
+/*
  * relation_cache_decode — one autoregressive step over the KV-style Relation
  * Cache (named in the paper's first version as its decoding form). The new
  * token of every sequence is at 1-based position i = n_hist + 1; its output

@@ -630,6 +630,31 @@ def test_bwd_dk_dv_deterministic():
     assert a[3] == b[3]  # dlambda is reduced in a fixed order
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 80), ("f32", 64)])
+def test_bwd_events_entry_point_matches_bwd(dtype, D):
+    """relation_bwd_events gives relation_bwd's results (dk, dv and dlambda bit
+    for bit; dq, accumulated by fp32 atomics in no fixed order, within the
+    tolerance) and its events bracket a non-empty part of the call."""
+    inp = make_inputs(2, 4, 700, D, dtype, seed=21, with_dy=True)
+    scale = 1 / math.sqrt(D)
+    q, k, v, dy = (inp[n].to(DEV) for n in ("q", "k", "v", "dy"))
+    y, lse, _ = rel.relation_fwd(q, k, v, lam=inp["lam"], scale=scale)
+    a = rel.relation_bwd(q, k, v, y, dy, lse, lam=inp["lam"], scale=scale)
+    stream = torch.cuda.current_stream(DEV)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    b = rel.relation_bwd(q, k, v, y, dy, lse, lam=inp["lam"], scale=scale, main_events=(m0, m1))
+    c1.record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert float(a[3].item()) == float(b[3].item())
+    check("dq", f64(b[0]), f64(a[0]), dtype)
+    t_main, t_call = m0.elapsed_time(m1), c0.elapsed_time(c1)
+    print(f"  main kernel(s) {t_main * 1e3:.1f} us of the call's {t_call * 1e3:.1f} us")
+    assert 0.0 < t_main <= t_call
+
+
 def test_decode_matches_forward_last_row():
     """The decode step's output equals the GPU forward's row at the same
     position (within bf16 tolerance)."""
