@@ -1,5 +1,6 @@
 """GPU parity over seeded random shapes: the bf16 forward and backward (and
-the fp32 forward) on every head of a launch against the fp64 oracle.
+the fp32 forward) on every head of a launch against the fp64 oracle, and the
+chunked cache prefill on ragged histories (its caches bit for bit).
 
 The shapes are drawn so that one sweep reaches every forward launch form:
 * the 64-row split-key blocks of grids that fit the GPU at once;
@@ -10,9 +11,9 @@ three widths, App. B, Table 6); the fp32 path runs 32 and 64.
 
 Tolerances are the same as in the other parity tests. bf16: element-wise
 2e-2 max(1, |ref| / 4) (2e-2 on the fp32 LSE) and mean-abs 3e-3 on y, lse,
-gate, dq, dk and dv. dL/dlambda (one scalar over all
-heads; Sec. 3.1, App. A.1.7) must be within 2e-2 relative, plus the bound
-that the bf16 rounding of the stored Y allows. fp32: max-abs 1e-5.
+gate, dq, dk and dv. dL/dlambda (one scalar over all heads; Sec. 3.1,
+App. A.1.7) must be within 2e-2 relative, plus the bound that the bf16
+rounding of the stored Y allows. fp32: max-abs 1e-5.
 """
 import math
 import os
@@ -139,3 +140,42 @@ def test_sweep_f32_fwd_every_head(i):
     check("y", f64(y), np.stack([r["Y"] for r in ref]).reshape(B, H, T, D), "f32")
     check("lse", f64(lse), np.stack([r["LSE"] for r in ref]).reshape(B, H, T), "f32")
     check("gate", f64(gate), np.stack([r["g"] for r in ref]).reshape(B, H, T), "f32")
+
+
+def prefill_case(i):
+    """(B, H, D, m, ns, cap) of prefill case i: m new tokens per sequence
+    after ragged histories ns (some long enough to split over keys)."""
+    rng = np.random.default_rng(9400 + i)
+    D = int(rng.choice([48, 64, 80]))
+    B, H, m = int(rng.integers(1, 5)), int(rng.integers(1, 7)), int(rng.integers(1, 301))
+    ns = [int(x) for x in rng.integers(0, 1800, size=B)]
+    if B > 1:
+        ns[0] = 0  # one sequence with no history
+    cap = max(ns) + m + int(rng.integers(0, 40))
+    return B, H, D, m, ns, cap
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_sweep_prefill_ragged_every_head(i):
+    """Chunked prefill (relation_cache_prefill) on ragged histories: every row
+    of every head against the oracle's rows of the whole sequence, and the
+    caches bit for bit."""
+    from workloads import make_decode_inputs
+    B, H, D, m, ns, cap = prefill_case(i)
+    print(f"prefill case {i}: B={B} H={H} D={D} m={m} histories={ns} capacity={cap}", flush=True)
+    d = make_decode_inputs(B, H, D, cap - m, m, cap, "bf16", seed=9500 + i)
+    new = {n: d[n].permute(1, 2, 0, 3).contiguous() for n in ("q", "k_new", "v_new")}
+    scale = 1 / math.sqrt(D)
+    kc, vc = d["k_cache"].to(DEV), d["v_cache"].to(DEV)
+    y, lse, g = rel.relation_cache_prefill(
+        new["q"].to(DEV), new["k_new"].to(DEV), new["v_new"].to(DEV), kc, vc,
+        torch.tensor(ns, dtype=torch.int32, device=DEV), max_n_hist=max(ns), lam=d["lam"],
+        scale=scale, want_stats=True)
+    torch.cuda.synchronize()
+    Y, L, G, KC, VC = oracle.relation_prefill_rows(f64(new["q"]), f64(new["k_new"]),
+                                                   f64(new["v_new"]), f64(d["k_cache"]),
+                                                   f64(d["v_cache"]), ns, scale, 2.0, d["lam"])
+    check("y", f64(y), Y, "bf16")
+    check("lse", f64(lse), L, "bf16")
+    check("gate", f64(g), G, "bf16")
+    assert np.array_equal(f64(kc), KC) and np.array_equal(f64(vc), VC)
