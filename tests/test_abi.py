@@ -122,6 +122,20 @@ def test_bwd_validation_and_workspace(lib):
     assert bwd(tau=0.0) == REL_ERR_PARAM
     assert bwd(T=0) == REL_ERR_SHAPE
 
+    # relation_bwd_events validates exactly as relation_bwd (the events are
+    # only recorded around a launch, which none of these calls reaches)
+    def bwd_ev(ws=P, wsb=None, dq=P, lse=P, tau=2.0, T=100, ev=P):
+        wsb = need if wsb is None else wsb
+        return lib.relation_bwd_events(BF16, 2, 3, T, 64, P, P, P, P, P, lse, dq, P, P, NUL, ws,
+                                       wsb, 0.125, tau, 0.3, NUL, None, ev, ev)
+
+    assert bwd_ev(dq=NUL) == REL_ERR_NULL
+    assert bwd_ev(ws=NUL) == REL_ERR_WORKSPACE
+    assert bwd_ev(wsb=need - 1) == REL_ERR_WORKSPACE
+    assert bwd_ev(ws=ctypes.c_void_p(0x7F0000000010)) == REL_ERR_ALIGN
+    assert bwd_ev(tau=0.0) == REL_ERR_PARAM
+    assert bwd_ev(T=0, ev=NUL) == REL_ERR_SHAPE
+
 
 def test_decode_validation(lib):
     need = lib.relation_decode_workspace_bytes(BF16, 2, 3, 64, 4352)
