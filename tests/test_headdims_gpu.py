@@ -1,8 +1,8 @@
 """GPU parity at the paper's other head widths (d_h = 48 for its 10M model and
 80 for its 100M model; App. B, Table 6): bf16 forward, decode (uniform and
 ragged), prefill and the Multi-Head Relation forward, against the fp64
-oracle. Tolerances as everywhere for bf16: element-wise 2e-2 max(1, |ref| / 4)
-(2e-2 on the fp32 LSE) and mean-abs <= 3e-3; caches bit for bit. The bf16 backward (plain and Multi-Head
+oracle. Tolerances as everywhere for bf16: max-abs <= 2e-2 and mean-abs
+<= 3e-3; caches bit for bit. The bf16 backward (plain and Multi-Head
 Relation) runs at both widths, checked the same way, with dL/dlambda within
 2e-2 relative plus the bound that the bf16 rounding of the stored Y allows.
 """
@@ -29,13 +29,7 @@ def check(name, got, ref):
     err = np.abs(np.asarray(got, dtype=np.float64) - ref)
     mx, mean = float(err.max()), float(err.mean())
     print(f"  {name}: max-abs {mx:.3e} mean-abs {mean:.3e}")
-    # element-wise 2e-2 max(1, |ref| / 4) for the bf16 outputs: one of magnitude
-    # >= 4 rounds by up to 2^-8 |ref| on its own. LSE is stored in fp32, so its
-    # bound stays 2e-2.
-    scale = 1.0 if name.startswith("lse") else np.maximum(1.0, np.abs(ref) / 4.0)
-    worst = float((err / (BF16_MAX * scale)).max())
-    print(f"    error / bound {worst:.3f}")
-    assert worst <= 1.0, f"{name}: error {worst:.3f} x the bound 2e-2 max(1, |ref|/4)"
+    assert mx <= BF16_MAX, f"{name}: max-abs {mx:.3e} > {BF16_MAX}"
     assert mean <= BF16_MEAN, f"{name}: mean-abs {mean:.3e} > {BF16_MEAN}"
 
 

@@ -9,9 +9,10 @@ The shapes are drawn so that one sweep reaches every forward launch form:
 Row counts are ragged, and the bf16 head widths are 48, 64 and 80 (the paper's
 three widths, App. B, Table 6); the fp32 path runs 32 and 64.
 
-Tolerances are the same as in the other parity tests. bf16: element-wise
-2e-2 max(1, |ref| / 4) (2e-2 on the fp32 LSE) and mean-abs 3e-3 on y, lse,
-gate, dq, dk and dv. dL/dlambda (one scalar over all heads; Sec. 3.1,
+Tolerances are the same as in the other parity tests. bf16: max-abs 2e-2 and
+mean-abs 3e-3 on y, lse, gate, dq, dk and dv. An output of magnitude >= 4
+loses up to 2^-8 |ref| (1.56e-2) to its bf16 rounding alone, so the
+largest errors of the sweep sit there (dv 1.95e-2 at |ref| = 4.43). dL/dlambda (one scalar over all heads; Sec. 3.1,
 App. A.1.7) must be within 2e-2 relative, plus the bound that the bf16
 rounding of the stored Y allows. fp32: max-abs 1e-5.
 """
@@ -65,13 +66,7 @@ def check(name, got, ref, dtype):
     if dtype == "f32":
         assert mx <= F32_MAX, f"{name}: max-abs {mx:.3e} > {F32_MAX}"
         return
-    # element-wise 2e-2 max(1, |ref| / 4) for the bf16 outputs: one of magnitude
-    # >= 4 rounds by up to 2^-8 |ref| on its own. LSE is stored in fp32, so its
-    # bound stays 2e-2.
-    scale = 1.0 if name.startswith("lse") else np.maximum(1.0, np.abs(ref) / 4.0)
-    worst = float((err / (BF16_MAX * scale)).max())
-    print(f"    error / bound {worst:.3f}")
-    assert worst <= 1.0, f"{name}: error {worst:.3f} x the bound 2e-2 max(1, |ref|/4)"
+    assert mx <= BF16_MAX, f"{name}: max-abs {mx:.3e} > {BF16_MAX}"
     assert mean <= BF16_MEAN, f"{name}: mean-abs {mean:.3e} > {BF16_MEAN}"
 
 
