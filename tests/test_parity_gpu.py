@@ -170,6 +170,26 @@ def test_fwd_bf16_split_key_blocks_match_full_blocks(D):
     close_to_unsplit("gate", g2, gate[3:4, 10:12], vmax)
 
 
+@pytest.mark.parametrize("H,D", [(48, 64), (49, 64), (32, 80), (33, 80), (48, 48), (49, 48)])
+def test_fwd_bf16_block_form_boundary(H, D):
+    """Grids on either side of the limit for 64-row split-key blocks (768 of
+    them at d_h <= 64, 512 at 80, at one workgroup slot per block): B=1, T=1024
+    with H = 48 / 32 heads take split-key blocks, one more head 128-row
+    blocks. First, middle and last heads, every row, against the oracle."""
+    B, T = 1, 1024
+    inp = make_inputs(B, H, T, D, "bf16", seed=860 + H + D)
+    scale = 1 / math.sqrt(D)
+    y, lse, gate = run_fwd(inp, "bf16", scale)
+    heads = [(0, 0), (0, H // 2), (0, H - 1)]
+    refs = oracle_heads(inp, heads, scale, 2.0, inp["lam"])
+    check("y", np.stack([f64(y[b, h]) for b, h in heads]), np.stack([r["Y"] for r in refs]),
+          "bf16")
+    check("lse", np.stack([f64(lse[b, h]) for b, h in heads]), np.stack([r["LSE"] for r in refs]),
+          "bf16")
+    check("gate", np.stack([f64(gate[b, h]) for b, h in heads]), np.stack([r["g"] for r in refs]),
+          "bf16")
+
+
 @pytest.mark.parametrize("lam", [0.0, 1.0, -0.5, 4.0])
 @pytest.mark.parametrize("scale", [1 / 8, 1 / 64, 0.5])
 def test_fwd_bf16_params(lam, scale):
