@@ -27,6 +27,9 @@
 // In the gradient kernel wave w owns the 16 rows of sub-chunk w and does, for
 // them, dq against key blocks s' <= w and dk / dI against query blocks
 // w' >= w: nine block pairs on every wave.
+#include <cstdlib>
+#include <cstring>
+
 #include "launch.hpp"
 #include "linear_common.hpp"
 
@@ -46,6 +49,7 @@ struct SmemG {
   float dec[NW][D];          // e^{L_s[c]}
   float tot[NW][D];          // sum of dB over each sub-chunk
   float carry[D];            // sum of dB over every token after the chunk
+  float carry2[2][D];        // fused form: halves of the next chunk's carry
 };
 
 struct SmemR {
@@ -181,58 +185,22 @@ __global__ __launch_bounds__(NT, 1) void linear_dstate_kernel(
   }
 }
 
-// One workgroup per (chunk, head): blockIdx.x = head * nch + n. states:
-// [BH][nch + 1][D][D] (the state before every chunk, then the final state);
-// dstates: [BH][nch][D][D] (the gradient of the state after every chunk).
+// One chunk's gradients for the 16 rows of this wave's sub-chunk, given the
+// chunk's raw rows (raw, rdy: loaded, not yet consumed) and, already in LDS,
+// the state before the chunk (chi / clo), the gradient of the state after it
+// (dhi / dlo) and carry[c], the sum of dB over every token after the chunk
+// (the final state's term included). Publishes the rows, retentions and the
+// sub-chunk sums of dB (barriers (1) and (2)); stores dp1, dp2, dI and dg of
+// the rows. The published tiles stay valid until the caller's next barrier.
 template <bool ROPE>
-__global__ __launch_bounds__(NT, 1) void linear_grad_kernel(
-    const uint16_t* __restrict__ p1, const uint16_t* __restrict__ p2,
-    const uint16_t* __restrict__ iv, const float* __restrict__ g, const float* __restrict__ rc,
-    const float* __restrict__ rs, const uint16_t* __restrict__ dy,
-    const float* __restrict__ states, const float* __restrict__ dstates,
-    uint16_t* __restrict__ dp1, uint16_t* __restrict__ dp2, uint16_t* __restrict__ dI,
-    float* __restrict__ dg, int T, float sl2, float slope) {
-  __shared__ SmemG sm;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void grad_chunk(SmemG& sm, Raw& raw, u32x4 (&rdy)[2],
+                                           const float* __restrict__ rc,
+                                           const float* __restrict__ rs,
+                                           uint16_t* __restrict__ dp1, uint16_t* __restrict__ dp2,
+                                           uint16_t* __restrict__ dI, float* __restrict__ dg,
+                                           size_t base, int trow, int T, float sl2, float slope,
+                                           int tid) {
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int nch = (T + CH - 1) / CH;
-  const int head = blockIdx.x / nch, n = blockIdx.x % nch;
-  const size_t base = static_cast<size_t>(head) * T * D;
-  const int trow = n * CH + 16 * w + l16;
-  const float* cprev = states + (static_cast<size_t>(head) * (nch + 1) + n) * D * D;
-  const float* cnext = cprev + D * D;  // the state after the chunk
-  const float* dcn = dstates + (static_cast<size_t>(head) * nch + n) * D * D;
-
-  Raw raw;
-  load_raw<ROPE>(raw, p1, p2, iv, g, rc, rs, base, trow, T, grp);
-  u32x4 rdy[2];
-  {
-    const size_t row = base + static_cast<size_t>(trow < T ? trow : T - 1) * D + 8 * grp;
-    rdy[0] = *reinterpret_cast<const u32x4*>(dy + row);
-    rdy[1] = *reinterpret_cast<const u32x4*>(dy + row + 32);
-  }
-  // the states (8 consecutive elements of row c = tid / 8) and the reverse
-  // sum of dB over the tokens after the chunk
-  {
-    const int c = tid >> 3, v0 = 8 * (tid & 7);
-    const int o = c * D + v0;
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(cprev + o);
-    const f32x4 a1 = *reinterpret_cast<const f32x4*>(cprev + o + 4);
-    const f32x4 d0 = *reinterpret_cast<const f32x4*>(dcn + o);
-    const f32x4 d1 = *reinterpret_cast<const f32x4*>(dcn + o + 4);
-    const f32x4 n0 = *reinterpret_cast<const f32x4*>(cnext + o);
-    const f32x4 n1 = *reinterpret_cast<const f32x4*>(cnext + o + 4);
-    put_hilo(&sm.chi[c * IS + v0], &sm.clo[c * IS + v0], a0, a1);
-    put_hilo(&sm.dhi[c * IS + v0], &sm.dlo[c * IS + v0], d0, d1);
-    float f = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f = fmaf(d0[e], n0[e], fmaf(d1[e], n1[e], f));
-    f += __shfl_xor(f, 1);
-    f += __shfl_xor(f, 2);
-    f += __shfl_xor(f, 4);
-    if ((tid & 7) == 0) sm.carry[c] = f;
-  }
-
   RowLocal rl;
   row_local<ROPE>(raw, sl2, kSafeLog2Bwd, rl);
   const bool ok = raw.ok;
@@ -612,7 +580,230 @@ __global__ __launch_bounds__(NT, 1) void linear_grad_kernel(
   }
 }
 
+// One workgroup per (chunk, head): blockIdx.x = head * nch + n. states:
+// [BH][nch + 1][D][D] (the state before every chunk, then the final state);
+// dstates: [BH][nch][D][D] (the gradient of the state after every chunk).
+template <bool ROPE>
+__global__ __launch_bounds__(NT, 1) void linear_grad_kernel(
+    const uint16_t* __restrict__ p1, const uint16_t* __restrict__ p2,
+    const uint16_t* __restrict__ iv, const float* __restrict__ g, const float* __restrict__ rc,
+    const float* __restrict__ rs, const uint16_t* __restrict__ dy,
+    const float* __restrict__ states, const float* __restrict__ dstates,
+    uint16_t* __restrict__ dp1, uint16_t* __restrict__ dp2, uint16_t* __restrict__ dI,
+    float* __restrict__ dg, int T, float sl2, float slope) {
+  __shared__ SmemG sm;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int nch = (T + CH - 1) / CH;
+  const int head = blockIdx.x / nch, n = blockIdx.x % nch;
+  const size_t base = static_cast<size_t>(head) * T * D;
+  const int trow = n * CH + 16 * w + l16;
+  const float* cprev = states + (static_cast<size_t>(head) * (nch + 1) + n) * D * D;
+  const float* cnext = cprev + D * D;  // the state after the chunk
+  const float* dcn = dstates + (static_cast<size_t>(head) * nch + n) * D * D;
+
+  Raw raw;
+  load_raw<ROPE>(raw, p1, p2, iv, g, rc, rs, base, trow, T, grp);
+  u32x4 rdy[2];
+  {
+    const size_t row = base + static_cast<size_t>(trow < T ? trow : T - 1) * D + 8 * grp;
+    rdy[0] = *reinterpret_cast<const u32x4*>(dy + row);
+    rdy[1] = *reinterpret_cast<const u32x4*>(dy + row + 32);
+  }
+  // the states (8 consecutive elements of row c = tid / 8) and the reverse
+  // sum of dB over the tokens after the chunk
+  {
+    const int c = tid >> 3, v0 = 8 * (tid & 7);
+    const int o = c * D + v0;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(cprev + o);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(cprev + o + 4);
+    const f32x4 d0 = *reinterpret_cast<const f32x4*>(dcn + o);
+    const f32x4 d1 = *reinterpret_cast<const f32x4*>(dcn + o + 4);
+    const f32x4 n0 = *reinterpret_cast<const f32x4*>(cnext + o);
+    const f32x4 n1 = *reinterpret_cast<const f32x4*>(cnext + o + 4);
+    put_hilo(&sm.chi[c * IS + v0], &sm.clo[c * IS + v0], a0, a1);
+    put_hilo(&sm.dhi[c * IS + v0], &sm.dlo[c * IS + v0], d0, d1);
+    float f = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f = fmaf(d0[e], n0[e], fmaf(d1[e], n1[e], f));
+    f += __shfl_xor(f, 1);
+    f += __shfl_xor(f, 2);
+    f += __shfl_xor(f, 4);
+    if ((tid & 7) == 0) sm.carry[c] = f;
+  }
+
+  grad_chunk<ROPE>(sm, raw, rdy, rc, rs, dp1, dp2, dI, dg, base, trow, T, sl2, slope, tid);
+}
+
+// The state-gradient pass and the gradient pass fused, for batches with at
+// least one head per CU: one workgroup per head walks the chunks from the
+// last, keeping dC (the gradient of the state after the current chunk) in
+// fp32 registers (the dstate kernel's layout), so no dC is stored. The
+// reverse sum of dB over the tokens after a chunk (carry) is
+// sum_v dC[c][v] C[c][v] of the state after it, as in the chunk-parallel
+// form: formed from the fp32 dC and the next chunk's C_prev tile in LDS
+// (bf16 hi + lo). Adding up the chunks' own sums of dB instead would carry
+// their bf16-operand errors over every later chunk.
+template <bool ROPE>
+__global__ __launch_bounds__(NT, 1) void linear_bwd_fused_kernel(
+    const uint16_t* __restrict__ p1, const uint16_t* __restrict__ p2,
+    const uint16_t* __restrict__ iv, const float* __restrict__ g, const float* __restrict__ rc,
+    const float* __restrict__ rs, const uint16_t* __restrict__ dy,
+    const float* __restrict__ states, const float* __restrict__ dcT,
+    uint16_t* __restrict__ dp1, uint16_t* __restrict__ dp2, uint16_t* __restrict__ dI,
+    float* __restrict__ dg, float* __restrict__ dc0, int T, float sl2, float slope) {
+  __shared__ SmemG sm;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int nch = (T + CH - 1) / CH;
+  const int head = blockIdx.x;
+  const size_t base = static_cast<size_t>(head) * T * D;
+  const size_t sbase = static_cast<size_t>(head) * D * D;
+  const float* hstates = states + static_cast<size_t>(head) * (nch + 1) * D * D;
+  const int rb = w >> 1, cb0 = 2 * (w & 1);
+  // dC after the last chunk, rows 16 rb + 4 grp + r, columns 16 (cb0 + i) + l16
+  f32x4 dcs[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      dcs[i][r] = dcT ? dcT[sbase + (16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] : 0.f;
+  {  // carry = the final state's term (8 consecutive elements of row c = tid / 8)
+    const int c = tid >> 3, o = c * D + 8 * (tid & 7);
+    float f = 0.f;
+    if (dcT) {
+      const float* cf = hstates + static_cast<size_t>(nch) * D * D;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f = fmaf(dcT[sbase + o + e], cf[o + e], f);
+    }
+    f += __shfl_xor(f, 1);
+    f += __shfl_xor(f, 2);
+    f += __shfl_xor(f, 4);
+    if ((tid & 7) == 0) sm.carry[c] = f;
+  }
+#pragma unroll 1
+  for (int n = nch - 1; n >= 0; --n) {
+    // the thread index passed through an empty asm, so that the compiler
+    // forms the LDS addresses inside the loop instead of keeping them all
+    // live across it (which spills)
+    int tidv = tid;
+    asm volatile("" : "+v"(tidv));
+    const int w = tidv >> 6, lane = tidv & 63, l16 = lane & 15, grp = lane >> 4;
+    const int rb = w >> 1, cb0 = 2 * (w & 1);
+    const int trow = n * CH + 16 * w + l16;
+    Raw raw;
+    load_raw<ROPE>(raw, p1, p2, iv, g, rc, rs, base, trow, T, grp);
+    u32x4 rdy[2];
+    {
+      const size_t row = base + static_cast<size_t>(trow < T ? trow : T - 1) * D + 8 * grp;
+      rdy[0] = *reinterpret_cast<const u32x4*>(dy + row);
+      rdy[1] = *reinterpret_cast<const u32x4*>(dy + row + 32);
+    }
+    {  // the state before the chunk as bf16 hi / lo
+      const int c = tidv >> 3, v0 = 8 * (tidv & 7);
+      const float* cprev = hstates + static_cast<size_t>(n) * D * D + c * D + v0;
+      put_hilo(&sm.chi[c * IS + v0], &sm.clo[c * IS + v0], *reinterpret_cast<const f32x4*>(cprev),
+               *reinterpret_cast<const f32x4*>(cprev + 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)  // dC after the chunk as bf16 hi / lo
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int o = (16 * rb + 4 * grp + r) * IS + 16 * (cb0 + i) + l16;
+        const float x = dcs[i][r];
+        const uint16_t hi = f32_to_bf16_bits(x);
+        sm.dhi[o] = hi;
+        sm.dlo[o] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+      }
+    grad_chunk<ROPE>(sm, raw, rdy, rc, rs, dp1, dp2, dI, dg, base, trow, T, sl2, slope, tidv);
+    // dC before the chunk = e^{B_L - B_0} dC + sum_t (q_t e^{B_t - B_0}) dE_t^T,
+    // from the chunk's published q e^{B_t - B_start(s)}, dY and e^{L_s}
+    f32x4 tot4 = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.dec[s][16 * rb + 4 * grp]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tot4[r] *= u[r];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dcs[i][r] *= tot4[r];
+    f32x4 pb = {1.f, 1.f, 1.f, 1.f};  // e^{B_start(s) - B_0} at rows 16 rb + 4 grp + r
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      const int o = (16 * s + 4 * grp + (l16 >> 2)) * IS + 4 * (l16 & 3);
+      const s16x4 a = __builtin_bit_cast(s16x4, lds_read_tr16(&sm.qq[o + 16 * rb]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const f32x4 t = mfma16(
+            a, __builtin_bit_cast(s16x4, lds_read_tr16(&sm.dy[o + 16 * (cb0 + i)])),
+            f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dcs[i][r] = fmaf(t[r], pb[r], dcs[i][r]);
+      }
+      const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.dec[s][16 * rb + 4 * grp]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[r] *= u[r];
+    }
+    // the previous chunk's carry, sum_v dC[c][v] C[c][v] of the state between
+    // the two chunks (this chunk's C_prev, still in LDS as hi / lo): this
+    // wave's 32 columns of its 16 rows, summed over the 16 lanes of a row
+    float part[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int o = (16 * rb + 4 * grp + r) * IS + 16 * cb0 + l16;
+      part[r] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float c = bf16_bits_to_f32(sm.chi[o + 16 * i]) + bf16_bits_to_f32(sm.clo[o + 16 * i]);
+        part[r] = fmaf(dcs[i][r], c, part[r]);
+      }
+      part[r] = row_suffix(part[r]);  // lane 0 of the row: the row's sum
+    }
+    if (l16 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.carry2[w & 1][16 * rb + 4 * grp + r] = part[r];
+    }
+    __syncthreads();  // (3) every wave done with the chunk's tiles and carry
+    if (tidv < D) sm.carry[tidv] = sm.carry2[0][tidv] + sm.carry2[1][tidv];
+  }
+  if (dc0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dc0[sbase + (16 * rb + 4 * grp + r) * D + 16 * (cb0 + i) + l16] = dcs[i][r];
+  }
+}
+
 }  // namespace linrel
+
+namespace {
+// The fused backward form walks each head's chunks in sequence on one CU, so
+// it needs heads for most CUs: from 3/4 of the CU count on it is faster
+// (B*H = 192 on 256 CUs at T = 1024: 162 against 168 us; 128: 164 against
+// 138 us); smaller batches keep the chunk-parallel gradient pass.
+// RELATION_LINEAR_BWD=fused or =chunked in the environment forces one form
+// (the two agree to fp32 rounding).
+bool use_fused_bwd(size_t BH) {
+  if (const char* f = std::getenv("RELATION_LINEAR_BWD")) {
+    if (std::strcmp(f, "fused") == 0) return true;
+    if (std::strcmp(f, "chunked") == 0) return false;
+  }
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return false;
+    cus[dev] = n;
+  }
+  return 4 * BH >= 3 * static_cast<size_t>(cus[dev]);
+}
+}  // namespace
 
 hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint16_t* p2,
                              const uint16_t* iv, const float* g, const float* rope_cos,
@@ -638,6 +829,18 @@ hipError_t launch_linear_bwd(int B, int H, int T, const uint16_t* p1, const uint
   }
   const float sl2 = scale * kLog2e / tau, slope = scale / tau;
   const dim3 gh(static_cast<unsigned>(BH)), gc(static_cast<unsigned>(BH * nch));
+  if (use_fused_bwd(BH)) {
+    // passes 2 and 3 in one launch: one workgroup per head, chunks from the last
+    if (rope_cos)
+      hipLaunchKernelGGL(linear_bwd_fused_kernel<true>, gh, dim3(NT), 0, stream, p1, p2, iv, g,
+                         rope_cos, rope_sin, dy, states, dstate_out, dp1, dp2, dI, dg, dstate_in,
+                         T, sl2, slope);
+    else
+      hipLaunchKernelGGL(linear_bwd_fused_kernel<false>, gh, dim3(NT), 0, stream, p1, p2, iv, g,
+                         nullptr, nullptr, dy, states, dstate_out, dp1, dp2, dI, dg, dstate_in,
+                         T, sl2, slope);
+    return hipGetLastError();
+  }
   // pass 2: the gradient of the state after every chunk
   if (rope_cos)
     hipLaunchKernelGGL(linear_dstate_kernel<true>, gh, dim3(NT), 0, stream, p1, p2, g, rope_cos,

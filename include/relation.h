@@ -407,7 +407,12 @@ relation_status relation_linear_fwd(relation_dtype dtype, int B, int H, int T, i
  * p2, I, g and state_in, given dy and (optionally) the gradient of the final
  * state. Three passes: the state before every 128-token chunk (forward),
  * the gradient of the state after every chunk (backward over the chunks),
- * then every chunk's gradients independently.
+ * then every chunk's gradients independently. When B * H is at least 3/4 of
+ * the device's CU count, the last two run as one pass (one workgroup per
+ * head, chunks from the last, the state gradient kept on chip). The
+ * environment variable RELATION_LINEAR_BWD=fused or =chunked forces one form;
+ * both give the same gradients up to fp32 rounding of dg. The workspace
+ * sizes below cover either form.
  *
  *   p1, p2, I, g, rope_cos/rope_sin, state_in : as relation_linear_fwd
  *   dy               : in  [B, H, T, D] bf16, gradient of y

@@ -184,6 +184,15 @@ def test_linear_fwd_30m_layer_shape_sampled_heads():
 
 
 # ---------------------------------------------------------------- backward
+@pytest.fixture(params=["fused", "chunked"])
+def bwd_form(request, monkeypatch):
+    """Forces the backward's form: the fused per-head pass (chunks walked from
+    the last, dC in registers) or the state-gradient pass + chunk-parallel
+    gradient pass. Without the variable the library picks by batch size."""
+    monkeypatch.setenv("RELATION_LINEAR_BWD", request.param)
+    return request.param
+
+
 def run_bwd(d, rope=None, C0=None, dCT=None):
     cs, sn = rope if rope is not None else (None, None)
     out = rel.relation_linear_bwd(
@@ -195,7 +204,7 @@ def run_bwd(d, rope=None, C0=None, dCT=None):
     return [t.cpu() for t in out]
 
 
-def test_linear_bwd_reuses_forward_states():
+def test_linear_bwd_reuses_forward_states(bwd_form):
     """The forward can store the state before every chunk (and the final
     state); the backward given them skips its own state pass. y and the final
     state are unchanged bit for bit, the last stored state is state_out, and
@@ -262,7 +271,7 @@ def check_grads(got, ref):
 
 @pytest.mark.parametrize("use_rope", [False, True])
 @pytest.mark.parametrize("T", [1, 17, 128, 129, 300])
-def test_linear_bwd_vs_oracle(T, use_rope):
+def test_linear_bwd_vs_oracle(T, use_rope, bwd_form):
     d = make_linear_inputs(2, 2, T, 64, seed=2500 + T, with_dy=True)
     rope = tables(T) if use_rope else None
     got = run_bwd(d, rope)
@@ -270,7 +279,7 @@ def test_linear_bwd_vs_oracle(T, use_rope):
     check_grads(got, ref)
 
 
-def test_linear_bwd_with_states_and_extreme_retention():
+def test_linear_bwd_with_states_and_extreme_retention(bwd_form):
     B, H, T = 2, 2, 300
     d = make_linear_inputs(B, H, T, 64, seed=2600, with_dy=True, resets=True, keep=True)
     rng = np.random.default_rng(3)
@@ -292,3 +301,45 @@ def test_linear_bwd_30m_layer_shape_sampled_heads():
         sub = {k: v[b:b + 1, h:h + 1] for k, v in d.items()}
         ref = oracle_bwd(sub, rope)
         check_grads([t[b:b + 1, h:h + 1] for t in got], ref)
+
+
+def test_linear_bwd_fused_matches_chunked_at_30m_layer_shape(monkeypatch):
+    """The 30M-class layer (B=32, H=8, T=1024, 256 heads: the fused form by
+    default) with RoPE and an initial state, in both backward forms (a
+    final-state gradient is covered at T = 300 by the tests above, in both
+    forms). They run the same dC recurrence and the same per-chunk
+    arithmetic, so dp1, dp2, dI and dstate_in agree bit for bit. dg differs
+    only in how the sum of dB over the tokens after a chunk reads the state
+    after the chunk (the fused form from its bf16 hi + lo tile in LDS, the
+    chunked form in fp32): both must meet the oracle's dg bound on sampled
+    heads, and agree with each other within twice that bound on every head."""
+    B, H, T = 32, 8, 1024
+    d = make_linear_inputs(B, H, T, 64, seed=4242, with_dy=True)
+    rope = tables(T)
+    rng = np.random.default_rng(11)
+    C0 = torch.from_numpy((0.1 * rng.standard_normal((B, H, 64, 64))).astype(np.float32))
+    dCT = None
+    outs = {}
+    for form in ("fused", "chunked"):
+        monkeypatch.setenv("RELATION_LINEAR_BWD", form)
+        outs[form] = run_bwd(d, rope, C0, dCT)
+    monkeypatch.delenv("RELATION_LINEAR_BWD")
+    outs["auto"] = run_bwd(d, rope, C0, dCT)
+    for i, name in enumerate(("dp1", "dp2", "dI", "dg", "dstate_in")):
+        assert torch.equal(outs["auto"][i], outs["fused"][i]), name
+    for i, name in ((0, "dp1"), (1, "dp2"), (2, "dI"), (4, "dstate_in")):
+        assert torch.equal(outs["fused"][i], outs["chunked"][i]), name
+    # every head: each form is within check_dg's bound of the exact dg, so
+    # the two are within twice that bound of each other (the walk taken from
+    # the chunked form's dB)
+    gf, gc = f64(outs["fused"][3]), f64(outs["chunked"][3])
+    dB = gc - np.concatenate([gc[..., 1:, :], np.zeros_like(gc[..., :1, :])], axis=-2)
+    walk = np.sqrt(np.flip(np.cumsum(np.flip(dB ** 2, axis=-2), axis=-2), axis=-2))
+    worst = float((np.abs(gf - gc) / (2 * (2e-2 + 2.0 ** -7 * walk))).max())
+    print(f"  dg fused vs chunked, every head: worst diff / (2 x bound) {worst:.3f}")
+    assert worst <= 1.0
+    for b, h in ((0, 0), (17, 3), (31, 7)):
+        sub = {k: v[b:b + 1, h:h + 1] for k, v in d.items()}
+        ref = oracle_bwd(sub, rope, C0[b:b + 1, h:h + 1])
+        for form in ("fused", "chunked"):
+            check_grads([t[b:b + 1, h:h + 1] for t in outs[form]], ref)
