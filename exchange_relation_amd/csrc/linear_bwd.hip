@@ -20,6 +20,9 @@
 // (and the final state); linear_dstate_kernel walks the chunks backwards and
 // stores dC, the gradient of the state after every chunk; linear_grad_kernel
 // then handles every chunk independently (one workgroup per chunk and head).
+// For batches with heads for most CUs, linear_bwd_fused_kernel does passes 2
+// and 3 in one: one workgroup per head runs the same per-chunk body from the
+// last chunk, with dC in registers instead of memory.
 // The reverse sum of dg needs no sequential pass: the sum of (q dq - k dk)
 // over all tokens after chunk n equals sum_v dC[c][v] C[c][v] of the state
 // after chunk n (shifting the log retention of every later token by d only
